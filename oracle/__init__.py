@@ -1,0 +1,165 @@
+"""Plain fp64 CPU oracle for residual-add + RMSNorm (+ OCP e4m3).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The
+product library never loads it, and it shares no code with the HIP path.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, one step per
+function, each citing the passage it follows).  This module only compiles it
+with gcc and marshals numpy arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_HDR = os.path.join(_HERE, "oracle.h")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+BF16 = 0
+FP16 = 1
+FP8_NONE = -1
+FP8_STATIC = 0
+FP8_DYNAMIC = 1
+
+DTYPES = {"bf16": BF16, "fp16": FP16}
+
+# ISO C, no contraction of a*b+c into fma, no fast-math: every double
+# operation in oracle.c is rounded exactly as written.
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(src: str = _SRC, out: str = LIB_PATH) -> str:
+    """Compile oracle.c into a shared library with gcc."""
+    cmd = ["gcc", *GCC_FLAGS, src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _stale(lib_path: str) -> bool:
+    if not os.path.exists(lib_path):
+        return True
+    t = os.path.getmtime(lib_path)
+    return any(os.path.getmtime(p) > t for p in (_SRC, _HDR))
+
+
+def bind(lib_path: str) -> ctypes.CDLL:
+    """Load a compiled oracle and declare its C signatures."""
+    lib = ctypes.CDLL(lib_path)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    lib.orc_decode16.argtypes = [ctypes.c_int, ctypes.c_uint16]
+    lib.orc_decode16.restype = ctypes.c_double
+    lib.orc_encode16.argtypes = [ctypes.c_int, ctypes.c_double]
+    lib.orc_encode16.restype = ctypes.c_uint16
+    lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_decode.restype = ctypes.c_double
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    lib.orc_add_rmsnorm.argtypes = [
+        ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+        u16p, ctypes.c_int64,
+        u16p, ctypes.c_int64,
+        u16p, ctypes.c_float,
+        u16p, ctypes.POINTER(ctypes.c_double), u16p,
+        ctypes.c_int, ctypes.c_float,
+        ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float),
+    ]
+    lib.orc_add_rmsnorm.restype = ctypes.c_int
+    return lib
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    with _lock:
+        if _lib is None:
+            if _stale(LIB_PATH):
+                build()
+            _lib = bind(LIB_PATH)
+        return _lib
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+class Oracle:
+    """numpy front end over one compiled oracle library."""
+
+    def __init__(self, cdll: ctypes.CDLL | None = None):
+        self.c = cdll if cdll is not None else lib()
+
+    # -- scalar codecs ---------------------------------------------------
+    def decode16(self, dtype: int, bits: int) -> float:
+        return self.c.orc_decode16(dtype, bits)
+
+    def encode16(self, dtype: int, v: float) -> int:
+        return self.c.orc_encode16(dtype, v)
+
+    def e4m3_decode(self, code: int) -> float:
+        return self.c.orc_e4m3_decode(code)
+
+    def e4m3_encode(self, v: float) -> int:
+        return self.c.orc_e4m3_encode(v)
+
+    # -- the operator ------------------------------------------------------
+    def add_rmsnorm(self, dtype, x, residual, weight, eps, hidden=None,
+                    fp8_mode=FP8_NONE, static_scale=0.0, want_y=True):
+        """Run the reference on 2-D uint16 arrays (row stride = shape[1]).
+
+        ``hidden`` defaults to the full row; a smaller value leaves the
+        columns beyond it (row padding) out of the computation.
+        Returns a dict with r16, y (float64), y16, and q / scales for FP8.
+        """
+        if isinstance(dtype, str):
+            dtype = DTYPES[dtype]
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        rows, stride = x.shape
+        hidden = stride if hidden is None else int(hidden)
+        if residual is not None:
+            residual = np.ascontiguousarray(residual, dtype=np.uint16)
+            assert residual.shape[0] == rows
+        if weight is not None:
+            weight = np.ascontiguousarray(weight, dtype=np.uint16)
+            assert weight.shape[0] >= hidden
+        r16 = np.empty((rows, hidden), np.uint16)
+        y = np.empty((rows, hidden), np.float64) if want_y else None
+        y16 = np.empty((rows, hidden), np.uint16)
+        q = np.empty((rows, hidden), np.uint8) if fp8_mode != FP8_NONE else None
+        scales = np.empty((rows,), np.float32) if fp8_mode == FP8_DYNAMIC else None
+        rc = self.c.orc_add_rmsnorm(
+            dtype, rows, hidden,
+            _ptr(x, ctypes.c_uint16), stride,
+            _ptr(residual, ctypes.c_uint16),
+            residual.shape[1] if residual is not None else 0,
+            _ptr(weight, ctypes.c_uint16), float(eps),
+            _ptr(r16, ctypes.c_uint16), _ptr(y, ctypes.c_double),
+            _ptr(y16, ctypes.c_uint16),
+            fp8_mode, float(static_scale),
+            _ptr(q, ctypes.c_uint8), _ptr(scales, ctypes.c_float),
+        )
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        out = {"r16": r16, "y16": y16}
+        if want_y:
+            out["y"] = y
+        if q is not None:
+            out["q"] = q
+        if scales is not None:
+            out["scales"] = scales
+        return out
+
+
+def oracle() -> Oracle:
+    return Oracle()

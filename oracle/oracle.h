@@ -1,0 +1,71 @@
+/*
+ * oracle.h -- plain fp64 CPU reference for residual-add + RMSNorm (+ OCP e4m3).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this code: only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark do.  It shares no code, header, table or
+ * constant with the HIP library.
+ *
+ * Every function computes the textbook definition, one step at a time, in
+ * double precision; see oracle.c for the citation of each step.
+ */
+#ifndef ARN_ORACLE_H
+#define ARN_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* 16-bit storage formats understood by the oracle. */
+#define ORC_BF16 0
+#define ORC_FP16 1
+
+/* FP8 modes: none, per-tensor static scale, per-row dynamic scale. */
+#define ORC_FP8_NONE    (-1)
+#define ORC_FP8_STATIC  0
+#define ORC_FP8_DYNAMIC 1
+
+/* Exact decode of a 16-bit pattern (bf16 or IEEE binary16) to double. */
+double orc_decode16(int dtype, uint16_t bits);
+
+/* Round a double to the nearest 16-bit value, ties to even mantissa,
+ * overflow to +-Inf, NaN to a quiet NaN. */
+uint16_t orc_encode16(int dtype, double v);
+
+/* Exact decode of an OCP E4M3FN code (0x7F / 0xFF decode to NaN). */
+double orc_e4m3_decode(uint8_t code);
+
+/* OCP E4M3FN encoder: nearest finite value, ties to even mantissa,
+ * saturating at +-448, NaN -> 0x7F, signed zero kept. */
+uint8_t orc_e4m3_encode(double v);
+
+/*
+ * The operator, row by row.
+ *   x, residual : rows x hidden 16-bit patterns, row strides in elements.
+ *                 residual == NULL selects plain RMSNorm (r = x).
+ *   weight      : hidden 16-bit patterns, or NULL for w = 1.
+ *   eps         : fp32 value, widened exactly.
+ * Outputs (each may be NULL; all dense, row stride = hidden):
+ *   r16_out   : the rounded sum that is stored back into residual.
+ *   y_out     : unrounded y in double.
+ *   y16_out   : y rounded to the 16-bit type.
+ *   q_out     : e4m3 codes (fp8_mode STATIC or DYNAMIC).
+ *   scale_out : per-row dequant scales (DYNAMIC only, rows floats).
+ * static_scale is the dequant scale s of STATIC mode (q = E(y / s)).
+ * Returns 0, or -1 on an argument error.
+ */
+int orc_add_rmsnorm(int dtype, int64_t rows, int64_t hidden,
+                    const uint16_t *x, int64_t x_stride,
+                    const uint16_t *residual, int64_t residual_stride,
+                    const uint16_t *weight, float eps,
+                    uint16_t *r16_out, double *y_out, uint16_t *y16_out,
+                    int fp8_mode, float static_scale,
+                    uint8_t *q_out, float *scale_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARN_ORACLE_H */

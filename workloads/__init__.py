@@ -1,0 +1,175 @@
+"""Seeded synthetic inputs for the residual-add + RMSNorm workloads.
+
+This module only draws random numbers and stores them as 16-bit patterns.
+It holds none of the operator's arithmetic and imports neither the oracle
+nor the HIP library, so both sides can be fed from it.
+
+Generator: numpy's counter-based Philox (Salmon et al., "Parallel random
+numbers: as easy as 1, 2, 3", SC'11), keyed by (seed, tensor stream, block of
+256 rows).  Keying per row block makes any row range reproducible on its own,
+which lets a parity test regenerate sampled rows of a full-size workload
+cheaply.  Streams: x = 1, residual = 2, weight = 3, outlier columns = 4.
+
+float32 draws are rounded to bf16 by torch's CPU conversion and to fp16 by
+numpy's -- both round to nearest even.
+
+The pages measure only end-to-end serving on model weights, which are not
+available here; these draws stand in for activations of the row widths the
+workloads name (3840 is the Gemma 4 12B width printed in the MI300X AITER
+write-up's untuned-GEMM table).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BLOCK_ROWS = 256
+STREAM_X, STREAM_RES, STREAM_W, STREAM_OUTLIER = 1, 2, 3, 4
+
+# bf16 NaN pattern written into row padding; a kernel that reads it into a
+# row's sum of squares turns that row's output into NaN.
+PAD_SENTINEL = 0x7FA5
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    op: str            # rmsnorm | fused_add_rmsnorm | *_fp8
+    dtype: str         # bf16 | fp16
+    rows: int
+    hidden: int
+    stride: int
+    eps: float
+    x_std: float = 1.0
+    res_std: float = 1.0
+    weight: str = "1+0.1n"          # "1+0.1n" | "u(0.5,1.5)"
+    fp8: str | None = None          # None | "static" | "dynamic"
+    outliers: int = 0               # columns of x multiplied by outlier_gain
+    outlier_gain: float = 50.0
+    row_counts: tuple = field(default=())  # decode sweeps: prefixes of `rows`
+
+    @property
+    def has_residual(self) -> bool:
+        return self.op.startswith("fused_add")
+
+    def algorithmic_bytes(self, rows: int | None = None) -> int:
+        """Minimum HBM bytes one call must move: 16-bit x read, residual
+        read and written, output written (16-bit or e4m3), weight once, the
+        static scale read once or the dynamic scales written."""
+        r = self.rows if rows is None else rows
+        h = self.hidden
+        elem = 2
+        per_row = h * elem                      # x
+        if self.has_residual:
+            per_row += 2 * h * elem             # residual read + write
+        per_row += h * (1 if self.fp8 else elem)  # output
+        if self.fp8 == "dynamic":
+            per_row += 4
+        total = r * per_row + h * elem          # weight once
+        if self.fp8 == "static":
+            total += 4
+        return total
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("rmsnorm_bf16_64x4096", "rmsnorm", "bf16", 64, 4096, 4096, 1e-6),
+        Workload("fused_add_rmsnorm_bf16_4096x8192", "fused_add_rmsnorm", "bf16",
+                 4096, 8192, 8192, 1e-5),
+        Workload("fused_add_rmsnorm_fp8_static_fp16_decode_x16384",
+                 "fused_add_rmsnorm_fp8", "fp16", 256, 16384, 16384, 1e-5,
+                 res_std=2.0, weight="u(0.5,1.5)", fp8="static",
+                 row_counts=(1, 8, 64, 256)),
+        Workload("fused_add_rmsnorm_fp8_dynamic_bf16_32768x7168",
+                 "fused_add_rmsnorm_fp8", "bf16", 32768, 7168, 7168, 1e-6,
+                 fp8="dynamic", outliers=8),
+        Workload("fused_add_rmsnorm_bf16_65536x3840_stride4096", "fused_add_rmsnorm",
+                 "bf16", 65536, 3840, 4096, 1e-6),
+        Workload("fused_add_rmsnorm_bf16_65536x2880_stride4096", "fused_add_rmsnorm",
+                 "bf16", 65536, 2880, 4096, 1e-6),
+    ]
+}
+
+# The benchmark's headline workload.
+HEADLINE = "fused_add_rmsnorm_bf16_4096x8192"
+
+
+def _rng(seed: int, stream: int, block: int) -> np.random.Generator:
+    return np.random.Generator(np.random.Philox(np.random.SeedSequence([seed, stream, block])))
+
+
+def to_bits(f32: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to the 16-bit type; return the bit patterns."""
+    f32 = np.ascontiguousarray(f32, dtype=np.float32)
+    if dtype == "fp16":
+        return f32.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        import torch
+
+        t = torch.from_numpy(f32).to(torch.bfloat16)
+        return t.view(torch.int16).numpy().view(np.uint16)
+    raise ValueError(dtype)
+
+
+def outlier_columns(w: Workload, seed: int = 0) -> np.ndarray:
+    if w.outliers == 0:
+        return np.zeros((0,), np.int64)
+    cols = _rng(seed, STREAM_OUTLIER, 0).choice(w.hidden, size=w.outliers, replace=False)
+    return np.sort(cols.astype(np.int64))
+
+
+def _normal_rows(seed, stream, row0, row1, hidden, std):
+    """float32 N(0, std^2) draws for rows [row0, row1), block-keyed."""
+    out = np.empty((row1 - row0, hidden), np.float32)
+    b0, b1 = row0 // BLOCK_ROWS, (row1 - 1) // BLOCK_ROWS
+    for b in range(b0, b1 + 1):
+        blk = _rng(seed, stream, b).standard_normal((BLOCK_ROWS, hidden), dtype=np.float32)
+        lo = max(row0, b * BLOCK_ROWS)
+        hi = min(row1, (b + 1) * BLOCK_ROWS)
+        out[lo - row0:hi - row0] = blk[lo - b * BLOCK_ROWS:hi - b * BLOCK_ROWS]
+    if std != 1.0:
+        out *= np.float32(std)
+    return out
+
+
+def weight_bits(w: Workload, seed: int = 0) -> np.ndarray:
+    rng = _rng(seed, STREAM_W, 0)
+    if w.weight == "1+0.1n":
+        f = 1.0 + 0.1 * rng.standard_normal(w.hidden, dtype=np.float32)
+    elif w.weight == "u(0.5,1.5)":
+        f = rng.uniform(0.5, 1.5, w.hidden).astype(np.float32)
+    else:
+        raise ValueError(w.weight)
+    return to_bits(f.astype(np.float32), w.dtype)
+
+
+def padded(bits: np.ndarray, stride: int, fill: int = PAD_SENTINEL) -> np.ndarray:
+    rows, hidden = bits.shape
+    if stride == hidden:
+        return bits
+    out = np.full((rows, stride), fill, np.uint16)
+    out[:, :hidden] = bits
+    return out
+
+
+def make_rows(w: Workload, row0: int, row1: int, seed: int = 0) -> dict:
+    """Inputs for rows [row0, row1) of a workload, rows laid out at the
+    workload's stride with padding filled by PAD_SENTINEL."""
+    xf = _normal_rows(seed, STREAM_X, row0, row1, w.hidden, w.x_std)
+    if w.outliers:
+        xf[:, outlier_columns(w, seed)] *= np.float32(w.outlier_gain)
+    out = {"x": padded(to_bits(xf, w.dtype), w.stride)}
+    del xf
+    if w.has_residual:
+        rf = _normal_rows(seed, STREAM_RES, row0, row1, w.hidden, w.res_std)
+        out["residual"] = padded(to_bits(rf, w.dtype), w.stride)
+    out["weight"] = weight_bits(w, seed)
+    return out
+
+
+def make(w: Workload | str, rows: int | None = None, seed: int = 0) -> dict:
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    return make_rows(w, 0, w.rows if rows is None else rows, seed)
