@@ -1,0 +1,313 @@
+"""Benchmark of the fused residual-add + RMSNorm (+ e4m3) HIP path on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
+
+A step is one call of the operator over one batch of the workload, inputs
+already resident in device memory.  The headline workload is fused add +
+RMSNorm, bf16, 4096 rows x 8192.  Its 192 MiB working set is under the
+256 MB Infinity Cache, so steps rotate over several buffer sets whose total
+exceeds that cache: every step streams from HBM.
+
+The printed JSON line carries the throughput (algorithmic bytes / time), the
+roofline entry of the kernel (average launch duration from HIP events on the
+launch stream), the HBM traffic measured by rocprofv3 counters when it was
+taken on the current kernel source, and the plain CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = ("achieved HBM GB/s (% of MI355X peak) for fused add+RMSNorm(+fp8); "
+          "µs/call at decode")
+MALL_BYTES = 256 * 1024 * 1024
+KERNEL_SOURCES = ["residual_add_rmsnorm_amd/csrc/arn_kernels.hip",
+                  "residual_add_rmsnorm_amd/csrc/arn_api.hip",
+                  "residual_add_rmsnorm_amd/csrc/arn_internal.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# device-side inputs
+# ---------------------------------------------------------------------------
+
+class Batch:
+    """Device buffers of one workload, `sets` copies to rotate over."""
+
+    def __init__(self, w, sets: int, rows: int | None = None):
+        import torch
+
+        import workloads
+        from tests._helpers import dev
+
+        self.w = w
+        self.rows = rows or w.rows
+        d = workloads.make(w, rows=self.rows)
+        H, S = w.hidden, w.stride
+        self.x, self.res, self.out, self.scale = [], [], [], []
+        x0 = dev(d["x"], w.dtype)
+        r0 = dev(d["residual"], w.dtype) if w.has_residual else None
+        self.weight = dev(d["weight"], w.dtype)
+        for _ in range(sets):
+            self.x.append(x0.clone()[:, :H])
+            self.res.append(r0.clone()[:, :H] if r0 is not None else None)
+            if w.fp8:
+                o = torch.empty((self.rows, S), dtype=torch.uint8, device="cuda")
+                self.out.append(o.view(torch.float8_e4m3fn)[:, :H])
+                if w.fp8 == "dynamic":
+                    self.scale.append(torch.empty(self.rows, dtype=torch.float32, device="cuda"))
+                else:
+                    from tests._helpers import static_scale
+
+                    self.scale.append(torch.tensor([static_scale()], dtype=torch.float32,
+                                                   device="cuda"))
+            else:
+                self.out.append(torch.empty((self.rows, S), dtype=x0.dtype, device="cuda")[:, :H])
+        del x0, r0
+        self.sets = sets
+
+    def call(self, i: int) -> None:
+        import residual_add_rmsnorm_amd as arn
+
+        w, k = self.w, i % self.sets
+        if w.fp8:
+            kw = dict(dynamic=True, scales_out=self.scale[k]) if w.fp8 == "dynamic" \
+                else dict(scale=self.scale[k])
+            if w.has_residual:
+                arn.fused_add_rmsnorm_fp8(self.x[k], self.res[k], self.weight, w.eps,
+                                          out=self.out[k], **kw)
+            else:
+                arn.rmsnorm_fp8(self.x[k], self.weight, w.eps, out=self.out[k], **kw)
+        elif w.has_residual:
+            arn.fused_add_rmsnorm(self.x[k], self.res[k], self.weight, w.eps, out=self.out[k])
+        else:
+            arn.rmsnorm(self.x[k], self.weight, w.eps, out=self.out[k])
+
+
+def working_set(w, rows) -> int:
+    return w.algorithmic_bytes(rows)
+
+
+def time_steps(batch: Batch, steps: int, warmup: int):
+    """(elapsed_ms by HIP events on the launch stream, host wall ms)."""
+    import torch
+
+    for i in range(warmup):
+        batch.call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        batch.call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    return start.elapsed_time(end), wall
+
+
+def time_graph(batch: Batch, calls: int, replays: int):
+    """Device time per call with host overhead removed: `calls` launches
+    captured in one HIP graph, replayed `replays` times."""
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(3):
+            batch.call(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            batch.call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / (calls * replays)  # us per call
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, single thread, bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, target_s: float = 10.0) -> dict:
+    import oracle
+    import workloads
+    from tests._helpers import static_scale
+
+    orc = oracle.oracle()
+    mode = {None: oracle.FP8_NONE, "static": oracle.FP8_STATIC,
+            "dynamic": oracle.FP8_DYNAMIC}[w.fp8]
+    s = static_scale() if w.fp8 == "static" else 0.0
+
+    def run(rows):
+        d = workloads.make(w, rows=rows)
+        t0 = time.perf_counter()
+        orc.add_rmsnorm(w.dtype, d["x"], d.get("residual"), d["weight"], w.eps, hidden=w.hidden,
+                        fp8_mode=mode, static_scale=s)
+        return time.perf_counter() - t0
+
+    probe_rows = min(w.rows, 16)
+    t = run(probe_rows)
+    rows = int(min(w.rows, max(probe_rows, probe_rows * target_s / max(t, 1e-6))))
+    rows = max(1, (rows // 16) * 16) if rows >= 16 else rows
+    elapsed = run(rows)
+    gbs = w.algorithmic_bytes(rows) / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of {w.rows} rows of the same workload, "
+                      f"{elapsed:.1f} s single-threaded fp64 C oracle",
+            "seconds": round(elapsed, 3)}
+
+
+# ---------------------------------------------------------------------------
+
+def traffic_for(name: str, launch_bytes: int):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool) -> dict:
+    import torch
+
+    import residual_add_rmsnorm_amd as arn
+    import workloads
+
+    w = workloads.WORKLOADS[name]
+    rows = w.rows
+    ws = working_set(w, rows)
+    sets = max(1, math.ceil(4 * MALL_BYTES / ws)) if ws < 4 * MALL_BYTES else 1
+    sets = min(sets, 64)
+    log(f"[bench] {name}: {rows} x {w.hidden} (stride {w.stride}), {sets} buffer set(s)")
+    batch = Batch(w, sets)
+    elapsed_ms, wall_ms = time_steps(batch, steps, warmup)
+    plan = arn.last_plan()
+    per_call_ms = elapsed_ms / steps
+    bytes_step = w.algorithmic_bytes(rows)
+    achieved = bytes_step / (per_call_ms * 1e-3) / 1e9
+    log(f"[bench] plan {plan}: {per_call_ms * 1e3:.2f} us/call, {achieved:.1f} GB/s "
+        f"({100 * achieved / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
+    traffic = traffic_for(name, bytes_step)
+    line = {
+        "metric": METRIC,
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(per_call_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": name, "rows": rows, "hidden": w.hidden, "row_stride": w.stride,
+            "io_dtype": w.dtype, "fp8": w.fp8, "eps": w.eps, "buffer_sets": sets,
+            "bytes_per_step": bytes_step, "kernel_plan": plan,
+            "us_per_call": round(per_call_ms * 1e3, 3),
+            "pct_of_hbm_peak": round(100 * achieved / PEAK_HBM_GBS, 2),
+            "host_wall_ms_per_step": round(wall_ms / steps, 6),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+        },
+    }
+    if w.row_counts:
+        per_rows = {}
+        for r in w.row_counts:
+            b = Batch(w, 8, rows=r)
+            dev_us = time_graph(b, calls=64, replays=20)
+            e_ms, wall = time_steps(b, 200, 20)
+            per_rows[str(r)] = {"device_us_per_call_graph": round(dev_us, 3),
+                                "event_us_per_call": round(e_ms * 1e3 / 200, 3),
+                                "host_wall_us_per_call": round(wall * 1e3 / 200, 3),
+                                "plan": arn.last_plan()}
+            log(f"[bench] rows={r}: {per_rows[str(r)]}")
+        line["config"]["decode_us_per_call"] = per_rows
+    del batch
+    torch.cuda.empty_cache()
+    if with_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(w)
+    return line
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=None,
+                    help="workload name, or 'all' (default: the headline workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the operator is row-independent: rows shard across GPUs with no exchange, "
+              "so per-GPU throughput is the single-GPU figure)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    from residual_add_rmsnorm_amd import _lib
+
+    _lib.load()  # fails loudly if the HIP library is missing
+
+    names = list(workloads.WORKLOADS) if args.workload == "all" else \
+        [args.workload or workloads.HEADLINE]
+    for n in names:
+        line = bench_workload(n, args.steps, args.warmup,
+                              with_cpu=not args.no_cpu_baseline and n == names[0])
+        print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,146 @@
+/*
+ * arn.h -- C ABI of the MI355X (gfx950) residual-add + RMSNorm library.
+ *
+ * One operator in four forms.  For every row i of a 16-bit activation
+ * matrix (bf16 or fp16), with H = hidden:
+ *
+ *     r   = x[i] + residual[i]          (fused forms; plain forms use r = x[i])
+ *     residual[i] <- r                   rounded to the 16-bit type
+ *     y   = r / sqrt(mean_j(r_j^2) + eps) * w
+ *     out[i] <- y                        16-bit, or OCP e4m3 codes (_fp8)
+ *
+ * RMSNorm is the definition of Zhang & Sennrich, "Root Mean Square Layer
+ * Normalization" (NeurIPS 2019), eq. 4.  Fusing the residual add, the RMS
+ * normalisation and the FP8 conversion into one pass over each row is the
+ * first kernel of "Custom CUDA kernels juice Llama 3.1 405B on AMD MI300X,
+ * skipping Nvidia lock-in" (paragraph 2).  The argument rules follow the
+ * vLLM API page "vllm.kernels.aiter_ops" (attributes rms_add_no_var_16bit_only
+ * and rms_no_var_16bit_only, and flatten_to_2d_is_free): 16-bit activations
+ * only, a weight of the same dtype or none, no variance-size override (the
+ * mean always runs over all H channels), and 2-D rows whose elements are
+ * contiguous -- a layout that is not expressible that way is refused, never
+ * copied, so the caller can fall back as vLLM's op priority list does.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers owned by the caller (hipMalloc, or a
+ *    framework's allocator).  The library allocates nothing and keeps no
+ *    state across calls other than a per-device cache of the CU count.
+ *  - Layout: row-major, element stride 1, row stride given per tensor in
+ *    ELEMENTS of that tensor (one e4m3 code = one element).  stride >= hidden.
+ *    Elements [hidden, stride) of a row are neither read nor written.
+ *  - dtype: ARN_BF16 or ARN_FP16, shared by x, residual, weight and 16-bit out.
+ *  - weight: hidden elements of dtype, or NULL meaning w = 1.
+ *  - eps: finite and >= 0, added to the mean square inside the square root.
+ *  - Arithmetic: fp32 accumulation; the residual sum is one fp32 add rounded
+ *    to nearest-even 16-bit; y is computed from that rounded sum.
+ *  - Aliasing: out may equal x (same pointer and stride: in-place); residual
+ *    must not overlap x or out; any other overlap is undefined.
+ *  - Asynchrony: the call validates its arguments on the host, enqueues one
+ *    kernel on `stream` and returns; execution errors surface at the
+ *    caller's next synchronisation, as in HIP.  rows == 0 launches nothing.
+ *  - Return value: ARN_OK, or
+ *      ARN_EINVAL       an argument is invalid (nothing is launched);
+ *      ARN_EUNSUPPORTED valid but not served, e.g. hidden above the largest
+ *                       compiled row size (nothing is launched);
+ *      ARN_ELAUNCH      the HIP runtime refused the launch.
+ *    No C++ exception crosses this interface.
+ */
+#ifndef ARN_H
+#define ARN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ARN_ABI_VERSION 1
+
+enum arn_dtype { ARN_BF16 = 0, ARN_FP16 = 1 };
+enum arn_fp8_mode { ARN_FP8_STATIC = 0, ARN_FP8_DYNAMIC = 1 };
+enum arn_status { ARN_OK = 0, ARN_EINVAL = 1, ARN_EUNSUPPORTED = 2, ARN_ELAUNCH = 3 };
+
+/*
+ * Plain RMSNorm: out[i] = x[i] / sqrt(mean(x[i]^2) + eps) * w.
+ * (vllm.kernels.aiter_ops, rms_no_var_16bit_only.)
+ *   out, out_stride : rows x hidden of dtype, written.
+ *   x, x_stride     : rows x hidden of dtype, read.
+ */
+int arn_rmsnorm(void *out, int64_t out_stride,
+                const void *x, int64_t x_stride,
+                const void *weight, float eps,
+                int64_t rows, int64_t hidden, int dtype, hipStream_t stream);
+
+/*
+ * Fused residual add + RMSNorm.  residual[i] is read, replaced by the
+ * rounded r = x[i] + residual[i], and out[i] = RMSNorm(r).
+ * (vllm.kernels.aiter_ops, rms_add_no_var_16bit_only; the residual and
+ * RMS-norm steps of the fused kernel in "Custom CUDA kernels juice Llama
+ * 3.1 405B on AMD MI300X", paragraph 2.)
+ *   residual, residual_stride : rows x hidden of dtype, read then written.
+ */
+int arn_fused_add_rmsnorm(void *out, int64_t out_stride,
+                          const void *x, int64_t x_stride,
+                          void *residual, int64_t residual_stride,
+                          const void *weight, float eps,
+                          int64_t rows, int64_t hidden, int dtype, hipStream_t stream);
+
+/*
+ * RMSNorm with an OCP e4m3 (E4M3FN) output, round to nearest even,
+ * saturating at +-448.  The FP8 step of the fused kernel in "Custom CUDA
+ * kernels juice Llama 3.1 405B on AMD MI300X" (paragraph 2).
+ *   out, out_stride : rows x hidden bytes of e4m3 codes, written.
+ *   scale           : fp8_mode ARN_FP8_STATIC -- ONE fp32 on the device, the
+ *                     dequant scale s, read: code = e4m3(y / s), y ~ code * s.
+ *                     fp8_mode ARN_FP8_DYNAMIC -- `rows` fp32 on the device,
+ *                     written: scale[i] = max_j |y_ij| / 448 and
+ *                     code = e4m3(y / scale[i]); a row whose max is 0 gets
+ *                     scale 0 and all-zero codes.
+ */
+int arn_rmsnorm_fp8(uint8_t *out, int64_t out_stride, float *scale, int fp8_mode,
+                    const void *x, int64_t x_stride,
+                    const void *weight, float eps,
+                    int64_t rows, int64_t hidden, int dtype, hipStream_t stream);
+
+/* Fused residual add + RMSNorm + e4m3 output: the full single-pass kernel
+ * of "Custom CUDA kernels juice Llama 3.1 405B on AMD MI300X" (paragraph 2).
+ * Arguments as in arn_fused_add_rmsnorm and arn_rmsnorm_fp8. */
+int arn_fused_add_rmsnorm_fp8(uint8_t *out, int64_t out_stride, float *scale, int fp8_mode,
+                              const void *x, int64_t x_stride,
+                              void *residual, int64_t residual_stride,
+                              const void *weight, float eps,
+                              int64_t rows, int64_t hidden, int dtype, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *arn_status_str(int status);
+
+/* ARN_ABI_VERSION of the loaded library. */
+int arn_abi_version(void);
+
+/*
+ * Tuning and test aids (not needed for normal use).
+ *
+ * arn_set_tile forces the kernel shape of later calls from any thread:
+ * waves_per_row (1, 2, 4, 8, 16) 64-lane waves share one row, and each lane
+ * keeps up to vec_per_lane vectors of the row in registers.  A call whose
+ * shape the forced tile cannot serve returns ARN_EUNSUPPORTED.  (0, 0)
+ * restores automatic selection.  Returns ARN_EINVAL for a tile that is not
+ * compiled.
+ *
+ * arn_last_plan copies into buf (size len, always NUL-terminated when
+ * len > 0) a description of the kernel the calling thread's last successful
+ * launch used, e.g. "fused_add/bf16/vec8/wpr1/nv16/rpb4/grid1024".
+ * Returns the full length of the description.
+ */
+int arn_set_tile(int waves_per_row, int vec_per_lane);
+int arn_last_plan(char *buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARN_H */

@@ -1,0 +1,212 @@
+"""Fused residual-add + RMSNorm (+ OCP e4m3) for AMD Instinct MI355X (gfx950).
+
+A thin binding over the C ABI of libarn.so (include/arn.h): each function
+checks and marshals torch tensors into (device pointer, row stride) pairs and
+calls the C entry point of the same name on torch's current stream.  Every
+step of the operator runs in the library's HIP kernels; there is no fallback.
+torch provides device memory and streams only.
+
+Layouts follow the vLLM API page "vllm.kernels.aiter_ops"
+(flatten_to_2d_is_free): the last dimension must have unit stride and the
+leading dimensions must flatten to rows with one uniform pitch without a
+copy.  A padded pitch (row stride > hidden) is accepted; anything that
+would need a copy raises ValueError instead of copying.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import ArnError  # noqa: F401
+
+__all__ = [
+    "rmsnorm", "fused_add_rmsnorm", "rmsnorm_fp8", "fused_add_rmsnorm_fp8",
+    "set_tile", "last_plan", "ArnError",
+]
+
+_DTYPES = {torch.bfloat16: _lib.BF16, torch.float16: _lib.FP16}
+FP8_DTYPE = torch.float8_e4m3fn
+
+
+def _rows(t: torch.Tensor, name: str):
+    """(rows, hidden, row_stride) of a tensor viewed as 2-D rows, no copy."""
+    if t.dim() == 0:
+        raise ValueError(f"{name}: needs at least one dimension")
+    hidden = t.shape[-1]
+    if hidden > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: last dimension must have unit stride")
+    rows = 1
+    for s in t.shape[:-1]:
+        rows *= s
+    pitch = None
+    expected = None
+    for i in range(t.dim() - 2, -1, -1):
+        if t.shape[i] == 1:
+            continue
+        if pitch is None:
+            pitch = t.stride(i)
+            expected = pitch * t.shape[i]
+        else:
+            if t.stride(i) != expected:
+                raise ValueError(f"{name}: leading dims do not flatten to one row pitch "
+                                 "without a copy")
+            expected *= t.shape[i]
+    if pitch is None:
+        pitch = hidden
+    if rows > 1 and pitch < hidden:
+        raise ValueError(f"{name}: rows overlap (row stride {pitch} < hidden {hidden})")
+    return rows, hidden, pitch
+
+
+def _dtype_code(x: torch.Tensor) -> int:
+    try:
+        return _DTYPES[x.dtype]
+    except KeyError:
+        raise ValueError(f"activations must be bfloat16 or float16, got {x.dtype}") from None
+
+
+def _check_weight(weight, x, hidden):
+    if weight is None:
+        return None
+    if weight.dtype != x.dtype:
+        raise ValueError("weight dtype must match x dtype")
+    if weight.dim() != 1 or weight.shape[0] != hidden or (hidden > 1 and weight.stride(0) != 1):
+        raise ValueError(f"weight must be a contiguous vector of {hidden} elements")
+    if weight.device != x.device:
+        raise ValueError("weight must be on x's device")
+    return weight.data_ptr()
+
+
+def _check_device(x: torch.Tensor):
+    if x.device.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+
+
+def _stream(x: torch.Tensor) -> int:
+    return torch.cuda.current_stream(x.device).cuda_stream
+
+
+def _out_like(x, out, dtype, name="out"):
+    if out is None:
+        return torch.empty(x.shape, dtype=dtype, device=x.device)
+    if out.shape != x.shape or out.dtype != dtype or out.device != x.device:
+        raise ValueError(f"{name} must have x's shape and dtype {dtype} on x's device")
+    return out
+
+
+def rmsnorm(x: torch.Tensor, weight: torch.Tensor | None, eps: float,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """out = x / sqrt(mean(x^2, -1) + eps) * weight  (arn_rmsnorm)."""
+    _check_device(x)
+    dt = _dtype_code(x)
+    rows, hidden, xs = _rows(x, "x")
+    out = _out_like(x, out, x.dtype)
+    _, _, os_ = _rows(out, "out")
+    wp = _check_weight(weight, x, hidden)
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        st = lib.arn_rmsnorm(out.data_ptr(), os_, x.data_ptr(), xs, wp, float(eps),
+                             rows, hidden, dt, _stream(x))
+    _lib.check(st, "arn_rmsnorm")
+    return out
+
+
+def fused_add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, weight: torch.Tensor | None,
+                      eps: float, out: torch.Tensor | None = None) -> torch.Tensor:
+    """residual <- x + residual (rounded to the 16-bit type, in place);
+    returns out = RMSNorm(residual)  (arn_fused_add_rmsnorm)."""
+    _check_device(x)
+    dt = _dtype_code(x)
+    if residual.dtype != x.dtype or residual.shape != x.shape or residual.device != x.device:
+        raise ValueError("residual must match x in shape, dtype and device")
+    rows, hidden, xs = _rows(x, "x")
+    _, _, rs = _rows(residual, "residual")
+    out = _out_like(x, out, x.dtype)
+    _, _, os_ = _rows(out, "out")
+    wp = _check_weight(weight, x, hidden)
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        st = lib.arn_fused_add_rmsnorm(out.data_ptr(), os_, x.data_ptr(), xs,
+                                       residual.data_ptr(), rs, wp, float(eps),
+                                       rows, hidden, dt, _stream(x))
+    _lib.check(st, "arn_fused_add_rmsnorm")
+    return out
+
+
+def _fp8_scale(x, rows, scale, dynamic, scales_out):
+    if dynamic:
+        if scales_out is None:
+            scales_out = torch.empty(x.shape[:-1] if x.dim() > 1 else (1,),
+                                     dtype=torch.float32, device=x.device)
+        if (scales_out.dtype != torch.float32 or scales_out.numel() != rows
+                or not scales_out.is_contiguous() or scales_out.device != x.device):
+            raise ValueError(f"scales_out must be {rows} contiguous float32 values on x's device")
+        return scales_out, _lib.FP8_DYNAMIC
+    if scale is None:
+        raise ValueError("static FP8 needs `scale` (one float32 dequant scale on the device)")
+    if scale.dtype != torch.float32 or scale.numel() != 1 or scale.device != x.device:
+        raise ValueError("scale must be one float32 value on x's device")
+    return scale, _lib.FP8_STATIC
+
+
+def rmsnorm_fp8(x: torch.Tensor, weight: torch.Tensor | None, eps: float,
+                scale: torch.Tensor | None = None, dynamic: bool = False,
+                out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None):
+    """RMSNorm with an OCP e4m3 output  (arn_rmsnorm_fp8).
+
+    Static (``scale`` given, dequant scale s): codes = e4m3(y / s).
+    Dynamic: per-row scales = max|y| / 448 are written and returned.
+    Returns (codes as float8_e4m3fn, scale tensor)."""
+    _check_device(x)
+    dt = _dtype_code(x)
+    rows, hidden, xs = _rows(x, "x")
+    out = _out_like(x, out, FP8_DTYPE)
+    _, _, os_ = _rows(out, "out")
+    wp = _check_weight(weight, x, hidden)
+    sc, mode = _fp8_scale(x, rows, scale, dynamic, scales_out)
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        st = lib.arn_rmsnorm_fp8(out.data_ptr(), os_, sc.data_ptr(), mode, x.data_ptr(), xs,
+                                 wp, float(eps), rows, hidden, dt, _stream(x))
+    _lib.check(st, "arn_rmsnorm_fp8")
+    return out, sc
+
+
+def fused_add_rmsnorm_fp8(x: torch.Tensor, residual: torch.Tensor,
+                          weight: torch.Tensor | None, eps: float,
+                          scale: torch.Tensor | None = None, dynamic: bool = False,
+                          out: torch.Tensor | None = None,
+                          scales_out: torch.Tensor | None = None):
+    """residual <- x + residual; codes = e4m3(RMSNorm(residual) / scale)
+    (arn_fused_add_rmsnorm_fp8).  Returns (codes, scale tensor)."""
+    _check_device(x)
+    dt = _dtype_code(x)
+    if residual.dtype != x.dtype or residual.shape != x.shape or residual.device != x.device:
+        raise ValueError("residual must match x in shape, dtype and device")
+    rows, hidden, xs = _rows(x, "x")
+    _, _, rs = _rows(residual, "residual")
+    out = _out_like(x, out, FP8_DTYPE)
+    _, _, os_ = _rows(out, "out")
+    wp = _check_weight(weight, x, hidden)
+    sc, mode = _fp8_scale(x, rows, scale, dynamic, scales_out)
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        st = lib.arn_fused_add_rmsnorm_fp8(out.data_ptr(), os_, sc.data_ptr(), mode,
+                                           x.data_ptr(), xs, residual.data_ptr(), rs, wp,
+                                           float(eps), rows, hidden, dt, _stream(x))
+    _lib.check(st, "arn_fused_add_rmsnorm_fp8")
+    return out, sc
+
+
+def set_tile(waves_per_row: int = 0, vec_per_lane: int = 0) -> None:
+    """Force a kernel shape for later calls ((0, 0) = automatic)."""
+    _lib.check(_lib.load().arn_set_tile(waves_per_row, vec_per_lane), "arn_set_tile")
+
+
+def last_plan() -> str:
+    """The kernel shape of this thread's last launch."""
+    import ctypes
+
+    buf = ctypes.create_string_buffer(160)
+    _lib.load().arn_last_plan(buf, len(buf))
+    return buf.value.decode()

@@ -1,0 +1,84 @@
+"""ctypes loader for libarn.so (the C ABI in include/arn.h).
+
+torch is imported first: it ships its own HIP runtime, and loading libarn.so
+afterwards makes the library's libamdhip64.so.7 dependency resolve to that
+same, already loaded runtime, so torch's streams and device pointers are
+valid in the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # noqa: F401  (must precede the library load; see above)
+
+from . import build as _build
+
+LIB_PATH = _build.LIB_PATH
+
+OK, EINVAL, EUNSUPPORTED, ELAUNCH = 0, 1, 2, 3
+BF16, FP16 = 0, 1
+FP8_STATIC, FP8_DYNAMIC = 0, 1
+
+# Every function include/arn.h declares, with its ctypes signature.
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+SIGNATURES = {
+    "arn_rmsnorm": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, ctypes.c_float, _i64, _i64,
+                                   ctypes.c_int, _vp]),
+    "arn_fused_add_rmsnorm": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                             ctypes.c_float, _i64, _i64, ctypes.c_int, _vp]),
+    "arn_rmsnorm_fp8": (ctypes.c_int, [_vp, _i64, _vp, ctypes.c_int, _vp, _i64, _vp,
+                                       ctypes.c_float, _i64, _i64, ctypes.c_int, _vp]),
+    "arn_fused_add_rmsnorm_fp8": (ctypes.c_int, [_vp, _i64, _vp, ctypes.c_int, _vp, _i64, _vp,
+                                                 _i64, _vp, ctypes.c_float, _i64, _i64,
+                                                 ctypes.c_int, _vp]),
+    "arn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "arn_abi_version": (ctypes.c_int, []),
+    "arn_set_tile": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
+    "arn_last_plan": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_size_t]),
+}
+
+ABI_VERSION = 1
+
+
+class ArnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libarn.so, building it first only if it is not there at all."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path) and path == LIB_PATH:
+            _build.build()
+        if not os.path.exists(path):
+            raise ImportError(f"libarn.so not found at {path}; run "
+                              "`python -m residual_add_rmsnorm_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if lib.arn_abi_version() != ABI_VERSION:
+            raise ImportError(f"libarn.so ABI {lib.arn_abi_version()} != {ABI_VERSION}")
+        _lib = lib
+        return lib
+
+
+def status_str(status: int) -> str:
+    return load().arn_status_str(status).decode()
+
+
+def check(status: int, what: str) -> None:
+    if status != OK:
+        raise ArnError(status, what)

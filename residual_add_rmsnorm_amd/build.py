@@ -1,0 +1,89 @@
+"""Build libarn.so (HIP, gfx950 only) in-tree.
+
+One object per operator kind and dtype is compiled from arn_kernels.hip
+(they build in parallel), plus the host dispatcher arn_api.hip; hipcc links
+them into residual_add_rmsnorm_amd/lib/libarn.so.
+
+    python -m residual_add_rmsnorm_amd.build
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_DIR = os.path.join(PKG, "lib")
+LIB_PATH = os.path.join(LIB_DIR, "libarn.so")
+OBJ_DIR = os.path.join(ROOT, "_build", "arn")
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+
+# -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32;
+# ordinary scalar fp32 code is what the kernels are written as.
+CFLAGS = [
+    "-O3", f"--offload-arch={ARCH}", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+KINDS = range(6)
+DTYPES = range(2)
+
+
+def sources() -> list[str]:
+    return [os.path.join(CSRC, f) for f in ("arn_kernels.hip", "arn_api.hip", "arn_internal.h")] + [
+        os.path.join(INCLUDE, "arn.h")]
+
+
+def _compile(src: str, obj: str, defines: list[str]) -> None:
+    cmd = [HIPCC, *CFLAGS, *defines, "-c", src, "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature and says so;
+    # that note is expected.  Anything else is shown.
+    noise = "packed-fp32-ops"
+    msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({' '.join(cmd)}):\n{msg}")
+    if msg.strip():
+        print(msg, file=sys.stderr)
+
+
+def build(jobs: int | None = None, verbose: bool = True) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    os.makedirs(LIB_DIR, exist_ok=True)
+    units = []
+    for k in KINDS:
+        for d in DTYPES:
+            units.append((os.path.join(CSRC, "arn_kernels.hip"),
+                          os.path.join(OBJ_DIR, f"arn_kernels_k{k}_d{d}.o"),
+                          [f"-DARN_KIND={k}", f"-DARN_DT={d}"]))
+    units.append((os.path.join(CSRC, "arn_api.hip"), os.path.join(OBJ_DIR, "arn_api.o"), []))
+    jobs = jobs or min(16, os.cpu_count() or 4)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(lambda u: _compile(*u), units))
+    tmp = LIB_PATH + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[u[1] for u in units]]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print(f"built {LIB_PATH}", file=sys.stderr)
+    return LIB_PATH
+
+
+def is_stale() -> bool:
+    if not os.path.exists(LIB_PATH):
+        return True
+    t = os.path.getmtime(LIB_PATH)
+    return any(os.path.getmtime(s) > t for s in sources())
+
+
+if __name__ == "__main__":
+    build()

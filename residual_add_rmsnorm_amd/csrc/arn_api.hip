@@ -1,0 +1,285 @@
+// arn_api.hip -- the C ABI declared in include/arn.h: argument checks, the
+// choice of kernel shape, and the launch.  Host code only.
+//
+// Argument rules follow the vLLM API page "vllm.kernels.aiter_ops"
+// (rms_add_no_var_16bit_only, rms_no_var_16bit_only, flatten_to_2d_is_free):
+// 16-bit activations, a weight of the same dtype or none, no variance-size
+// override, unit element stride.  Anything else is refused before any HIP
+// call, and nothing is ever copied to make an input acceptable.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "arn.h"
+#include "arn_internal.h"
+
+namespace {
+
+using arn::Args;
+using arn::Tile;
+using arn::TileTable;
+
+const TileTable* table_for(int kind, int dtype) {
+  static const TileTable* const tables[arn::kNumKinds][arn::kNumDtypes] = {
+      {&ARN_TABLE_NAME(0, 0), &ARN_TABLE_NAME(0, 1)},
+      {&ARN_TABLE_NAME(1, 0), &ARN_TABLE_NAME(1, 1)},
+      {&ARN_TABLE_NAME(2, 0), &ARN_TABLE_NAME(2, 1)},
+      {&ARN_TABLE_NAME(3, 0), &ARN_TABLE_NAME(3, 1)},
+      {&ARN_TABLE_NAME(4, 0), &ARN_TABLE_NAME(4, 1)},
+      {&ARN_TABLE_NAME(5, 0), &ARN_TABLE_NAME(5, 1)},
+  };
+  return tables[kind][dtype];
+}
+
+const char* const kKindNames[arn::kNumKinds] = {"plain",      "fused_add",      "plain_fp8s",
+                                                "fused_add_fp8s", "plain_fp8d", "fused_add_fp8d"};
+
+// Forced tile (arn_set_tile); 0 = automatic.  Packed as wpr << 8 | nv.
+std::atomic<int> g_forced_tile{0};
+
+thread_local char g_last_plan[160] = "";
+thread_local int g_last_plan_len = 0;
+
+// Compute units of the current device, cached per device.
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    cus = 256;
+  }
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+struct Request {
+  int kind;
+  int dtype;
+  void* out;
+  int64_t out_stride;
+  const void* x;
+  int64_t x_stride;
+  void* res;
+  int64_t res_stride;
+  const void* w;
+  float* scale;
+  float eps;
+  int64_t rows;
+  int64_t hidden;
+  hipStream_t stream;
+};
+
+bool aligned(const void* p, uintptr_t bytes) {
+  return (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
+}
+
+// Widest access (in 16-bit elements) that every row start and the row
+// length allow.
+int choose_vec(const Request& r) {
+  const bool fp8 = (r.kind & 6) != 0;
+  for (int vec = 8; vec > 1; vec /= 2) {
+    const uintptr_t b16 = 2u * vec;
+    bool ok = r.hidden % vec == 0 && r.x_stride % vec == 0 && aligned(r.x, b16);
+    if (r.res) ok = ok && r.res_stride % vec == 0 && aligned(r.res, b16);
+    if (r.w) ok = ok && aligned(r.w, b16);
+    if (fp8) {
+      ok = ok && r.out_stride % vec == 0 && aligned(r.out, vec);
+    } else {
+      ok = ok && r.out_stride % vec == 0 && aligned(r.out, b16);
+    }
+    if (ok) return vec;
+  }
+  return 1;
+}
+
+// Kernel shape.  Many rows: few waves per row and long per-lane vectors
+// (no barrier; the chip fills with rows).  Few rows (decode): more waves
+// per row so each row finishes sooner.
+const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t rows, int cus) {
+  const int forced = g_forced_tile.load(std::memory_order_relaxed);
+  if (forced != 0) {
+    const int fw = forced >> 8, fn = forced & 0xFF;
+    for (int i = 0; i < table->count; ++i) {
+      const Tile& t = table->tiles[i];
+      if (t.vec == vec && t.wpr == fw && t.nv == fn) {
+        return (int64_t)64 * t.wpr * t.nv >= nvec ? &t : nullptr;
+      }
+    }
+    return nullptr;
+  }
+  const bool many_rows = rows >= (int64_t)4 * cus;
+  const int targets[2] = {many_rows ? 16 : 4, 1 << 20};
+  for (int target : targets) {
+    for (int wpr = 1; wpr <= 16; wpr *= 2) {
+      const int64_t per_lane = (nvec + 64 * wpr - 1) / (64 * wpr);
+      if (per_lane > target) continue;
+      const Tile* best = nullptr;
+      for (int i = 0; i < table->count; ++i) {
+        const Tile& t = table->tiles[i];
+        if (t.vec == vec && t.wpr == wpr && t.nv >= per_lane && (!best || t.nv < best->nv)) {
+          best = &t;
+        }
+      }
+      if (best) return best;
+    }
+  }
+  return nullptr;
+}
+
+// Grid limit per launch; larger row counts are split into several launches.
+constexpr int64_t kMaxBlocksPerLaunch = int64_t(1) << 22;
+
+int run(const Request& r) {
+  const bool fp8 = (r.kind & 6) != 0;
+  const bool dynamic = (r.kind & 4) != 0;
+
+  // ---- argument checks (no HIP call before they pass) ----
+  if (r.dtype != ARN_BF16 && r.dtype != ARN_FP16) return ARN_EINVAL;
+  if (r.rows < 0 || r.hidden <= 0) return ARN_EINVAL;
+  if (r.x_stride < r.hidden || r.out_stride < r.hidden) return ARN_EINVAL;
+  if ((r.kind & 1) && r.res_stride < r.hidden) return ARN_EINVAL;
+  if (!(r.eps >= 0.0f) || !std::isfinite(r.eps)) return ARN_EINVAL;
+  if (r.rows == 0) return ARN_OK;
+  if (!r.out || !r.x) return ARN_EINVAL;
+  if ((r.kind & 1) && !r.res) return ARN_EINVAL;
+  if (fp8 && (!r.scale || !aligned(r.scale, 4))) return ARN_EINVAL;
+  if (!aligned(r.x, 2) || (r.res && !aligned(r.res, 2)) || (r.w && !aligned(r.w, 2)) ||
+      (!fp8 && !aligned(r.out, 2))) {
+    return ARN_EINVAL;
+  }
+  // Aliasing: out may be x itself (same stride, 16-bit output); the
+  // residual may alias neither.
+  if (r.res && (r.res == r.x || r.res == r.out)) return ARN_EINVAL;
+  if (r.out == r.x && (fp8 || r.out_stride != r.x_stride)) return ARN_EINVAL;
+  if (r.hidden > (int64_t)1 << 30) return ARN_EUNSUPPORTED;
+
+  const int vec = choose_vec(r);
+  const int64_t nvec = r.hidden / vec;
+  const Tile* tile = choose_tile(table_for(r.kind, r.dtype), vec, nvec, r.rows, cu_count());
+  if (!tile) return ARN_EUNSUPPORTED;
+
+  const int esize_out = fp8 ? 1 : 2;
+  const int64_t rows_per_launch = kMaxBlocksPerLaunch * tile->rpb;
+  int64_t done = 0;
+  int64_t grid = 0;
+  while (done < r.rows) {
+    const int64_t n = (r.rows - done < rows_per_launch) ? r.rows - done : rows_per_launch;
+    Args a;
+    a.out = static_cast<char*>(r.out) + done * r.out_stride * esize_out;
+    a.out_stride = r.out_stride;
+    a.x = static_cast<const char*>(r.x) + done * r.x_stride * 2;
+    a.x_stride = r.x_stride;
+    a.res = r.res ? static_cast<char*>(r.res) + done * r.res_stride * 2 : nullptr;
+    a.res_stride = r.res_stride;
+    a.w = r.w;
+    a.scale = dynamic ? r.scale + done : r.scale;
+    a.rows = n;
+    a.hidden = (int32_t)r.hidden;
+    a.eps = r.eps;
+    a.inv_hidden = 1.0f / (float)r.hidden;
+
+    grid = (n + tile->rpb - 1) / tile->rpb;
+    void* params[] = {&a};
+    const hipError_t e = hipLaunchKernel(tile->fn, dim3((unsigned)grid),
+                                         dim3(64u * tile->wpr * tile->rpb), params, 0, r.stream);
+    if (e != hipSuccess) return ARN_ELAUNCH;
+    done += n;
+  }
+
+  g_last_plan_len = std::snprintf(g_last_plan, sizeof(g_last_plan),
+                                  "%s/%s/vec%d/wpr%d/nv%d/rpb%d/grid%lld", kKindNames[r.kind],
+                                  r.dtype == ARN_BF16 ? "bf16" : "fp16", vec, tile->wpr, tile->nv,
+                                  tile->rpb, (long long)grid);
+  return ARN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int arn_rmsnorm(void* out, int64_t out_stride, const void* x, int64_t x_stride,
+                const void* weight, float eps, int64_t rows, int64_t hidden, int dtype,
+                hipStream_t stream) {
+  Request r{arn::kPlain, dtype, out,     out_stride, x,    x_stride, nullptr,
+            0,           weight, nullptr, eps,       rows, hidden,   stream};
+  return run(r);
+}
+
+int arn_fused_add_rmsnorm(void* out, int64_t out_stride, const void* x, int64_t x_stride,
+                          void* residual, int64_t residual_stride, const void* weight, float eps,
+                          int64_t rows, int64_t hidden, int dtype, hipStream_t stream) {
+  Request r{arn::kFused, dtype,  out,     out_stride, x,    x_stride, residual,
+            residual_stride, weight, nullptr, eps,     rows, hidden,   stream};
+  return run(r);
+}
+
+int arn_rmsnorm_fp8(uint8_t* out, int64_t out_stride, float* scale, int fp8_mode, const void* x,
+                    int64_t x_stride, const void* weight, float eps, int64_t rows, int64_t hidden,
+                    int dtype, hipStream_t stream) {
+  if (fp8_mode != ARN_FP8_STATIC && fp8_mode != ARN_FP8_DYNAMIC) return ARN_EINVAL;
+  const int kind = fp8_mode == ARN_FP8_STATIC ? arn::kPlainFp8Static : arn::kPlainFp8Dynamic;
+  Request r{kind, dtype,  out,   out_stride, x,    x_stride, nullptr,
+            0,    weight, scale, eps,        rows, hidden,   stream};
+  return run(r);
+}
+
+int arn_fused_add_rmsnorm_fp8(uint8_t* out, int64_t out_stride, float* scale, int fp8_mode,
+                              const void* x, int64_t x_stride, void* residual,
+                              int64_t residual_stride, const void* weight, float eps,
+                              int64_t rows, int64_t hidden, int dtype, hipStream_t stream) {
+  if (fp8_mode != ARN_FP8_STATIC && fp8_mode != ARN_FP8_DYNAMIC) return ARN_EINVAL;
+  const int kind = fp8_mode == ARN_FP8_STATIC ? arn::kFusedFp8Static : arn::kFusedFp8Dynamic;
+  Request r{kind,           dtype,  out,   out_stride, x,    x_stride, residual,
+            residual_stride, weight, scale, eps,        rows, hidden,   stream};
+  return run(r);
+}
+
+const char* arn_status_str(int status) {
+  switch (status) {
+    case ARN_OK:
+      return "ok";
+    case ARN_EINVAL:
+      return "invalid argument";
+    case ARN_EUNSUPPORTED:
+      return "unsupported shape or layout";
+    case ARN_ELAUNCH:
+      return "kernel launch failed";
+    default:
+      return "unknown status";
+  }
+}
+
+int arn_abi_version(void) { return ARN_ABI_VERSION; }
+
+int arn_set_tile(int waves_per_row, int vec_per_lane) {
+  if (waves_per_row == 0 && vec_per_lane == 0) {
+    g_forced_tile.store(0);
+    return ARN_OK;
+  }
+  // The tile must exist in the tables (all tables list the same shapes).
+  const TileTable* t = table_for(arn::kPlain, ARN_BF16);
+  for (int i = 0; i < t->count; ++i) {
+    if (t->tiles[i].wpr == waves_per_row && t->tiles[i].nv == vec_per_lane) {
+      g_forced_tile.store((waves_per_row << 8) | vec_per_lane);
+      return ARN_OK;
+    }
+  }
+  return ARN_EINVAL;
+}
+
+int arn_last_plan(char* buf, size_t len) {
+  if (buf && len > 0) {
+    std::strncpy(buf, g_last_plan, len - 1);
+    buf[len - 1] = '\0';
+  }
+  return g_last_plan_len;
+}
+
+}  // extern "C"

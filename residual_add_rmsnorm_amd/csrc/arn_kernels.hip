@@ -1,0 +1,425 @@
+// arn_kernels.hip -- gfx950 (CDNA4) kernels for residual-add + RMSNorm
+// (+ OCP e4m3 output).  Compiled once per operator kind and dtype
+// (-DARN_KIND=0..5 -DARN_DT=0|1); each unit exports one table of tiles.
+//
+// The method: per row, r = x + residual (stored back, rounded to 16 bits),
+// y = r / sqrt(mean(r^2) + eps) * w (Zhang & Sennrich 2019, eq. 4), then
+// optionally an e4m3 cast -- the three steps the first kernel of "Custom
+// CUDA kernels juice Llama 3.1 405B on AMD MI300X" (paragraph 2) fuses into
+// one pass.  That kernel targeted MI300X; this one is laid out for gfx950:
+//
+//  * The op moves 7-8 bytes per element and does a handful of VALU ops per
+//    element, so HBM bandwidth bounds it; there is no contraction and no
+//    MFMA.  Each row is read once and written once.
+//  * Lane l of the T = 64*WPR threads that share a row owns the VEC-element
+//    vectors l, l+T, l+2T, ... (VEC = 8 x 16-bit = 128-bit loads, so one
+//    wave instruction moves 1 KiB of contiguous row).  The whole row stays
+//    in VGPRs between the sum-of-squares pass and the output pass.
+//  * WPR = 1 (row per wave) reduces with DPP row ops + 4 readlanes and no
+//    LDS or barrier; WPR > 1 (row per workgroup) adds one LDS exchange of
+//    per-wave partials behind one barrier.  Sum and, for dynamic FP8, the
+//    max |r*w| travel together, so dynamic FP8 costs no extra barrier:
+//    max |y| = max |r*w| * inv because inv > 0.
+//  * Reductions use a fixed order, so results are bitwise reproducible.
+//  * e4m3 codes come from the packed gfx950 v_cvt_pk_fp8_f32 (OCP format
+//    on this target) after an explicit fmed3 clamp to +-448.
+//  * x and out may alias: every element is loaded before the reduction and
+//    stored after it by the same lane, so nothing is marked __restrict__.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "arn_internal.h"
+
+#if !defined(ARN_KIND) || !defined(ARN_DT)
+#error "compile with -DARN_KIND=<0..5> -DARN_DT=<0|1>"
+#endif
+
+namespace arn {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// 16-bit <-> fp32.  bf16 is the upper half of an fp32; fp16 converts with
+// v_cvt_f32_f16.  fp32 -> 16-bit rounds to nearest even: v_cvt_pk_bf16_f32
+// on gfx950 for bf16, v_cvt_f16_f32 for fp16 (never the round-toward-zero
+// v_cvt_pkrtz_f16_f32).
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ float lo_f32(uint32_t w) {
+  if constexpr (DT == kBF16) {
+    return __uint_as_float(w << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float hi_f32(uint32_t w) {
+  if constexpr (DT == kBF16) {
+    return __uint_as_float(w & 0xFFFF0000u);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  f32x2 v;
+  v.x = a;
+  v.y = b;
+  if constexpr (DT == kBF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+}
+
+// VEC 16-bit elements as one memory access.
+template <int VEC> struct RawT;
+template <> struct RawT<8> { using type = u32x4; };
+template <> struct RawT<4> { using type = u32x2; };
+template <> struct RawT<2> { using type = uint32_t; };
+template <> struct RawT<1> { using type = uint16_t; };
+template <int VEC> using Raw = typename RawT<VEC>::type;
+
+// VEC e4m3 codes as one memory access.
+template <int VEC> struct Fp8RawT;
+template <> struct Fp8RawT<8> { using type = u32x2; };
+template <> struct Fp8RawT<4> { using type = uint32_t; };
+template <> struct Fp8RawT<2> { using type = uint16_t; };
+template <> struct Fp8RawT<1> { using type = uint8_t; };
+template <int VEC> using Fp8Raw = typename Fp8RawT<VEC>::type;
+
+template <int DT, int VEC>
+__device__ __forceinline__ float elem(const Raw<VEC>& r, int e) {
+  if constexpr (VEC == 1) {
+    return lo_f32<DT>((uint32_t)r);
+  } else if constexpr (VEC == 2) {
+    return (e & 1) ? hi_f32<DT>(r) : lo_f32<DT>(r);
+  } else {
+    const uint32_t w = r[e >> 1];
+    return (e & 1) ? hi_f32<DT>(w) : lo_f32<DT>(w);
+  }
+}
+
+template <int DT, int VEC>
+__device__ __forceinline__ Raw<VEC> pack(const float (&f)[VEC]) {
+  if constexpr (VEC == 1) {
+    return (uint16_t)(pack2<DT>(f[0], 0.0f) & 0xFFFFu);
+  } else if constexpr (VEC == 2) {
+    return pack2<DT>(f[0], f[1]);
+  } else {
+    Raw<VEC> r;
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) r[i] = pack2<DT>(f[2 * i], f[2 * i + 1]);
+    return r;
+  }
+}
+
+template <int DT, int VEC>
+__device__ __forceinline__ Raw<VEC> ones() {
+  constexpr uint32_t one = (DT == kBF16) ? 0x3F80u : 0x3C00u;
+  if constexpr (VEC == 1) {
+    return (uint16_t)one;
+  } else if constexpr (VEC == 2) {
+    return one | (one << 16);
+  } else {
+    Raw<VEC> r;
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) r[i] = one | (one << 16);
+    return r;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// OCP e4m3: clamp to the finite range, then the packed gfx950 convert
+// (round to nearest even).  word_sel picks which 16-bit half of the
+// destination dword receives the two codes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sat448(float v) {
+  return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+}
+
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+  return (uint32_t)w;
+}
+
+template <int VEC>
+__device__ __forceinline__ Fp8Raw<VEC> pack_fp8(const float (&f)[VEC]) {
+  if constexpr (VEC == 8) {
+    u32x2 r;
+    r.x = fp8x4(f[0], f[1], f[2], f[3]);
+    r.y = fp8x4(f[4], f[5], f[6], f[7]);
+    return r;
+  } else if constexpr (VEC == 4) {
+    return fp8x4(f[0], f[1], f[2], f[3]);
+  } else if constexpr (VEC == 2) {
+    return (uint16_t)(__builtin_amdgcn_cvt_pk_fp8_f32(sat448(f[0]), sat448(f[1]), 0, false) &
+                      0xFFFF);
+  } else {
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(sat448(f[0]), sat448(f[0]), 0, false) &
+                     0xFF);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions: four DPP steps give every lane its 16-lane row total
+// (xor 1, xor 2, half-row mirror, row mirror), then the four row totals are
+// read with v_readlane and combined in a fixed order.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+constexpr int kDppXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
+// ---------------------------------------------------------------------------
+// Row accesses go through buffer instructions: a descriptor in SGPRs holds
+// the row's base address and its length in bytes (num_records), and each
+// lane supplies a 32-bit byte offset.  An access at or beyond num_records
+// reads zeros and drops stores, so the ragged end of a row needs no
+// branches, a row past the last one (num_records = 0) touches nothing, and
+// no access can leave its own row.  Word 3 is the gfx9 raw-buffer format
+// (DATA_FORMAT = 32 bit).
+// ---------------------------------------------------------------------------
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+
+template <int VEC>
+__device__ __forceinline__ Raw<VEC> load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (VEC == 8) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  } else if constexpr (VEC == 4) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  } else if constexpr (VEC == 2) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+  } else {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void store16(Raw<VEC> v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (VEC == 8) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+  } else if constexpr (VEC == 4) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+  } else if constexpr (VEC == 2) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, 0);
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void store8(Fp8Raw<VEC> v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (VEC == 8) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+  } else if constexpr (VEC == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+  } else if constexpr (VEC == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b8(v, r, (int)off, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.
+// ---------------------------------------------------------------------------
+template <int DT, int KIND, int VEC, int NV, int WPR, int RPB>
+__global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
+  constexpr bool kRes = (KIND & 1) != 0;
+  constexpr bool kStatic = (KIND & 2) != 0;
+  constexpr bool kDynamic = (KIND & 4) != 0;
+  constexpr bool kFp8 = kStatic || kDynamic;
+  constexpr int kTPR = 64 * WPR;                     // threads per row
+  constexpr uint32_t kStep16 = kTPR * VEC * 2;       // bytes between a lane's vectors
+  constexpr uint32_t kStep8 = kTPR * VEC;            // same, e4m3 output
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  // kTPR is a multiple of 64, so every lane of a wave has the same row;
+  // readfirstlane lets the compiler keep row addresses in SGPRs.
+  const int rib = __builtin_amdgcn_readfirstlane(tid / kTPR);  // row within the block
+  const int t = tid - rib * kTPR;                              // thread within the row
+  const uint32_t off16 = (uint32_t)t * (VEC * 2);
+  const uint32_t off8 = (uint32_t)t * VEC;
+  const uint32_t row_bytes16 = (uint32_t)a.hidden * 2u;
+  const uint32_t row_bytes8 = (uint32_t)a.hidden;
+
+  // One block handles RPB consecutive rows (the host splits launches whose
+  // row count exceeds the grid limit).  A row past the end gets
+  // num_records = 0, so its lanes still take part in the reduction but
+  // read zeros and write nothing.
+  const int64_t row = (int64_t)blockIdx.x * RPB + rib;
+  const bool active = row < a.rows;
+  const int64_t arow = active ? row : 0;
+  const uint32_t n16 = active ? row_bytes16 : 0u;
+
+  const __amdgpu_buffer_rsrc_t xrs =
+      row_rsrc(static_cast<const uint16_t*>(a.x) + arow * a.x_stride, n16);
+  __amdgpu_buffer_rsrc_t rrs = xrs;
+  if constexpr (kRes) rrs = row_rsrc(static_cast<const uint16_t*>(a.res) + arow * a.res_stride, n16);
+
+  __shared__ float red_sum[WPR * RPB];  // one slot per wave
+  __shared__ float red_max[WPR * RPB];
+
+  {
+    // 1. Load the row: x (and residual) into registers.  Vectors past the
+    //    row end read as zero.
+    Raw<VEC> xr[NV];
+    Raw<VEC> rr[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      xr[k] = load16<VEC>(xrs, off16 + k * kStep16);
+      if constexpr (kRes) rr[k] = load16<VEC>(rrs, off16 + k * kStep16);
+    }
+    // The weight (shared by all rows; an L2 hit after the first blocks).
+    Raw<VEC> wr[NV];
+    if (a.w != nullptr) {
+      const __amdgpu_buffer_rsrc_t wrs = row_rsrc(a.w, row_bytes16);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) wr[k] = load16<VEC>(wrs, off16 + k * kStep16);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) wr[k] = ones<DT, VEC>();
+    }
+    float qmul = 0.0f;
+    if constexpr (kStatic) qmul = 1.0f / *a.scale;
+
+    // 2. r = x + residual in fp32, rounded to 16 bits and stored back;
+    //    sum of squares of the rounded r (and max |r*w| for dynamic FP8).
+    //    Zero-filled vectors add nothing and their stores are dropped.
+    float ss = 0.0f;
+    float mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if constexpr (kRes) {
+        float f[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) f[e] = elem<DT, VEC>(xr[k], e) + elem<DT, VEC>(rr[k], e);
+        xr[k] = pack<DT, VEC>(f);
+        store16<VEC>(xr[k], rrs, off16 + k * kStep16);
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float rf = elem<DT, VEC>(xr[k], e);
+        ss = __builtin_fmaf(rf, rf, ss);
+        if constexpr (kDynamic) mx = fmaxf(mx, fabsf(rf * elem<DT, VEC>(wr[k], e)));
+      }
+    }
+
+    // 3. Row reduction: wave, then (row per workgroup) across waves via LDS.
+    ss = wave_sum(ss);
+    if constexpr (kDynamic) mx = wave_max(mx);
+    if constexpr (WPR > 1) {
+      if (lane == 0) {
+        red_sum[wave] = ss;
+        if constexpr (kDynamic) red_max[wave] = mx;
+      }
+      __syncthreads();
+      ss = 0.0f;
+      mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < WPR; ++i) {
+        ss += red_sum[rib * WPR + i];
+        if constexpr (kDynamic) mx = fmaxf(mx, red_max[rib * WPR + i]);
+      }
+    }
+    const float inv = rsqrtf(__builtin_fmaf(ss, a.inv_hidden, a.eps));
+
+    if constexpr (kDynamic) {
+      const float amax = mx * inv;
+      qmul = amax > 0.0f ? 448.0f / amax : 0.0f;
+      if (active && t == 0) a.scale[row] = amax / 448.0f;
+    }
+
+    // 4. y = r * inv * w, stored as 16 bits or as e4m3 codes.
+    if constexpr (kFp8) {
+      const __amdgpu_buffer_rsrc_t ors = row_rsrc(
+          static_cast<uint8_t*>(a.out) + arow * a.out_stride, active ? row_bytes8 : 0u);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        float y[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          y[e] = elem<DT, VEC>(xr[k], e) * inv * elem<DT, VEC>(wr[k], e) * qmul;
+        }
+        store8<VEC>(pack_fp8<VEC>(y), ors, off8 + k * kStep8);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t ors =
+          row_rsrc(static_cast<uint16_t*>(a.out) + arow * a.out_stride, n16);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        float y[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          y[e] = elem<DT, VEC>(xr[k], e) * inv * elem<DT, VEC>(wr[k], e);
+        }
+        store16<VEC>(pack<DT, VEC>(y), ors, off16 + k * kStep16);
+      }
+    }
+  }
+}
+
+constexpr int rows_per_block(int wpr) { return wpr >= 4 ? 1 : 4 / wpr; }
+
+}  // namespace
+}  // namespace arn
+
+#define ARN_TILE(VEC, WPR, NV)                                                          \
+  {VEC, WPR, NV, arn::rows_per_block(WPR),                                             \
+   (const void*)&arn::row_kernel<ARN_DT, ARN_KIND, VEC, NV, WPR, arn::rows_per_block(WPR)>}
+
+static const arn::Tile kTiles[] = {
+    // 128-bit accesses (hidden % 8 == 0, 16-byte aligned rows)
+    ARN_TILE(8, 1, 2), ARN_TILE(8, 1, 4), ARN_TILE(8, 1, 8), ARN_TILE(8, 1, 12),
+    ARN_TILE(8, 1, 16), ARN_TILE(8, 2, 4), ARN_TILE(8, 2, 8), ARN_TILE(8, 2, 16), ARN_TILE(8, 4, 4),
+    ARN_TILE(8, 4, 8), ARN_TILE(8, 4, 16), ARN_TILE(8, 8, 4), ARN_TILE(8, 8, 8),
+    ARN_TILE(8, 16, 2), ARN_TILE(8, 16, 4), ARN_TILE(8, 16, 8),
+    // narrower accesses for rows that are not 16-byte aligned
+    ARN_TILE(4, 1, 4), ARN_TILE(4, 1, 16), ARN_TILE(4, 4, 16), ARN_TILE(4, 16, 16),
+    ARN_TILE(2, 1, 4), ARN_TILE(2, 1, 16), ARN_TILE(2, 4, 16), ARN_TILE(2, 16, 16),
+    ARN_TILE(1, 1, 4), ARN_TILE(1, 1, 16), ARN_TILE(1, 4, 16), ARN_TILE(1, 16, 16),
+};
+
+extern const arn::TileTable ARN_TABLE_NAME(ARN_KIND, ARN_DT) = {
+    kTiles, (int)(sizeof(kTiles) / sizeof(kTiles[0]))};

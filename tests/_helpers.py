@@ -1,0 +1,98 @@
+"""Shared helpers for the GPU parity tests: moving 16-bit patterns to the
+device and the comparison rules.
+
+Comparison rules (the stated tolerances of the operator):
+  * stored residual: bit-exact;
+  * 16-bit y: |y_gpu - y_ref| <= max(rho * |y_ref|, ulp16(y_ref)), rho = 2^-7
+    (bf16) or 2^-10 (fp16), where ulp16(v) = 2^(max(floor(log2|v|), emin) - p + 1)
+    with p = 8, emin = -126 (bf16) or p = 11, emin = -14 (fp16); NaN matches NaN;
+  * e4m3 codes: within one step, |ord(q_gpu) - ord(q_ref)| <= 1 with
+    ord(c) = +-(c & 0x7f) by the sign bit (so +0 and -0 are equal);
+  * dynamic scales: relative error <= rho.
+"""
+import json
+import os
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+TORCH_DT = {"bf16": torch.bfloat16, "fp16": torch.float16}
+RHO = {"bf16": 2.0**-7, "fp16": 2.0**-10}
+PREC = {"bf16": (8, -126), "fp16": (11, -14)}
+
+
+def dev(bits: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """uint16 patterns -> device tensor of the 16-bit dtype (same shape)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy())
+    return t.view(TORCH_DT[dtype]).to(device)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """device 16-bit tensor -> uint16 patterns on the host."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def codes(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
+def values16(b: np.ndarray, dtype: str) -> np.ndarray:
+    """uint16 patterns -> float64 values (library conversions only)."""
+    if dtype == "fp16":
+        return b.view(np.float16).astype(np.float64)
+    return torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+
+
+def ulp16(v: np.ndarray, dtype: str) -> np.ndarray:
+    p, emin = PREC[dtype]
+    a = np.abs(v)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.where(a > 0, np.maximum(e, emin), emin)
+    return np.ldexp(1.0, (e - p + 1).astype(np.int64))
+
+
+def assert_y_close(y_bits: np.ndarray, y_ref: np.ndarray, dtype: str, what="y"):
+    got = values16(y_bits, dtype)
+    nan_ref = np.isnan(y_ref)
+    nan_got = np.isnan(got)
+    assert np.array_equal(nan_ref, nan_got), f"{what}: NaN positions differ ({nan_got.sum()} vs {nan_ref.sum()})"
+    ok = ~nan_ref
+    tol = np.maximum(RHO[dtype] * np.abs(y_ref[ok]), ulp16(y_ref[ok], dtype))
+    err = np.abs(got[ok] - y_ref[ok])
+    bad = err > tol
+    if bad.any():
+        i = np.flatnonzero(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; first: "
+                             f"got {got[ok][i]!r} ref {y_ref[ok][i]!r} tol {tol[i]!r}")
+
+
+def _ord(c: np.ndarray) -> np.ndarray:
+    c = c.astype(np.int64)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def assert_codes_close(q_gpu: np.ndarray, q_ref: np.ndarray, what="codes"):
+    d = np.abs(_ord(q_gpu) - _ord(q_ref))
+    bad = d > 1
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[0]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} codes more than one step off; "
+                             f"first: got {q_gpu.ravel()[i]:#04x} ref {q_ref.ravel()[i]:#04x}")
+
+
+def assert_scales_close(s_gpu: np.ndarray, s_ref: np.ndarray, dtype: str):
+    s_gpu = s_gpu.astype(np.float64)
+    s_ref = s_ref.astype(np.float64)
+    zero = s_ref == 0
+    assert np.all(s_gpu[zero] == 0)
+    rel = np.abs(s_gpu[~zero] - s_ref[~zero]) / np.abs(s_ref[~zero])
+    assert np.all(rel <= RHO[dtype]), f"scales: max rel err {rel.max()}"
+
+
+def static_scale() -> float:
+    with open(os.path.join(HERE, "golden", "fp16_16384_static_scale.json")) as f:
+        return json.load(f)["dequant_scale"]

@@ -1,0 +1,47 @@
+"""Write the stored expected/input values under tests/golden/.
+
+Calls only the oracle (and the seeded input generator).  Run from the repo
+root:  python tests/golden/make_golden.py
+
+fp16_16384_static_scale.json -- the per-tensor dequant scale of the decode
+workload (fused add + RMSNorm + static e4m3, fp16, hidden 16384).  The
+workload fixes the multiplier 448 / (4 * max|y|) over a seed-0 calibration
+batch; the library takes the dequant scale s with code = e4m3(y / s), so the
+stored value is s = fp32(4 * max|y| / 448), with max|y| taken from the
+oracle's unrounded fp64 y over the 256-row seed-0 batch (the decode row
+counts 1, 8, 64, 256 are prefixes of that batch).
+"""
+import json
+import os
+import sys
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+
+
+def static_scale():
+    w = workloads.WORKLOADS["fused_add_rmsnorm_fp8_static_fp16_decode_x16384"]
+    d = workloads.make(w, rows=256, seed=0)
+    r = oracle.oracle().add_rmsnorm(w.dtype, d["x"], d["residual"], d["weight"], w.eps)
+    ymax = float(np.max(np.abs(r["y"])))
+    s = float(np.float32(4.0 * ymax / 448.0))
+    return {
+        "workload": w.name,
+        "calibration": "seed 0, rows 0..255, oracle fp64 y",
+        "max_abs_y": ymax,
+        "dequant_scale": s,
+        "multiplier": 448.0 / (4.0 * ymax),
+    }
+
+
+if __name__ == "__main__":
+    out = os.path.join(HERE, "fp16_16384_static_scale.json")
+    with open(out, "w") as f:
+        json.dump(static_scale(), f, indent=1)
+        f.write("\n")
+    print(open(out).read())

@@ -1,0 +1,146 @@
+"""The C ABI without a GPU: the library loads, exports every function
+include/arn.h declares, and rejects invalid arguments before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import residual_add_rmsnorm_amd as arn
+from residual_add_rmsnorm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "arn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(arn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_bound_functions():
+    assert header_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_function(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (arn_\w+)", out))
+    for name in header_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    assert lib.arn_abi_version() == 1
+
+
+def test_hip_imports_resolve_in_torch_runtime():
+    """libarn.so is loaded into processes whose HIP runtime is torch's
+    bundled libamdhip64; every HIP symbol it imports must exist there."""
+    imports = subprocess.run(["nm", "-D", "--undefined-only", _lib.LIB_PATH],
+                             capture_output=True, text=True, check=True).stdout
+    need = set(re.findall(r"U (_*hip\w+)@", imports))
+    assert "hipLaunchKernel" in need
+    torch_hip = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+    have = subprocess.run(["nm", "-D", "--defined-only", torch_hip],
+                          capture_output=True, text=True, check=True).stdout
+    have = set(re.findall(r" T (_*hip\w+)@", have))
+    assert need <= have, need - have
+
+
+def test_status_strings(lib):
+    assert lib.arn_status_str(0) == b"ok"
+    assert lib.arn_status_str(1) == b"invalid argument"
+    assert lib.arn_status_str(2) == b"unsupported shape or layout"
+    assert lib.arn_status_str(3) == b"kernel launch failed"
+    assert lib.arn_status_str(99) == b"unknown status"
+
+
+# Fake, never dereferenced device addresses: validation must fail first.
+P = 0x7F0000000000
+Q = 0x7F0000100000
+R = 0x7F0000200000
+S = 0x7F0000300000
+
+
+def _plain(lib, out=P, os_=64, x=Q, xs=64, w=None, eps=1e-6, rows=4, hidden=64, dt=0):
+    return lib.arn_rmsnorm(out, os_, x, xs, w, eps, rows, hidden, dt, None)
+
+
+def _fused(lib, out=P, os_=64, x=Q, xs=64, res=R, rs=64, w=None, eps=1e-6, rows=4, hidden=64,
+           dt=0):
+    return lib.arn_fused_add_rmsnorm(out, os_, x, xs, res, rs, w, eps, rows, hidden, dt, None)
+
+
+def _fp8(lib, fused, out=P, os_=64, scale=S, mode=0, x=Q, xs=64, res=R, rs=64, w=None, eps=1e-6,
+         rows=4, hidden=64, dt=0):
+    if fused:
+        return lib.arn_fused_add_rmsnorm_fp8(out, os_, scale, mode, x, xs, res, rs, w, eps, rows,
+                                             hidden, dt, None)
+    return lib.arn_rmsnorm_fp8(out, os_, scale, mode, x, xs, w, eps, rows, hidden, dt, None)
+
+
+@pytest.mark.parametrize("case", [
+    dict(dt=2), dict(dt=-1), dict(rows=-1), dict(hidden=0), dict(hidden=-5),
+    dict(xs=63), dict(os_=32), dict(eps=-1e-6), dict(eps=float("nan")), dict(eps=float("inf")),
+    dict(out=None), dict(x=None), dict(x=Q + 1), dict(out=P + 1), dict(w=S + 1),
+    dict(out=Q, os_=128, xs=64),
+])
+def test_rmsnorm_rejects(lib, case):
+    assert _plain(lib, **case) == _lib.EINVAL
+
+
+@pytest.mark.parametrize("case", [
+    dict(res=None), dict(rs=10), dict(res=Q), dict(res=P), dict(res=R + 1),
+])
+def test_fused_rejects(lib, case):
+    assert _fused(lib, **case) == _lib.EINVAL
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("case", [
+    dict(mode=2), dict(mode=-1), dict(scale=None), dict(scale=S + 2), dict(out=Q),
+    dict(dt=5), dict(os_=3),
+])
+def test_fp8_rejects(lib, fused, case):
+    assert _fp8(lib, fused, **case) == _lib.EINVAL
+
+
+def test_zero_rows_is_a_no_op(lib):
+    # no pointer is looked at and nothing is launched
+    assert _plain(lib, out=None, x=None, rows=0) == _lib.OK
+    assert _fused(lib, out=None, x=None, res=None, rows=0) == _lib.OK
+    assert _fp8(lib, True, out=None, x=None, res=None, scale=None, rows=0) == _lib.OK
+
+
+def test_set_tile(lib):
+    assert lib.arn_set_tile(3, 3) == _lib.EINVAL
+    assert lib.arn_set_tile(1, 16) == _lib.OK
+    assert lib.arn_set_tile(16, 8) == _lib.OK
+    assert lib.arn_set_tile(0, 0) == _lib.OK
+
+
+def test_binding_row_views():
+    t = torch.empty(4, 6, 100, dtype=torch.bfloat16)
+    assert arn._rows(t, "x") == (24, 100, 100)
+    padded = torch.empty(16, 128, dtype=torch.bfloat16)[:, :96]
+    assert arn._rows(padded, "x") == (16, 96, 128)
+    p3 = torch.empty(2, 8, 128, dtype=torch.bfloat16)[:, :, :96]
+    assert arn._rows(p3, "x") == (16, 96, 128)
+    assert arn._rows(torch.empty(96, dtype=torch.bfloat16), "x") == (1, 96, 96)
+    with pytest.raises(ValueError):
+        arn._rows(torch.empty(8, 96, dtype=torch.bfloat16).t(), "x")
+    with pytest.raises(ValueError):  # would need a copy to flatten
+        arn._rows(torch.empty(4, 8, 96, dtype=torch.bfloat16).transpose(0, 1), "x")
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(2, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        arn.rmsnorm(x, None, 1e-6)

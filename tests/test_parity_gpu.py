@@ -1,0 +1,410 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Every case feeds the same seeded inputs to both sides and applies the
+comparison rules in tests/_helpers.py.  Outputs start as NaN canaries, row
+padding starts as a NaN sentinel and one guard row follows the last row, so
+a kernel that drops stores, reads padding into a row's sum, or writes past
+the last row fails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from tests._helpers import (TORCH_DT, assert_codes_close, assert_scales_close, assert_y_close,
+                            bits, codes, dev, static_scale)
+
+pytestmark = pytest.mark.gpu
+
+CANARY16 = 0x7FC1  # a NaN in bf16 and in fp16
+CANARY8 = 0x7F     # the e4m3 NaN code
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import residual_add_rmsnorm_amd as arn
+
+    arn.set_tile(0, 0)
+    yield
+    arn.set_tile(0, 0)
+
+
+def _arn():
+    import residual_add_rmsnorm_amd as arn
+
+    return arn
+
+
+def run_case(orc, *, dtype, x, res, w, eps, hidden, fp8=None, s=None, out_stride=None,
+             alias_out=False):
+    """x, res: (rows, stride) uint16 host arrays (padding included);
+    w: (hidden,) uint16 or None.  Returns nothing; asserts parity."""
+    arn = _arn()
+    rows, stride = x.shape
+    out_stride = out_stride or stride
+    fused = res is not None
+
+    # device buffers with one guard row each
+    def with_guard(a, fill):
+        g = np.full((rows + 1, a.shape[1]), fill, np.uint16)
+        g[:rows] = a
+        return g
+
+    xd = dev(with_guard(x, W.PAD_SENTINEL), dtype)
+    rd = dev(with_guard(res, W.PAD_SENTINEL), dtype) if fused else None
+    wd = dev(w, dtype) if w is not None else None
+    xv = xd[:rows, :hidden]
+    rv = rd[:rows, :hidden] if fused else None
+
+    if fp8:
+        od = torch.full((rows + 1, out_stride), CANARY8, dtype=torch.uint8, device="cuda")
+        ov = od.view(torch.float8_e4m3fn)[:rows, :hidden]
+        if fp8 == "static":
+            sd = torch.tensor([s], dtype=torch.float32, device="cuda")
+            kw = dict(scale=sd)
+        else:
+            sd = torch.full((rows + 1,), float("nan"), dtype=torch.float32, device="cuda")
+            kw = dict(dynamic=True, scales_out=sd[:rows])
+        if fused:
+            arn.fused_add_rmsnorm_fp8(xv, rv, wd, eps, out=ov, **kw)
+        else:
+            arn.rmsnorm_fp8(xv, wd, eps, out=ov, **kw)
+    else:
+        if alias_out:
+            od, ov = xd, xv
+        else:
+            od = dev(np.full((rows + 1, out_stride), CANARY16, np.uint16), dtype)
+            ov = od[:rows, :hidden]
+        if fused:
+            arn.fused_add_rmsnorm(xv, rv, wd, eps, out=ov)
+        else:
+            arn.rmsnorm(xv, wd, eps, out=ov)
+    torch.cuda.synchronize()
+
+    mode = {None: O.FP8_NONE, "static": O.FP8_STATIC, "dynamic": O.FP8_DYNAMIC}[fp8]
+    ref = orc.add_rmsnorm(dtype, x, res, w, eps, hidden=hidden, fp8_mode=mode,
+                          static_scale=s or 0.0)
+
+    if fused:
+        rb = bits(rd)
+        assert np.array_equal(rb[:rows, :hidden], ref["r16"]), "stored residual not bit-exact"
+        assert np.all(rb[:rows, hidden:] == W.PAD_SENTINEL), "residual padding written"
+        assert np.all(rb[rows] == W.PAD_SENTINEL), "residual guard row written"
+    xb = bits(xd)
+    if not alias_out:
+        assert np.array_equal(xb[:rows], x), "x modified"
+    assert np.all(xb[rows] == W.PAD_SENTINEL), "x guard row written"
+
+    if fp8:
+        q = codes(od)
+        assert_codes_close(q[:rows, :hidden], ref["q"])
+        assert np.all(q[:rows, hidden:] == CANARY8), "output padding written"
+        assert np.all(q[rows] == CANARY8), "output guard row written"
+        if fp8 == "dynamic":
+            sc = sd.cpu().numpy()
+            assert_scales_close(sc[:rows], ref["scales"], dtype)
+            assert np.isnan(sc[rows]), "scale guard written"
+    else:
+        ob = bits(od)
+        assert_y_close(ob[:rows, :hidden], ref["y"], dtype)
+        if not alias_out:
+            assert np.all(ob[:rows, hidden:] == CANARY16), "output padding written"
+            assert np.all(ob[rows] == CANARY16), "output guard row written"
+
+
+def _random(dtype, rows, hidden, stride, seed, std=1.0):
+    rng = np.random.default_rng(seed)
+    a = np.full((rows, stride), W.PAD_SENTINEL, np.uint16)
+    a[:, :hidden] = W.to_bits((rng.standard_normal((rows, hidden)) * std).astype(np.float32), dtype)
+    return a
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at oracle-friendly sizes (several tiles + a ragged tail)
+# ---------------------------------------------------------------------------
+
+def _workload_case(orc, name, rows, **over):
+    w = W.WORKLOADS[name]
+    d = W.make(w, rows=rows)
+    fp8 = w.fp8
+    s = static_scale() if fp8 == "static" else None
+    run_case(orc, dtype=w.dtype, x=d["x"], res=d.get("residual"), w=d["weight"],
+             eps=w.eps, hidden=w.hidden, fp8=fp8, s=s, **over)
+
+
+def test_rmsnorm_bf16_64x4096(orc):
+    _workload_case(orc, "rmsnorm_bf16_64x4096", 64)
+
+
+@pytest.mark.parametrize("rows", [1, 77, 512])
+def test_fused_bf16_x8192(orc, rows):
+    _workload_case(orc, "fused_add_rmsnorm_bf16_4096x8192", rows)
+
+
+@pytest.mark.parametrize("rows", [1, 8, 64, 256])
+def test_fused_fp8_static_fp16_decode(orc, rows):
+    _workload_case(orc, "fused_add_rmsnorm_fp8_static_fp16_decode_x16384", rows)
+
+
+@pytest.mark.parametrize("rows", [3, 300])
+def test_fused_fp8_dynamic_bf16_x7168(orc, rows):
+    _workload_case(orc, "fused_add_rmsnorm_fp8_dynamic_bf16_32768x7168", rows)
+
+
+@pytest.mark.parametrize("name", ["fused_add_rmsnorm_bf16_65536x3840_stride4096",
+                                  "fused_add_rmsnorm_bf16_65536x2880_stride4096"])
+@pytest.mark.parametrize("rows", [5, 1029])
+def test_fused_strided_rows(orc, name, rows):
+    _workload_case(orc, name, rows)
+
+
+# ---------------------------------------------------------------------------
+# Shapes, layouts and degenerate cases
+# ---------------------------------------------------------------------------
+
+HIDDENS = [1, 2, 3, 7, 8, 16, 31, 64, 100, 511, 512, 513, 1000, 2880, 3840, 4095, 4096, 5120,
+           8192, 12288, 16384, 32768, 65536]
+
+
+@pytest.mark.parametrize("hidden", HIDDENS)
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_hidden_sweep_fused(orc, dtype, hidden):
+    rows = 3 if hidden > 8192 else 37
+    x = _random(dtype, rows, hidden, hidden, 1)
+    r = _random(dtype, rows, hidden, hidden, 2)
+    w = _random(dtype, 1, hidden, hidden, 3)[0] if hidden % 3 else None
+    run_case(orc, dtype=dtype, x=x, res=r, w=w, eps=1e-5, hidden=hidden)
+
+
+@pytest.mark.parametrize("hidden", [1, 24, 513, 4096, 7168, 16384])
+@pytest.mark.parametrize("fp8", ["static", "dynamic"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_hidden_sweep_fp8(orc, hidden, fp8, fused):
+    dtype = "bf16" if hidden % 2 else "fp16"
+    rows = 5
+    x = _random(dtype, rows, hidden, hidden, 4)
+    r = _random(dtype, rows, hidden, hidden, 5) if fused else None
+    w = _random(dtype, 1, hidden, hidden, 6)[0]
+    run_case(orc, dtype=dtype, x=x, res=r, w=w, eps=1e-6, hidden=hidden, fp8=fp8,
+             s=0.01 if fp8 == "static" else None)
+
+
+@pytest.mark.parametrize("rows", [1, 2, 255, 256, 257, 1025, 4099])
+def test_row_counts(orc, rows):
+    x = _random("bf16", rows, 1024, 1024, 7)
+    r = _random("bf16", rows, 1024, 1024, 8)
+    run_case(orc, dtype="bf16", x=x, res=r, w=None, eps=1e-6, hidden=1024)
+
+
+@pytest.mark.parametrize("hidden,stride", [(96, 100), (4096, 4104), (1000, 1001), (384, 385)])
+def test_odd_strides_fall_back_to_narrow_accesses(orc, hidden, stride):
+    x = _random("fp16", 9, hidden, stride, 9)
+    r = _random("fp16", 9, hidden, stride, 10)
+    w = _random("fp16", 1, hidden, hidden, 11)[0]
+    run_case(orc, dtype="fp16", x=x, res=r, w=w, eps=1e-5, hidden=hidden,
+             out_stride=stride + 3)
+    plan = _arn().last_plan()
+    assert "vec8" not in plan, plan
+
+
+def test_misaligned_base_pointer(orc):
+    arn = _arn()
+    rows, hidden = 6, 512
+    x = _random("bf16", rows, hidden, hidden, 12)
+    r = _random("bf16", rows, hidden, hidden, 13)
+    buf = torch.zeros(rows * hidden + 1, dtype=torch.bfloat16, device="cuda")
+    xv = buf[1:].view(rows, hidden)  # 2-byte aligned only
+    xv.copy_(dev(x, "bf16"))
+    rd = dev(r, "bf16")
+    out = arn.fused_add_rmsnorm(xv, rd, None, 1e-6)
+    torch.cuda.synchronize()
+    assert "vec1" in arn.last_plan()
+    ref = orc.add_rmsnorm("bf16", x, r, None, 1e-6)
+    assert np.array_equal(bits(rd), ref["r16"])
+    assert_y_close(bits(out), ref["y"], "bf16")
+
+
+def test_out_aliases_x(orc):
+    x = _random("bf16", 33, 2048, 2048, 14)
+    r = _random("bf16", 33, 2048, 2048, 15)
+    w = _random("bf16", 1, 2048, 2048, 16)[0]
+    run_case(orc, dtype="bf16", x=x, res=r, w=w, eps=1e-6, hidden=2048,
+             alias_out=True)
+
+
+def test_plain_out_aliases_x(orc):
+    x = _random("fp16", 7, 4096, 4096, 17)
+    run_case(orc, dtype="fp16", x=x, res=None, w=None, eps=1e-6, hidden=4096,
+             alias_out=True)
+
+
+def test_fp16_subnormal_inputs(orc):
+    rng = np.random.default_rng(18)
+    rows, hidden = 8, 1024
+    f = (rng.standard_normal((rows, hidden)) * 2.0**-18).astype(np.float32)  # mostly subnormal
+    x = W.to_bits(f, "fp16")
+    r = W.to_bits(-0.5 * f, "fp16")
+    run_case(orc, dtype="fp16", x=x, res=r, w=None, eps=0.0, hidden=hidden)
+
+
+@pytest.mark.parametrize("eps,scales", [
+    (1e-6, [2.0**-130, 2.0**-100, 1e-20, 1e-3]),   # subnormal and tiny rows: eps dominates
+    (0.0, [1e-10, 1e10, 1e15, 1.0]),                # squares stay in fp32 range
+])
+def test_bf16_tiny_and_huge_inputs(orc, eps, scales):
+    """fp32 accumulation: rows whose squares underflow fp32 (|r| below about
+    1e-23) are only meaningful with eps > 0, and rows whose sum of squares
+    overflows fp32 are outside the supported range; both ends are probed
+    inside those limits."""
+    rng = np.random.default_rng(19)
+    hidden = 2048
+    f = (rng.standard_normal((len(scales), hidden)) * np.array(scales)[:, None]).astype(np.float32)
+    x = W.to_bits(f, "bf16")
+    r = W.to_bits(f * np.float32(0.25), "bf16")
+    run_case(orc, dtype="bf16", x=x, res=r, w=None, eps=eps, hidden=hidden)
+
+
+def test_zero_rows_eps0_give_nan(orc):
+    x = np.zeros((4, 256), np.uint16)
+    run_case(orc, dtype="bf16", x=x, res=None, w=None, eps=0.0, hidden=256)
+
+
+def test_zero_rows_dynamic_fp8(orc):
+    x = _random("bf16", 6, 768, 768, 20)
+    r = _random("bf16", 6, 768, 768, 21)
+    x[2] = 0
+    r[2] = 0
+    x[4] = 0x8000  # -0 + -0 = -0
+    r[4] = 0x8000
+    run_case(orc, dtype="bf16", x=x, res=r, w=None, eps=1e-6, hidden=768,
+             fp8="dynamic")
+
+
+def test_fp8_static_saturates(orc):
+    x = _random("fp16", 4, 2048, 2048, 22, std=4.0)
+    run_case(orc, dtype="fp16", x=x, res=None, w=None, eps=1e-6, hidden=2048,
+             fp8="static", s=1.0 / 256)
+
+
+def test_zero_rows_launch_nothing():
+    arn = _arn()
+    x = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
+    r = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
+    out = arn.fused_add_rmsnorm(x, r, None, 1e-6)
+    assert out.shape == (0, 128)
+
+
+def test_3d_input_flattens(orc):
+    arn = _arn()
+    x = _random("bf16", 24, 640, 640, 23)
+    r = _random("bf16", 24, 640, 640, 24)
+    xd = dev(x, "bf16").view(4, 6, 640)
+    rd = dev(r, "bf16").view(4, 6, 640)
+    out = arn.fused_add_rmsnorm(xd, rd, None, 1e-6)
+    torch.cuda.synchronize()
+    ref = orc.add_rmsnorm("bf16", x, r, None, 1e-6)
+    assert np.array_equal(bits(rd).reshape(24, 640), ref["r16"])
+    assert_y_close(bits(out).reshape(24, 640), ref["y"], "bf16")
+
+
+def test_deterministic():
+    arn = _arn()
+    x = dev(_random("bf16", 300, 7168, 7168, 25), "bf16")
+    r0 = dev(_random("bf16", 300, 7168, 7168, 26), "bf16")
+    outs = []
+    for _ in range(2):
+        r = r0.clone()
+        q, s = arn.fused_add_rmsnorm_fp8(x, r, None, 1e-6, dynamic=True)
+        y = arn.fused_add_rmsnorm(x, r0.clone(), None, 1e-6)
+        torch.cuda.synchronize()
+        outs.append((codes(q), s.cpu().numpy(), bits(y), bits(r)))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+# ---------------------------------------------------------------------------
+# Every compiled 128-bit kernel shape, forced
+# ---------------------------------------------------------------------------
+
+TILES_VEC8 = [(1, 2), (1, 4), (1, 8), (1, 12), (1, 16), (2, 4), (2, 8), (2, 16), (4, 4), (4, 8),
+              (4, 16), (8, 4), (8, 8), (16, 2), (16, 4), (16, 8)]
+
+
+@pytest.mark.parametrize("wpr,nv", TILES_VEC8)
+@pytest.mark.parametrize("kind", ["fused", "dynamic"])
+def test_forced_tiles(orc, wpr, nv, kind):
+    arn = _arn()
+    cover = 64 * wpr * nv * 8
+    hidden = max(8, cover - 8 * 64 * wpr - 24) if cover > 1024 else cover - 16
+    x = _random("bf16", 11, hidden, hidden, 27)
+    r = _random("bf16", 11, hidden, hidden, 28)
+    w = _random("bf16", 1, hidden, hidden, 29)[0]
+    arn.set_tile(wpr, nv)
+    try:
+        run_case(orc, dtype="bf16", x=x, res=r, w=w, eps=1e-6, hidden=hidden,
+                 fp8="dynamic" if kind == "dynamic" else None)
+        assert f"wpr{wpr}/nv{nv}/" in arn.last_plan()
+    finally:
+        arn.set_tile(0, 0)
+
+
+def test_forced_tile_too_small_is_unsupported():
+    arn = _arn()
+    x = torch.zeros(2, 4096, dtype=torch.bfloat16, device="cuda")
+    arn.set_tile(1, 2)
+    try:
+        with pytest.raises(arn.ArnError) as e:
+            arn.rmsnorm(x, None, 1e-6)
+        assert e.value.status == 2
+    finally:
+        arn.set_tile(0, 0)
+
+
+# ---------------------------------------------------------------------------
+# The e4m3 conversion, exhaustively, through the ABI
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("log2s", [0, -4, 3])
+def test_e4m3_conversion_every_16bit_weight(orc, dtype, log2s):
+    """x = 1 in every channel and eps = 0 make the normaliser exactly 1, so
+    y = w and the codes are e4m3(w / s) for every one of the 65536 16-bit
+    weight patterns at once (hidden = 65536).  s is a power of two, so w / s
+    is exact and the GPU's rounding and saturation must match the oracle's
+    encoder code for code (NaN weights aside)."""
+    arn = _arn()
+    hidden = 65536
+    one = 0x3F80 if dtype == "bf16" else 0x3C00
+    x = np.full((1, hidden), one, np.uint16)
+    w = np.arange(hidden, dtype=np.uint32).astype(np.uint16)
+    xd, wd = dev(x, dtype), dev(w, dtype)
+    y = arn.rmsnorm(xd, wd, 0.0)
+    s = 2.0**log2s
+    q, _ = arn.rmsnorm_fp8(xd, wd, 0.0, scale=torch.tensor([s], device="cuda"))
+    torch.cuda.synchronize()
+    ref = orc.add_rmsnorm(dtype, x, None, w, 0.0, fp8_mode=O.FP8_STATIC, static_scale=s)
+    finite = np.isfinite(ref["y"][0])
+    # normaliser exactly 1: y reproduces the weight bit for bit
+    assert np.array_equal(bits(y)[0][finite], w[finite])
+    qg = codes(q)[0]
+    mism = np.flatnonzero((qg != ref["q"][0]) & finite)
+    assert mism.size == 0, (f"{mism.size} codes differ; first w={w[mism[0]]:#06x} "
+                            f"gpu={qg[mism[0]]:#04x} ref={ref['q'][0][mism[0]]:#04x}")
+    # +-Inf weights saturate
+    inf = np.isinf(ref["y"][0])
+    assert np.all((qg[inf] & 0x7F) == 0x7E)
+
+
+def test_e4m3_dynamic_every_finite_bf16_weight(orc):
+    arn = _arn()
+    w = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = torch.from_numpy(w.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    w = w[np.isfinite(vals) & (np.abs(vals) < 1e30)]
+    w = w[: (w.size // 8) * 8]
+    hidden = w.size
+    x = np.full((1, hidden), 0x3F80, np.uint16)
+    run_case(orc, dtype="bf16", x=x, res=None, w=w, eps=0.0, hidden=hidden,
+             fp8="dynamic")

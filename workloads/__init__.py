@@ -20,6 +20,8 @@ write-up's untuned-GEMM table).
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -124,11 +126,16 @@ def _normal_rows(seed, stream, row0, row1, hidden, std):
     """float32 N(0, std^2) draws for rows [row0, row1), block-keyed."""
     out = np.empty((row1 - row0, hidden), np.float32)
     b0, b1 = row0 // BLOCK_ROWS, (row1 - 1) // BLOCK_ROWS
-    for b in range(b0, b1 + 1):
+
+    def fill(b):
         blk = _rng(seed, stream, b).standard_normal((BLOCK_ROWS, hidden), dtype=np.float32)
         lo = max(row0, b * BLOCK_ROWS)
         hi = min(row1, (b + 1) * BLOCK_ROWS)
         out[lo - row0:hi - row0] = blk[lo - b * BLOCK_ROWS:hi - b * BLOCK_ROWS]
+
+    # Blocks are independent streams, so they can be drawn in parallel.
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+        list(ex.map(fill, range(b0, b1 + 1)))
     if std != 1.0:
         out *= np.float32(std)
     return out
