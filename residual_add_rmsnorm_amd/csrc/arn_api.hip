@@ -99,9 +99,20 @@ int choose_vec(const Request& r) {
   return 1;
 }
 
-// Kernel shape.  Many rows: few waves per row and long per-lane vectors
-// (no barrier; the chip fills with rows).  Few rows (decode): more waves
-// per row so each row finishes sooner.
+int pow2_ceil(int64_t v) {
+  int p = 1;
+  while (p < v && p < (1 << 20)) p *= 2;
+  return p;
+}
+
+// Kernel shape.  A row is split over `wpr` waves so that each lane holds at
+// most a few vectors: with many rows, rows of four waves (256-thread blocks)
+// and up to 4 vectors per lane keep VGPR use near 60, so eight waves fit per
+// SIMD and many rows are in flight per CU.  With few rows (decode), up to 16
+// waves share a row and each lane holds at most 2 vectors, so each row
+// finishes sooner.  Among the compiled tiles of that wave count, the one
+// with the fewest per-lane vectors that still covers the row is taken; if
+// there is none, any tile that covers the row is.
 const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t rows, int cus) {
   const int forced = g_forced_tile.load(std::memory_order_relaxed);
   if (forced != 0) {
@@ -115,20 +126,27 @@ const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t r
     return nullptr;
   }
   const bool many_rows = rows >= (int64_t)4 * cus;
-  const int targets[2] = {many_rows ? 16 : 4, 1 << 20};
-  for (int target : targets) {
-    for (int wpr = 1; wpr <= 16; wpr *= 2) {
-      const int64_t per_lane = (nvec + 64 * wpr - 1) / (64 * wpr);
-      if (per_lane > target) continue;
-      const Tile* best = nullptr;
-      for (int i = 0; i < table->count; ++i) {
-        const Tile& t = table->tiles[i];
-        if (t.vec == vec && t.wpr == wpr && t.nv >= per_lane && (!best || t.nv < best->nv)) {
-          best = &t;
-        }
+  const int64_t target_nv = many_rows ? 4 : 2;
+  const int wpr_floor = many_rows ? 4 : 16;
+  int wpr = pow2_ceil((nvec + 64 * target_nv - 1) / (64 * target_nv));
+  const int need1 = pow2_ceil((nvec + 63) / 64);  // waves if each lane held one vector
+  if (wpr < wpr_floor) wpr = need1 < wpr_floor ? need1 : wpr_floor;
+  if (wpr > 16) wpr = 16;
+
+  const Tile* best = nullptr;
+  for (int w = wpr; w <= 16 && !best; w *= 2) {
+    const int64_t per_lane = (nvec + 64 * w - 1) / (64 * w);
+    for (int i = 0; i < table->count; ++i) {
+      const Tile& t = table->tiles[i];
+      if (t.vec == vec && t.wpr == w && t.nv >= per_lane && (!best || t.nv < best->nv)) {
+        best = &t;
       }
-      if (best) return best;
     }
+  }
+  if (best) return best;
+  for (int i = 0; i < table->count; ++i) {  // any covering tile
+    const Tile& t = table->tiles[i];
+    if (t.vec == vec && (int64_t)64 * t.wpr * t.nv >= nvec) return &t;
   }
   return nullptr;
 }

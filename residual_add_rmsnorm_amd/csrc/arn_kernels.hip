@@ -215,47 +215,53 @@ __device__ __forceinline__ float wave_max(float v) {
 // ---------------------------------------------------------------------------
 constexpr int kRsrcWord3 = 0x00020000;
 
+// Cache policy of the memory instructions.  x, residual and out are each
+// touched once per call, so they stream with the non-temporal hint (nt);
+// the weight, read by every row, stays cacheable.
+constexpr int kCacheDefault = 0;
+constexpr int kCacheStream = 2;  // nt
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            kRsrcWord3);
 }
 
-template <int VEC>
+template <int VEC, int CP>
 __device__ __forceinline__ Raw<VEC> load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (VEC == 8) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP);
   } else if constexpr (VEC == 4) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, CP);
   } else if constexpr (VEC == 2) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, CP);
   } else {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, CP);
   }
 }
 
 template <int VEC>
 __device__ __forceinline__ void store16(Raw<VEC> v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (VEC == 8) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kCacheStream);
   } else if constexpr (VEC == 4) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kCacheStream);
   } else if constexpr (VEC == 2) {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kCacheStream);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, kCacheStream);
   }
 }
 
 template <int VEC>
 __device__ __forceinline__ void store8(Fp8Raw<VEC> v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (VEC == 8) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kCacheStream);
   } else if constexpr (VEC == 4) {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kCacheStream);
   } else if constexpr (VEC == 2) {
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, kCacheStream);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b8(v, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8(v, r, (int)off, 0, kCacheStream);
   }
 }
 
@@ -308,15 +314,15 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
     Raw<VEC> rr[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      xr[k] = load16<VEC>(xrs, off16 + k * kStep16);
-      if constexpr (kRes) rr[k] = load16<VEC>(rrs, off16 + k * kStep16);
+      xr[k] = load16<VEC, kCacheStream>(xrs, off16 + k * kStep16);
+      if constexpr (kRes) rr[k] = load16<VEC, kCacheStream>(rrs, off16 + k * kStep16);
     }
     // The weight (shared by all rows; an L2 hit after the first blocks).
     Raw<VEC> wr[NV];
     if (a.w != nullptr) {
       const __amdgpu_buffer_rsrc_t wrs = row_rsrc(a.w, row_bytes16);
 #pragma unroll
-      for (int k = 0; k < NV; ++k) wr[k] = load16<VEC>(wrs, off16 + k * kStep16);
+      for (int k = 0; k < NV; ++k) wr[k] = load16<VEC, kCacheDefault>(wrs, off16 + k * kStep16);
     } else {
 #pragma unroll
       for (int k = 0; k < NV; ++k) wr[k] = ones<DT, VEC>();
@@ -411,14 +417,15 @@ constexpr int rows_per_block(int wpr) { return wpr >= 4 ? 1 : 4 / wpr; }
 
 static const arn::Tile kTiles[] = {
     // 128-bit accesses (hidden % 8 == 0, 16-byte aligned rows)
-    ARN_TILE(8, 1, 2), ARN_TILE(8, 1, 4), ARN_TILE(8, 1, 8), ARN_TILE(8, 1, 12),
-    ARN_TILE(8, 1, 16), ARN_TILE(8, 2, 4), ARN_TILE(8, 2, 8), ARN_TILE(8, 2, 16), ARN_TILE(8, 4, 4),
-    ARN_TILE(8, 4, 8), ARN_TILE(8, 4, 16), ARN_TILE(8, 8, 4), ARN_TILE(8, 8, 8),
-    ARN_TILE(8, 16, 2), ARN_TILE(8, 16, 4), ARN_TILE(8, 16, 8),
+    ARN_TILE(8, 1, 2), ARN_TILE(8, 1, 4), ARN_TILE(8, 1, 8), ARN_TILE(8, 1, 16),
+    ARN_TILE(8, 2, 2), ARN_TILE(8, 2, 4), ARN_TILE(8, 2, 8),
+    ARN_TILE(8, 4, 1), ARN_TILE(8, 4, 2), ARN_TILE(8, 4, 3), ARN_TILE(8, 4, 4), ARN_TILE(8, 4, 8),
+    ARN_TILE(8, 8, 1), ARN_TILE(8, 8, 2), ARN_TILE(8, 8, 4), ARN_TILE(8, 8, 8),
+    ARN_TILE(8, 16, 1), ARN_TILE(8, 16, 2), ARN_TILE(8, 16, 4), ARN_TILE(8, 16, 8),
     // narrower accesses for rows that are not 16-byte aligned
-    ARN_TILE(4, 1, 4), ARN_TILE(4, 1, 16), ARN_TILE(4, 4, 16), ARN_TILE(4, 16, 16),
-    ARN_TILE(2, 1, 4), ARN_TILE(2, 1, 16), ARN_TILE(2, 4, 16), ARN_TILE(2, 16, 16),
-    ARN_TILE(1, 1, 4), ARN_TILE(1, 1, 16), ARN_TILE(1, 4, 16), ARN_TILE(1, 16, 16),
+    ARN_TILE(4, 1, 4), ARN_TILE(4, 4, 4), ARN_TILE(4, 16, 4), ARN_TILE(4, 16, 16),
+    ARN_TILE(2, 1, 4), ARN_TILE(2, 4, 4), ARN_TILE(2, 16, 4), ARN_TILE(2, 16, 16),
+    ARN_TILE(1, 1, 4), ARN_TILE(1, 4, 4), ARN_TILE(1, 16, 4), ARN_TILE(1, 16, 16),
 };
 
 extern const arn::TileTable ARN_TABLE_NAME(ARN_KIND, ARN_DT) = {
