@@ -281,7 +281,20 @@ def main() -> int:
     ap.add_argument("--workload", default=None,
                     help="workload name, or 'all' (default: the headline workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run plain device copies of a known size (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --calibrate-copy` into profiles/traffic_<workload>.json")
+    ap.add_argument("--pmc-command", default="", help="command line recorded with the summary")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        import workloads
+
+        summarize_pmc(args.workload or workloads.HEADLINE, *args.summarize_pmc,
+                      command=args.pmc_command)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -306,7 +319,66 @@ def main() -> int:
         line = bench_workload(n, args.steps, args.warmup,
                               with_cpu=not args.no_cpu_baseline and n == names[0])
         print(json.dumps(line), flush=True)
+    if args.calibrate_copy:
+        copy_calibration()
     return 0
+
+
+COPY_BYTES = 256 * 1024 * 1024
+COPY_REPS = 10
+
+
+def _pmc_rows(path: str, counter: str):
+    import csv
+
+    with open(path) as f:
+        return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+
+
+def summarize_pmc(name: str, fetch_csv: str, write_csv: str, command: str = "") -> dict:
+    """HBM traffic of the operator's kernel per launch, from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter
+    reads for the plain device copies of COPY_BYTES that close the run."""
+    import workloads
+
+    w = workloads.WORKLOADS[name]
+    out = {"workload": name, "kernel_source_sha": kernel_source_sha(),
+           "algorithmic_bytes_per_launch": w.algorithmic_bytes(), "command": command}
+    for counter, path, key in (("FETCH_SIZE", fetch_csv, "read"), ("WRITE_SIZE", write_csv, "write")):
+        rows = _pmc_rows(path, counter)
+        kern = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].startswith("void arn::")]
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copyBuffer" in r["Kernel_Name"]][-COPY_REPS:]
+        kib = sum(kern) / len(kern)
+        copy_kib = sum(copies) / len(copies)
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        out[f"{key}_counter_kib_per_launch"] = round(kib, 3)
+        out[f"{key}_copy_counter_kib"] = round(copy_kib, 3)
+        out[f"{key}_scale_factor"] = round(factor, 6)
+        out[f"{key}_bytes_per_launch"] = int(round(kib * 1024.0 * factor))
+        out[f"{key}_dispatches"] = len(kern)
+    out["traffic_bytes_per_launch"] = out["read_bytes_per_launch"] + out["write_bytes_per_launch"]
+    out["traffic_over_algorithmic"] = round(out["traffic_bytes_per_launch"] /
+                                            out["algorithmic_bytes_per_launch"], 5)
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    log(json.dumps(out, indent=1))
+    return out
+
+
+def copy_calibration(reps: int = 10) -> None:
+    """Plain device-to-device copies of COPY_BYTES (read COPY_BYTES, write
+    COPY_BYTES): the reference that scales the HBM byte counters."""
+    import torch
+
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = [torch.empty_like(src) for _ in range(2)]
+    for i in range(reps):
+        dst[i % 2].copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} copies of {COPY_BYTES} bytes")
 
 
 if __name__ == "__main__":
