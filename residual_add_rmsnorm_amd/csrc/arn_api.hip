@@ -105,14 +105,15 @@ int pow2_ceil(int64_t v) {
   return p;
 }
 
-// Kernel shape.  A row is split over `wpr` waves so that each lane holds at
-// most a few vectors: with many rows, rows of four waves (256-thread blocks)
-// and up to 4 vectors per lane keep VGPR use near 60, so eight waves fit per
-// SIMD and many rows are in flight per CU.  With few rows (decode), up to 16
-// waves share a row and each lane holds at most 2 vectors, so each row
-// finishes sooner.  Among the compiled tiles of that wave count, the one
-// with the fewest per-lane vectors that still covers the row is taken; if
-// there is none, any tile that covers the row is.
+// Kernel shape.  A row is split over `wpr` waves so that each lane holds
+// only a few vectors.  Measured on MI355X: with many rows, rows of eight
+// waves (512-thread blocks) holding at most two 128-bit vectors per lane
+// stream best (about 40 VGPRs, eight waves per SIMD); one-wave rows that
+// keep a whole 8192-wide row in registers run 20-25% slower.  With few rows
+// (decode) eight waves per row with up to four vectors per lane finish each
+// row soonest.  Among the compiled tiles of the chosen wave count, the one
+// with the fewest per-lane vectors that covers the row (and at least
+// `min_nv`) is taken; failing that, any tile that covers the row.
 const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t rows, int cus) {
   const int forced = g_forced_tile.load(std::memory_order_relaxed);
   if (forced != 0) {
@@ -126,8 +127,9 @@ const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t r
     return nullptr;
   }
   const bool many_rows = rows >= (int64_t)4 * cus;
-  const int64_t target_nv = many_rows ? 4 : 2;
-  const int wpr_floor = many_rows ? 4 : 16;
+  const int64_t target_nv = many_rows ? 2 : 4;
+  const int64_t min_nv = many_rows ? 2 : 1;
+  const int wpr_floor = 8;
   int wpr = pow2_ceil((nvec + 64 * target_nv - 1) / (64 * target_nv));
   const int need1 = pow2_ceil((nvec + 63) / 64);  // waves if each lane held one vector
   if (wpr < wpr_floor) wpr = need1 < wpr_floor ? need1 : wpr_floor;
@@ -135,7 +137,8 @@ const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t r
 
   const Tile* best = nullptr;
   for (int w = wpr; w <= 16 && !best; w *= 2) {
-    const int64_t per_lane = (nvec + 64 * w - 1) / (64 * w);
+    int64_t per_lane = (nvec + 64 * w - 1) / (64 * w);
+    if (per_lane < min_nv) per_lane = min_nv;
     for (int i = 0; i < table->count; ++i) {
       const Tile& t = table->tiles[i];
       if (t.vec == vec && t.wpr == w && t.nv >= per_lane && (!best || t.nv < best->nv)) {
