@@ -1,0 +1,86 @@
+"""The library on non-default streams and inside HIP graphs.
+
+Each call enqueues one kernel on torch's current stream, so it must work on
+any stream and be capturable.  A captured fused call updates the residual in
+place, so replay k must equal k applications of the operator; every replay is
+checked against the oracle iterated on the CPU, with eager work and
+synchronisations between replays.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from tests._helpers import assert_codes_close, assert_y_close, bits, codes, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def _inputs(rows=96, hidden=4096, seed=40):
+    rng = np.random.default_rng(seed)
+    x = W.to_bits(rng.standard_normal((rows, hidden)).astype(np.float32), "bf16")
+    r = W.to_bits(rng.standard_normal((rows, hidden)).astype(np.float32), "bf16")
+    w = W.to_bits((1 + 0.1 * rng.standard_normal(hidden)).astype(np.float32), "bf16")
+    return x, r, w
+
+
+def test_non_default_stream(orc):
+    import residual_add_rmsnorm_amd as arn
+
+    x, r, w = _inputs()
+    s = torch.cuda.Stream()
+    xd, rd, wd = dev(x, "bf16"), dev(r, "bf16"), dev(w, "bf16")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        y = arn.fused_add_rmsnorm(xd, rd, wd, 1e-6)
+    s.synchronize()
+    ref = orc.add_rmsnorm("bf16", x, r, w, 1e-6)
+    assert np.array_equal(bits(rd), ref["r16"])
+    assert_y_close(bits(y), ref["y"], "bf16")
+
+
+def test_graph_replays_match_iterated_oracle(orc):
+    import residual_add_rmsnorm_amd as arn
+
+    x, r, w = _inputs()
+    xd, rd, wd = dev(x, "bf16"), dev(r, "bf16"), dev(w, "bf16")
+    out = torch.empty_like(xd)
+    q = torch.empty(xd.shape, dtype=torch.float8_e4m3fn, device="cuda")
+    sc = torch.empty(xd.shape[0], dtype=torch.float32, device="cuda")
+    rd2 = rd.clone()
+    # warm up on a side stream, as graph capture requires
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        tmp = rd.clone()
+        arn.fused_add_rmsnorm(xd, tmp, wd, 1e-6, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        arn.fused_add_rmsnorm(xd, rd, wd, 1e-6, out=out)
+        arn.fused_add_rmsnorm_fp8(xd, rd2, wd, 1e-6, dynamic=True, out=q, scales_out=sc)
+
+    res_ref, res_ref2 = r.copy(), r.copy()
+    for k in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        ref = orc.add_rmsnorm("bf16", x, res_ref, w, 1e-6)
+        ref2 = orc.add_rmsnorm("bf16", x, res_ref2, w, 1e-6, fp8_mode=O.FP8_DYNAMIC)
+        res_ref, res_ref2 = ref["r16"], ref2["r16"]
+        assert np.array_equal(bits(rd), res_ref), f"replay {k}: residual"
+        assert_y_close(bits(out), ref["y"], "bf16", what=f"replay {k}: y")
+        assert np.array_equal(bits(rd2), res_ref2), f"replay {k}: fp8 residual"
+        assert_codes_close(codes(q), ref2["q"], what=f"replay {k}: codes")
+        # eager work between replays
+        junk = torch.randn(1024, 1024, device="cuda") @ torch.randn(1024, 1024, device="cuda")
+        torch.cuda.synchronize()
+        del junk
