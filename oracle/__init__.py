@@ -75,6 +75,16 @@ def bind(lib_path: str) -> ctypes.CDLL:
         ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float),
     ]
     lib.orc_add_rmsnorm.restype = ctypes.c_int
+    lib.orc_silu.argtypes = [ctypes.c_double]
+    lib.orc_silu.restype = ctypes.c_double
+    lib.orc_silu_and_mul.argtypes = [
+        ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+        u16p, ctypes.c_int64, u16p, ctypes.c_int64,
+        ctypes.POINTER(ctypes.c_double), u16p,
+        ctypes.c_int, ctypes.c_float,
+        ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float),
+    ]
+    lib.orc_silu_and_mul.restype = ctypes.c_int
     return lib
 
 
@@ -152,6 +162,61 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected its arguments")
         out = {"r16": r16, "y16": y16}
+        if want_y:
+            out["y"] = y
+        if q is not None:
+            out["q"] = q
+        if scales is not None:
+            out["scales"] = scales
+        return out
+
+    def silu(self, g: float) -> float:
+        return self.c.orc_silu(g)
+
+    def silu_and_mul(self, dtype, x, d=None, fp8_mode=FP8_NONE, static_scale=0.0, want_y=True):
+        """SwiGLU on a 2-D uint16 array whose row holds the gate in columns
+        [0, d) and up in [d, 2d) (row stride = shape[1]; d defaults to half
+        of it).  Returns a dict with y (float64), y16, and q / scales."""
+        if isinstance(dtype, str):
+            dtype = DTYPES[dtype]
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        rows, stride = x.shape
+        d = stride // 2 if d is None else int(d)
+        assert 2 * d <= stride
+        self._keep = x
+        base = x.ctypes.data
+        gate = ctypes.cast(base, ctypes.POINTER(ctypes.c_uint16))
+        up = ctypes.cast(base + 2 * d, ctypes.POINTER(ctypes.c_uint16))
+        return self._silu_and_mul(dtype, rows, d, gate, stride, up, stride, fp8_mode,
+                                  static_scale, want_y)
+
+    def silu_and_mul_split(self, dtype, gate, up, d=None, fp8_mode=FP8_NONE, static_scale=0.0):
+        """SwiGLU with the gate and up halves in two separate 2-D arrays,
+        each with its own row stride (shape[1])."""
+        if isinstance(dtype, str):
+            dtype = DTYPES[dtype]
+        gate = np.ascontiguousarray(gate, dtype=np.uint16)
+        up = np.ascontiguousarray(up, dtype=np.uint16)
+        assert gate.shape[0] == up.shape[0]
+        d = min(gate.shape[1], up.shape[1]) if d is None else int(d)
+        self._keep = (gate, up)
+        return self._silu_and_mul(dtype, gate.shape[0], d, _ptr(gate, ctypes.c_uint16),
+                                  gate.shape[1], _ptr(up, ctypes.c_uint16), up.shape[1],
+                                  fp8_mode, static_scale, True)
+
+    def _silu_and_mul(self, dtype, rows, d, gate, gate_stride, up, up_stride, fp8_mode,
+                      static_scale, want_y):
+        y = np.empty((rows, d), np.float64) if want_y else None
+        y16 = np.empty((rows, d), np.uint16)
+        q = np.empty((rows, d), np.uint8) if fp8_mode != FP8_NONE else None
+        scales = np.empty((rows,), np.float32) if fp8_mode == FP8_DYNAMIC else None
+        rc = self.c.orc_silu_and_mul(dtype, rows, d, gate, gate_stride, up, up_stride,
+                                     _ptr(y, ctypes.c_double), _ptr(y16, ctypes.c_uint16),
+                                     fp8_mode, float(static_scale),
+                                     _ptr(q, ctypes.c_uint8), _ptr(scales, ctypes.c_float))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        out = {"y16": y16}
         if want_y:
             out["y"] = y
         if q is not None:

@@ -19,6 +19,10 @@
  *     bf16) activations, weight of the same dtype or None, and no
  *     variance-size override -- so the mean runs over all `hidden`
  *     channels, and a missing weight means w = 1.
+ *   - The second kernel of that article fuses the SwiGLU activation with
+ *     the FP8 cast.  SwiGLU is Shazeer, "GLU Variants Improve
+ *     Transformer" (2020): Swish_1(x W) * (x V), Swish_1 = SiLU; here the
+ *     two projections arrive as the gate and up halves of one row.
  *   - The FP8 format is OCP E4M3FN (bias 7, 3 mantissa bits, max 448, no
  *     infinities, NaN = S.1111.111).  "MI210 LLM Stack", key insight 4,
  *     counts 254 non-NaN e4m3 byte patterns, which is that format.
@@ -379,6 +383,73 @@ int orc_add_rmsnorm(int dtype, int64_t rows, int64_t hidden,
 
     free(r16);
     free(r);
+    free(y);
+    free(q);
+    return 0;
+}
+
+/* --------------------------------------------------------------------- */
+/* SwiGLU: y = silu(gate) * up.                                          */
+/* --------------------------------------------------------------------- */
+
+/* silu(g) = g * sigmoid(g) = g / (1 + exp(-g)). */
+double orc_silu(double g)
+{
+    return g / (1.0 + exp(-g));
+}
+
+int orc_silu_and_mul(int dtype, int64_t rows, int64_t d,
+                     const uint16_t *gate, int64_t gate_stride,
+                     const uint16_t *up, int64_t up_stride,
+                     double *y_out, uint16_t *y16_out,
+                     int fp8_mode, float static_scale,
+                     uint8_t *q_out, float *scale_out)
+{
+    double *y;
+    uint8_t *q;
+    int64_t i, j;
+
+    if ((dtype != ORC_BF16 && dtype != ORC_FP16) || rows < 0 || d <= 0 ||
+        gate == NULL || up == NULL || gate_stride < d || up_stride < d ||
+        (fp8_mode != ORC_FP8_NONE && fp8_mode != ORC_FP8_STATIC &&
+         fp8_mode != ORC_FP8_DYNAMIC)) {
+        return -1;
+    }
+    y = (double *)malloc((size_t)d * sizeof(double));
+    q = (uint8_t *)malloc((size_t)d);
+    if (!y || !q) {
+        free(y);
+        free(q);
+        return -1;
+    }
+
+    for (i = 0; i < rows; i++) {
+        float scale = 0.0f;
+        for (j = 0; j < d; j++) {
+            double g = orc_decode16(dtype, gate[i * gate_stride + j]);
+            double u = orc_decode16(dtype, up[i * up_stride + j]);
+            y[j] = orc_silu(g) * u;
+        }
+        if (fp8_mode == ORC_FP8_STATIC) {
+            quant_static_row(d, y, static_scale, q);
+        } else if (fp8_mode == ORC_FP8_DYNAMIC) {
+            scale = quant_dynamic_row(d, y, q);
+        }
+        for (j = 0; j < d; j++) {
+            if (y_out) {
+                y_out[i * d + j] = y[j];
+            }
+            if (y16_out) {
+                y16_out[i * d + j] = orc_encode16(dtype, y[j]);
+            }
+            if (q_out && fp8_mode != ORC_FP8_NONE) {
+                q_out[i * d + j] = q[j];
+            }
+        }
+        if (scale_out && fp8_mode == ORC_FP8_DYNAMIC) {
+            scale_out[i] = scale;
+        }
+    }
     free(y);
     free(q);
     return 0;

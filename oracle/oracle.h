@@ -64,6 +64,22 @@ int orc_add_rmsnorm(int dtype, int64_t rows, int64_t hidden,
                     int fp8_mode, float static_scale,
                     uint8_t *q_out, float *scale_out);
 
+/*
+ * SwiGLU activation of a gate/up pair (Shazeer, "GLU Variants Improve
+ * Transformer", 2020, the FFN_SwiGLU definition with Swish_1 = SiLU):
+ *     y_j = silu(g_j) * u_j,   silu(g) = g / (1 + exp(-g)).
+ * Row i reads gate[i*gate_stride + j] and up[i*up_stride + j], j < d (the
+ * usual layout passes up = gate + d inside one [rows, 2d] tensor).
+ * Outputs as in orc_add_rmsnorm (dense, row stride d; each may be NULL).
+ */
+double orc_silu(double g);
+int orc_silu_and_mul(int dtype, int64_t rows, int64_t d,
+                     const uint16_t *gate, int64_t gate_stride,
+                     const uint16_t *up, int64_t up_stride,
+                     double *y_out, uint16_t *y16_out,
+                     int fp8_mode, float static_scale,
+                     uint8_t *q_out, float *scale_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ import pytest
 
 import oracle as O
 from tests import test_oracle_pins as pins
+from tests import test_oracle_swiglu_pins as swiglu_pins
 
 MUTANTS = {
     "dropped_eps": ("sqrt(ms + (double)eps)", "sqrt(ms)"),
@@ -34,12 +35,20 @@ MUTANTS = {
     "square_not_squared": ("sum += r[j] * r[j];", "sum += fabs(r[j]);"),
     "e4m3_bias": ("ldexp((double)(8 + m), e - 7 - 3)", "ldexp((double)(8 + m), e - 8 - 3)"),
     "overflow_not_inf": ("if (e + f.bias >= emax_field) {", "if (e + f.bias > emax_field) {"),
+    "silu_sign": ("return g / (1.0 + exp(-g));", "return g / (1.0 + exp(g));"),
+    "silu_no_sigmoid": ("return g / (1.0 + exp(-g));", "return g;"),
+    "gate_up_swapped": ("y[j] = orc_silu(g) * u;", "y[j] = orc_silu(u) * g;"),
+    "up_row_stride": ("up[i * up_stride + j]", "up[i * gate_stride + j + 0 * up_stride]"),
+    "glu_dynamic_scale_of_u": ("double u = orc_decode16(dtype, up[i * up_stride + j]);",
+                               "double u = orc_decode16(dtype, up[i * up_stride + j]) * 2.0;"),
 }
 
 
 def _pin_functions():
     fns = []
-    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+    members = inspect.getmembers(pins, inspect.isfunction) + \
+        inspect.getmembers(swiglu_pins, inspect.isfunction)
+    for name, fn in members:
         if not name.startswith("test_"):
             continue
         params = inspect.signature(fn).parameters
@@ -91,6 +100,6 @@ def test_mutant_is_caught(tmp_path, name):
 
 
 def test_unmutated_copy_passes_every_pin(tmp_path):
-    orc = O.Oracle(_compile_mutant(tmp_path, "none", "int64_t i, j;", "int64_t i, j;"))
+    orc = O.Oracle(_compile_mutant(tmp_path, "none", "#include <stdlib.h>", "#include <stdlib.h>"))
     for fname, fn, kwargs in _pin_functions():
         fn(orc=orc, **kwargs)
