@@ -32,6 +32,8 @@ METRIC = ("achieved HBM GB/s (% of MI355X peak) for fused add+RMSNorm(+fp8); "
           "µs/call at decode")
 MALL_BYTES = 256 * 1024 * 1024
 KERNEL_SOURCES = ["residual_add_rmsnorm_amd/csrc/arn_kernels.hip",
+                  "residual_add_rmsnorm_amd/csrc/arn_glu.hip",
+                  "residual_add_rmsnorm_amd/csrc/arn_device.h",
                   "residual_add_rmsnorm_amd/csrc/arn_api.hip",
                   "residual_add_rmsnorm_amd/csrc/arn_internal.h"]
 
@@ -65,25 +67,26 @@ class Batch:
         self.rows = rows or w.rows
         d = workloads.make(w, rows=self.rows)
         H, S = w.hidden, w.stride
+        OS = H if w.is_glu else S  # output row stride: dense for SwiGLU
         self.x, self.res, self.out, self.scale = [], [], [], []
         x0 = dev(d["x"], w.dtype)
         r0 = dev(d["residual"], w.dtype) if w.has_residual else None
-        self.weight = dev(d["weight"], w.dtype)
+        self.weight = dev(d["weight"], w.dtype) if d["weight"] is not None else None
         for _ in range(sets):
-            self.x.append(x0.clone()[:, :H])
+            self.x.append(x0.clone()[:, :w.in_width])
             self.res.append(r0.clone()[:, :H] if r0 is not None else None)
             if w.fp8:
-                o = torch.empty((self.rows, S), dtype=torch.uint8, device="cuda")
+                o = torch.empty((self.rows, OS), dtype=torch.uint8, device="cuda")
                 self.out.append(o.view(torch.float8_e4m3fn)[:, :H])
                 if w.fp8 == "dynamic":
                     self.scale.append(torch.empty(self.rows, dtype=torch.float32, device="cuda"))
                 else:
                     from tests._helpers import static_scale
 
-                    self.scale.append(torch.tensor([static_scale()], dtype=torch.float32,
+                    self.scale.append(torch.tensor([static_scale(w.name)], dtype=torch.float32,
                                                    device="cuda"))
             else:
-                self.out.append(torch.empty((self.rows, S), dtype=x0.dtype, device="cuda")[:, :H])
+                self.out.append(torch.empty((self.rows, OS), dtype=x0.dtype, device="cuda")[:, :H])
         del x0, r0
         self.sets = sets
 
@@ -91,7 +94,15 @@ class Batch:
         import residual_add_rmsnorm_amd as arn
 
         w, k = self.w, i % self.sets
-        if w.fp8:
+        if w.is_glu:
+            if w.fp8 == "dynamic":
+                arn.silu_and_mul_fp8(self.x[k], dynamic=True, out=self.out[k],
+                                     scales_out=self.scale[k])
+            elif w.fp8 == "static":
+                arn.silu_and_mul_fp8(self.x[k], scale=self.scale[k], out=self.out[k])
+            else:
+                arn.silu_and_mul(self.x[k], out=self.out[k])
+        elif w.fp8:
             kw = dict(dynamic=True, scales_out=self.scale[k]) if w.fp8 == "dynamic" \
                 else dict(scale=self.scale[k])
             if w.has_residual:
@@ -169,13 +180,16 @@ def cpu_baseline(w, target_s: float = 10.0) -> dict:
     orc = oracle.oracle()
     mode = {None: oracle.FP8_NONE, "static": oracle.FP8_STATIC,
             "dynamic": oracle.FP8_DYNAMIC}[w.fp8]
-    s = static_scale() if w.fp8 == "static" else 0.0
+    s = static_scale(w.name) if w.fp8 == "static" else 0.0
 
     def run(rows):
         d = workloads.make(w, rows=rows)
         t0 = time.perf_counter()
-        orc.add_rmsnorm(w.dtype, d["x"], d.get("residual"), d["weight"], w.eps, hidden=w.hidden,
-                        fp8_mode=mode, static_scale=s)
+        if w.is_glu:
+            orc.silu_and_mul(w.dtype, d["x"], d=w.hidden, fp8_mode=mode, static_scale=s)
+        else:
+            orc.add_rmsnorm(w.dtype, d["x"], d.get("residual"), d["weight"], w.eps,
+                            hidden=w.hidden, fp8_mode=mode, static_scale=s)
         return time.perf_counter() - t0
 
     probe_rows = min(w.rows, 16)

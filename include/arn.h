@@ -1,8 +1,8 @@
 /*
  * arn.h -- C ABI of the MI355X (gfx950) residual-add + RMSNorm library.
  *
- * One operator in four forms.  For every row i of a 16-bit activation
- * matrix (bf16 or fp16), with H = hidden:
+ * One operator in four forms (plus the SwiGLU activation further below).
+ * For every row i of a 16-bit activation matrix (bf16 or fp16), H = hidden:
  *
  *     r   = x[i] + residual[i]          (fused forms; plain forms use r = x[i])
  *     residual[i] <- r                   rounded to the 16-bit type
@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define ARN_ABI_VERSION 1
+#define ARN_ABI_VERSION 2
 
 enum arn_dtype { ARN_BF16 = 0, ARN_FP16 = 1 };
 enum arn_fp8_mode { ARN_FP8_STATIC = 0, ARN_FP8_DYNAMIC = 1 };
@@ -114,6 +114,31 @@ int arn_fused_add_rmsnorm_fp8(uint8_t *out, int64_t out_stride, float *scale, in
                               void *residual, int64_t residual_stride,
                               const void *weight, float eps,
                               int64_t rows, int64_t hidden, int dtype, hipStream_t stream);
+
+/*
+ * SwiGLU activation: out[i][j] = silu(gate[i][j]) * up[i][j], j < d, with
+ * silu(g) = g / (1 + exp(-g)) (Shazeer, "GLU Variants Improve Transformer",
+ * 2020, FFN_SwiGLU with Swish_1).  The usual layout is one [rows, 2d] tensor
+ * from the fused gate/up projection: gate = base, up = base + d, both with
+ * that tensor's row stride; separate tensors work too.  All of gate, up and
+ * out are of `dtype`; fp32 arithmetic, one rounding of the output.  The
+ * second kernel of "Custom CUDA kernels juice Llama 3.1 405B on AMD MI300X"
+ * (paragraph 2) fuses this activation with the FP8 cast, which is
+ * arn_silu_and_mul_fp8.  out may not alias gate or up.  Conventions as above
+ * (device pointers, element strides >= d, asynchronous on `stream`).
+ */
+int arn_silu_and_mul(void *out, int64_t out_stride,
+                     const void *gate, int64_t gate_stride,
+                     const void *up, int64_t up_stride,
+                     int64_t rows, int64_t d, int dtype, hipStream_t stream);
+
+/* SwiGLU with an OCP e4m3 output; `scale` and fp8_mode as in
+ * arn_rmsnorm_fp8 (static: one dequant scale read; dynamic: `rows` scales
+ * max_j |y_ij| / 448 written). */
+int arn_silu_and_mul_fp8(uint8_t *out, int64_t out_stride, float *scale, int fp8_mode,
+                         const void *gate, int64_t gate_stride,
+                         const void *up, int64_t up_stride,
+                         int64_t rows, int64_t d, int dtype, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *arn_status_str(int status);

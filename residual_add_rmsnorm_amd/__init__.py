@@ -21,7 +21,7 @@ from ._lib import ArnError  # noqa: F401
 
 __all__ = [
     "rmsnorm", "fused_add_rmsnorm", "rmsnorm_fp8", "fused_add_rmsnorm_fp8",
-    "set_tile", "last_plan", "ArnError",
+    "silu_and_mul", "silu_and_mul_fp8", "set_tile", "last_plan", "ArnError",
 ]
 
 _DTYPES = {torch.bfloat16: _lib.BF16, torch.float16: _lib.FP16}
@@ -195,6 +195,57 @@ def fused_add_rmsnorm_fp8(x: torch.Tensor, residual: torch.Tensor,
                                            x.data_ptr(), xs, residual.data_ptr(), rs, wp,
                                            float(eps), rows, hidden, dt, _stream(x))
     _lib.check(st, "arn_fused_add_rmsnorm_fp8")
+    return out, sc
+
+
+def _glu_views(x: torch.Tensor):
+    """(rows, d, row_stride) of a [..., 2d] gate|up tensor, no copy."""
+    _check_device(x)
+    _dtype_code(x)
+    rows, two_d, xs = _rows(x, "x")
+    if two_d % 2:
+        raise ValueError("the last dimension of x must be 2*d (gate | up)")
+    return rows, two_d // 2, xs
+
+
+def _glu_out(x, out, dtype, d):
+    shape = (*x.shape[:-1], d)
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=x.device)
+    if tuple(out.shape) != shape or out.dtype != dtype or out.device != x.device:
+        raise ValueError(f"out must have shape {shape} and dtype {dtype} on x's device")
+    return out
+
+
+def silu_and_mul(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """out = silu(x[..., :d]) * x[..., d:] for x of shape [..., 2d]
+    (arn_silu_and_mul with gate = x, up = x + d)."""
+    rows, d, xs = _glu_views(x)
+    out = _glu_out(x, out, x.dtype, d)
+    _, _, os_ = _rows(out, "out")
+    lib = _lib.load()
+    base = x.data_ptr()
+    with torch.cuda.device(x.device):
+        st = lib.arn_silu_and_mul(out.data_ptr(), os_, base, xs, base + 2 * d, xs, rows, d,
+                                  _DTYPES[x.dtype], _stream(x))
+    _lib.check(st, "arn_silu_and_mul")
+    return out
+
+
+def silu_and_mul_fp8(x: torch.Tensor, scale: torch.Tensor | None = None, dynamic: bool = False,
+                     out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None):
+    """SwiGLU of a [..., 2d] gate|up tensor with an OCP e4m3 output
+    (arn_silu_and_mul_fp8).  Returns (codes, scale tensor)."""
+    rows, d, xs = _glu_views(x)
+    out = _glu_out(x, out, FP8_DTYPE, d)
+    _, _, os_ = _rows(out, "out")
+    sc, mode = _fp8_scale(x, rows, scale, dynamic, scales_out)
+    lib = _lib.load()
+    base = x.data_ptr()
+    with torch.cuda.device(x.device):
+        st = lib.arn_silu_and_mul_fp8(out.data_ptr(), os_, sc.data_ptr(), mode, base, xs,
+                                      base + 2 * d, xs, rows, d, _DTYPES[x.dtype], _stream(x))
+    _lib.check(st, "arn_silu_and_mul_fp8")
     return out, sc
 
 

@@ -34,13 +34,17 @@ SIGNATURES = {
     "arn_fused_add_rmsnorm_fp8": (ctypes.c_int, [_vp, _i64, _vp, ctypes.c_int, _vp, _i64, _vp,
                                                  _i64, _vp, ctypes.c_float, _i64, _i64,
                                                  ctypes.c_int, _vp]),
+    "arn_silu_and_mul": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
+                                        ctypes.c_int, _vp]),
+    "arn_silu_and_mul_fp8": (ctypes.c_int, [_vp, _i64, _vp, ctypes.c_int, _vp, _i64, _vp, _i64,
+                                            _i64, _i64, ctypes.c_int, _vp]),
     "arn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "arn_abi_version": (ctypes.c_int, []),
     "arn_set_tile": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "arn_last_plan": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_size_t]),
 }
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class ArnError(RuntimeError):

@@ -34,6 +34,17 @@ const TileTable* table_for(int kind, int dtype) {
   return tables[kind][dtype];
 }
 
+const TileTable* glu_table_for(int mode, int dtype) {
+  static const TileTable* const tables[arn::kNumGluModes][arn::kNumDtypes] = {
+      {&ARN_GLU_TABLE_NAME(0, 0), &ARN_GLU_TABLE_NAME(0, 1)},
+      {&ARN_GLU_TABLE_NAME(1, 0), &ARN_GLU_TABLE_NAME(1, 1)},
+      {&ARN_GLU_TABLE_NAME(2, 0), &ARN_GLU_TABLE_NAME(2, 1)},
+  };
+  return tables[mode][dtype];
+}
+
+const char* const kGluNames[arn::kNumGluModes] = {"silu_mul", "silu_mul_fp8s", "silu_mul_fp8d"};
+
 const char* const kKindNames[arn::kNumKinds] = {"plain",      "fused_add",      "plain_fp8s",
                                                 "fused_add_fp8s", "plain_fp8d", "fused_add_fp8d"};
 
@@ -221,9 +232,84 @@ int run(const Request& r) {
   return ARN_OK;
 }
 
+// SwiGLU: out = silu(gate) * up over d columns per row.
+int run_glu(int mode, int dtype, void* out, int64_t out_stride, float* scale, const void* gate,
+            int64_t gate_stride, const void* up, int64_t up_stride, int64_t rows, int64_t d,
+            hipStream_t stream) {
+  const bool fp8 = mode != arn::kGluPlain;
+  if (dtype != ARN_BF16 && dtype != ARN_FP16) return ARN_EINVAL;
+  if (rows < 0 || d <= 0) return ARN_EINVAL;
+  if (gate_stride < d || up_stride < d || out_stride < d) return ARN_EINVAL;
+  if (rows == 0) return ARN_OK;
+  if (!out || !gate || !up) return ARN_EINVAL;
+  if (fp8 && (!scale || !aligned(scale, 4))) return ARN_EINVAL;
+  if (!aligned(gate, 2) || !aligned(up, 2) || (!fp8 && !aligned(out, 2))) return ARN_EINVAL;
+  if (out == gate || out == up) return ARN_EINVAL;
+  if (d > (int64_t)1 << 30) return ARN_EUNSUPPORTED;
+
+  int vec = 1;
+  for (int v = 8; v > 1; v /= 2) {
+    const uintptr_t b16 = 2u * v;
+    bool ok = d % v == 0 && gate_stride % v == 0 && up_stride % v == 0 && out_stride % v == 0 &&
+              aligned(gate, b16) && aligned(up, b16) && aligned(out, fp8 ? v : b16);
+    if (ok) {
+      vec = v;
+      break;
+    }
+  }
+  const int64_t nvec = d / vec;
+  const Tile* tile = choose_tile(glu_table_for(mode, dtype), vec, nvec, rows, cu_count());
+  if (!tile) return ARN_EUNSUPPORTED;
+
+  const int esize_out = fp8 ? 1 : 2;
+  const int64_t rows_per_launch = kMaxBlocksPerLaunch * tile->rpb;
+  int64_t done = 0;
+  int64_t grid = 0;
+  while (done < rows) {
+    const int64_t n = (rows - done < rows_per_launch) ? rows - done : rows_per_launch;
+    arn::GluArgs a;
+    a.out = static_cast<char*>(out) + done * out_stride * esize_out;
+    a.out_stride = out_stride;
+    a.gate = static_cast<const char*>(gate) + done * gate_stride * 2;
+    a.gate_stride = gate_stride;
+    a.up = static_cast<const char*>(up) + done * up_stride * 2;
+    a.up_stride = up_stride;
+    a.scale = mode == arn::kGluDynamic ? scale + done : scale;
+    a.rows = n;
+    a.d = (int32_t)d;
+    grid = (n + tile->rpb - 1) / tile->rpb;
+    void* params[] = {&a};
+    const hipError_t e = hipLaunchKernel(tile->fn, dim3((unsigned)grid),
+                                         dim3(64u * tile->wpr * tile->rpb), params, 0, stream);
+    if (e != hipSuccess) return ARN_ELAUNCH;
+    done += n;
+  }
+  g_last_plan_len = std::snprintf(g_last_plan, sizeof(g_last_plan),
+                                  "%s/%s/vec%d/wpr%d/nv%d/rpb%d/grid%lld", kGluNames[mode],
+                                  dtype == ARN_BF16 ? "bf16" : "fp16", vec, tile->wpr, tile->nv,
+                                  tile->rpb, (long long)grid);
+  return ARN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int arn_silu_and_mul(void* out, int64_t out_stride, const void* gate, int64_t gate_stride,
+                     const void* up, int64_t up_stride, int64_t rows, int64_t d, int dtype,
+                     hipStream_t stream) {
+  return run_glu(arn::kGluPlain, dtype, out, out_stride, nullptr, gate, gate_stride, up,
+                 up_stride, rows, d, stream);
+}
+
+int arn_silu_and_mul_fp8(uint8_t* out, int64_t out_stride, float* scale, int fp8_mode,
+                         const void* gate, int64_t gate_stride, const void* up, int64_t up_stride,
+                         int64_t rows, int64_t d, int dtype, hipStream_t stream) {
+  if (fp8_mode != ARN_FP8_STATIC && fp8_mode != ARN_FP8_DYNAMIC) return ARN_EINVAL;
+  return run_glu(fp8_mode == ARN_FP8_STATIC ? arn::kGluStatic : arn::kGluDynamic, dtype, out,
+                 out_stride, scale, gate, gate_stride, up, up_stride, rows, d, stream);
+}
+
 
 int arn_rmsnorm(void* out, int64_t out_stride, const void* x, int64_t x_stride,
                 const void* weight, float eps, int64_t rows, int64_t hidden, int dtype,

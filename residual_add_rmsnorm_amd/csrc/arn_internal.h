@@ -1,6 +1,6 @@
 // Internal interface between the host dispatcher (arn_api.hip) and the
 // kernel instantiation units (arn_kernels.hip, compiled once per operator
-// kind and dtype).
+// kind and dtype; arn_glu.hip, once per SwiGLU output mode and dtype).
 #pragma once
 
 #include <stdint.h>
@@ -38,6 +38,22 @@ struct Args {
   float inv_hidden;   // 1.0f / hidden
 };
 
+// SwiGLU output modes.
+enum GluMode : int { kGluPlain = 0, kGluStatic = 1, kGluDynamic = 2, kNumGluModes = 3 };
+
+// SwiGLU kernel arguments: out = silu(gate) * up over `d` columns per row.
+struct GluArgs {
+  void* out;
+  int64_t out_stride;
+  const void* gate;
+  int64_t gate_stride;
+  const void* up;
+  int64_t up_stride;
+  float* scale;  // static: 1 value read; dynamic: `rows` values written
+  int64_t rows;
+  int32_t d;
+};
+
 // One compiled kernel shape.  A lane owns vectors of VEC contiguous
 // elements; WPR waves (64 lanes each) share a row; a lane keeps up to NV
 // vectors of its row in registers; a block holds RPB rows.
@@ -73,3 +89,14 @@ ARN_DECLARE_TABLE(4, 0)
 ARN_DECLARE_TABLE(4, 1)
 ARN_DECLARE_TABLE(5, 0)
 ARN_DECLARE_TABLE(5, 1)
+
+#define ARN_GLU_TABLE_NAME_(MODE, DT) arn_glu_tiles_m##MODE##_d##DT
+#define ARN_GLU_TABLE_NAME(MODE, DT) ARN_GLU_TABLE_NAME_(MODE, DT)
+#define ARN_DECLARE_GLU_TABLE(MODE, DT) extern const arn::TileTable ARN_GLU_TABLE_NAME(MODE, DT);
+
+ARN_DECLARE_GLU_TABLE(0, 0)
+ARN_DECLARE_GLU_TABLE(0, 1)
+ARN_DECLARE_GLU_TABLE(1, 0)
+ARN_DECLARE_GLU_TABLE(1, 1)
+ARN_DECLARE_GLU_TABLE(2, 0)
+ARN_DECLARE_GLU_TABLE(2, 1)

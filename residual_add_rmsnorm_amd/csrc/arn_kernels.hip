@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "arn_device.h"
 #include "arn_internal.h"
 
 #if !defined(ARN_KIND) || !defined(ARN_DT)
@@ -37,233 +38,7 @@
 namespace arn {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// ---------------------------------------------------------------------------
-// 16-bit <-> fp32.  bf16 is the upper half of an fp32; fp16 converts with
-// v_cvt_f32_f16.  fp32 -> 16-bit rounds to nearest even: v_cvt_pk_bf16_f32
-// on gfx950 for bf16, v_cvt_f16_f32 for fp16 (never the round-toward-zero
-// v_cvt_pkrtz_f16_f32).
-// ---------------------------------------------------------------------------
-template <int DT>
-__device__ __forceinline__ float lo_f32(uint32_t w) {
-  if constexpr (DT == kBF16) {
-    return __uint_as_float(w << 16);
-  } else {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ float hi_f32(uint32_t w) {
-  if constexpr (DT == kBF16) {
-    return __uint_as_float(w & 0xFFFF0000u);
-  } else {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  f32x2 v;
-  v.x = a;
-  v.y = b;
-  if constexpr (DT == kBF16) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-  }
-}
-
-// VEC 16-bit elements as one memory access.
-template <int VEC> struct RawT;
-template <> struct RawT<8> { using type = u32x4; };
-template <> struct RawT<4> { using type = u32x2; };
-template <> struct RawT<2> { using type = uint32_t; };
-template <> struct RawT<1> { using type = uint16_t; };
-template <int VEC> using Raw = typename RawT<VEC>::type;
-
-// VEC e4m3 codes as one memory access.
-template <int VEC> struct Fp8RawT;
-template <> struct Fp8RawT<8> { using type = u32x2; };
-template <> struct Fp8RawT<4> { using type = uint32_t; };
-template <> struct Fp8RawT<2> { using type = uint16_t; };
-template <> struct Fp8RawT<1> { using type = uint8_t; };
-template <int VEC> using Fp8Raw = typename Fp8RawT<VEC>::type;
-
-template <int DT, int VEC>
-__device__ __forceinline__ float elem(const Raw<VEC>& r, int e) {
-  if constexpr (VEC == 1) {
-    return lo_f32<DT>((uint32_t)r);
-  } else if constexpr (VEC == 2) {
-    return (e & 1) ? hi_f32<DT>(r) : lo_f32<DT>(r);
-  } else {
-    const uint32_t w = r[e >> 1];
-    return (e & 1) ? hi_f32<DT>(w) : lo_f32<DT>(w);
-  }
-}
-
-template <int DT, int VEC>
-__device__ __forceinline__ Raw<VEC> pack(const float (&f)[VEC]) {
-  if constexpr (VEC == 1) {
-    return (uint16_t)(pack2<DT>(f[0], 0.0f) & 0xFFFFu);
-  } else if constexpr (VEC == 2) {
-    return pack2<DT>(f[0], f[1]);
-  } else {
-    Raw<VEC> r;
-#pragma unroll
-    for (int i = 0; i < VEC / 2; ++i) r[i] = pack2<DT>(f[2 * i], f[2 * i + 1]);
-    return r;
-  }
-}
-
-template <int DT, int VEC>
-__device__ __forceinline__ Raw<VEC> ones() {
-  constexpr uint32_t one = (DT == kBF16) ? 0x3F80u : 0x3C00u;
-  if constexpr (VEC == 1) {
-    return (uint16_t)one;
-  } else if constexpr (VEC == 2) {
-    return one | (one << 16);
-  } else {
-    Raw<VEC> r;
-#pragma unroll
-    for (int i = 0; i < VEC / 2; ++i) r[i] = one | (one << 16);
-    return r;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// OCP e4m3: clamp to the finite range, then the packed gfx950 convert
-// (round to nearest even).  word_sel picks which 16-bit half of the
-// destination dword receives the two codes.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float sat448(float v) {
-  return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
-}
-
-__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
-  return (uint32_t)w;
-}
-
-template <int VEC>
-__device__ __forceinline__ Fp8Raw<VEC> pack_fp8(const float (&f)[VEC]) {
-  if constexpr (VEC == 8) {
-    u32x2 r;
-    r.x = fp8x4(f[0], f[1], f[2], f[3]);
-    r.y = fp8x4(f[4], f[5], f[6], f[7]);
-    return r;
-  } else if constexpr (VEC == 4) {
-    return fp8x4(f[0], f[1], f[2], f[3]);
-  } else if constexpr (VEC == 2) {
-    return (uint16_t)(__builtin_amdgcn_cvt_pk_fp8_f32(sat448(f[0]), sat448(f[1]), 0, false) &
-                      0xFFFF);
-  } else {
-    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(sat448(f[0]), sat448(f[0]), 0, false) &
-                     0xFF);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Wave64 reductions: four DPP steps give every lane its 16-lane row total
-// (xor 1, xor 2, half-row mirror, row mirror), then the four row totals are
-// read with v_readlane and combined in a fixed order.
-// ---------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-__device__ __forceinline__ float lane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-constexpr int kDppXor1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;
-constexpr int kDppMirror = 0x140;
-
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp<kDppXor1>(v);
-  v += dpp<kDppXor2>(v);
-  v += dpp<kDppHalfMirror>(v);
-  v += dpp<kDppMirror>(v);
-  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp<kDppXor1>(v));
-  v = fmaxf(v, dpp<kDppXor2>(v));
-  v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp<kDppMirror>(v));
-  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
-}
-
-// ---------------------------------------------------------------------------
-// Row accesses go through buffer instructions: a descriptor in SGPRs holds
-// the row's base address and its length in bytes (num_records), and each
-// lane supplies a 32-bit byte offset.  An access at or beyond num_records
-// reads zeros and drops stores, so the ragged end of a row needs no
-// branches, a row past the last one (num_records = 0) touches nothing, and
-// no access can leave its own row.  Word 3 is the gfx9 raw-buffer format
-// (DATA_FORMAT = 32 bit).
-// ---------------------------------------------------------------------------
-constexpr int kRsrcWord3 = 0x00020000;
-
-// Cache policy of the memory instructions.  x, residual and out are each
-// touched once per call, so they stream with the non-temporal hint (nt);
-// the weight, read by every row, stays cacheable.
-constexpr int kCacheDefault = 0;
-constexpr int kCacheStream = 2;  // nt
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kRsrcWord3);
-}
-
-template <int VEC, int CP>
-__device__ __forceinline__ Raw<VEC> load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if constexpr (VEC == 8) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP);
-  } else if constexpr (VEC == 4) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, CP);
-  } else if constexpr (VEC == 2) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, CP);
-  } else {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, CP);
-  }
-}
-
-template <int VEC>
-__device__ __forceinline__ void store16(Raw<VEC> v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if constexpr (VEC == 8) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kCacheStream);
-  } else if constexpr (VEC == 4) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kCacheStream);
-  } else if constexpr (VEC == 2) {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kCacheStream);
-  } else {
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, kCacheStream);
-  }
-}
-
-template <int VEC>
-__device__ __forceinline__ void store8(Fp8Raw<VEC> v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if constexpr (VEC == 8) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kCacheStream);
-  } else if constexpr (VEC == 4) {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kCacheStream);
-  } else if constexpr (VEC == 2) {
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, kCacheStream);
-  } else {
-    __builtin_amdgcn_raw_buffer_store_b8(v, r, (int)off, 0, kCacheStream);
-  }
-}
+using namespace dev;
 
 // ---------------------------------------------------------------------------
 // The kernel.

@@ -93,6 +93,10 @@ def assert_scales_close(s_gpu: np.ndarray, s_ref: np.ndarray, dtype: str):
     assert np.all(rel <= RHO[dtype]), f"scales: max rel err {rel.max()}"
 
 
-def static_scale() -> float:
-    with open(os.path.join(HERE, "golden", "fp16_16384_static_scale.json")) as f:
+def static_scale(workload: str = "fused_add_rmsnorm_fp8_static_fp16_decode_x16384") -> float:
+    """The stored per-tensor dequant scale of a static-e4m3 workload."""
+    name = {"fused_add_rmsnorm_fp8_static_fp16_decode_x16384": "fp16_16384_static_scale.json",
+            "silu_and_mul_fp8_static_bf16_decode_x6656": "bf16_6656_swiglu_static_scale.json",
+            }[workload]
+    with open(os.path.join(HERE, "golden", name)) as f:
         return json.load(f)["dequant_scale"]

@@ -3,6 +3,9 @@
 Calls only the oracle (and the seeded input generator).  Run from the repo
 root:  python tests/golden/make_golden.py
 
+bf16_6656_swiglu_static_scale.json -- the same for the SwiGLU decode
+workload (silu(gate) * up, bf16, d 6656).
+
 fp16_16384_static_scale.json -- the per-tensor dequant scale of the decode
 workload (fused add + RMSNorm + static e4m3, fp16, hidden 16384).  The
 workload fixes the multiplier 448 / (4 * max|y|) over a seed-0 calibration
@@ -39,9 +42,28 @@ def static_scale():
     }
 
 
+def glu_static_scale():
+    """The same convention for the SwiGLU decode workload: dequant scale
+    s = fp32(4 * max|y| / 448) over its seed-0 256-row calibration batch,
+    max|y| from the oracle's fp64 silu(gate) * up."""
+    w = workloads.WORKLOADS["silu_and_mul_fp8_static_bf16_decode_x6656"]
+    d = workloads.make(w, rows=256, seed=0)
+    r = oracle.oracle().silu_and_mul(w.dtype, d["x"], d=w.hidden)
+    ymax = float(np.max(np.abs(r["y"])))
+    return {
+        "workload": w.name,
+        "calibration": "seed 0, rows 0..255, oracle fp64 y",
+        "max_abs_y": ymax,
+        "dequant_scale": float(np.float32(4.0 * ymax / 448.0)),
+        "multiplier": 448.0 / (4.0 * ymax),
+    }
+
+
 if __name__ == "__main__":
-    out = os.path.join(HERE, "fp16_16384_static_scale.json")
-    with open(out, "w") as f:
-        json.dump(static_scale(), f, indent=1)
-        f.write("\n")
-    print(open(out).read())
+    for name, fn in (("fp16_16384_static_scale.json", static_scale),
+                     ("bf16_6656_swiglu_static_scale.json", glu_static_scale)):
+        out = os.path.join(HERE, name)
+        with open(out, "w") as f:
+            json.dump(fn(), f, indent=1)
+            f.write("\n")
+        print(open(out).read())

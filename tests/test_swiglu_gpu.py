@@ -1,0 +1,182 @@
+"""Parity of the SwiGLU (+ e4m3) HIP path with the oracle, through the C ABI.
+
+out = silu(gate) * up with gate | up the two halves of a [rows, 2d] row
+(the fused gate/up projection layout), or two separate tensors.  Outputs
+start as NaN canaries and a guard row follows the last row.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from tests._helpers import (assert_codes_close, assert_scales_close, assert_y_close, bits, codes,
+                            dev, static_scale)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import residual_add_rmsnorm_amd as arn
+
+    arn.set_tile(0, 0)
+    yield
+    arn.set_tile(0, 0)
+
+
+def _x(dtype, rows, d, stride=None, seed=50, std=2.0):
+    stride = stride or 2 * d
+    rng = np.random.default_rng(seed)
+    a = np.full((rows, stride), W.PAD_SENTINEL, np.uint16)
+    a[:, :2 * d] = W.to_bits((rng.standard_normal((rows, 2 * d)) * std).astype(np.float32), dtype)
+    return a
+
+
+def run_glu(orc, dtype, x, d, fp8=None, s=None):
+    import residual_add_rmsnorm_amd as arn
+
+    rows, stride = x.shape
+    g = np.full((rows + 1, stride), W.PAD_SENTINEL, np.uint16)
+    g[:rows] = x
+    xd = dev(g, dtype)
+    xv = xd[:rows, :2 * d]
+    if fp8:
+        od = torch.full((rows + 1, d), 0x7F, dtype=torch.uint8, device="cuda")
+        ov = od.view(torch.float8_e4m3fn)[:rows]
+        if fp8 == "static":
+            sd = torch.tensor([s], dtype=torch.float32, device="cuda")
+            arn.silu_and_mul_fp8(xv, scale=sd, out=ov)
+        else:
+            sd = torch.full((rows + 1,), float("nan"), dtype=torch.float32, device="cuda")
+            arn.silu_and_mul_fp8(xv, dynamic=True, out=ov, scales_out=sd[:rows])
+    else:
+        od = dev(np.full((rows + 1, d), 0x7FC1, np.uint16), dtype)
+        ov = od[:rows]
+        arn.silu_and_mul(xv, out=ov)
+    torch.cuda.synchronize()
+    mode = {None: O.FP8_NONE, "static": O.FP8_STATIC, "dynamic": O.FP8_DYNAMIC}[fp8]
+    ref = orc.silu_and_mul(dtype, x, d=d, fp8_mode=mode, static_scale=s or 0.0)
+    assert np.array_equal(bits(xd)[:rows], x), "input modified"
+    if fp8:
+        q = codes(od)
+        assert_codes_close(q[:rows], ref["q"])
+        assert np.all(q[rows] == 0x7F), "guard row written"
+        if fp8 == "dynamic":
+            sc = sd.cpu().numpy()
+            assert_scales_close(sc[:rows], ref["scales"], dtype)
+            assert np.isnan(sc[rows])
+    else:
+        ob = bits(od)
+        assert_y_close(ob[:rows], ref["y"], dtype)
+        assert np.all(ob[rows] == 0x7FC1), "guard row written"
+
+
+DS = [1, 3, 8, 24, 100, 512, 1000, 3584, 4096, 6656, 14336, 28672]
+
+
+@pytest.mark.parametrize("d", DS)
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_silu_and_mul(orc, dtype, d):
+    run_glu(orc, dtype, _x(dtype, 7 if d > 4096 else 33, d), d)
+
+
+@pytest.mark.parametrize("d", [1, 24, 1000, 6656, 14336])
+@pytest.mark.parametrize("fp8", ["static", "dynamic"])
+def test_silu_and_mul_fp8(orc, d, fp8):
+    run_glu(orc, "bf16", _x("bf16", 9, d, seed=51), d, fp8=fp8, s=0.05 if fp8 == "static" else None)
+
+
+@pytest.mark.parametrize("rows", [1, 255, 256, 257, 2049])
+def test_row_counts(orc, rows):
+    run_glu(orc, "bf16", _x("bf16", rows, 512, seed=52), 512, fp8="dynamic")
+
+
+def test_padded_rows(orc):
+    run_glu(orc, "fp16", _x("fp16", 13, 1000, stride=2048, seed=53), 1000)
+
+
+def test_extreme_gates(orc):
+    """Large negative gates (silu ~ g * e^g, tiny but representable), large
+    positive gates (silu = g), zeros."""
+    rows, d = 4, 512
+    rng = np.random.default_rng(54)
+    g = np.concatenate([-rng.uniform(20, 95, (1, d)), rng.uniform(20, 1000, (1, d)),
+                        np.zeros((1, d)), rng.standard_normal((1, d))]).astype(np.float32)
+    u = rng.uniform(0.5, 2, (rows, d)).astype(np.float32)
+    x = W.to_bits(np.concatenate([g, u], axis=1), "bf16")
+    run_glu(orc, "bf16", x, d)
+
+
+def test_zero_row_dynamic(orc):
+    x = _x("bf16", 5, 768, seed=55)
+    x[2] = 0
+    run_glu(orc, "bf16", x, 768, fp8="dynamic")
+
+
+def test_split_gate_and_up_tensors(orc):
+    """The C ABI with gate and up in separate tensors of different strides."""
+    from residual_add_rmsnorm_amd import _lib
+
+    lib = _lib.load()
+    rows, d = 20, 1024
+    g = _x("bf16", rows, d // 2, seed=56)[:, :d]      # (rows, d) values
+    u = _x("bf16", rows, d // 2, seed=57)[:, :d]
+    gate = np.full((rows, 1536), W.PAD_SENTINEL, np.uint16)
+    up = np.full((rows, 1280), W.PAD_SENTINEL, np.uint16)
+    gate[:, :d], up[:, :d] = g, u
+    gd, ud = dev(gate, "bf16"), dev(up, "bf16")
+    out = torch.empty(rows, d, dtype=torch.bfloat16, device="cuda")
+    st = lib.arn_silu_and_mul(out.data_ptr(), d, gd.data_ptr(), 1536, ud.data_ptr(), 1280, rows, d,
+                              _lib.BF16, torch.cuda.current_stream().cuda_stream)
+    assert st == _lib.OK
+    torch.cuda.synchronize()
+    ref = orc.silu_and_mul_split("bf16", gate, up, d=d)
+    assert_y_close(bits(out), ref["y"], "bf16")
+
+
+@pytest.mark.parametrize("wpr,nv", [(1, 2), (1, 4), (2, 2), (2, 4), (4, 1), (4, 2), (4, 4), (8, 1),
+                                    (8, 2), (8, 4), (16, 1), (16, 2), (16, 4), (16, 8)])
+def test_forced_tiles(orc, wpr, nv):
+    import residual_add_rmsnorm_amd as arn
+
+    d = 64 * wpr * nv * 8 - 24
+    arn.set_tile(wpr, nv)
+    try:
+        run_glu(orc, "bf16", _x("bf16", 5, d, seed=58), d, fp8="dynamic")
+        assert f"wpr{wpr}/nv{nv}/" in arn.last_plan(), arn.last_plan()
+    finally:
+        arn.set_tile(0, 0)
+
+
+@pytest.mark.parametrize("name", ["silu_and_mul_fp8_dynamic_bf16_32768x6656",
+                                  "silu_and_mul_fp8_static_bf16_decode_x6656"])
+def test_workloads_sampled(orc, name):
+    """Full-size workloads in the benchmark's launch configuration; sampled
+    rows against the oracle."""
+    import residual_add_rmsnorm_amd as arn
+
+    w = W.WORKLOADS[name]
+    d_in = W.make(w)
+    x = dev(d_in["x"], w.dtype)
+    out = torch.full((w.rows, w.hidden), 0x7F, dtype=torch.uint8, device="cuda")
+    ov = out.view(torch.float8_e4m3fn)
+    if w.fp8 == "dynamic":
+        sc = torch.empty(w.rows, dtype=torch.float32, device="cuda")
+        arn.silu_and_mul_fp8(x, dynamic=True, out=ov, scales_out=sc)
+        s = 0.0
+    else:
+        s = static_scale(name)
+        sc = torch.tensor([s], dtype=torch.float32, device="cuda")
+        arn.silu_and_mul_fp8(x, scale=sc, out=ov)
+    torch.cuda.synchronize()
+    idx = np.unique(np.linspace(0, w.rows - 1, 96).astype(np.int64))
+    mode = O.FP8_DYNAMIC if w.fp8 == "dynamic" else O.FP8_STATIC
+    ref = orc.silu_and_mul(w.dtype, d_in["x"][idx], d=w.hidden, fp8_mode=mode, static_scale=s)
+    assert_codes_close(codes(out)[idx], ref["q"])
+    if w.fp8 == "dynamic":
+        assert_scales_close(sc.cpu().numpy()[idx], ref["scales"], w.dtype)

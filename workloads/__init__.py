@@ -55,20 +55,32 @@ class Workload:
     def has_residual(self) -> bool:
         return self.op.startswith("fused_add")
 
+    @property
+    def is_glu(self) -> bool:
+        return self.op.startswith("silu_and_mul")
+
+    @property
+    def in_width(self) -> int:
+        """Columns of x per row: gate | up (2 * hidden) for SwiGLU."""
+        return 2 * self.hidden if self.is_glu else self.hidden
+
     def algorithmic_bytes(self, rows: int | None = None) -> int:
-        """Minimum HBM bytes one call must move: 16-bit x read, residual
-        read and written, output written (16-bit or e4m3), weight once, the
-        static scale read once or the dynamic scales written."""
+        """Minimum HBM bytes one call must move: 16-bit x read (gate and up
+        for SwiGLU), residual read and written, output written (16-bit or
+        e4m3), the norm weight once, the static scale read once or the
+        dynamic scales written."""
         r = self.rows if rows is None else rows
         h = self.hidden
         elem = 2
-        per_row = h * elem                      # x
+        per_row = self.in_width * elem          # x (or gate | up)
         if self.has_residual:
             per_row += 2 * h * elem             # residual read + write
         per_row += h * (1 if self.fp8 else elem)  # output
         if self.fp8 == "dynamic":
             per_row += 4
-        total = r * per_row + h * elem          # weight once
+        total = r * per_row
+        if not self.is_glu:
+            total += h * elem                   # weight once
         if self.fp8 == "static":
             total += 4
         return total
@@ -91,6 +103,13 @@ WORKLOADS = {
                  "bf16", 65536, 3840, 4096, 1e-6),
         Workload("fused_add_rmsnorm_bf16_65536x2880_stride4096", "fused_add_rmsnorm",
                  "bf16", 65536, 2880, 4096, 1e-6),
+        # SwiGLU + e4m3: one GPU's shard of the Llama 3.1 405B MLP (intermediate
+        # width 53248 split over the 8 GPUs of one node): d = 6656, rows of
+        # gate | up = 13312 columns.
+        Workload("silu_and_mul_fp8_dynamic_bf16_32768x6656", "silu_and_mul_fp8", "bf16",
+                 32768, 6656, 13312, 0.0, fp8="dynamic"),
+        Workload("silu_and_mul_fp8_static_bf16_decode_x6656", "silu_and_mul_fp8", "bf16",
+                 256, 6656, 13312, 0.0, fp8="static", row_counts=(1, 8, 64, 256)),
     ]
 }
 
@@ -153,18 +172,19 @@ def weight_bits(w: Workload, seed: int = 0) -> np.ndarray:
 
 
 def padded(bits: np.ndarray, stride: int, fill: int = PAD_SENTINEL) -> np.ndarray:
-    rows, hidden = bits.shape
-    if stride == hidden:
+    rows, width = bits.shape
+    if stride == width:
         return bits
     out = np.full((rows, stride), fill, np.uint16)
-    out[:, :hidden] = bits
+    out[:, :width] = bits
     return out
 
 
 def make_rows(w: Workload, row0: int, row1: int, seed: int = 0) -> dict:
     """Inputs for rows [row0, row1) of a workload, rows laid out at the
-    workload's stride with padding filled by PAD_SENTINEL."""
-    xf = _normal_rows(seed, STREAM_X, row0, row1, w.hidden, w.x_std)
+    workload's stride with padding filled by PAD_SENTINEL.  For SwiGLU, x
+    holds gate | up (2 * hidden columns) and there is no weight."""
+    xf = _normal_rows(seed, STREAM_X, row0, row1, w.in_width, w.x_std)
     if w.outliers:
         xf[:, outlier_columns(w, seed)] *= np.float32(w.outlier_gain)
     out = {"x": padded(to_bits(xf, w.dtype), w.stride)}
@@ -172,7 +192,7 @@ def make_rows(w: Workload, row0: int, row1: int, seed: int = 0) -> dict:
     if w.has_residual:
         rf = _normal_rows(seed, STREAM_RES, row0, row1, w.hidden, w.res_std)
         out["residual"] = padded(to_bits(rf, w.dtype), w.stride)
-    out["weight"] = weight_bits(w, seed)
+    out["weight"] = None if w.is_glu else weight_bits(w, seed)
     return out
 
 
