@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define ARN_ABI_VERSION 2
+#define ARN_ABI_VERSION 3
 
 enum arn_dtype { ARN_BF16 = 0, ARN_FP16 = 1 };
 enum arn_fp8_mode { ARN_FP8_STATIC = 0, ARN_FP8_DYNAMIC = 1 };
@@ -114,6 +114,42 @@ int arn_fused_add_rmsnorm_fp8(uint8_t *out, int64_t out_stride, float *scale, in
                               void *residual, int64_t residual_stride,
                               const void *weight, float eps,
                               int64_t rows, int64_t hidden, int dtype, hipStream_t stream);
+
+/*
+ * All four norm forms through one descriptor, plus a variance-size
+ * override: the mean of squares runs over the first `variance_size`
+ * channels only (1 <= variance_size <= hidden; 0 means hidden) and still
+ * normalises every channel -- vLLM's RMSNorm variance_size_override, which
+ * the AITER wrappers of "vllm.kernels.aiter_ops" (rms_add_no_var_16bit_only)
+ * decline and this library serves.
+ *   struct_size   : sizeof(arn_norm_args), checked (EINVAL if smaller)
+ *   out_format    : ARN_OUT_16BIT, ARN_OUT_FP8_STATIC or ARN_OUT_FP8_DYNAMIC
+ *   residual      : NULL selects plain RMSNorm, else the fused form
+ *   scale         : as in arn_rmsnorm_fp8 (ignored for 16-bit output)
+ * Other fields and the return value as in the entry points above.
+ */
+enum arn_out_format { ARN_OUT_16BIT = 0, ARN_OUT_FP8_STATIC = 1, ARN_OUT_FP8_DYNAMIC = 2 };
+
+typedef struct arn_norm_args {
+  size_t struct_size;
+  int dtype;
+  int out_format;
+  void *out;
+  int64_t out_stride;
+  float *scale;
+  const void *x;
+  int64_t x_stride;
+  void *residual;
+  int64_t residual_stride;
+  const void *weight;
+  float eps;
+  int64_t rows;
+  int64_t hidden;
+  int64_t variance_size;
+  hipStream_t stream;
+} arn_norm_args;
+
+int arn_norm(const arn_norm_args *args);
 
 /*
  * SwiGLU activation: out[i][j] = silu(gate[i][j]) * up[i][j], j < d, with

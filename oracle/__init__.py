@@ -75,6 +75,9 @@ def bind(lib_path: str) -> ctypes.CDLL:
         ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float),
     ]
     lib.orc_add_rmsnorm.restype = ctypes.c_int
+    lib.orc_add_rmsnorm_var.argtypes = (lib.orc_add_rmsnorm.argtypes[:3] + [ctypes.c_int64]
+                                        + lib.orc_add_rmsnorm.argtypes[3:])
+    lib.orc_add_rmsnorm_var.restype = ctypes.c_int
     lib.orc_silu.argtypes = [ctypes.c_double]
     lib.orc_silu.restype = ctypes.c_double
     lib.orc_silu_and_mul.argtypes = [
@@ -125,11 +128,13 @@ class Oracle:
 
     # -- the operator ------------------------------------------------------
     def add_rmsnorm(self, dtype, x, residual, weight, eps, hidden=None,
-                    fp8_mode=FP8_NONE, static_scale=0.0, want_y=True):
+                    fp8_mode=FP8_NONE, static_scale=0.0, want_y=True, variance_size=None):
         """Run the reference on 2-D uint16 arrays (row stride = shape[1]).
 
         ``hidden`` defaults to the full row; a smaller value leaves the
         columns beyond it (row padding) out of the computation.
+        ``variance_size`` (default ``hidden``) limits the mean of squares to
+        the first that many channels.
         Returns a dict with r16, y (float64), y16, and q / scales for FP8.
         """
         if isinstance(dtype, str):
@@ -148,8 +153,8 @@ class Oracle:
         y16 = np.empty((rows, hidden), np.uint16)
         q = np.empty((rows, hidden), np.uint8) if fp8_mode != FP8_NONE else None
         scales = np.empty((rows,), np.float32) if fp8_mode == FP8_DYNAMIC else None
-        rc = self.c.orc_add_rmsnorm(
-            dtype, rows, hidden,
+        rc = self.c.orc_add_rmsnorm_var(
+            dtype, rows, hidden, hidden if variance_size is None else int(variance_size),
             _ptr(x, ctypes.c_uint16), stride,
             _ptr(residual, ctypes.c_uint16),
             residual.shape[1] if residual is not None else 0,

@@ -246,16 +246,18 @@ static void copy_row(int dtype, int64_t hidden, const uint16_t *x, uint16_t *r16
     }
 }
 
-/* Step 2: mean of squares over all `hidden` channels (no variance-size
- * override), summed left to right. */
-static double mean_square(int64_t hidden, const double *r)
+/* Step 2: mean of squares over the first n channels, summed left to right.
+ * n = hidden, unless the caller overrides the variance size (vLLM's RMSNorm
+ * variance_size_override: the variance of the first n channels normalises
+ * all of them). */
+static double mean_square(int64_t n, const double *r)
 {
     double sum = 0.0;
     int64_t j;
-    for (j = 0; j < hidden; j++) {
+    for (j = 0; j < n; j++) {
         sum += r[j] * r[j];
     }
-    return sum / (double)hidden;
+    return sum / (double)n;
 }
 
 /* Step 3: y_j = r_j * (1 / sqrt(ms + eps)) * w_j. */
@@ -318,12 +320,26 @@ int orc_add_rmsnorm(int dtype, int64_t rows, int64_t hidden,
                     int fp8_mode, float static_scale,
                     uint8_t *q_out, float *scale_out)
 {
+    return orc_add_rmsnorm_var(dtype, rows, hidden, hidden, x, x_stride, residual,
+                               residual_stride, weight, eps, r16_out, y_out, y16_out,
+                               fp8_mode, static_scale, q_out, scale_out);
+}
+
+int orc_add_rmsnorm_var(int dtype, int64_t rows, int64_t hidden, int64_t variance_size,
+                        const uint16_t *x, int64_t x_stride,
+                        const uint16_t *residual, int64_t residual_stride,
+                        const uint16_t *weight, float eps,
+                        uint16_t *r16_out, double *y_out, uint16_t *y16_out,
+                        int fp8_mode, float static_scale,
+                        uint8_t *q_out, float *scale_out)
+{
     uint16_t *r16;
     double *r, *y;
     uint8_t *q;
     int64_t i, j;
 
     if ((dtype != ORC_BF16 && dtype != ORC_FP16) || rows < 0 || hidden <= 0 ||
+        variance_size <= 0 || variance_size > hidden ||
         x == NULL || x_stride < hidden ||
         (residual != NULL && residual_stride < hidden) ||
         (fp8_mode != ORC_FP8_NONE && fp8_mode != ORC_FP8_STATIC &&
@@ -353,7 +369,7 @@ int orc_add_rmsnorm(int dtype, int64_t rows, int64_t hidden,
         } else {
             copy_row(dtype, hidden, xi, r16, r);
         }
-        ms = mean_square(hidden, r);
+        ms = mean_square(variance_size, r);
         normalise_row(dtype, hidden, r, ms, eps, weight, y);
 
         if (fp8_mode == ORC_FP8_STATIC) {

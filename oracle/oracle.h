@@ -64,6 +64,17 @@ int orc_add_rmsnorm(int dtype, int64_t rows, int64_t hidden,
                     int fp8_mode, float static_scale,
                     uint8_t *q_out, float *scale_out);
 
+/* The same with the mean of squares taken over the first variance_size
+ * channels only (1 <= variance_size <= hidden); every channel is still
+ * normalised by it. */
+int orc_add_rmsnorm_var(int dtype, int64_t rows, int64_t hidden, int64_t variance_size,
+                        const uint16_t *x, int64_t x_stride,
+                        const uint16_t *residual, int64_t residual_stride,
+                        const uint16_t *weight, float eps,
+                        uint16_t *r16_out, double *y_out, uint16_t *y16_out,
+                        int fp8_mode, float static_scale,
+                        uint8_t *q_out, float *scale_out);
+
 /*
  * SwiGLU activation of a gate/up pair (Shazeer, "GLU Variants Improve
  * Transformer", 2020, the FFN_SwiGLU definition with Swish_1 = SiLU):

@@ -21,7 +21,7 @@ from ._lib import ArnError  # noqa: F401
 
 __all__ = [
     "rmsnorm", "fused_add_rmsnorm", "rmsnorm_fp8", "fused_add_rmsnorm_fp8",
-    "silu_and_mul", "silu_and_mul_fp8", "set_tile", "last_plan", "ArnError",
+    "silu_and_mul", "silu_and_mul_fp8", "norm", "set_tile", "last_plan", "ArnError",
 ]
 
 _DTYPES = {torch.bfloat16: _lib.BF16, torch.float16: _lib.FP16}
@@ -196,6 +196,49 @@ def fused_add_rmsnorm_fp8(x: torch.Tensor, residual: torch.Tensor,
                                            float(eps), rows, hidden, dt, _stream(x))
     _lib.check(st, "arn_fused_add_rmsnorm_fp8")
     return out, sc
+
+
+def norm(x: torch.Tensor, weight: torch.Tensor | None, eps: float,
+         residual: torch.Tensor | None = None, variance_size: int | None = None,
+         fp8: str | None = None, scale: torch.Tensor | None = None,
+         out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None):
+    """Every norm form through arn_norm, with an optional variance-size
+    override (mean of squares over the first ``variance_size`` channels).
+    ``fp8``: None (16-bit out), "static" (needs ``scale``) or "dynamic".
+    Returns out, or (codes, scale tensor) for FP8."""
+    import ctypes
+
+    _check_device(x)
+    dt = _dtype_code(x)
+    rows, hidden, xs = _rows(x, "x")
+    rs = 0
+    if residual is not None:
+        if residual.dtype != x.dtype or residual.shape != x.shape or residual.device != x.device:
+            raise ValueError("residual must match x in shape, dtype and device")
+        _, _, rs = _rows(residual, "residual")
+    out = _out_like(x, out, FP8_DTYPE if fp8 else x.dtype)
+    _, _, os_ = _rows(out, "out")
+    wp = _check_weight(weight, x, hidden)
+    sc = None
+    fmt = _lib.OUT_16BIT
+    if fp8:
+        if fp8 not in ("static", "dynamic"):
+            raise ValueError("fp8 must be None, 'static' or 'dynamic'")
+        sc, _ = _fp8_scale(x, rows, scale, fp8 == "dynamic", scales_out)
+        fmt = _lib.OUT_FP8_DYNAMIC if fp8 == "dynamic" else _lib.OUT_FP8_STATIC
+    args = _lib.NormArgs(
+        struct_size=ctypes.sizeof(_lib.NormArgs), dtype=dt, out_format=fmt,
+        out=out.data_ptr(), out_stride=os_, scale=sc.data_ptr() if sc is not None else None,
+        x=x.data_ptr(), x_stride=xs,
+        residual=residual.data_ptr() if residual is not None else None, residual_stride=rs,
+        weight=wp, eps=float(eps), rows=rows, hidden=hidden,
+        variance_size=0 if variance_size is None else int(variance_size),
+        stream=_stream(x))
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        st = lib.arn_norm(ctypes.byref(args))
+    _lib.check(st, "arn_norm")
+    return (out, sc) if fp8 else out
 
 
 def _glu_views(x: torch.Tensor):

@@ -38,13 +38,38 @@ SIGNATURES = {
                                         ctypes.c_int, _vp]),
     "arn_silu_and_mul_fp8": (ctypes.c_int, [_vp, _i64, _vp, ctypes.c_int, _vp, _i64, _vp, _i64,
                                             _i64, _i64, ctypes.c_int, _vp]),
+    "arn_norm": (ctypes.c_int, [_vp]),
     "arn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "arn_abi_version": (ctypes.c_int, []),
     "arn_set_tile": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "arn_last_plan": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_size_t]),
 }
 
-ABI_VERSION = 2
+ABI_VERSION = 3
+
+OUT_16BIT, OUT_FP8_STATIC, OUT_FP8_DYNAMIC = 0, 1, 2
+
+
+class NormArgs(ctypes.Structure):
+    """struct arn_norm_args of include/arn.h."""
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("dtype", ctypes.c_int),
+        ("out_format", ctypes.c_int),
+        ("out", ctypes.c_void_p),
+        ("out_stride", ctypes.c_int64),
+        ("scale", ctypes.c_void_p),
+        ("x", ctypes.c_void_p),
+        ("x_stride", ctypes.c_int64),
+        ("residual", ctypes.c_void_p),
+        ("residual_stride", ctypes.c_int64),
+        ("weight", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+        ("rows", ctypes.c_int64),
+        ("hidden", ctypes.c_int64),
+        ("variance_size", ctypes.c_int64),
+        ("stream", ctypes.c_void_p),
+    ]
 
 
 class ArnError(RuntimeError):

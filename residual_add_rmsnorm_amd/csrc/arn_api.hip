@@ -85,6 +85,7 @@ struct Request {
   int64_t rows;
   int64_t hidden;
   hipStream_t stream;
+  int64_t var_cols = 0;  // 0: hidden
 };
 
 bool aligned(const void* p, uintptr_t bytes) {
@@ -178,6 +179,7 @@ int run(const Request& r) {
   if (r.x_stride < r.hidden || r.out_stride < r.hidden) return ARN_EINVAL;
   if ((r.kind & 1) && r.res_stride < r.hidden) return ARN_EINVAL;
   if (!(r.eps >= 0.0f) || !std::isfinite(r.eps)) return ARN_EINVAL;
+  if (r.var_cols < 0 || r.var_cols > r.hidden) return ARN_EINVAL;
   if (r.rows == 0) return ARN_OK;
   if (!r.out || !r.x) return ARN_EINVAL;
   if ((r.kind & 1) && !r.res) return ARN_EINVAL;
@@ -215,7 +217,8 @@ int run(const Request& r) {
     a.rows = n;
     a.hidden = (int32_t)r.hidden;
     a.eps = r.eps;
-    a.inv_hidden = 1.0f / (float)r.hidden;
+    a.var_cols = (int32_t)(r.var_cols > 0 ? r.var_cols : r.hidden);
+    a.inv_var = 1.0f / (float)a.var_cols;
 
     grid = (n + tile->rpb - 1) / tile->rpb;
     void* params[] = {&a};
@@ -345,6 +348,29 @@ int arn_fused_add_rmsnorm_fp8(uint8_t* out, int64_t out_stride, float* scale, in
   const int kind = fp8_mode == ARN_FP8_STATIC ? arn::kFusedFp8Static : arn::kFusedFp8Dynamic;
   Request r{kind,           dtype,  out,   out_stride, x,    x_stride, residual,
             residual_stride, weight, scale, eps,        rows, hidden,   stream};
+  return run(r);
+}
+
+int arn_norm(const arn_norm_args* p) {
+  if (!p || p->struct_size < sizeof(arn_norm_args)) return ARN_EINVAL;
+  int kind;
+  switch (p->out_format) {
+    case ARN_OUT_16BIT:
+      kind = arn::kPlain;
+      break;
+    case ARN_OUT_FP8_STATIC:
+      kind = arn::kPlainFp8Static;
+      break;
+    case ARN_OUT_FP8_DYNAMIC:
+      kind = arn::kPlainFp8Dynamic;
+      break;
+    default:
+      return ARN_EINVAL;
+  }
+  if (p->residual) kind |= arn::kFused;
+  Request r{kind,      p->dtype,  p->out,    p->out_stride, p->x,      p->x_stride,
+            p->residual, p->residual_stride, p->weight, kind & 6 ? p->scale : nullptr, p->eps,
+            p->rows,   p->hidden, p->stream, p->variance_size};
   return run(r);
 }
 

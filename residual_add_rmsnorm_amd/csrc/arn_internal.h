@@ -34,8 +34,9 @@ struct Args {
   float* scale;       // static: 1 value read; dynamic: `rows` values written
   int64_t rows;
   int32_t hidden;
+  int32_t var_cols;   // channels in the mean of squares (== hidden unless overridden)
   float eps;
-  float inv_hidden;   // 1.0f / hidden
+  float inv_var;      // 1.0f / var_cols
 };
 
 // SwiGLU output modes.

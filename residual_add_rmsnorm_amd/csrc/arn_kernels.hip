@@ -106,24 +106,49 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
     if constexpr (kStatic) qmul = 1.0f / *a.scale;
 
     // 2. r = x + residual in fp32, rounded to 16 bits and stored back;
-    //    sum of squares of the rounded r (and max |r*w| for dynamic FP8).
-    //    Zero-filled vectors add nothing and their stores are dropped.
-    float ss = 0.0f;
-    float mx = 0.0f;
+    //    sum of squares of the rounded r over the first var_cols channels
+    //    (all of them unless the variance size is overridden), and max |r*w|
+    //    for dynamic FP8.  Zero-filled vectors add nothing and their stores
+    //    are dropped.
+    if constexpr (kRes) {
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      if constexpr (kRes) {
+      for (int k = 0; k < NV; ++k) {
         float f[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) f[e] = elem<DT, VEC>(xr[k], e) + elem<DT, VEC>(rr[k], e);
         xr[k] = pack<DT, VEC>(f);
         store16<VEC>(xr[k], rrs, off16 + k * kStep16);
       }
+    }
+    float ss = 0.0f;
+    float mx = 0.0f;
+    if (a.var_cols == a.hidden) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float rf = elem<DT, VEC>(xr[k], e);
-        ss = __builtin_fmaf(rf, rf, ss);
-        if constexpr (kDynamic) mx = fmaxf(mx, fabsf(rf * elem<DT, VEC>(wr[k], e)));
+      for (int k = 0; k < NV; ++k) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float rf = elem<DT, VEC>(xr[k], e);
+          ss = __builtin_fmaf(rf, rf, ss);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int col0 = (t + k * kTPR) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float rf = elem<DT, VEC>(xr[k], e);
+          ss = __builtin_fmaf(rf, col0 + e < a.var_cols ? rf : 0.0f, ss);
+        }
+      }
+    }
+    if constexpr (kDynamic) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          mx = fmaxf(mx, fabsf(elem<DT, VEC>(xr[k], e) * elem<DT, VEC>(wr[k], e)));
+        }
       }
     }
 
@@ -144,7 +169,7 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
         if constexpr (kDynamic) mx = fmaxf(mx, red_max[rib * WPR + i]);
       }
     }
-    const float inv = rsqrtf(__builtin_fmaf(ss, a.inv_hidden, a.eps));
+    const float inv = rsqrtf(__builtin_fmaf(ss, a.inv_var, a.eps));
 
     if constexpr (kDynamic) {
       const float amax = mx * inv;

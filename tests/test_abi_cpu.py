@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function(lib):
     for name in header_functions():
         assert name in exported, name
         assert getattr(lib, name) is not None
-    assert lib.arn_abi_version() == _lib.ABI_VERSION == 2
+    assert lib.arn_abi_version() == _lib.ABI_VERSION == 3
 
 
 def test_hip_imports_resolve_in_torch_runtime():
@@ -144,3 +144,49 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(2, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         arn.rmsnorm(x, None, 1e-6)
+
+
+def _norm_args(**kw):
+    a = _lib.NormArgs(struct_size=ctypes.sizeof(_lib.NormArgs), dtype=0, out_format=0, out=P,
+                      out_stride=64, scale=None, x=Q, x_stride=64, residual=R, residual_stride=64,
+                      weight=None, eps=1e-6, rows=4, hidden=64, variance_size=0, stream=None)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("case", [
+    dict(struct_size=8), dict(out_format=3), dict(variance_size=-1), dict(variance_size=65),
+    dict(out_format=1, scale=None), dict(dtype=4), dict(residual=Q),
+])
+def test_norm_descriptor_rejects(lib, case):
+    a = _norm_args(**case)
+    assert lib.arn_norm(ctypes.byref(a)) == _lib.EINVAL
+    assert lib.arn_norm(None) == _lib.EINVAL
+
+
+def test_norm_descriptor_zero_rows(lib):
+    a = _norm_args(rows=0, out=None, x=None, residual=None, variance_size=10)
+    assert lib.arn_norm(ctypes.byref(a)) == _lib.OK
+
+
+def test_norm_struct_layout_matches_header():
+    """Field offsets of the ctypes mirror equal those of the C struct,
+    measured by compiling a probe against include/arn.h with the host
+    compiler (no GPU code)."""
+    import tempfile
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"arn.h\"\nint main(void){\n"
+    for name, _ in _lib.NormArgs._fields_:
+        src += f'  printf("{name} %zu\\n", offsetof(arn_norm_args, {name}));\n'
+    src += '  printf("size %zu\\n", sizeof(arn_norm_args));\n  return 0;\n}\n'
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "probe.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "probe")
+        subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", c, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()
+    got = dict(zip(out[0::2], map(int, out[1::2])))
+    for name, _ in _lib.NormArgs._fields_:
+        assert got[name] == getattr(_lib.NormArgs, name).offset, name
+    assert got["size"] == ctypes.sizeof(_lib.NormArgs)

@@ -16,7 +16,11 @@ from tests import test_oracle_swiglu_pins as swiglu_pins
 
 MUTANTS = {
     "dropped_eps": ("sqrt(ms + (double)eps)", "sqrt(ms)"),
-    "divisor_h_minus_1": ("sum / (double)hidden", "sum / (double)(hidden - 1)"),
+    "divisor_h_minus_1": ("sum / (double)n", "sum / (double)(n - 1)"),
+    "variance_over_all_channels": ("ms = mean_square(variance_size, r);",
+                                   "ms = mean_square(hidden, r);"),
+    "variance_divisor_hidden": ("ms = mean_square(variance_size, r);",
+                                "ms = mean_square(variance_size, r) * variance_size / hidden;"),
     "abs_instead_of_r": ("y[j] = r[j] * inv * w;", "y[j] = fabs(r[j]) * inv * w;"),
     "weight_index_shift": ("orc_decode16(dtype, weight[j])",
                            "orc_decode16(dtype, weight[(j + 1) % hidden])"),

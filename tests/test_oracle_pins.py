@@ -415,3 +415,16 @@ def test_fp8_dynamic_zero_row_only(orc):
     r = orc.add_rmsnorm("fp16", np.zeros((2, 64), np.uint16), None, None, 1e-5,
                         fp8_mode=O.FP8_DYNAMIC)
     assert np.all(r["scales"] == 0) and np.all(r["q"] == 0)
+
+
+def test_variance_size_override_closed_form(orc):
+    """variance_size = k: the mean square of the first k channels
+    normalises every channel.  Row (a, .., a | b, .., b) with k a's gives
+    y = r / sqrt(a^2 + eps)."""
+    H, k, a, b, eps = 64, 24, 0.5, 3.0, 0.25
+    x = _bits([[a] * k + [b] * (H - k)])
+    r = orc.add_rmsnorm("bf16", x, None, None, eps, variance_size=k)
+    assert np.allclose(r["y"][0, :k], a / math.sqrt(a * a + eps), rtol=1e-15, atol=0)
+    assert np.allclose(r["y"][0, k:], b / math.sqrt(a * a + eps), rtol=1e-15, atol=0)
+    full = orc.add_rmsnorm("bf16", x, None, None, eps, variance_size=H)
+    assert np.array_equal(full["y"], orc.add_rmsnorm("bf16", x, None, None, eps)["y"])

@@ -408,3 +408,45 @@ def test_e4m3_dynamic_every_finite_bf16_weight(orc):
     x = np.full((1, hidden), 0x3F80, np.uint16)
     run_case(orc, dtype="bf16", x=x, res=None, w=w, eps=0.0, hidden=hidden,
              fp8="dynamic")
+
+
+# ---------------------------------------------------------------------------
+# arn_norm: the descriptor entry point and the variance-size override
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("hidden,k", [(4096, 4096), (4096, 1000), (4096, 1), (3840, 2048),
+                                      (100, 37), (16384, 12288)])
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("fp8", [None, "dynamic"])
+def test_norm_variance_size(orc, hidden, k, fused, fp8):
+    arn = _arn()
+    dtype = "bf16"
+    rows = 9
+    x = _random(dtype, rows, hidden, hidden, 60)
+    r = _random(dtype, rows, hidden, hidden, 61)
+    w = _random(dtype, 1, hidden, hidden, 62)[0]
+    xd, rd, wd = dev(x, dtype), dev(r, dtype), dev(w, dtype)
+    out = arn.norm(xd, wd, 1e-6, residual=rd if fused else None, variance_size=k, fp8=fp8)
+    torch.cuda.synchronize()
+    mode = O.FP8_DYNAMIC if fp8 else O.FP8_NONE
+    ref = orc.add_rmsnorm(dtype, x, r if fused else None, w, 1e-6, fp8_mode=mode,
+                          variance_size=k)
+    if fused:
+        assert np.array_equal(bits(rd), ref["r16"])
+    if fp8:
+        q, sc = out
+        assert_codes_close(codes(q), ref["q"])
+        assert_scales_close(sc.cpu().numpy(), ref["scales"], dtype)
+    else:
+        assert_y_close(bits(out), ref["y"], dtype)
+
+
+def test_norm_descriptor_matches_entry_points(orc):
+    arn = _arn()
+    x = _random("fp16", 33, 2048, 2048, 63)
+    r = _random("fp16", 33, 2048, 2048, 64)
+    xd, r1, r2 = dev(x, "fp16"), dev(r, "fp16"), dev(r, "fp16")
+    a = arn.fused_add_rmsnorm(xd, r1, None, 1e-5)
+    b = arn.norm(xd, None, 1e-5, residual=r2)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(a), bits(b)) and np.array_equal(bits(r1), bits(r2))

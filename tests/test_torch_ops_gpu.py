@@ -1,0 +1,66 @@
+"""The arn:: torch custom ops on the GPU: eager results equal the binding's,
+and a function using them compiles with fullgraph=True (no graph breaks)
+and gives the same results."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from tests._helpers import assert_codes_close, assert_y_close, bits, codes, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import residual_add_rmsnorm_amd.torch_ops  # noqa: F401
+
+
+def _inputs(rows=48, hidden=2048, seed=70):
+    rng = np.random.default_rng(seed)
+    x = W.to_bits(rng.standard_normal((rows, hidden)).astype(np.float32), "bf16")
+    r = W.to_bits(rng.standard_normal((rows, hidden)).astype(np.float32), "bf16")
+    w = W.to_bits((1 + 0.1 * rng.standard_normal(hidden)).astype(np.float32), "bf16")
+    g = W.to_bits(rng.standard_normal((rows, 2 * hidden)).astype(np.float32), "bf16")
+    return x, r, w, g
+
+
+def block_tail(x, residual, weight, gate_up):
+    """residual += x; h = norm(residual) as dynamic e4m3; a = SwiGLU(gate_up)
+    as dynamic e4m3 -- the two fused kernels of one decoder block."""
+    q, s = torch.ops.arn.fused_add_rmsnorm_fp8_dynamic(x, residual, weight, 1e-6)
+    a, sa = torch.ops.arn.silu_and_mul_fp8_dynamic(gate_up)
+    return q, s, a, sa
+
+
+@pytest.mark.parametrize("compiled", [False, True])
+def test_block_tail(orc, compiled):
+    x, r, w, g = _inputs()
+    xd, rd, wd, gd = dev(x, "bf16"), dev(r, "bf16"), dev(w, "bf16"), dev(g, "bf16")
+    fn = torch.compile(block_tail, backend="aot_eager", fullgraph=True) if compiled else block_tail
+    q, s, a, sa = fn(xd, rd, wd, gd)
+    torch.cuda.synchronize()
+    ref = orc.add_rmsnorm("bf16", x, r, w, 1e-6, fp8_mode=O.FP8_DYNAMIC)
+    ref_g = orc.silu_and_mul("bf16", g, fp8_mode=O.FP8_DYNAMIC)
+    assert np.array_equal(bits(rd), ref["r16"]), "residual not updated in place"
+    assert_codes_close(codes(q), ref["q"])
+    assert_codes_close(codes(a), ref_g["q"])
+
+
+def test_ops_equal_binding():
+    import residual_add_rmsnorm_amd as arn
+
+    x, r, w, g = _inputs(seed=71)
+    xd, wd, gd = dev(x, "bf16"), dev(w, "bf16"), dev(g, "bf16")
+    r1, r2 = dev(r, "bf16"), dev(r, "bf16")
+    assert torch.equal(torch.ops.arn.fused_add_rmsnorm(xd, r1, wd, 1e-5),
+                       arn.fused_add_rmsnorm(xd, r2, wd, 1e-5))
+    assert torch.equal(r1, r2)
+    assert torch.equal(torch.ops.arn.rmsnorm(xd, wd, 1e-5), arn.rmsnorm(xd, wd, 1e-5))
+    assert torch.equal(torch.ops.arn.silu_and_mul(gd), arn.silu_and_mul(gd))
+    s = torch.tensor([0.02], device="cuda")
+    assert torch.equal(torch.ops.arn.silu_and_mul_fp8_static(gd, s).view(torch.uint8),
+                       arn.silu_and_mul_fp8(gd, scale=s)[0].view(torch.uint8))
