@@ -88,6 +88,16 @@ def bind(lib_path: str) -> ctypes.CDLL:
         ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float),
     ]
     lib.orc_silu_and_mul.restype = ctypes.c_int
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    lib.orc_fp8_gemm.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        u8p, ctypes.c_int64, f32p, ctypes.c_int,
+        u8p, ctypes.c_int64, f32p, ctypes.c_int,
+        ctypes.c_int, f64p, u16p, f64p,
+    ]
+    lib.orc_fp8_gemm.restype = ctypes.c_int
     return lib
 
 
@@ -229,6 +239,32 @@ class Oracle:
         if scales is not None:
             out["scales"] = scales
         return out
+
+
+    def fp8_gemm(self, a, sa, b, sb, k=None, out_dtype="bf16"):
+        """C = diag(sa) dec(A) dec(B)^T diag(sb) for uint8 code arrays
+        A (M x lda) and B (N x ldb); sa / sb hold M / N per-row scales or one
+        per-tensor scale.  Returns dict c (float64), c16 and abs (sum of
+        |products| times |scales|)."""
+        a = np.ascontiguousarray(a, dtype=np.uint8)
+        b = np.ascontiguousarray(b, dtype=np.uint8)
+        sa = np.ascontiguousarray(np.atleast_1d(sa), dtype=np.float32)
+        sb = np.ascontiguousarray(np.atleast_1d(sb), dtype=np.float32)
+        m, lda = a.shape
+        n, ldb = b.shape
+        k = min(lda, ldb) if k is None else int(k)
+        c = np.empty((m, n), np.float64)
+        c16 = np.empty((m, n), np.uint16)
+        ab = np.empty((m, n), np.float64)
+        rc = self.c.orc_fp8_gemm(m, n, k, _ptr(a, ctypes.c_uint8), lda, _ptr(sa, ctypes.c_float),
+                                 int(sa.size > 1),
+                                 _ptr(b, ctypes.c_uint8), ldb, _ptr(sb, ctypes.c_float),
+                                 int(sb.size > 1), DTYPES[out_dtype],
+                                 _ptr(c, ctypes.c_double), _ptr(c16, ctypes.c_uint16),
+                                 _ptr(ab, ctypes.c_double))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        return {"c": c, "c16": c16, "abs": ab}
 
 
 def oracle() -> Oracle:

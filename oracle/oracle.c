@@ -23,6 +23,9 @@
  *     the FP8 cast.  SwiGLU is Shazeer, "GLU Variants Improve
  *     Transformer" (2020): Swish_1(x W) * (x V), Swish_1 = SiLU; here the
  *     two projections arrive as the gate and up halves of one row.
+ *   - The third kernel of that article is a "skinny" GEMM for the small
+ *     batch shapes of decoding; here it is the plain definition of a
+ *     matrix product of decoded e4m3 codes times their dequant scales.
  *   - The FP8 format is OCP E4M3FN (bias 7, 3 mantissa bits, max 448, no
  *     infinities, NaN = S.1111.111).  "MI210 LLM Stack", key insight 4,
  *     counts 254 non-NaN e4m3 byte patterns, which is that format.
@@ -468,5 +471,45 @@ int orc_silu_and_mul(int dtype, int64_t rows, int64_t d,
     }
     free(y);
     free(q);
+    return 0;
+}
+
+/* --------------------------------------------------------------------- */
+/* e4m3 GEMM: C = diag(sa) (dec(A) dec(B)^T) diag(sb).                    */
+/* --------------------------------------------------------------------- */
+
+int orc_fp8_gemm(int64_t m, int64_t n, int64_t k,
+                 const uint8_t *a, int64_t lda, const float *sa, int a_per_row,
+                 const uint8_t *b, int64_t ldb, const float *sb, int b_per_row,
+                 int out_dtype, double *c_out, uint16_t *c16_out, double *abs_out)
+{
+    int64_t i, j, t;
+
+    if (m < 0 || n < 0 || k <= 0 || a == NULL || b == NULL || sa == NULL || sb == NULL ||
+        lda < k || ldb < k || (out_dtype != ORC_BF16 && out_dtype != ORC_FP16)) {
+        return -1;
+    }
+    for (i = 0; i < m; i++) {
+        double scale_a = (double)(a_per_row ? sa[i] : sa[0]);
+        for (j = 0; j < n; j++) {
+            double scale_b = (double)(b_per_row ? sb[j] : sb[0]);
+            double sum = 0.0;
+            double sum_abs = 0.0;
+            for (t = 0; t < k; t++) {
+                double p = orc_e4m3_decode(a[i * lda + t]) * orc_e4m3_decode(b[j * ldb + t]);
+                sum += p;
+                sum_abs += fabs(p);
+            }
+            if (c_out) {
+                c_out[i * n + j] = scale_a * scale_b * sum;
+            }
+            if (c16_out) {
+                c16_out[i * n + j] = orc_encode16(out_dtype, scale_a * scale_b * sum);
+            }
+            if (abs_out) {
+                abs_out[i * n + j] = fabs(scale_a * scale_b) * sum_abs;
+            }
+        }
+    }
     return 0;
 }

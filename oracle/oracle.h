@@ -91,6 +91,22 @@ int orc_silu_and_mul(int dtype, int64_t rows, int64_t d,
                      int fp8_mode, float static_scale,
                      uint8_t *q_out, float *scale_out);
 
+/*
+ * e4m3 GEMM with dequant scales (the "skinny GEMM" that consumes the FP8
+ * codes and per-row scales of the kernels above):
+ *     C[m][n] = sa(m) * sb(n) * sum_k dec(A[m][k]) * dec(B[n][k])
+ * A: M x K codes (row stride lda), B: N x K codes (row stride ldb, the
+ * weight of a linear layer stored out-feature major), sa: M per-row scales
+ * or 1 per-tensor scale (a_per_row = 0), sb likewise over N.  The sum runs
+ * k = 0..K-1 in fp64.  Outputs (dense, row stride N; may be NULL): c_out in
+ * fp64, c16_out rounded to the 16-bit dtype, and abs_out = the same sum of
+ * |products| (for error bounds).
+ */
+int orc_fp8_gemm(int64_t m, int64_t n, int64_t k,
+                 const uint8_t *a, int64_t lda, const float *sa, int a_per_row,
+                 const uint8_t *b, int64_t ldb, const float *sb, int b_per_row,
+                 int out_dtype, double *c_out, uint16_t *c16_out, double *abs_out);
+
 #ifdef __cplusplus
 }
 #endif

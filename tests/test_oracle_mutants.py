@@ -12,6 +12,7 @@ import pytest
 
 import oracle as O
 from tests import test_oracle_pins as pins
+from tests import test_oracle_gemm_pins as gemm_pins
 from tests import test_oracle_swiglu_pins as swiglu_pins
 
 MUTANTS = {
@@ -43,6 +44,12 @@ MUTANTS = {
     "silu_no_sigmoid": ("return g / (1.0 + exp(-g));", "return g;"),
     "gate_up_swapped": ("y[j] = orc_silu(g) * u;", "y[j] = orc_silu(u) * g;"),
     "up_row_stride": ("up[i * up_stride + j]", "up[i * gate_stride + j + 0 * up_stride]"),
+    "gemm_b_transposed": ("orc_e4m3_decode(b[j * ldb + t])", "orc_e4m3_decode(b[t * ldb + j])"),
+    "gemm_scale_b_per_row_ignored": ("double scale_b = (double)(b_per_row ? sb[j] : sb[0]);",
+                                     "double scale_b = (double)sb[0];"),
+    "gemm_k_off_by_one": ("for (t = 0; t < k; t++) {\n                double p",
+                          "for (t = 1; t < k; t++) {\n                double p"),
+    "gemm_a_row_stride": ("orc_e4m3_decode(a[i * lda + t])", "orc_e4m3_decode(a[i * k + t])"),
     "glu_dynamic_scale_of_u": ("double u = orc_decode16(dtype, up[i * up_stride + j]);",
                                "double u = orc_decode16(dtype, up[i * up_stride + j]) * 2.0;"),
 }
@@ -51,7 +58,8 @@ MUTANTS = {
 def _pin_functions():
     fns = []
     members = inspect.getmembers(pins, inspect.isfunction) + \
-        inspect.getmembers(swiglu_pins, inspect.isfunction)
+        inspect.getmembers(swiglu_pins, inspect.isfunction) + \
+        inspect.getmembers(gemm_pins, inspect.isfunction)
     for name, fn in members:
         if not name.startswith("test_"):
             continue
