@@ -33,6 +33,7 @@ METRIC = ("achieved HBM GB/s (% of MI355X peak) for fused add+RMSNorm(+fp8); "
 MALL_BYTES = 256 * 1024 * 1024
 KERNEL_SOURCES = ["residual_add_rmsnorm_amd/csrc/arn_kernels.hip",
                   "residual_add_rmsnorm_amd/csrc/arn_glu.hip",
+                  "residual_add_rmsnorm_amd/csrc/arn_gemm.hip",
                   "residual_add_rmsnorm_amd/csrc/arn_device.h",
                   "residual_add_rmsnorm_amd/csrc/arn_api.hip",
                   "residual_add_rmsnorm_amd/csrc/arn_internal.h"]
@@ -287,6 +288,58 @@ def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool) -> dict:
     return line
 
 
+def bench_gemm(name: str, steps: int, warmup: int) -> dict:
+    """The e4m3 skinny GEMM at each activation row count, with the weight
+    pre-shuffled (arn_fp8_gemm_preshuffled, the shuffle done once before the
+    timed region) and row-major (arn_fp8_gemm): device time per call,
+    weight-stream GB/s and TFLOP/s.  Weight copies rotate past the Infinity
+    Cache."""
+    import torch
+
+    import residual_add_rmsnorm_amd as arn
+    import workloads
+
+    g = workloads.GEMMS[name]
+    d = workloads.make_gemm(g, max(g.m_counts))
+    wbytes = g.n * g.k
+    sets = max(1, math.ceil(4 * MALL_BYTES / wbytes))
+    log(f"[bench] {name}: n {g.n} k {g.k}, {sets} weight copies")
+    b0 = torch.from_numpy(d["b"]).cuda()
+    sb = torch.from_numpy(d["scale_b"]).cuda()
+    a_all = torch.from_numpy(d["a"]).cuda()
+    sa_all = torch.from_numpy(d["scale_a"]).cuda()
+    layouts = {}
+    for layout in ("preshuffled", "rowmajor"):
+        if layout == "preshuffled":
+            bs = [arn.fp8_weight_preshuffle(b0) for _ in range(sets)]
+        else:
+            bs = [b0] + [b0.clone() for _ in range(sets - 1)]
+        per_m = {}
+        for m in g.m_counts:
+            a, sa = a_all[:m], sa_all[:m]
+            out = torch.empty((m, g.n), dtype=torch.bfloat16, device="cuda")
+
+            class _B:
+                def call(self, i):
+                    arn.fp8_gemm(a, sa, bs[i % sets], sb, out=out)
+
+            e_ms, wall = time_steps(_B(), steps, warmup)
+            us = e_ms * 1e3 / steps
+            per_m[str(m)] = {"us_per_call": round(us, 3),
+                             "GB_per_s": round(g.algorithmic_bytes(m) / us / 1e3, 1),
+                             "TFLOP_per_s": round(g.flops(m) / us / 1e6, 2),
+                             "plan": arn.last_plan()}
+            log(f"[bench] {layout} m={m}: {per_m[str(m)]}")
+        layouts[layout] = per_m
+        del bs
+        torch.cuda.empty_cache()
+    best = max(layouts["preshuffled"].values(), key=lambda v: v["GB_per_s"])
+    return {"workload": name, "n": g.n, "k": g.k, "weight_copies": sets,
+            "per_m": layouts["preshuffled"], "per_m_rowmajor": layouts["rowmajor"],
+            "roofline": {"bound": "hbm", "achieved": best["GB_per_s"], "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(best["GB_per_s"] / PEAK_HBM_GBS, 4)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -327,6 +380,12 @@ def main() -> int:
 
     _lib.load()  # fails loudly if the HIP library is missing
 
+    if args.workload in workloads.GEMMS or args.workload == "gemms":
+        gnames = list(workloads.GEMMS) if args.workload == "gemms" else [args.workload]
+        for n in gnames:
+            print(json.dumps(bench_gemm(n, min(args.steps, 200), min(args.warmup, 20))),
+                  flush=True)
+        return 0
     names = list(workloads.WORKLOADS) if args.workload == "all" else \
         [args.workload or workloads.HEADLINE]
     for n in names:

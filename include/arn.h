@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define ARN_ABI_VERSION 3
+#define ARN_ABI_VERSION 4
 
 enum arn_dtype { ARN_BF16 = 0, ARN_FP16 = 1 };
 enum arn_fp8_mode { ARN_FP8_STATIC = 0, ARN_FP8_DYNAMIC = 1 };
@@ -176,6 +176,56 @@ int arn_silu_and_mul_fp8(uint8_t *out, int64_t out_stride, float *scale, int fp8
                          const void *up, int64_t up_stride,
                          int64_t rows, int64_t d, int dtype, hipStream_t stream);
 
+/*
+ * e4m3 "skinny" GEMM for decode-sized activations (the third kernel of
+ * "Custom CUDA kernels juice Llama 3.1 405B on AMD MI300X", paragraph 2):
+ *     c[i][j] = sa(i) * sb(j) * sum_{t<k} dec(a[i][t]) * dec(b[j][t])
+ * with OCP e4m3 codes: a is m x k activations (row stride lda BYTES), e.g.
+ * the codes of arn_*_fp8; b is the n x k weight of a linear layer stored
+ * out-feature major (row stride ldb bytes).  scale_a holds m per-row
+ * dequant scales (a_per_row != 0) or one; scale_b holds n per-row scales
+ * (b_per_row != 0) or one.  c is m x n of out_dtype (bf16/fp16, row stride
+ * ldc elements), fp32 accumulation, one rounding.  Served: 1 <= m <= 64,
+ * k % 16 == 0, lda and ldb multiples of 16, a and b 16-byte aligned (else
+ * ARN_EUNSUPPORTED).  m or n == 0 launches nothing.  Device pointers,
+ * asynchronous on `stream`.
+ */
+int arn_fp8_gemm(void *c, int64_t ldc, int out_dtype,
+                 const uint8_t *a, int64_t lda, const float *scale_a, int a_per_row,
+                 const uint8_t *b, int64_t ldb, const float *scale_b, int b_per_row,
+                 int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
+/*
+ * Pre-shuffled weights.  The fp8 multiply that vLLM hands to AITER (page
+ * "vllm/rocm/use_aiter=1 slows Gemma 4 on an AMD MI300X", section "Why the
+ * fp8 Multiplies Run Slower") reads its weight in a pre-shuffled layout.
+ * Here the shuffled copy is a sequence of 2 KiB tiles, one per 16 weight
+ * rows and 128-wide k step (column tiles outer, k steps inner), each laid
+ * out so that every load instruction of the GEMM reads 1 KiB contiguous
+ * bytes.  Rows past n and k past the last whole step are zero codes.  The
+ * layout is private to this library: produce it with
+ * arn_fp8_weight_preshuffle and read it only with arn_fp8_gemm_preshuffled.
+ *
+ * arn_fp8_weight_preshuffled_bytes: size of the copy for an n x k weight
+ * (ceil(n/16) * ceil(k/128) * 2048), or -1 for n < 0 or k <= 0.
+ *
+ * arn_fp8_weight_preshuffle: writes the copy of the n x k row-major weight b
+ * (row stride ldb >= k bytes, any alignment) into dst (caller-allocated, the
+ * size above, 16-byte aligned, not overlapping b).  Served: k <= 2^23.
+ * Asynchronous on `stream`; done once per weight.
+ *
+ * arn_fp8_gemm_preshuffled: arn_fp8_gemm with the weight given as that copy
+ * (same n and k as at the shuffle); same results, same served shapes.
+ */
+int64_t arn_fp8_weight_preshuffled_bytes(int64_t n, int64_t k);
+int arn_fp8_weight_preshuffle(uint8_t *dst, const uint8_t *b, int64_t ldb,
+                              int64_t n, int64_t k, hipStream_t stream);
+int arn_fp8_gemm_preshuffled(void *c, int64_t ldc, int out_dtype,
+                             const uint8_t *a, int64_t lda, const float *scale_a,
+                             int a_per_row, const uint8_t *b_shuffled,
+                             const float *scale_b, int b_per_row,
+                             int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *arn_status_str(int status);
 
@@ -198,6 +248,13 @@ int arn_abi_version(void);
  * Returns the full length of the description.
  */
 int arn_set_tile(int waves_per_row, int vec_per_lane);
+
+/* arn_set_gemm_config forces the shape of later GEMM calls: each
+ * block computes col_tiles x 16 output columns (1, 2 or 4) with K split
+ * over `waves` waves (4, 8 or 16).  A call whose row tiling has no such
+ * compiled shape returns ARN_EUNSUPPORTED.  (0, 0) restores automatic
+ * selection; a shape never compiled returns ARN_EINVAL. */
+int arn_set_gemm_config(int col_tiles, int waves);
 int arn_last_plan(char *buf, size_t len);
 
 #ifdef __cplusplus

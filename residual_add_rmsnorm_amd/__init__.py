@@ -21,7 +21,7 @@ from ._lib import ArnError  # noqa: F401
 
 __all__ = [
     "rmsnorm", "fused_add_rmsnorm", "rmsnorm_fp8", "fused_add_rmsnorm_fp8",
-    "silu_and_mul", "silu_and_mul_fp8", "norm", "set_tile", "last_plan", "ArnError",
+    "silu_and_mul", "silu_and_mul_fp8", "norm", "fp8_gemm", "fp8_weight_preshuffle", "PreshuffledWeight", "set_tile", "set_gemm_config", "last_plan", "ArnError",
 ]
 
 _DTYPES = {torch.bfloat16: _lib.BF16, torch.float16: _lib.FP16}
@@ -292,9 +292,93 @@ def silu_and_mul_fp8(x: torch.Tensor, scale: torch.Tensor | None = None, dynamic
     return out, sc
 
 
+class PreshuffledWeight:
+    """An e4m3 weight [N, K] in the GEMM's pre-shuffled tile order
+    (arn_fp8_weight_preshuffle); pass it to fp8_gemm in place of the
+    row-major weight."""
+
+    def __init__(self, data: torch.Tensor, n: int, k: int):
+        self.data = data  # uint8, arn_fp8_weight_preshuffled_bytes(n, k) bytes
+        self.n = n
+        self.k = k
+        self.device = data.device
+
+    @property
+    def shape(self):
+        return (self.n, self.k)
+
+
+def fp8_weight_preshuffle(b: torch.Tensor) -> PreshuffledWeight:
+    """The pre-shuffled copy of an e4m3 weight b [N, K] (out-feature major)."""
+    _check_device(b)
+    if b.dtype not in (FP8_DTYPE, torch.uint8) or b.dim() != 2 or b.stride(1) != 1:
+        raise ValueError("b must be a 2-D e4m3 (or uint8) tensor with unit column stride")
+    n, k = b.shape
+    lib = _lib.load()
+    size = lib.arn_fp8_weight_preshuffled_bytes(n, k)
+    if size < 0:
+        raise ValueError("b must have K >= 1")
+    dst = torch.empty(max(size, 16), dtype=torch.uint8, device=b.device)
+    with torch.cuda.device(b.device):
+        st = lib.arn_fp8_weight_preshuffle(dst.data_ptr(), b.data_ptr(), b.stride(0), n, k,
+                                           _stream(b))
+    _lib.check(st, "arn_fp8_weight_preshuffle")
+    return PreshuffledWeight(dst, n, k)
+
+
+def fp8_gemm(a: torch.Tensor, scale_a: torch.Tensor, b, scale_b: torch.Tensor,
+             out_dtype: torch.dtype = torch.bfloat16,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    """out[i, j] = scale_a(i) * scale_b(j) * sum_t a[i, t] * b[j, t]
+    (arn_fp8_gemm) for e4m3 codes a [M, K] (float8_e4m3fn or uint8) and b
+    [N, K] (the weight, out-feature major) or its PreshuffledWeight
+    (arn_fp8_gemm_preshuffled); scale_a holds M or 1 float32 values,
+    scale_b N or 1."""
+    pre = isinstance(b, PreshuffledWeight)
+    for t, nm in ((a, "a"),) if pre else ((a, "a"), (b, "b")):
+        _check_device(t)
+        if t.dtype not in (FP8_DTYPE, torch.uint8) or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{nm} must be a 2-D e4m3 (or uint8) tensor with unit column stride")
+    if pre and b.device != a.device:
+        raise ValueError("a and b must be on the same device")
+    m, k = a.shape
+    n, kb = b.shape
+    if kb != k:
+        raise ValueError("a and b must have the same K")
+    for sc, cnt, nm in ((scale_a, m, "scale_a"), (scale_b, n, "scale_b")):
+        if (sc.dtype != torch.float32 or not sc.is_contiguous() or sc.numel() not in (1, cnt)
+                or sc.device != a.device):
+            raise ValueError(f"{nm} must hold 1 or {cnt} contiguous float32 values")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    if out.shape != (m, n) or out.dtype not in _DTYPES or out.stride(1) != 1:
+        raise ValueError("out must be [M, N] bfloat16/float16 with unit column stride")
+    lib = _lib.load()
+    a_rows = int(scale_a.numel() > 1 or m == 1)
+    b_rows = int(scale_b.numel() > 1 or n == 1)
+    with torch.cuda.device(a.device):
+        if pre:
+            st = lib.arn_fp8_gemm_preshuffled(out.data_ptr(), out.stride(0), _DTYPES[out.dtype],
+                                              a.data_ptr(), a.stride(0), scale_a.data_ptr(),
+                                              a_rows, b.data.data_ptr(), scale_b.data_ptr(),
+                                              b_rows, m, n, k, _stream(a))
+        else:
+            st = lib.arn_fp8_gemm(out.data_ptr(), out.stride(0), _DTYPES[out.dtype],
+                                  a.data_ptr(), a.stride(0), scale_a.data_ptr(), a_rows,
+                                  b.data_ptr(), b.stride(0), scale_b.data_ptr(), b_rows,
+                                  m, n, k, _stream(a))
+    _lib.check(st, "arn_fp8_gemm_preshuffled" if pre else "arn_fp8_gemm")
+    return out
+
+
 def set_tile(waves_per_row: int = 0, vec_per_lane: int = 0) -> None:
     """Force a kernel shape for later calls ((0, 0) = automatic)."""
     _lib.check(_lib.load().arn_set_tile(waves_per_row, vec_per_lane), "arn_set_tile")
+
+
+def set_gemm_config(col_tiles: int = 0, waves: int = 0) -> None:
+    """Force the e4m3 GEMM's block shape for later calls ((0, 0) = automatic)."""
+    _lib.check(_lib.load().arn_set_gemm_config(col_tiles, waves), "arn_set_gemm_config")
 
 
 def last_plan() -> str:

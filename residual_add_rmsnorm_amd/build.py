@@ -40,8 +40,9 @@ DTYPES = range(2)
 
 
 def sources() -> list[str]:
-    return [os.path.join(CSRC, f) for f in ("arn_kernels.hip", "arn_glu.hip", "arn_api.hip",
-                                            "arn_internal.h", "arn_device.h")] + [
+    return [os.path.join(CSRC, f) for f in ("arn_kernels.hip", "arn_glu.hip", "arn_gemm.hip",
+                                            "arn_api.hip", "arn_internal.h",
+                                            "arn_device.h")] + [
         os.path.join(INCLUDE, "arn.h")]
 
 
@@ -72,6 +73,9 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
             units.append((os.path.join(CSRC, "arn_glu.hip"),
                           os.path.join(OBJ_DIR, f"arn_glu_m{m}_d{d}.o"),
                           [f"-DARN_GLU_MODE={m}", f"-DARN_DT={d}"]))
+    for d in DTYPES:
+        units.append((os.path.join(CSRC, "arn_gemm.hip"),
+                      os.path.join(OBJ_DIR, f"arn_gemm_d{d}.o"), [f"-DARN_DT={d}"]))
     units.append((os.path.join(CSRC, "arn_api.hip"), os.path.join(OBJ_DIR, "arn_api.o"), []))
     jobs = jobs or min(16, os.cpu_count() or 4)
     with ThreadPoolExecutor(max_workers=jobs) as ex:

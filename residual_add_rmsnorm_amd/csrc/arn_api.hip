@@ -19,6 +19,9 @@
 namespace {
 
 using arn::Args;
+using arn::GemmArgs;
+using arn::GemmCfg;
+using arn::GemmTable;
 using arn::Tile;
 using arn::TileTable;
 
@@ -294,9 +297,170 @@ int run_glu(int mode, int dtype, void* out, int64_t out_stride, float* scale, co
   return ARN_OK;
 }
 
+// Forced GEMM shape (arn_set_gemm_config); 0 = automatic.  nt << 8 | waves.
+std::atomic<int> g_forced_gemm{0};
+
+// GEMM shape, from sweeps of decode projections on MI355X (N 2304..16384,
+// K 2048..16384, M 1..64).  The weight stream wants about one block per CU
+// or more: the widest column tile (fewest re-reads of the activations) that
+// still gives at least 3/4 of a block per CU.  With one row tile, K is split
+// over as many waves as keep each wave at four or more 128-wide k steps (up
+// to 16); with two or four row tiles the accumulators and operands of a
+// wave fill its registers, and four waves per block do best.
+const GemmCfg* choose_gemm(const GemmTable* table, int mt, int64_t n, int64_t k, int cus) {
+  const int forced = g_forced_gemm.load(std::memory_order_relaxed);
+  auto find = [&](int nt, int waves) -> const GemmCfg* {
+    for (int i = 0; i < table->count; ++i) {
+      const GemmCfg& g = table->cfgs[i];
+      if (g.mt == mt && g.nt == nt && g.waves == waves) return &g;
+    }
+    return nullptr;
+  };
+  if (forced != 0) return find(forced >> 8, forced & 0xFF);
+  const int64_t ksteps = (k + 127) / 128;
+  const int64_t want_blocks = (3 * (int64_t)cus) / 4;
+  auto blocks = [&](int nt) { return (n + 16 * nt - 1) / (16 * nt); };
+  int nt = 1;
+  if (mt == 1 && blocks(4) >= want_blocks) {
+    nt = 4;
+  } else if (blocks(2) >= want_blocks) {
+    nt = 2;
+  }
+  int waves = 4;
+  if (mt == 1) waves = ksteps >= 64 ? 16 : (ksteps >= 32 ? 8 : 4);
+  return find(nt, waves);
+}
+
+// Largest weight slice one GEMM launch addresses (buffer records are 32-bit).
+constexpr int64_t kMaxGemmBBytes = int64_t(1) << 31;
+// Largest K of a pre-shuffled weight: a block's slice (up to 16 column tiles
+// of ceil(K/128) 2 KiB tiles) stays under 2 GiB.
+constexpr int64_t kMaxPreshuffleK = int64_t(1) << 23;
+
+int64_t preshuffled_bytes(int64_t n, int64_t k) {
+  return ((n + 15) / 16) * ((k + 127) / 128) * 2048;
+}
+
+// pre: b is the pre-shuffled copy (ldb ignored), else N x K row-major.
+int run_gemm(bool pre, void* c, int64_t ldc, int out_dtype, const uint8_t* a, int64_t lda,
+             const float* scale_a, int a_per_row, const uint8_t* b, int64_t ldb,
+             const float* scale_b, int b_per_row, int64_t m, int64_t n, int64_t k,
+             hipStream_t stream) {
+  if (out_dtype != ARN_BF16 && out_dtype != ARN_FP16) return ARN_EINVAL;
+  if (m < 0 || n < 0 || k <= 0) return ARN_EINVAL;
+  if (lda < k || (!pre && ldb < k) || ldc < n) return ARN_EINVAL;
+  if (m == 0 || n == 0) return ARN_OK;
+  if (!c || !a || !b || !scale_a || !scale_b) return ARN_EINVAL;
+  if (!aligned(c, 2) || !aligned(scale_a, 4) || !aligned(scale_b, 4)) return ARN_EINVAL;
+  // Served shapes: up to 64 activation rows, K a multiple of 16, 16-byte
+  // aligned operand rows.
+  if (m > 64 || k % 16 != 0 || lda % 16 != 0 || !aligned(a, 16) || !aligned(b, 16) ||
+      m * lda > kMaxGemmBBytes) {
+    return ARN_EUNSUPPORTED;
+  }
+  if (pre ? k > kMaxPreshuffleK : (ldb % 16 != 0 || ldb > kMaxGemmBBytes / 16)) {
+    return ARN_EUNSUPPORTED;
+  }
+  const int mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+  const GemmTable* table = &ARN_GEMM_TABLE_NAME(0);
+  if (out_dtype == ARN_FP16) table = &ARN_GEMM_TABLE_NAME(1);
+  const GemmCfg* cfg = choose_gemm(table, mt, n, k, cu_count());
+  if (!cfg) return ARN_EUNSUPPORTED;
+  const int nt = cfg->nt;
+  const int64_t nsteps = (k + 127) / 128;
+
+  // Split N so that each launch's weight slice stays under 2 GiB (row-major)
+  // and the grid stays well inside the launch limit.
+  int64_t rows_per_launch = pre ? (int64_t(1) << 30) : (kMaxGemmBBytes / ldb);
+  rows_per_launch = rows_per_launch / (16 * nt) * (16 * nt);
+  if (rows_per_launch <= 0) return ARN_EUNSUPPORTED;
+  int64_t done = 0;
+  int64_t grid = 0;
+  while (done < n) {
+    const int64_t cols = (n - done < rows_per_launch) ? n - done : rows_per_launch;
+    GemmArgs g;
+    g.c = static_cast<char*>(c) + done * 2;
+    g.ldc = ldc;
+    g.a = a;
+    g.lda = lda;
+    g.scale_a = scale_a;
+    g.b = pre ? b + (done / 16) * nsteps * 2048 : b + done * ldb;
+    g.ldb = pre ? 0 : ldb;
+    g.scale_b = b_per_row ? scale_b + done : scale_b;
+    g.m = m;
+    g.n = cols;
+    g.k = k;
+    g.a_per_row = a_per_row ? 1 : 0;
+    g.b_per_row = b_per_row ? 1 : 0;
+    grid = (cols + 16 * nt - 1) / (16 * nt);
+    void* params[] = {&g};
+    const hipError_t e = hipLaunchKernel(pre ? cfg->fn_pre : cfg->fn, dim3((unsigned)grid),
+                                         dim3(64u * cfg->waves), params, 0, stream);
+    if (e != hipSuccess) return ARN_ELAUNCH;
+    done += cols;
+  }
+  g_last_plan_len = std::snprintf(g_last_plan, sizeof(g_last_plan),
+                                  "fp8_gemm%s/%s/mt%d/nt%d/waves%d/grid%lld",
+                                  pre ? "_preshuffled" : "",
+                                  out_dtype == ARN_BF16 ? "bf16" : "fp16", cfg->mt, cfg->nt,
+                                  cfg->waves, (long long)grid);
+  return ARN_OK;
+}
+
+int run_preshuffle(uint8_t* dst, const uint8_t* b, int64_t ldb, int64_t n, int64_t k,
+                   hipStream_t stream) {
+  if (n < 0 || k <= 0 || ldb < k) return ARN_EINVAL;
+  if (n == 0) return ARN_OK;
+  if (!dst || !b) return ARN_EINVAL;
+  if (!aligned(dst, 16) || k > kMaxPreshuffleK) return ARN_EUNSUPPORTED;
+  const int64_t pieces = preshuffled_bytes(n, k) / 16;
+  const int64_t grid = (pieces + 255) / 256;
+  if (grid > int64_t(0x7FFFFFFF)) return ARN_EUNSUPPORTED;
+  arn::PreshuffleArgs p;
+  p.dst = dst;
+  p.src = b;
+  p.ldb = ldb;
+  p.n = n;
+  p.k = k;
+  p.ntiles = (n + 15) / 16;
+  p.nsteps = (k + 127) / 128;
+  p.aligned = (ldb % 16 == 0 && aligned(b, 16)) ? 1 : 0;
+  void* params[] = {&p};
+  const hipError_t e =
+      hipLaunchKernel(arn_preshuffle_fn, dim3((unsigned)grid), dim3(256u), params, 0, stream);
+  return e == hipSuccess ? ARN_OK : ARN_ELAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
+
+int arn_fp8_gemm(void* c, int64_t ldc, int out_dtype, const uint8_t* a, int64_t lda,
+                 const float* scale_a, int a_per_row, const uint8_t* b, int64_t ldb,
+                 const float* scale_b, int b_per_row, int64_t m, int64_t n, int64_t k,
+                 hipStream_t stream) {
+  return run_gemm(false, c, ldc, out_dtype, a, lda, scale_a, a_per_row, b, ldb, scale_b,
+                  b_per_row, m, n, k, stream);
+}
+
+int64_t arn_fp8_weight_preshuffled_bytes(int64_t n, int64_t k) {
+  if (n < 0 || k <= 0) return -1;
+  return preshuffled_bytes(n, k);
+}
+
+int arn_fp8_weight_preshuffle(uint8_t* dst, const uint8_t* b, int64_t ldb, int64_t n, int64_t k,
+                              hipStream_t stream) {
+  return run_preshuffle(dst, b, ldb, n, k, stream);
+}
+
+int arn_fp8_gemm_preshuffled(void* c, int64_t ldc, int out_dtype, const uint8_t* a, int64_t lda,
+                             const float* scale_a, int a_per_row, const uint8_t* b_shuffled,
+                             const float* scale_b, int b_per_row, int64_t m, int64_t n, int64_t k,
+                             hipStream_t stream) {
+  return run_gemm(true, c, ldc, out_dtype, a, lda, scale_a, a_per_row, b_shuffled, 0, scale_b,
+                  b_per_row, m, n, k, stream);
+}
+
 
 int arn_silu_and_mul(void* out, int64_t out_stride, const void* gate, int64_t gate_stride,
                      const void* up, int64_t up_stride, int64_t rows, int64_t d, int dtype,
@@ -401,6 +565,21 @@ int arn_set_tile(int waves_per_row, int vec_per_lane) {
   for (int i = 0; i < t->count; ++i) {
     if (t->tiles[i].wpr == waves_per_row && t->tiles[i].nv == vec_per_lane) {
       g_forced_tile.store((waves_per_row << 8) | vec_per_lane);
+      return ARN_OK;
+    }
+  }
+  return ARN_EINVAL;
+}
+
+int arn_set_gemm_config(int col_tiles, int waves) {
+  if (col_tiles == 0 && waves == 0) {
+    g_forced_gemm.store(0);
+    return ARN_OK;
+  }
+  const GemmTable* t = &ARN_GEMM_TABLE_NAME(0);
+  for (int i = 0; i < t->count; ++i) {
+    if (t->cfgs[i].nt == col_tiles && t->cfgs[i].waves == waves) {
+      g_forced_gemm.store((col_tiles << 8) | waves);
       return ARN_OK;
     }
   }

@@ -1,0 +1,259 @@
+// arn_gemm.hip -- gfx950 "skinny" GEMM on OCP e4m3 codes:
+//     C[m][n] = sa(m) * sb(n) * sum_k A[m][k] * B[n][k]
+// with A the e4m3 activations (M x K, per-row or per-tensor dequant scale,
+// e.g. the codes and scales the fused norm / SwiGLU kernels write) and B an
+// e4m3 weight stored out-feature major (N x K, per-row or per-tensor
+// scale).  The third kernel of "Custom CUDA kernels juice Llama 3.1 405B on
+// AMD MI300X" (paragraph 2) is a GEMM tuned for the small-batch shapes of
+// decoding; this is that contraction built for gfx950.  Compiled once per
+// output dtype (-DARN_DT=0|1).
+//
+// Decode GEMMs stream the weight: with M <= 64 rows of activations the
+// bytes of B dominate and the kernel is HBM-bound, so the layout serves the
+// weight stream:
+//  * v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3 -> fp32): each lane brings 32
+//    bytes of one row of A and of B for a 128-wide k step, as two 16-byte
+//    pieces laid out so that one load instruction reads 64 contiguous bytes
+//    of each of 16 weight rows.  The k order inside an MFMA is the same for
+//    both operands, and a dot product does not depend on it, so the pieces
+//    need no shuffling.
+//  * a block owns a (16 MT) x (16 NT) output tile and splits K over WAVES
+//    waves in interleaved 128-wide steps (the block reads each weight row
+//    front to back); A tiles are reused across the NT weight tiles of a
+//    step.  Partial tiles are summed through LDS in a fixed order, so the
+//    result is deterministic; the dequant scales are applied at the store.
+//  * operands are read with bounded buffer loads: rows past M or N read as
+//    zero, and a k step past K is given an out-of-range offset.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "arn_device.h"
+#include "arn_internal.h"
+
+#if !defined(ARN_DT)
+#error "compile with -DARN_DT=<0|1>"
+#endif
+
+namespace arn {
+namespace {
+
+using namespace dev;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Byte offset past any slice a launch addresses (the host keeps slices
+// under 2 GiB): a 16-byte load there reads zeros.
+constexpr uint32_t kOutOfRange = 0xFFFFFF00u;
+
+// A lane's 32 bytes of one 128-byte k step come from two 16-byte pieces:
+// bytes [16 q, 16 q + 16) and [64 + 16 q, 64 + 16 q + 16) for lane group q.
+// Each load instruction then reads 64 contiguous bytes of every row it
+// touches.  The MFMA pairs A and B bytes by their position in the lane, and
+// both operands use this same map, so the dot product is unchanged.  Each
+// piece gets its own offset, out of range when it lies past K.
+template <int CP>
+__device__ __forceinline__ i32x8 load32(__amdgpu_buffer_rsrc_t r, uint32_t lo, uint32_t hi) {
+  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)lo, 0, CP);
+  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)hi, 0, CP);
+  i32x8 v;
+  v[0] = (int)a.x;
+  v[1] = (int)a.y;
+  v[2] = (int)a.z;
+  v[3] = (int)a.w;
+  v[4] = (int)b.x;
+  v[5] = (int)b.y;
+  v[6] = (int)b.z;
+  v[7] = (int)b.w;
+  return v;
+}
+
+template <int DT, int MT, int NT, int WAVES, bool PRE>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 4)))
+void gemm_fp8_kernel(const GemmArgs g) {
+  constexpr int kTile = MT * NT * 256;  // outputs per block
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;  // operand row within a 16-row tile
+  const int kq = lane >> 4;   // 32-byte quarter of a 128-wide k step
+
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * NT;
+  const int64_t n_here = (g.n - n0) < 16 * NT ? (g.n - n0) : 16 * NT;
+  const int nsteps = (int)((g.k + 127) / 128);
+  const __amdgpu_buffer_rsrc_t ars = row_rsrc(g.a, (uint32_t)(g.m * g.lda));
+  // Row-major weight: this block's rows.  Pre-shuffled weight: this block's
+  // column tiles, each nsteps consecutive 2 KiB MFMA tiles.
+  const __amdgpu_buffer_rsrc_t brs =
+      PRE ? row_rsrc(static_cast<const uint8_t*>(g.b) + (n0 / 16) * nsteps * 2048,
+                     (uint32_t)(((n_here + 15) / 16) * nsteps * 2048))
+          : row_rsrc(static_cast<const uint8_t*>(g.b) + n0 * g.ldb, (uint32_t)(n_here * g.ldb));
+
+  uint32_t aoff[MT], boff[NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    aoff[i] = (uint32_t)((i * 16 + r16) * g.lda) + (PRE ? 32u : 16u) * kq;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    boff[t] = PRE ? (uint32_t)(t * nsteps * 2048) + 16u * lane
+                  : (uint32_t)((t * 16 + r16) * g.ldb) + 16u * kq;
+  }
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[i][t] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+  // K steps of 128 are dealt to the waves round-robin.  Two register sets
+  // ping-pong: the loads of a wave's next step are in flight while the MFMAs
+  // of its current step run, and no register copy forces an early wait.  A
+  // step past K reads zeros through out-of-range offsets (no memory
+  // traffic), so the loop always runs whole pairs.
+  auto load_step = [&](int s, i32x8 (&bq)[NT], i32x8 (&aq)[MT]) {
+    const uint32_t kb = (uint32_t)s * 128u;
+    if constexpr (PRE) {
+      // Pre-shuffled: a 2 KiB tile per (column tile, k step), read as two
+      // 1 KiB contiguous halves; lane l gets bytes [32 q, 32 q + 32) of
+      // k step s for row l % 16 (q = l / 16).  K is padded with zero codes
+      // to whole steps in the shuffled copy; A pieces past K read zeros.
+      const bool in_s = s < nsteps;
+      const bool a_lo = kb + 32u * kq < (uint32_t)g.k;
+      const bool a_hi = kb + 32u * kq + 16u < (uint32_t)g.k;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t o = boff[t] + (uint32_t)s * 2048u;
+        bq[t] = load32<kCacheStream>(brs, in_s ? o : kOutOfRange, in_s ? o + 1024u : kOutOfRange);
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        aq[i] = load32<kCacheDefault>(ars, a_lo ? aoff[i] + kb : kOutOfRange,
+                                      a_hi ? aoff[i] + kb + 16u : kOutOfRange);
+      }
+    } else {
+      // K % 16 == 0: every 16-byte piece is wholly inside or outside K
+      const bool lo_in = kb + 16u * kq < (uint32_t)g.k;
+      const bool hi_in = kb + 64u + 16u * kq < (uint32_t)g.k;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        bq[t] = load32<kCacheStream>(brs, lo_in ? boff[t] + kb : kOutOfRange,
+                                     hi_in ? boff[t] + kb + 64u : kOutOfRange);
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        aq[i] = load32<kCacheDefault>(ars, lo_in ? aoff[i] + kb : kOutOfRange,
+                                      hi_in ? aoff[i] + kb + 64u : kOutOfRange);
+      }
+    }
+  };
+  auto mma = [&](const i32x8 (&bq)[NT], const i32x8 (&aq)[MT]) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[i][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[i], bq[t], acc[i][t], 0,
+                                                                     0, 0, 0, 0, 0);
+  };
+  // The scheduling barriers keep the compiler from sinking each load next
+  // to its use (which would serialise load and MFMA again).
+  i32x8 b0[NT], a0[MT], b1[NT], a1[MT];
+  load_step(wave, b0, a0);
+  for (int s = wave; s < nsteps; s += 2 * WAVES) {
+    load_step(s + WAVES, b1, a1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(b0, a0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(s + 2 * WAVES, b0, a0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(b1, a1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Sum the WAVES partial tiles.  In a 16x16 MFMA result, lane l holds
+  // rows 4*(l/16) .. 4*(l/16)+3 of column l%16.
+  __shared__ float part[WAVES * kTile];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        part[wave * kTile + ((i * NT + t) * 16 + 4 * kq + j) * 16 + r16] = acc[i][t][j];
+  __syncthreads();
+
+  for (int e = threadIdx.x; e < kTile; e += 64 * WAVES) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += part[w * kTile + e];
+    const int tile = e >> 8;
+    const int row = (e >> 4) & 15;
+    const int col = e & 15;
+    const int64_t gm = (int64_t)(tile / NT) * 16 + row;
+    const int64_t gn = n0 + (int64_t)(tile % NT) * 16 + col;
+    if (gm < g.m && gn < g.n) {
+      const float sa = g.a_per_row ? g.scale_a[gm] : g.scale_a[0];
+      const float sb = g.b_per_row ? g.scale_b[gn] : g.scale_b[0];
+      const float v = sum * sa * sb;
+      static_cast<uint16_t*>(g.c)[gm * g.ldc + gn] = (uint16_t)(pack2<DT>(v, 0.0f) & 0xFFFFu);
+    }
+  }
+}
+
+// Pre-shuffle: one thread per 16-byte piece of the shuffled weight.  The
+// shuffled copy holds ceil(n/16) column tiles x ceil(k/128) k steps of
+// 2 KiB; in a tile, piece p (16 bytes) holds, for row r = p % 16 of the
+// column tile and lane group q = (p % 64) / 16, k bytes
+// [32 q + 16 (p / 64), +16) of the step -- so that lane l of a load of
+// bytes [16 l, 16 l + 16) and of [1024 + 16 l, +16) receives the 32 bytes
+// [32 q, 32 q + 32) of row l % 16 that the MFMA operand layout wants.
+// Rows past n and k bytes past k are zero codes.  Any row stride works;
+// aligned rows are read 16 bytes at a time.
+__global__ __launch_bounds__(256) void preshuffle_kernel(const PreshuffleArgs p) {
+  const int64_t piece = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = p.ntiles * p.nsteps * 128;
+  if (piece >= total) return;
+  const int64_t tile = piece / 128;
+  const int pp = (int)(piece % 128);
+  const int64_t nt = tile / p.nsteps;
+  const int64_t s = tile % p.nsteps;
+  const int64_t row = nt * 16 + (pp % 16);
+  const int64_t k0 = s * 128 + 32 * ((pp % 64) / 16) + 16 * (pp / 64);
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (row < p.n) {
+    const uint8_t* src = static_cast<const uint8_t*>(p.src) + row * p.ldb;
+    if (p.aligned && k0 + 16 <= p.k) {
+      v = *reinterpret_cast<const u32x4*>(src + k0);  // b and ldb 16-byte aligned
+    } else {
+      uint8_t b[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) b[i] = (k0 + i < p.k) ? src[k0 + i] : 0;
+      v = __builtin_bit_cast(u32x4, b);
+    }
+  }
+  reinterpret_cast<u32x4*>(p.dst)[piece] = v;
+}
+
+}  // namespace
+}  // namespace arn
+
+#define ARN_GEMM_CFG(MT, NT, WAVES)                                             \
+  {MT, NT, WAVES, (const void*)&arn::gemm_fp8_kernel<ARN_DT, MT, NT, WAVES, false>, \
+   (const void*)&arn::gemm_fp8_kernel<ARN_DT, MT, NT, WAVES, true>}
+
+static const arn::GemmCfg kGemmCfgs[] = {
+    ARN_GEMM_CFG(1, 4, 4), ARN_GEMM_CFG(1, 4, 8), ARN_GEMM_CFG(1, 4, 16),
+    ARN_GEMM_CFG(1, 2, 4), ARN_GEMM_CFG(1, 2, 8), ARN_GEMM_CFG(1, 2, 16),
+    ARN_GEMM_CFG(1, 1, 4), ARN_GEMM_CFG(1, 1, 8), ARN_GEMM_CFG(1, 1, 16),
+    ARN_GEMM_CFG(2, 2, 4), ARN_GEMM_CFG(2, 2, 8), ARN_GEMM_CFG(2, 2, 16),
+    ARN_GEMM_CFG(2, 1, 4), ARN_GEMM_CFG(2, 1, 8), ARN_GEMM_CFG(2, 1, 16),
+    ARN_GEMM_CFG(4, 2, 4), ARN_GEMM_CFG(4, 2, 8),
+    ARN_GEMM_CFG(4, 1, 4), ARN_GEMM_CFG(4, 1, 8), ARN_GEMM_CFG(4, 1, 16),
+};
+
+extern const arn::GemmTable ARN_GEMM_TABLE_NAME(ARN_DT) = {
+    kGemmCfgs, (int)(sizeof(kGemmCfgs) / sizeof(kGemmCfgs[0]))};
+
+#if ARN_DT == 0
+extern const void* const arn_preshuffle_fn = (const void*)&arn::preshuffle_kernel;
+#endif

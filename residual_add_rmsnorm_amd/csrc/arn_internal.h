@@ -1,6 +1,7 @@
 // Internal interface between the host dispatcher (arn_api.hip) and the
 // kernel instantiation units (arn_kernels.hip, compiled once per operator
-// kind and dtype; arn_glu.hip, once per SwiGLU output mode and dtype).
+// kind and dtype; arn_glu.hip, once per SwiGLU output mode and dtype;
+// arn_gemm.hip, once per output dtype).
 #pragma once
 
 #include <stdint.h>
@@ -55,6 +56,50 @@ struct GluArgs {
   int32_t d;
 };
 
+// e4m3 GEMM arguments: C[m][n] = sa(m) sb(n) sum_k A[m][k] B[n][k].
+struct GemmArgs {
+  void* c;             // m x n of the 16-bit output dtype, row stride ldc elements
+  int64_t ldc;
+  const void* a;       // m x k codes, row stride lda bytes
+  int64_t lda;
+  const float* scale_a;
+  const void* b;       // n x k codes, row stride ldb bytes
+  int64_t ldb;
+  const float* scale_b;
+  int64_t m;
+  int64_t n;
+  int64_t k;
+  int32_t a_per_row;
+  int32_t b_per_row;
+};
+
+// One compiled GEMM shape: MT x NT tiles of 16 x 16 outputs per block, K
+// split over `waves` waves.
+struct GemmCfg {
+  int mt;
+  int nt;
+  int waves;
+  const void* fn;      // row-major weight
+  const void* fn_pre;  // pre-shuffled weight
+};
+
+// Weight pre-shuffle into MFMA tile order (see arn_gemm.hip).
+struct PreshuffleArgs {
+  void* dst;
+  const void* src;
+  int64_t ldb;
+  int64_t n;
+  int64_t k;
+  int64_t ntiles;  // ceil(n / 16)
+  int64_t nsteps;  // ceil(k / 128)
+  int aligned;     // src and ldb are multiples of 16 bytes
+};
+
+struct GemmTable {
+  const GemmCfg* cfgs;
+  int count;
+};
+
 // One compiled kernel shape.  A lane owns vectors of VEC contiguous
 // elements; WPR waves (64 lanes each) share a row; a lane keeps up to NV
 // vectors of its row in registers; a block holds RPB rows.
@@ -101,3 +146,9 @@ ARN_DECLARE_GLU_TABLE(1, 0)
 ARN_DECLARE_GLU_TABLE(1, 1)
 ARN_DECLARE_GLU_TABLE(2, 0)
 ARN_DECLARE_GLU_TABLE(2, 1)
+
+#define ARN_GEMM_TABLE_NAME_(DT) arn_gemm_cfgs_d##DT
+#define ARN_GEMM_TABLE_NAME(DT) ARN_GEMM_TABLE_NAME_(DT)
+extern const arn::GemmTable ARN_GEMM_TABLE_NAME(0);
+extern const arn::GemmTable ARN_GEMM_TABLE_NAME(1);
+extern const void* const arn_preshuffle_fn;

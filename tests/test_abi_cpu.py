@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function(lib):
     for name in header_functions():
         assert name in exported, name
         assert getattr(lib, name) is not None
-    assert lib.arn_abi_version() == _lib.ABI_VERSION == 3
+    assert lib.arn_abi_version() == _lib.ABI_VERSION == 4
 
 
 def test_hip_imports_resolve_in_torch_runtime():

@@ -1,0 +1,204 @@
+"""Parity of the e4m3 skinny GEMM (MFMA path, through the C ABI) with the
+oracle.
+
+Tolerance: the oracle sums in fp64; the GPU accumulates fp32 through a
+chain of about k/128 + 256 additions, each off by at most 2^-24 of the sum
+of |products|, and rounds once to 16 bits:
+    |c - c_ref| <= rho |c_ref| + ulp16(c_ref) + (k/128 + 256) 2^-24 abs_ref.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests._helpers import RHO, bits, dev, ulp16, values16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def _codes(rng, rows, cols, std):
+    f = torch.from_numpy((rng.standard_normal((rows, cols)) * std).astype(np.float32))
+    return f.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def check(orc, m, n, k, out="bf16", per_row=(True, True), seed=0, lda=None, ldb=None,
+          pre=False):
+    import residual_add_rmsnorm_amd as arn
+
+    rng = np.random.default_rng(seed)
+    lda, ldb = lda or k, ldb or k
+    a = np.full((m, lda), 0x7F, np.uint8)   # NaN codes in any padding
+    b = np.full((n, ldb), 0x7F, np.uint8)
+    a[:, :k] = _codes(rng, m, k, 24.0)
+    b[:, :k] = _codes(rng, n, k, 6.0)
+    sa = rng.uniform(0.01, 0.1, m if per_row[0] else 1).astype(np.float32)
+    sb = rng.uniform(0.001, 0.01, n if per_row[1] else 1).astype(np.float32)
+    ad = torch.from_numpy(a).cuda()[:, :k]
+    bd = torch.from_numpy(b).cuda()[:, :k]
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[out]
+    c = torch.full((m + 1, n), float("nan"), dtype=dt, device="cuda")
+    if pre:
+        bd = arn.fp8_weight_preshuffle(bd)
+    arn.fp8_gemm(ad, torch.from_numpy(sa).cuda(), bd, torch.from_numpy(sb).cuda(), out=c[:m])
+    torch.cuda.synchronize()
+    ref = orc.fp8_gemm(a, sa if per_row[0] else sa[0], b, sb if per_row[1] else sb[0], k=k,
+                       out_dtype=out)
+    got = values16(bits(c[:m]), out)
+    tol = RHO[out] * np.abs(ref["c"]) + ulp16(ref["c"], out) + \
+        (k / 128 + 256) * 2.0**-24 * ref["abs"]
+    err = np.abs(got - ref["c"])
+    assert np.all(err <= tol), f"max err/tol {np.max(err / tol)} at {np.unravel_index(np.argmax(err / tol), err.shape)}"
+    assert torch.isnan(c[m].float()).all(), "wrote past the last row"
+    return arn.last_plan()
+
+
+LAYOUTS = pytest.mark.parametrize("pre", [False, True], ids=["rowmajor", "preshuffled"])
+
+
+@LAYOUTS
+@pytest.mark.parametrize("m", [1, 2, 7, 16, 17, 32, 33, 64])
+def test_rows(orc, m, pre):
+    check(orc, m, 200, 1024, seed=m, pre=pre)
+
+
+@LAYOUTS
+@pytest.mark.parametrize("n,k", [(1, 32), (16, 16), (33, 48), (63, 96), (64, 128), (100, 160),
+                                 (70, 208), (517, 2048),
+                                 (1000, 4096), (2304, 16384), (13312, 512)])
+def test_shapes(orc, n, k, pre):
+    check(orc, 4, n, k, seed=n + k, pre=pre)
+
+
+@LAYOUTS
+@pytest.mark.parametrize("per_row", [(False, False), (True, False), (False, True)])
+def test_scale_modes(orc, per_row, pre):
+    check(orc, 5, 300, 640, per_row=per_row, seed=3, pre=pre)
+
+
+@LAYOUTS
+def test_fp16_out(orc, pre):
+    check(orc, 8, 512, 2048, out="fp16", seed=4, pre=pre)
+
+
+@LAYOUTS
+def test_padded_rows(orc, pre):
+    """Row strides past K hold NaN codes that must never be read."""
+    check(orc, 6, 130, 1040, lda=1056, ldb=1072, seed=5, pre=pre)
+
+
+@pytest.mark.parametrize("cfg", [(1, 4), (1, 8), (1, 16), (2, 4), (2, 8), (2, 16), (4, 4),
+                                 (4, 8), (4, 16)])
+@pytest.mark.parametrize("m", [3, 20, 40])
+def test_forced_configs(orc, m, cfg):
+    """Every compiled block shape that the row tiling has, both layouts."""
+    import residual_add_rmsnorm_amd as arn
+
+    mt = 1 if m <= 16 else (2 if m <= 32 else 4)
+    arn.set_gemm_config(*cfg)
+    try:
+        for pre in (False, True):
+            try:
+                plan = check(orc, m, 330, 1296, seed=m + cfg[0], pre=pre)
+            except arn.ArnError as e:
+                assert e.status == 2   # shape not compiled for this row tiling
+                continue
+            assert f"mt{mt}/nt{cfg[0]}/waves{cfg[1]}/" in plan
+    finally:
+        arn.set_gemm_config(0, 0)
+
+
+def test_preshuffled_size():
+    import residual_add_rmsnorm_amd as arn
+
+    w = arn.fp8_weight_preshuffle(torch.zeros(33, 208, dtype=torch.uint8, device="cuda"))
+    assert w.data.numel() == 3 * 2 * 2048 and w.shape == (33, 208)
+
+
+def test_preshuffle_unaligned_weight(orc):
+    """The shuffle reads any row stride; the GEMM then serves a weight whose
+    own rows are not 16-byte aligned (row-major arn_fp8_gemm refuses it)."""
+    import residual_add_rmsnorm_amd as arn
+
+    rng = np.random.default_rng(11)
+    m, n, k, ldb = 3, 90, 336, 345
+    a = _codes(rng, m, k, 24.0)
+    b = np.full((n * ldb + 1,), 0x7F, np.uint8)
+    bv = b[1:].reshape(n, ldb)            # odd base address, odd stride
+    bv[:, :k] = _codes(rng, n, k, 6.0)
+    sa = np.full(m, 0.05, np.float32)
+    sb = rng.uniform(0.001, 0.01, n).astype(np.float32)
+    bd = torch.from_numpy(b).cuda()[1:].view(n, ldb)[:, :k]
+    ad, sad, sbd = (torch.from_numpy(x).cuda() for x in (a, sa, sb))
+    with pytest.raises(arn.ArnError):
+        arn.fp8_gemm(ad, sad, bd, sbd)
+    c = arn.fp8_gemm(ad, sad, arn.fp8_weight_preshuffle(bd), sbd)
+    ref = orc.fp8_gemm(a, sa, np.ascontiguousarray(bv[:, :k]), sb)
+    got = values16(bits(c), "bf16")
+    tol = RHO["bf16"] * np.abs(ref["c"]) + ulp16(ref["c"], "bf16") + \
+        (k / 128 + 256) * 2.0**-24 * ref["abs"]
+    assert np.all(np.abs(got - ref["c"]) <= tol)
+
+
+def test_deterministic():
+    import residual_add_rmsnorm_amd as arn
+
+    rng = np.random.default_rng(6)
+    a = torch.from_numpy(_codes(rng, 8, 4096, 24)).cuda()
+    b = torch.from_numpy(_codes(rng, 2048, 4096, 6)).cuda()
+    sa = torch.full((8,), 0.05, device="cuda")
+    sb = torch.full((2048,), 0.004, device="cuda")
+    r1 = arn.fp8_gemm(a, sa, b, sb)
+    r2 = arn.fp8_gemm(a, sa, b, sb)
+    bw = arn.fp8_weight_preshuffle(b)
+    r3 = arn.fp8_gemm(a, sa, bw, sb)
+    r4 = arn.fp8_gemm(a, sa, bw, sb)
+    assert torch.equal(r1, r2)
+    assert torch.equal(r3, r4)
+
+
+def test_unsupported_shapes():
+    import residual_add_rmsnorm_amd as arn
+
+    a = torch.zeros(65, 128, dtype=torch.uint8, device="cuda")
+    b = torch.zeros(64, 128, dtype=torch.uint8, device="cuda")
+    s = torch.ones(1, device="cuda")
+    with pytest.raises(arn.ArnError) as e:
+        arn.fp8_gemm(a, s, b, s)           # m > 64
+    assert e.value.status == 2
+    with pytest.raises(arn.ArnError) as e:
+        arn.fp8_gemm(a[:4, :100], s, b[:, :100], s)   # k % 16 != 0
+    assert e.value.status == 2
+
+
+def test_swiglu_codes_feed_gemm(orc):
+    """The decode pipeline: SwiGLU with dynamic e4m3 writes codes and
+    per-row scales; the GEMM consumes them with a per-row-scaled weight.
+    Both stages checked against the oracle run on the same data."""
+    import residual_add_rmsnorm_amd as arn
+    import workloads as W
+
+    rng = np.random.default_rng(7)
+    m, d, n = 8, 2048, 768
+    x = W.to_bits((rng.standard_normal((m, 2 * d)) * 2).astype(np.float32), "bf16")
+    q, sq = arn.silu_and_mul_fp8(dev(x, "bf16"), dynamic=True)
+    b = _codes(rng, n, d, 6.0)
+    sb = rng.uniform(0.001, 0.01, n).astype(np.float32)
+    c = arn.fp8_gemm(q, sq, torch.from_numpy(b).cuda(), torch.from_numpy(sb).cuda())
+    torch.cuda.synchronize()
+    qa = q.view(torch.uint8).cpu().numpy()
+    sqa = sq.cpu().numpy()
+    ref_g = orc.silu_and_mul("bf16", x, fp8_mode=O.FP8_DYNAMIC)
+    # the GEMM is checked on the codes the GPU produced (those match the
+    # oracle's within one step, checked by the SwiGLU tests)
+    assert np.mean(qa == ref_g["q"]) > 0.99
+    ref = orc.fp8_gemm(qa, sqa, b, sb)
+    got = values16(bits(c), "bf16")
+    tol = RHO["bf16"] * np.abs(ref["c"]) + ulp16(ref["c"], "bf16") + \
+        (d / 128 + 256) * 2.0**-24 * ref["abs"]
+    assert np.all(np.abs(got - ref["c"]) <= tol)

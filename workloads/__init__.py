@@ -200,3 +200,60 @@ def make(w: Workload | str, rows: int | None = None, seed: int = 0) -> dict:
     if isinstance(w, str):
         w = WORKLOADS[w]
     return make_rows(w, 0, w.rows if rows is None else rows, seed)
+
+
+# ---------------------------------------------------------------------------
+# e4m3 GEMM workloads: the decode-time linear layers of one GPU's share of
+# Llama 3.1 405B under 8-way tensor parallelism (hidden 16384, 128 query
+# heads and 8 KV heads of width 128, MLP width 53248 -- the model's published
+# configuration -- divided by 8 along the parallel dimension).
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class GemmWorkload:
+    name: str
+    n: int                 # output features (rows of the weight)
+    k: int                 # input features
+    m_counts: tuple = (1, 8, 16, 32, 64)
+    out: str = "bf16"
+    a_std: float = 24.0    # activation codes: N(0, a_std^2) cast to e4m3
+    b_std: float = 6.0     # weight codes
+
+    def algorithmic_bytes(self, m: int) -> int:
+        """Weight codes once, activation codes, 16-bit output, the scales."""
+        return self.n * self.k + m * self.k + 2 * m * self.n + 4 * (m + self.n)
+
+    def flops(self, m: int) -> int:
+        return 2 * m * self.n * self.k
+
+
+GEMMS = {
+    g.name: g
+    for g in [
+        GemmWorkload("fp8_gemm_gate_up_13312x16384", 13312, 16384),
+        GemmWorkload("fp8_gemm_down_16384x6656", 16384, 6656),
+        GemmWorkload("fp8_gemm_qkv_2304x16384", 2304, 16384),
+        GemmWorkload("fp8_gemm_o_16384x2048", 16384, 2048),
+    ]
+}
+
+STREAM_GEMM_A, STREAM_GEMM_B, STREAM_GEMM_SCALE = 5, 6, 7
+
+
+def e4m3_codes(f32: np.ndarray) -> np.ndarray:
+    """float32 values -> OCP e4m3 codes by torch's cast (values clamped to
+    the finite range first)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(f32, dtype=np.float32)).clamp(-448, 448)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def make_gemm(g: GemmWorkload, m: int, seed: int = 0) -> dict:
+    """Codes and per-row dequant scales for one GEMM call with m rows."""
+    a = e4m3_codes(_normal_rows(seed, STREAM_GEMM_A, 0, m, g.k, g.a_std))
+    b = e4m3_codes(_normal_rows(seed, STREAM_GEMM_B, 0, g.n, g.k, g.b_std))
+    rng = _rng(seed, STREAM_GEMM_SCALE, 0)
+    sa = rng.uniform(0.01, 0.1, m).astype(np.float32)
+    sb = rng.uniform(0.001, 0.01, g.n).astype(np.float32)
+    return {"a": a, "scale_a": sa, "b": b, "scale_b": sb}
