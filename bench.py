@@ -31,17 +31,27 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = ("achieved HBM GB/s (% of MI355X peak) for fused add+RMSNorm(+fp8); "
           "µs/call at decode")
 MALL_BYTES = 256 * 1024 * 1024
-KERNEL_SOURCES = ["residual_add_rmsnorm_amd/csrc/arn_kernels.hip",
-                  "residual_add_rmsnorm_amd/csrc/arn_glu.hip",
-                  "residual_add_rmsnorm_amd/csrc/arn_gemm.hip",
-                  "residual_add_rmsnorm_amd/csrc/arn_device.h",
-                  "residual_add_rmsnorm_amd/csrc/arn_api.hip",
-                  "residual_add_rmsnorm_amd/csrc/arn_internal.h"]
+# Device code of each kernel family: a stored counter reading is used only
+# while these files, and the launch shape recorded with it, are unchanged.
+_CSRC = "residual_add_rmsnorm_amd/csrc/"
+KERNEL_SOURCES = {
+    "norm": [_CSRC + "arn_kernels.hip", _CSRC + "arn_device.h", _CSRC + "arn_internal.h"],
+    "glu": [_CSRC + "arn_glu.hip", _CSRC + "arn_device.h", _CSRC + "arn_internal.h"],
+    "gemm": [_CSRC + "arn_gemm.hip", _CSRC + "arn_device.h", _CSRC + "arn_internal.h"],
+}
 
 
-def kernel_source_sha() -> str:
+def kernel_family(name: str) -> str:
+    import workloads
+
+    if name.split("@")[0] in workloads.GEMMS:
+        return "gemm"
+    return "glu" if workloads.WORKLOADS[name].is_glu else "norm"
+
+
+def kernel_source_sha(family: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -207,15 +217,21 @@ def cpu_baseline(w, target_s: float = 10.0) -> dict:
 
 # ---------------------------------------------------------------------------
 
-def traffic_for(name: str, launch_bytes: int):
+def traffic_file(name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{name.replace('@', '_')}.json")
+
+
+def traffic_for(name: str, plan: str):
     """HBM bytes per launch from committed rocprofv3 counters, if they were
-    taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    taken on the current kernel source and launch shape."""
+    path = traffic_file(name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_sha():
+    if t.get("kernel_source_sha") != kernel_source_sha(kernel_family(name)):
+        return None
+    if t.get("kernel_plan") != plan:
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -240,7 +256,7 @@ def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool) -> dict:
     achieved = bytes_step / (per_call_ms * 1e-3) / 1e9
     log(f"[bench] plan {plan}: {per_call_ms * 1e3:.2f} us/call, {achieved:.1f} GB/s "
         f"({100 * achieved / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
-    traffic = traffic_for(name, bytes_step)
+    traffic = traffic_for(name, plan)
     line = {
         "metric": METRIC,
         "value": round(achieved, 2),
@@ -288,7 +304,8 @@ def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool) -> dict:
     return line
 
 
-def bench_gemm(name: str, steps: int, warmup: int) -> dict:
+def bench_gemm(name: str, steps: int, warmup: int, only_m: int | None = None,
+               only_layout: str | None = None) -> dict:
     """The e4m3 skinny GEMM at each activation row count, with the weight
     pre-shuffled (arn_fp8_gemm_preshuffled, the shuffle done once before the
     timed region) and row-major (arn_fp8_gemm): device time per call,
@@ -308,14 +325,18 @@ def bench_gemm(name: str, steps: int, warmup: int) -> dict:
     sb = torch.from_numpy(d["scale_b"]).cuda()
     a_all = torch.from_numpy(d["a"]).cuda()
     sa_all = torch.from_numpy(d["scale_a"]).cuda()
-    layouts = {}
+    layouts = {"preshuffled": {}, "rowmajor": {}}
     for layout in ("preshuffled", "rowmajor"):
+        if only_layout and layout != only_layout:
+            continue
         if layout == "preshuffled":
             bs = [arn.fp8_weight_preshuffle(b0) for _ in range(sets)]
         else:
             bs = [b0] + [b0.clone() for _ in range(sets - 1)]
-        per_m = {}
+        per_m = layouts[layout]
         for m in g.m_counts:
+            if only_m and m != only_m:
+                continue
             a, sa = a_all[:m], sa_all[:m]
             out = torch.empty((m, g.n), dtype=torch.bfloat16, device="cuda")
 
@@ -329,15 +350,17 @@ def bench_gemm(name: str, steps: int, warmup: int) -> dict:
                              "GB_per_s": round(g.algorithmic_bytes(m) / us / 1e3, 1),
                              "TFLOP_per_s": round(g.flops(m) / us / 1e6, 2),
                              "plan": arn.last_plan()}
+            per_m[str(m)]["traffic"] = traffic_for(f"{name}@m{m}_{layout}", per_m[str(m)]["plan"])
             log(f"[bench] {layout} m={m}: {per_m[str(m)]}")
-        layouts[layout] = per_m
         del bs
         torch.cuda.empty_cache()
-    best = max(layouts["preshuffled"].values(), key=lambda v: v["GB_per_s"])
+    best = max([v for lay in layouts.values() for v in lay.values()],
+               key=lambda v: v["GB_per_s"])
     return {"workload": name, "n": g.n, "k": g.k, "weight_copies": sets,
             "per_m": layouts["preshuffled"], "per_m_rowmajor": layouts["rowmajor"],
             "roofline": {"bound": "hbm", "achieved": best["GB_per_s"], "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(best["GB_per_s"] / PEAK_HBM_GBS, 4)}}
+                         "unit": "GB/s", "frac": round(best["GB_per_s"] / PEAK_HBM_GBS, 4),
+                         "traffic": best["traffic"], "plan": best["plan"]}}
 
 
 def main() -> int:
@@ -354,13 +377,21 @@ def main() -> int:
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --calibrate-copy` into profiles/traffic_<workload>.json")
     ap.add_argument("--pmc-command", default="", help="command line recorded with the summary")
+    ap.add_argument("--pmc-bench-output", default=None,
+                    help="the JSON line the profiled bench run printed (its kernel plan is "
+                         "recorded with the summary)")
+    ap.add_argument("--gemm-m", type=int, default=None,
+                    help="GEMM workloads: time only this activation row count")
+    ap.add_argument("--gemm-layout", choices=("preshuffled", "rowmajor"), default=None,
+                    help="GEMM workloads: time only this weight layout")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         import workloads
 
         summarize_pmc(args.workload or workloads.HEADLINE, *args.summarize_pmc,
-                      command=args.pmc_command)
+                      command=args.pmc_command, bench_output=args.pmc_bench_output,
+                      gemm_m=args.gemm_m, gemm_layout=args.gemm_layout)
         return 0
 
     if args.gpus != 1:
@@ -383,8 +414,10 @@ def main() -> int:
     if args.workload in workloads.GEMMS or args.workload == "gemms":
         gnames = list(workloads.GEMMS) if args.workload == "gemms" else [args.workload]
         for n in gnames:
-            print(json.dumps(bench_gemm(n, min(args.steps, 200), min(args.warmup, 20))),
-                  flush=True)
+            print(json.dumps(bench_gemm(n, min(args.steps, 200), min(args.warmup, 20),
+                                        args.gemm_m, args.gemm_layout)), flush=True)
+        if args.calibrate_copy:
+            copy_calibration()
         return 0
     names = list(workloads.WORKLOADS) if args.workload == "all" else \
         [args.workload or workloads.HEADLINE]
@@ -408,33 +441,53 @@ def _pmc_rows(path: str, counter: str):
         return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
 
 
-def summarize_pmc(name: str, fetch_csv: str, write_csv: str, command: str = "") -> dict:
+def summarize_pmc(name: str, fetch_csv: str, write_csv: str, command: str = "",
+                  bench_output: str | None = None, gemm_m: int | None = None,
+                  gemm_layout: str | None = None) -> dict:
     """HBM traffic of the operator's kernel per launch, from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the same counter
-    reads for the plain device copies of COPY_BYTES that close the run."""
+    reads for the plain device copies of COPY_BYTES that close the run.
+    For a GEMM workload the run timed one row count and layout (the weight
+    shuffle dispatched before it is left out)."""
     import workloads
 
-    w = workloads.WORKLOADS[name]
-    out = {"workload": name, "kernel_source_sha": kernel_source_sha(),
-           "algorithmic_bytes_per_launch": w.algorithmic_bytes(), "command": command}
-    for counter, path, key in (("FETCH_SIZE", fetch_csv, "read"), ("WRITE_SIZE", write_csv, "write")):
+    if name in workloads.GEMMS:
+        if not gemm_m or not gemm_layout:
+            raise SystemExit("a GEMM summary needs --gemm-m and --gemm-layout")
+        key = f"{name}@m{gemm_m}_{gemm_layout}"
+        alg = workloads.GEMMS[name].algorithmic_bytes(gemm_m)
+    else:
+        key = name
+        alg = workloads.WORKLOADS[name].algorithmic_bytes()
+    plan = None
+    if bench_output:
+        with open(bench_output) as f:
+            line = json.loads(f.readline())
+        if "per_m" in line:
+            lay = line["per_m"] if gemm_layout == "preshuffled" else line["per_m_rowmajor"]
+            plan = lay[str(gemm_m)]["plan"]
+        else:
+            plan = line["config"]["kernel_plan"]
+    out = {"workload": key, "kernel_source_sha": kernel_source_sha(kernel_family(key)),
+           "kernel_plan": plan, "algorithmic_bytes_per_launch": alg, "command": command}
+    for counter, path, kind in (("FETCH_SIZE", fetch_csv, "read"), ("WRITE_SIZE", write_csv, "write")):
         rows = _pmc_rows(path, counter)
-        kern = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].startswith("void arn::")]
+        kern = [float(r["Counter_Value"]) for r in rows
+                if r["Kernel_Name"].startswith("void arn::")
+                and "preshuffle_kernel" not in r["Kernel_Name"]]
         copies = [float(r["Counter_Value"]) for r in rows
                   if "copyBuffer" in r["Kernel_Name"]][-COPY_REPS:]
         kib = sum(kern) / len(kern)
         copy_kib = sum(copies) / len(copies)
         factor = COPY_BYTES / (copy_kib * 1024.0)
-        out[f"{key}_counter_kib_per_launch"] = round(kib, 3)
-        out[f"{key}_copy_counter_kib"] = round(copy_kib, 3)
-        out[f"{key}_scale_factor"] = round(factor, 6)
-        out[f"{key}_bytes_per_launch"] = int(round(kib * 1024.0 * factor))
-        out[f"{key}_dispatches"] = len(kern)
+        out[f"{kind}_counter_kib_per_launch"] = round(kib, 3)
+        out[f"{kind}_copy_counter_kib"] = round(copy_kib, 3)
+        out[f"{kind}_scale_factor"] = round(factor, 6)
+        out[f"{kind}_bytes_per_launch"] = int(round(kib * 1024.0 * factor))
+        out[f"{kind}_dispatches"] = len(kern)
     out["traffic_bytes_per_launch"] = out["read_bytes_per_launch"] + out["write_bytes_per_launch"]
-    out["traffic_over_algorithmic"] = round(out["traffic_bytes_per_launch"] /
-                                            out["algorithmic_bytes_per_launch"], 5)
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
-    with open(path, "w") as f:
+    out["traffic_over_algorithmic"] = round(out["traffic_bytes_per_launch"] / alg, 5)
+    with open(traffic_file(key), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     log(json.dumps(out, indent=1))

@@ -302,11 +302,13 @@ std::atomic<int> g_forced_gemm{0};
 
 // GEMM shape, from sweeps of decode projections on MI355X (N 2304..16384,
 // K 2048..16384, M 1..64).  The weight stream wants about one block per CU
-// or more: the widest column tile (fewest re-reads of the activations) that
-// still gives at least 3/4 of a block per CU.  With one row tile, K is split
-// over as many waves as keep each wave at four or more 128-wide k steps (up
-// to 16); with two or four row tiles the accumulators and operands of a
-// wave fill its registers, and four waves per block do best.
+// or more: the widest column tile that still gives at least 3/4 of a block
+// per CU.  Wide tiles matter more as M grows: every block reads all of A
+// (M x K), so A's share of the load traffic per block is M / (16 NT) of the
+// weight's.  With one row tile, K is split over as many waves as keep each
+// wave at four or more 128-wide k steps (up to 16); with two or four row
+// tiles the accumulators and operands of a wave fill its registers, and four
+// waves per block do best.
 const GemmCfg* choose_gemm(const GemmTable* table, int mt, int64_t n, int64_t k, int cus) {
   const int forced = g_forced_gemm.load(std::memory_order_relaxed);
   auto find = [&](int nt, int waves) -> const GemmCfg* {
@@ -321,7 +323,7 @@ const GemmCfg* choose_gemm(const GemmTable* table, int mt, int64_t n, int64_t k,
   const int64_t want_blocks = (3 * (int64_t)cus) / 4;
   auto blocks = [&](int nt) { return (n + 16 * nt - 1) / (16 * nt); };
   int nt = 1;
-  if (mt == 1 && blocks(4) >= want_blocks) {
+  if (blocks(4) >= want_blocks) {
     nt = 4;
   } else if (blocks(2) >= want_blocks) {
     nt = 2;

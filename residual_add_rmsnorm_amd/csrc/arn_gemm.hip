@@ -245,8 +245,10 @@ static const arn::GemmCfg kGemmCfgs[] = {
     ARN_GEMM_CFG(1, 4, 4), ARN_GEMM_CFG(1, 4, 8), ARN_GEMM_CFG(1, 4, 16),
     ARN_GEMM_CFG(1, 2, 4), ARN_GEMM_CFG(1, 2, 8), ARN_GEMM_CFG(1, 2, 16),
     ARN_GEMM_CFG(1, 1, 4), ARN_GEMM_CFG(1, 1, 8), ARN_GEMM_CFG(1, 1, 16),
+    ARN_GEMM_CFG(2, 4, 4), ARN_GEMM_CFG(2, 4, 8),
     ARN_GEMM_CFG(2, 2, 4), ARN_GEMM_CFG(2, 2, 8), ARN_GEMM_CFG(2, 2, 16),
     ARN_GEMM_CFG(2, 1, 4), ARN_GEMM_CFG(2, 1, 8), ARN_GEMM_CFG(2, 1, 16),
+    ARN_GEMM_CFG(4, 4, 4), ARN_GEMM_CFG(4, 4, 8),
     ARN_GEMM_CFG(4, 2, 4), ARN_GEMM_CFG(4, 2, 8),
     ARN_GEMM_CFG(4, 1, 4), ARN_GEMM_CFG(4, 1, 8), ARN_GEMM_CFG(4, 1, 16),
 };
