@@ -237,6 +237,74 @@ def cpu_baseline(w, target_s: float = 10.0) -> dict:
 
 
 # ---------------------------------------------------------------------------
+# practical ceilings: plain streaming kernels moving the operator's byte mix
+# ---------------------------------------------------------------------------
+
+# (read streams of 16 B, write streams of 16 B, write streams of 8 B) per element
+MIXES = {"read": (1, 0, 0), "write": (0, 1, 0), "copy": (1, 1, 0), "2r2w": (2, 2, 0),
+         "2r1.5w": (2, 1, 1), "2r0.5w": (2, 0, 1)}
+PROBE_STREAM_BYTES = 256 * 1024 * 1024
+
+
+def workload_mix(w):
+    """The probe mix with the same read:write byte ratio as the workload."""
+    if w.is_glu:
+        return "2r0.5w" if w.fp8 else None
+    if not w.has_residual:
+        return "copy" if not w.fp8 else None
+    return "2r1.5w" if w.fp8 else "2r2w"
+
+
+def mix_ceilings(names, reps: int = 10) -> dict:
+    """Best GB/s of the streaming probe (lib/libarn_probe.so) for each mix,
+    over block sizes and grids, on 256 MiB streams (past the MALL)."""
+    import ctypes
+
+    import torch
+
+    from residual_add_rmsnorm_amd import build as _build
+
+    lib = ctypes.CDLL(_build.PROBE_LIB_PATH)
+    lib.arn_probe_stream.restype = ctypes.c_int
+    lib.arn_probe_stream.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 4 + [
+        ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    n = PROBE_STREAM_BYTES // 16
+    bufs = [torch.empty(PROBE_STREAM_BYTES, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    for b in bufs:
+        b.fill_(1)
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name in names:
+        r, w16, w8 = MIXES[name]
+        nbytes = n * (16 * r + 16 * w16 + 8 * w8)
+        best = None
+        for block in (256, 512, 1024):
+            for grid in (256, 512, 1024, 2048, 4096, 8192, n // block):
+                def go():
+                    st = lib.arn_probe_stream(r, w16, w8, *[b.data_ptr() for b in bufs], n,
+                                              grid, block, stream)
+                    if st != 0:
+                        raise RuntimeError(f"arn_probe_stream status {st}")
+                for _ in range(3):
+                    go()
+                t0 = torch.cuda.Event(enable_timing=True)
+                t1 = torch.cuda.Event(enable_timing=True)
+                t0.record()
+                for _ in range(reps):
+                    go()
+                t1.record()
+                t1.synchronize()
+                gbs = nbytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+                if best is None or gbs > best["GB_per_s"]:
+                    best = {"GB_per_s": round(gbs, 1), "block": block, "grid": grid}
+        out[name] = best
+        log(f"[bench] ceiling {name}: {best}")
+    del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
 
 def traffic_file(name: str) -> str:
     return os.path.join(ROOT, "profiles", f"traffic_{name.replace('@', '_')}.json")
@@ -257,7 +325,8 @@ def traffic_for(name: str, plan: str):
     return t.get("traffic_bytes_per_launch")
 
 
-def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool) -> dict:
+def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool,
+                   with_ceiling: bool = True) -> dict:
     import torch
 
     import residual_add_rmsnorm_amd as arn
@@ -278,6 +347,8 @@ def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool) -> dict:
     log(f"[bench] plan {plan}: {per_call_ms * 1e3:.2f} us/call, {achieved:.1f} GB/s "
         f"({100 * achieved / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
     traffic = traffic_for(name, plan)
+    mix = workload_mix(w)
+    ceiling = mix_ceilings([mix])[mix] if mix and with_ceiling else None
     line = {
         "metric": METRIC,
         "value": round(achieved, 2),
@@ -305,6 +376,11 @@ def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool) -> dict:
             "traffic": traffic,
         },
     }
+    if ceiling:
+        line["roofline"]["mix_ceiling"] = {
+            "mix": mix, "GB_per_s": ceiling["GB_per_s"],
+            "frac": round(achieved / ceiling["GB_per_s"], 4),
+            "probe": f"plain streaming kernel, block {ceiling['block']}, grid {ceiling['grid']}"}
     if w.row_counts:
         per_rows = {}
         for r in w.row_counts:
@@ -392,6 +468,10 @@ def main() -> int:
     ap.add_argument("--workload", default=None,
                     help="workload name, or 'all' (default: the headline workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-probe ceiling of the workload's byte mix")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the streaming-probe ceilings of every mix")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run plain device copies of a known size (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -432,6 +512,11 @@ def main() -> int:
 
     _lib.load()  # fails loudly if the HIP library is missing
 
+    if args.ceilings:
+        print(json.dumps({"ceilings_GB_per_s": mix_ceilings(list(MIXES)),
+                          "stream_bytes": PROBE_STREAM_BYTES}), flush=True)
+        return 0
+
     if args.workload in workloads.GEMMS or args.workload == "gemms":
         gnames = list(workloads.GEMMS) if args.workload == "gemms" else [args.workload]
         for n in gnames:
@@ -444,7 +529,8 @@ def main() -> int:
         [args.workload or workloads.HEADLINE]
     for n in names:
         line = bench_workload(n, args.steps, args.warmup,
-                              with_cpu=not args.no_cpu_baseline and n == names[0])
+                              with_cpu=not args.no_cpu_baseline and n == names[0],
+                              with_ceiling=not args.no_ceiling)
         print(json.dumps(line), flush=True)
     if args.calibrate_copy:
         copy_calibration()

@@ -1,0 +1,37 @@
+/*
+ * arn_probe.h -- measurement aid, not part of the operator library: plain
+ * streaming kernels (lib/libarn_probe.so) that give the HBM bandwidth a mix
+ * of read and write streams reaches on this GPU.  An operator that moves
+ * the same byte mix cannot stream faster, so this is the practical ceiling
+ * its roofline fraction is read against, next to the published peak.
+ */
+#ifndef ARN_PROBE_H
+#define ARN_PROBE_H
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * One launch of a grid-stride streaming kernel over n elements (1 <= n <=
+ * 2^27): `reads` (0..2) streams of 16 bytes per element are read from a
+ * then b; `writes16` (0..2) streams of 16 bytes per element are written to c
+ * then d, and `writes8` (0..1) stream of 8 bytes per element to d.  Served
+ * mixes (reads, writes16, writes8): (1,0,0) (0,1,0) (1,1,0) (2,2,0) (2,1,1)
+ * (2,0,1).  c must be valid for every mix (the read-only mix keeps a
+ * never-taken store to it); a, b, c, d are device buffers of n x 16 bytes
+ * (d: n x 8 for the 8-byte stream), 16-byte aligned.  grid in 1..2^24,
+ * block 256, 512 or 1024 threads, asynchronous on `stream`.  Returns 0, or
+ * 1 (invalid argument), 2 (mix not served), 3 (launch failed).
+ */
+int arn_probe_stream(int reads, int writes16, int writes8, const void *a, const void *b,
+                     void *c, void *d, int64_t n, int grid, int block, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARN_PROBE_H */

@@ -1,8 +1,11 @@
 """Build libarn.so (HIP, gfx950 only) in-tree.
 
-One object per operator kind and dtype is compiled from arn_kernels.hip
-(they build in parallel), plus the host dispatcher arn_api.hip; hipcc links
-them into residual_add_rmsnorm_amd/lib/libarn.so.
+One object per operator kind and dtype is compiled from arn_kernels.hip,
+arn_glu.hip and arn_gemm.hip (they build in parallel), plus the host
+dispatcher arn_api.hip; hipcc links them into
+residual_add_rmsnorm_amd/lib/libarn.so.  The streaming probe that measures
+bandwidth ceilings (arn_probe.hip) becomes lib/libarn_probe.so, used only
+by the benchmark.
 
     python -m residual_add_rmsnorm_amd.build
 """
@@ -20,6 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libarn.so")
+PROBE_LIB_PATH = os.path.join(LIB_DIR, "libarn_probe.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "arn")
 
 ARCH = "gfx950"
@@ -41,9 +45,9 @@ DTYPES = range(2)
 
 def sources() -> list[str]:
     return [os.path.join(CSRC, f) for f in ("arn_kernels.hip", "arn_glu.hip", "arn_gemm.hip",
-                                            "arn_api.hip", "arn_internal.h",
-                                            "arn_device.h")] + [
-        os.path.join(INCLUDE, "arn.h")]
+                                            "arn_api.hip", "arn_internal.h", "arn_device.h",
+                                            "arn_probe.hip")] + [
+        os.path.join(INCLUDE, "arn.h"), os.path.join(INCLUDE, "arn_probe.h")]
 
 
 def _compile(src: str, obj: str, defines: list[str]) -> None:
@@ -77,9 +81,14 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
         units.append((os.path.join(CSRC, "arn_gemm.hip"),
                       os.path.join(OBJ_DIR, f"arn_gemm_d{d}.o"), [f"-DARN_DT={d}"]))
     units.append((os.path.join(CSRC, "arn_api.hip"), os.path.join(OBJ_DIR, "arn_api.o"), []))
+    probe = (os.path.join(CSRC, "arn_probe.hip"), os.path.join(OBJ_DIR, "arn_probe.o"), [])
     jobs = jobs or min(16, os.cpu_count() or 4)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        list(ex.map(lambda u: _compile(*u), units))
+        list(ex.map(lambda u: _compile(*u), units + [probe]))
+    tmp = PROBE_LIB_PATH + ".tmp"
+    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, probe[1]],
+                   check=True)
+    os.replace(tmp, PROBE_LIB_PATH)
     tmp = LIB_PATH + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[u[1] for u in units]]
     subprocess.run(cmd, check=True)
@@ -90,9 +99,9 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
 
 
 def is_stale() -> bool:
-    if not os.path.exists(LIB_PATH):
+    if not os.path.exists(LIB_PATH) or not os.path.exists(PROBE_LIB_PATH):
         return True
-    t = os.path.getmtime(LIB_PATH)
+    t = min(os.path.getmtime(LIB_PATH), os.path.getmtime(PROBE_LIB_PATH))
     return any(os.path.getmtime(s) > t for s in sources())
 
 

@@ -15,8 +15,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "arn.h")
 
 
-def header_functions():
-    text = open(HEADER).read()
+PROBE_HEADER = os.path.join(ROOT, "include", "arn_probe.h")
+
+
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(arn_\w+)\s*\(", text)))
 
@@ -38,6 +41,28 @@ def test_library_exports_every_declared_function(lib):
         assert name in exported, name
         assert getattr(lib, name) is not None
     assert lib.arn_abi_version() == _lib.ABI_VERSION == 4
+
+
+def test_probe_library_exports_its_header():
+    """The streaming probe the benchmark measures ceilings with lives in its
+    own library and exports what include/arn_probe.h declares."""
+    from residual_add_rmsnorm_amd import build
+
+    out = subprocess.run(["nm", "-D", "--defined-only", build.PROBE_LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (arn_\w+)", out))
+    assert header_functions(PROBE_HEADER) == ["arn_probe_stream"]
+    assert "arn_probe_stream" in exported
+    probe = ctypes.CDLL(build.PROBE_LIB_PATH)
+    f = probe.arn_probe_stream
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int,
+                                                               ctypes.c_int, ctypes.c_void_p]
+    # argument errors are caught before any HIP call
+    assert f(1, 1, 0, 16, 16, 16, 16, 0, 1, 256, None) == 1        # n = 0
+    assert f(1, 1, 0, 16, 16, 16, 16, 64, 1, 300, None) == 1       # block size
+    assert f(2, 2, 0, 16, 16, 16, None, 64, 1, 256, None) == 1     # d missing
+    assert f(2, 0, 0, 16, 16, 16, 16, 64, 1, 256, None) == 2       # mix not served
 
 
 def test_hip_imports_resolve_in_torch_runtime():
