@@ -1,7 +1,7 @@
 /*
  * arn.h -- C ABI of the MI355X (gfx950) residual-add + RMSNorm library.
  *
- * One operator in four forms (plus the SwiGLU activation further below).
+ * One operator in four forms (plus SwiGLU and an e4m3 GEMM further below).
  * For every row i of a 16-bit activation matrix (bf16 or fp16), H = hidden:
  *
  *     r   = x[i] + residual[i]          (fused forms; plain forms use r = x[i])
@@ -16,16 +16,20 @@
  * skipping Nvidia lock-in" (paragraph 2).  The argument rules follow the
  * vLLM API page "vllm.kernels.aiter_ops" (attributes rms_add_no_var_16bit_only
  * and rms_no_var_16bit_only, and flatten_to_2d_is_free): 16-bit activations
- * only, a weight of the same dtype or none, no variance-size override (the
- * mean always runs over all H channels), and 2-D rows whose elements are
+ * only, a weight of the same dtype or none, and 2-D rows whose elements are
  * contiguous -- a layout that is not expressible that way is refused, never
- * copied, so the caller can fall back as vLLM's op priority list does.
+ * copied, so the caller can fall back as vLLM's op priority list does.  The
+ * four named entry points take the mean over all H channels, as those
+ * wrappers require; arn_norm serves the same forms plus a variance-size
+ * override.  Further below: the SwiGLU activation and the e4m3 GEMM that
+ * consume and produce the same codes and scales.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Pointers are DEVICE pointers owned by the caller (hipMalloc, or a
  *    framework's allocator).  The library allocates nothing and keeps no
- *    state across calls other than a per-device cache of the CU count.
+ *    state across calls other than a per-device cache of the CU count and
+ *    the settings of the tuning aids at the end of this file.
  *  - Layout: row-major, element stride 1, row stride given per tensor in
  *    ELEMENTS of that tensor (one e4m3 code = one element).  stride >= hidden.
  *    Elements [hidden, stride) of a row are neither read nor written.

@@ -1,0 +1,138 @@
+"""The C boundary by itself: a plain C program (tests/c_abi/arn_client.c,
+host code built with gcc against include/arn.h, no Python or torch in its
+process) allocates device memory with hipMalloc, calls the library's entry
+points on a HIP stream it created, and writes the results to a file; they
+must match the oracle by the same rules as the Python-driven tests."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from tests._helpers import (RHO, assert_codes_close, assert_scales_close, assert_y_close,
+                            static_scale, ulp16, values16)
+from tests.c_abi import build as client_build
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def client():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    return client_build.ensure()
+
+
+def _run(client, args, tmp_path):
+    print("arn_client", " ".join(str(a) for a in args), flush=True)
+    res = subprocess.run([client, *[str(a) for a in args]], capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode == 0, res.stderr
+
+
+def _inputs(rng, rows, hidden, stride, dtype, res_std=1.0):
+    x = np.full((rows, stride), W.PAD_SENTINEL, np.uint16)
+    r = np.full((rows, stride), W.PAD_SENTINEL, np.uint16)
+    x[:, :hidden] = W.to_bits(rng.standard_normal((rows, hidden)).astype(np.float32), dtype)
+    r[:, :hidden] = W.to_bits((rng.standard_normal((rows, hidden)) * res_std).astype(np.float32),
+                              dtype)
+    w = W.to_bits((1 + 0.1 * rng.standard_normal(hidden)).astype(np.float32), dtype)
+    return x, r, w
+
+
+NORM_CASES = [
+    # form, fp8, dtype, rows, hidden, stride, eps, variance_size
+    ("fused", "none", "bf16", 37, 8192, 8200, 1e-5, 0),
+    ("fused", "dynamic", "bf16", 33, 7168, 7168, 1e-6, 0),
+    ("fused", "static", "fp16", 8, 16384, 16384, 1e-5, 0),
+    ("plain", "none", "bf16", 64, 4096, 4096, 1e-6, 0),
+    ("plain", "dynamic", "fp16", 5, 3840, 4096, 1e-6, 0),
+    ("fused", "none", "bf16", 9, 4096, 4096, 1e-6, 2048),      # arn_norm, variance size
+    ("plain", "static", "bf16", 6, 2880, 2880, 1e-6, 1000),    # arn_norm, variance size
+]
+
+
+@pytest.mark.parametrize("form,fp8,dtype,rows,hidden,stride,eps,var", NORM_CASES)
+def test_norm_from_c(client, orc, tmp_path, form, fp8, dtype, rows, hidden, stride, eps, var):
+    rng = np.random.default_rng(rows * 131 + hidden)
+    fused = form == "fused"
+    x, r, w = _inputs(rng, rows, hidden, stride, dtype, res_std=2.0 if dtype == "fp16" else 1.0)
+    s = static_scale() if fp8 == "static" and dtype == "fp16" else (0.01 if fp8 == "static" else 0.0)
+    s = float(np.float32(s))
+    fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(fin, "wb") as f:
+        f.write(x.tobytes())
+        if fused:
+            f.write(r.tobytes())
+        f.write(w.tobytes())
+    _run(client, ["norm", form, fp8, dtype, rows, hidden, stride, repr(eps), repr(s), var,
+                  fin, fout], tmp_path)
+
+    raw = open(fout, "rb").read()
+    pos = 0
+    n16 = rows * stride * 2
+    if fused:
+        r_after = np.frombuffer(raw[pos:pos + n16], np.uint16).reshape(rows, stride)
+        pos += n16
+    if fp8 == "none":
+        out = np.frombuffer(raw[pos:pos + n16], np.uint16).reshape(rows, stride)
+        pos += n16
+    else:
+        out = np.frombuffer(raw[pos:pos + rows * stride], np.uint8).reshape(rows, stride)
+        pos += rows * stride
+    scales = np.frombuffer(raw[pos:pos + 4 * rows], np.float32) if fp8 == "dynamic" else None
+
+    mode = {"none": O.FP8_NONE, "static": O.FP8_STATIC, "dynamic": O.FP8_DYNAMIC}[fp8]
+    ref = orc.add_rmsnorm(dtype, x, r if fused else None, w, eps, hidden=hidden, fp8_mode=mode,
+                          static_scale=s, variance_size=var or None)
+    if fused:
+        assert np.array_equal(r_after[:, :hidden], ref["r16"]), "stored residual"
+        assert np.all(r_after[:, hidden:] == W.PAD_SENTINEL), "residual padding touched"
+    if fp8 == "none":
+        assert_y_close(out[:, :hidden], ref["y"], dtype)
+        assert np.all(out[:, hidden:] == 0), "output padding touched"
+    else:
+        assert_codes_close(out[:, :hidden], ref["q"])
+        assert np.all(out[:, hidden:] == 0), "output padding touched"
+    if scales is not None:
+        assert_scales_close(scales, ref["scales"], dtype)
+
+
+@pytest.mark.parametrize("layout", ["rowmajor", "preshuffled"])
+def test_gemm_from_c(client, orc, tmp_path, layout):
+    rng = np.random.default_rng(17)
+    m, n, k = 5, 300, 1040
+    f = lambda rows, std: torch.from_numpy((rng.standard_normal((rows, k)) * std)
+                                           .astype(np.float32)).clamp(-448, 448) \
+        .to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    a, b = f(m, 24.0), f(n, 6.0)
+    sa = rng.uniform(0.01, 0.1, m).astype(np.float32)
+    sb = rng.uniform(0.001, 0.01, n).astype(np.float32)
+    fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(fin, "wb") as fh:
+        for arr in (a, b, sa, sb):
+            fh.write(np.ascontiguousarray(arr).tobytes())
+    _run(client, ["gemm", layout, m, n, k, fin, fout], tmp_path)
+    c = np.frombuffer(open(fout, "rb").read(), np.uint16).reshape(m, n)
+    ref = orc.fp8_gemm(a, sa, b, sb)
+    got = values16(c, "bf16")
+    tol = RHO["bf16"] * np.abs(ref["c"]) + ulp16(ref["c"], "bf16") + \
+        (k / 128 + 256) * 2.0**-24 * ref["abs"]
+    assert np.all(np.abs(got - ref["c"]) <= tol)
+
+
+def test_client_reports_status(client, tmp_path):
+    """An argument the library refuses comes back through arn_status_str."""
+    fin = tmp_path / "in.bin"
+    rows, hidden = 2, 100
+    with open(fin, "wb") as f:
+        f.write(np.zeros(rows * hidden * 2 + hidden, np.uint16).tobytes())
+    # stride < hidden is invalid: the library returns ARN_EINVAL before any launch
+    res = subprocess.run([client, "norm", "fused", "none", "bf16", str(rows), str(hidden),
+                          str(hidden // 2), "1e-6", "0", "0", str(fin), str(tmp_path / "o.bin")],
+                         capture_output=True, text=True, timeout=60)
+    assert res.returncode == 1
+    assert "invalid argument" in res.stderr
