@@ -78,6 +78,9 @@ def bind(lib_path: str) -> ctypes.CDLL:
     lib.orc_add_rmsnorm_var.argtypes = (lib.orc_add_rmsnorm.argtypes[:3] + [ctypes.c_int64]
                                         + lib.orc_add_rmsnorm.argtypes[3:])
     lib.orc_add_rmsnorm_var.restype = ctypes.c_int
+    lib.orc_residual16.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16),
+                                   ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(ctypes.c_uint16)]
+    lib.orc_residual16.restype = ctypes.c_int
     lib.orc_silu.argtypes = [ctypes.c_double]
     lib.orc_silu.restype = ctypes.c_double
     lib.orc_silu_and_mul.argtypes = [
@@ -183,6 +186,21 @@ class Oracle:
             out["q"] = q
         if scales is not None:
             out["scales"] = scales
+        return out
+
+    def residual16(self, dtype, x, res):
+        """The stored residual of each pair (x[i], res[i]) of two 1-D uint16
+        arrays of equal length."""
+        if isinstance(dtype, str):
+            dtype = DTYPES[dtype]
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        res = np.ascontiguousarray(res, dtype=np.uint16)
+        assert x.shape == res.shape and x.ndim == 1
+        out = np.empty_like(x)
+        rc = self.c.orc_residual16(dtype, x.size, _ptr(x, ctypes.c_uint16),
+                                   _ptr(res, ctypes.c_uint16), _ptr(out, ctypes.c_uint16))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
         return out
 
     def silu(self, g: float) -> float:

@@ -238,6 +238,26 @@ static void residual_add_row(int dtype, int64_t hidden, const uint16_t *x,
     }
 }
 
+/* The residual step alone, for n independent pairs: out[i] is the stored
+ * residual for x[i] + res[i], exactly as a row computes it. */
+int orc_residual16(int dtype, int64_t n, const uint16_t *x, const uint16_t *res,
+                   uint16_t *out)
+{
+    double r[1024];
+    int64_t i;
+    if (dtype != ORC_BF16 && dtype != ORC_FP16) {
+        return 1;
+    }
+    if (n < 0 || (n > 0 && (x == NULL || res == NULL || out == NULL))) {
+        return 1;
+    }
+    for (i = 0; i < n; i += 1024) {
+        int64_t len = n - i < 1024 ? n - i : 1024;
+        residual_add_row(dtype, len, x + i, res + i, out + i, r);
+    }
+    return 0;
+}
+
 /* Plain RMSNorm has no residual: r is x itself. */
 static void copy_row(int dtype, int64_t hidden, const uint16_t *x, uint16_t *r16,
                      double *r)

@@ -41,6 +41,12 @@ double orc_e4m3_decode(uint8_t code);
  * saturating at +-448, NaN -> 0x7F, signed zero kept. */
 uint8_t orc_e4m3_encode(double v);
 
+/* The stored residual of n independent pairs: out[i] = the 16-bit rounding
+ * of x[i] + res[i] (the first step of a fused row).  Returns 0, or 1 for an
+ * invalid argument. */
+int orc_residual16(int dtype, int64_t n, const uint16_t *x, const uint16_t *res,
+                   uint16_t *out);
+
 /*
  * The operator, row by row.
  *   x, residual : rows x hidden 16-bit patterns, row strides in elements.

@@ -8,6 +8,8 @@ torch float8_e4m3fn), the e4m3 bit identity printed in "MI210 LLM Stack"
 """
 import math
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -144,6 +146,54 @@ def test_residual_sum_equals_fp32_add_then_round(orc, dtype, window):
         ref = (x2.view(np.float16).astype(np.float32) + r2.view(np.float16).astype(np.float32)
                ).astype(np.float16).view(np.uint16)
     assert np.array_equal(got, ref)
+
+
+def _fp32_add_round16(dtype, xs, rs):
+    """What the GPU does: decode both to fp32 exactly, add in fp32 (round
+    to nearest even), round the fp32 sum to the 16-bit format (nearest
+    even).  numpy's own fp32 arithmetic and fp32 -> fp16 conversion; the
+    fp32 -> bf16 rounding by the bit rule for nearest-even on the upper 16
+    bits of the fp32 pattern.  Returns the 16-bit patterns and a NaN mask."""
+    if dtype == "fp16":
+        s = xs.view(np.float16).astype(np.float32) + rs.view(np.float16).astype(np.float32)
+        return s.astype(np.float16).view(np.uint16), np.isnan(s)
+    s = ((xs.astype(np.uint32) << 16).view(np.float32)
+         + (rs.astype(np.uint32) << 16).view(np.float32))
+    u = s.view(np.uint32)
+    out = ((u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16).astype(np.uint16)
+    return out, np.isnan(s)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_residual_sum_exhaustive(orc, dtype):
+    """Every one of the 2^32 (x, residual) pairs of 16-bit patterns: the
+    oracle's stored residual (exact sum, one rounding) equals fp32 add then
+    16-bit rounding, bit for bit (NaN matches NaN).  This is the double-
+    rounding theorem checked by brute force over the whole input space."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    allv = np.arange(65536, dtype=np.uint16)
+    chunk = 64
+
+    def check(lo):
+        xs = np.repeat(allv[lo:lo + chunk], 65536)
+        rs = np.tile(allv, chunk)
+        got = orc.residual16(dtype, xs, rs)
+        with np.errstate(over="ignore", invalid="ignore"):
+            ref, nan = _fp32_add_round16(dtype, xs, rs)
+        if dtype == "fp16":
+            got_nan = (got & 0x7C00) == 0x7C00
+            got_nan &= (got & 0x03FF) != 0
+        else:
+            got_nan = ((got & 0x7F80) == 0x7F80) & ((got & 0x007F) != 0)
+        bad = (got_nan != nan) | (~nan & (got != ref))
+        return int(np.count_nonzero(bad)), (int(xs[bad][0]), int(rs[bad][0])) if bad.any() else None
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
+        results = list(ex.map(check, range(0, 65536, chunk)))
+    nbad = sum(r[0] for r in results)
+    first = next((r[1] for r in results if r[1]), None)
+    assert nbad == 0, f"{nbad} pairs differ; first (x, res) = {first}"
 
 
 # --------------------------------------------------------------------------
