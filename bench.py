@@ -236,6 +236,35 @@ def cpu_baseline(w, target_s: float = 10.0) -> dict:
                           "cores": cores, "seconds": round(par, 3)}}
 
 
+def system_info() -> dict:
+    """What the run ran on: ROCm and torch versions, the device, and the
+    power cap and clocks rocm-smi reports (best effort, never fatal)."""
+    import subprocess
+
+    import torch
+
+    info = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    p = torch.cuda.get_device_properties(0)
+    info["device"] = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+                      "compute_units": p.multi_processor_count,
+                      "memory_GiB": round(p.total_memory / 2**30, 1)}
+    try:
+        res = subprocess.run(["rocm-smi", "--showpower", "--showmaxpower", "--showclocks",
+                              "--json"], capture_output=True, text=True, timeout=20)
+        smi = json.loads(res.stdout) if res.returncode == 0 else {}
+        card = next(iter(v for k, v in smi.items() if k.startswith("card")), {})
+        keep = ("power", "clock", "fclk", "mclk", "sclk", "socclk")
+        info["smi"] = {k: v for k, v in card.items() if any(t in k.lower() for t in keep)}
+    except (OSError, ValueError, subprocess.TimeoutExpired):
+        info["smi"] = None
+    return info
+
+
 # ---------------------------------------------------------------------------
 # practical ceilings: plain streaming kernels moving the operator's byte mix
 # ---------------------------------------------------------------------------
@@ -398,6 +427,7 @@ def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool,
     if with_cpu:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(w)
+        line["system"] = system_info()
     return line
 
 
