@@ -202,3 +202,37 @@ def test_swiglu_codes_feed_gemm(orc):
     tol = RHO["bf16"] * np.abs(ref["c"]) + ulp16(ref["c"], "bf16") + \
         (d / 128 + 256) * 2.0**-24 * ref["abs"]
     assert np.all(np.abs(got - ref["c"]) <= tol)
+
+
+@pytest.mark.parametrize("name", ["fp8_gemm_gate_up_13312x16384", "fp8_gemm_down_16384x6656",
+                                  "fp8_gemm_qkv_2304x16384", "fp8_gemm_o_16384x2048"])
+def test_full_size(orc, name):
+    """The benchmark's GEMM shapes and data (the bench's generator), in its
+    launch configuration (automatic block shape), both weight layouts, at
+    M = 1 and 64: sampled output columns against the oracle computed on
+    the matching weight rows."""
+    import residual_add_rmsnorm_amd as arn
+    import workloads as W
+
+    g = W.GEMMS[name]
+    print(f"\n[full-size] {name}", flush=True)
+    d = W.make_gemm(g, 64)
+    cols = np.unique(np.concatenate([np.linspace(0, g.n - 1, 160).astype(np.int64),
+                                     [0, 15, 16, 63, 64, g.n // 2, g.n - 17, g.n - 16,
+                                      g.n - 1]]))
+    bd = torch.from_numpy(d["b"]).cuda()
+    sbd = torch.from_numpy(d["scale_b"]).cuda()
+    layouts = {"rowmajor": bd, "preshuffled": arn.fp8_weight_preshuffle(bd)}
+    for m in (1, 64):
+        a, sa = d["a"][:m], d["scale_a"][:m]
+        ref = orc.fp8_gemm(a, sa, np.ascontiguousarray(d["b"][cols]), d["scale_b"][cols])
+        tol = RHO["bf16"] * np.abs(ref["c"]) + ulp16(ref["c"], "bf16") + \
+            (g.k / 128 + 256) * 2.0**-24 * ref["abs"]
+        ad, sad = torch.from_numpy(a).cuda(), torch.from_numpy(sa).cuda()
+        for layout, b in layouts.items():
+            c = arn.fp8_gemm(ad, sad, b, sbd)
+            torch.cuda.synchronize()
+            got = values16(bits(c[:, torch.from_numpy(cols).cuda()]), "bf16")
+            err = np.abs(got - ref["c"])
+            assert np.all(err <= tol), (m, layout, arn.last_plan(), float(np.max(err / tol)))
+            assert torch.isfinite(c.float()).all(), (m, layout)
