@@ -11,6 +11,9 @@ Importing this module registers, in the ``arn`` namespace:
     arn::silu_and_mul(x) -> y
     arn::silu_and_mul_fp8_static(x, scale) -> codes
     arn::silu_and_mul_fp8_dynamic(x) -> (codes, scales)
+    arn::fp8_weight_preshuffle(b) -> shuffled weight bytes
+    arn::fp8_gemm(a, scale_a, b, scale_b, out_dtype) -> c
+    arn::fp8_gemm_preshuffled(a, scale_a, b_shuffled, n, k, scale_b, out_dtype) -> c
 
 Each op calls the binding (one kernel on the current stream) and has a fake
 implementation giving output shapes and dtypes, so the ops stay opaque to
@@ -23,8 +26,8 @@ from typing import Optional
 
 import torch
 
-from . import (FP8_DTYPE, fused_add_rmsnorm, fused_add_rmsnorm_fp8, rmsnorm, rmsnorm_fp8,
-               silu_and_mul, silu_and_mul_fp8)
+from . import (FP8_DTYPE, PreshuffledWeight, fp8_gemm, fp8_weight_preshuffle, fused_add_rmsnorm,
+               fused_add_rmsnorm_fp8, rmsnorm, rmsnorm_fp8, silu_and_mul, silu_and_mul_fp8)
 
 Tensor = torch.Tensor
 
@@ -134,3 +137,44 @@ def silu_and_mul_fp8_dynamic_op(x: Tensor) -> tuple[Tensor, Tensor]:
 @silu_and_mul_fp8_dynamic_op.register_fake
 def _(x):
     return torch.empty(_glu_shape(x), dtype=FP8_DTYPE, device=x.device), _scales_like(x)
+
+
+def _preshuffled_bytes(n: int, k: int) -> int:
+    # ceil(n / 16) column tiles x ceil(k / 128) k steps of 2 KiB (arn.h)
+    return max(((n + 15) // 16) * ((k + 127) // 128) * 2048, 16)
+
+
+@torch.library.custom_op("arn::fp8_weight_preshuffle", mutates_args=())
+def fp8_weight_preshuffle_op(b: Tensor) -> Tensor:
+    return fp8_weight_preshuffle(b).data
+
+
+@fp8_weight_preshuffle_op.register_fake
+def _(b):
+    return torch.empty(_preshuffled_bytes(b.shape[0], b.shape[1]), dtype=torch.uint8,
+                       device=b.device)
+
+
+@torch.library.custom_op("arn::fp8_gemm", mutates_args=())
+def fp8_gemm_op(a: Tensor, scale_a: Tensor, b: Tensor, scale_b: Tensor,
+                out_dtype: torch.dtype = torch.bfloat16) -> Tensor:
+    return fp8_gemm(a, scale_a, b, scale_b, out_dtype=out_dtype)
+
+
+@fp8_gemm_op.register_fake
+def _(a, scale_a, b, scale_b, out_dtype=torch.bfloat16):
+    return torch.empty((a.shape[0], b.shape[0]), dtype=out_dtype, device=a.device)
+
+
+@torch.library.custom_op("arn::fp8_gemm_preshuffled", mutates_args=())
+def fp8_gemm_preshuffled_op(a: Tensor, scale_a: Tensor, b_shuffled: Tensor, n: int, k: int,
+                            scale_b: Tensor, out_dtype: torch.dtype = torch.bfloat16) -> Tensor:
+    if b_shuffled.numel() < _preshuffled_bytes(n, k):
+        raise ValueError("b_shuffled is smaller than a pre-shuffled n x k weight")
+    return fp8_gemm(a, scale_a, PreshuffledWeight(b_shuffled, n, k), scale_b,
+                    out_dtype=out_dtype)
+
+
+@fp8_gemm_preshuffled_op.register_fake
+def _(a, scale_a, b_shuffled, n, k, scale_b, out_dtype=torch.bfloat16):
+    return torch.empty((a.shape[0], n), dtype=out_dtype, device=a.device)

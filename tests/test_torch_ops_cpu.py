@@ -7,7 +7,8 @@ import residual_add_rmsnorm_amd.torch_ops  # noqa: F401  (registers arn::*)
 
 OPS = ["rmsnorm", "fused_add_rmsnorm", "rmsnorm_fp8_static", "rmsnorm_fp8_dynamic",
        "fused_add_rmsnorm_fp8_static", "fused_add_rmsnorm_fp8_dynamic", "silu_and_mul",
-       "silu_and_mul_fp8_static", "silu_and_mul_fp8_dynamic"]
+       "silu_and_mul_fp8_static", "silu_and_mul_fp8_dynamic", "fp8_weight_preshuffle",
+       "fp8_gemm", "fp8_gemm_preshuffled"]
 
 
 def test_ops_registered():
@@ -31,3 +32,11 @@ def test_fake_shapes():
         assert torch.ops.arn.silu_and_mul(g).shape == (5, 48)
         q, sc = torch.ops.arn.silu_and_mul_fp8_dynamic(g)
         assert q.shape == (5, 48) and sc.shape == (5,)
+        b = torch.empty(40, 48, dtype=torch.float8_e4m3fn)
+        sb = torch.empty(40, dtype=torch.float32)
+        c = torch.ops.arn.fp8_gemm(q, sc, b, sb)
+        assert c.shape == (5, 40) and c.dtype == torch.bfloat16
+        bs = torch.ops.arn.fp8_weight_preshuffle(b)
+        assert bs.shape == (3 * 1 * 2048,) and bs.dtype == torch.uint8
+        c = torch.ops.arn.fp8_gemm_preshuffled(q, sc, bs, 40, 48, sb, torch.float16)
+        assert c.shape == (5, 40) and c.dtype == torch.float16

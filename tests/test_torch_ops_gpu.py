@@ -64,3 +64,47 @@ def test_ops_equal_binding():
     s = torch.tensor([0.02], device="cuda")
     assert torch.equal(torch.ops.arn.silu_and_mul_fp8_static(gd, s).view(torch.uint8),
                        arn.silu_and_mul_fp8(gd, scale=s)[0].view(torch.uint8))
+
+
+def decode_mlp(x, residual, weight, w_gate_up, s_gate_up, w_down, s_down, n_gate_up, k):
+    """residual += x; h = e4m3(norm(residual)); gate_up = h @ W1^T;
+    a = e4m3(SwiGLU(gate_up)); out = a @ W2^T -- the decode MLP of one block
+    through the library's ops, with pre-shuffled weights."""
+    h, sh = torch.ops.arn.fused_add_rmsnorm_fp8_dynamic(x, residual, weight, 1e-6)
+    gu = torch.ops.arn.fp8_gemm_preshuffled(h, sh, w_gate_up, n_gate_up, k, s_gate_up,
+                                            torch.bfloat16)
+    a, sa = torch.ops.arn.silu_and_mul_fp8_dynamic(gu)
+    return torch.ops.arn.fp8_gemm_preshuffled(a, sa, w_down, k, n_gate_up // 2, s_down,
+                                              torch.bfloat16)
+
+
+@pytest.mark.parametrize("compiled", [False, True])
+def test_decode_mlp(compiled):
+    """The same chain compiled (fullgraph, no breaks) and eager gives the
+    same bits as the binding called step by step."""
+    import residual_add_rmsnorm_amd as arn
+
+    rng = np.random.default_rng(72)
+    rows, hidden, inter = 4, 1024, 1536
+    x = dev(W.to_bits(rng.standard_normal((rows, hidden)).astype(np.float32), "bf16"), "bf16")
+    r = dev(W.to_bits(rng.standard_normal((rows, hidden)).astype(np.float32), "bf16"), "bf16")
+    w = dev(W.to_bits((1 + 0.1 * rng.standard_normal(hidden)).astype(np.float32), "bf16"), "bf16")
+    w1 = torch.from_numpy(W.e4m3_codes(rng.standard_normal((2 * inter, hidden)) * 4)).cuda()
+    w2 = torch.from_numpy(W.e4m3_codes(rng.standard_normal((hidden, inter)) * 4)).cuda()
+    s1 = torch.full((2 * inter,), 0.01, device="cuda")
+    s2 = torch.full((hidden,), 0.01, device="cuda")
+    w1s = torch.ops.arn.fp8_weight_preshuffle(w1)
+    w2s = torch.ops.arn.fp8_weight_preshuffle(w2)
+    fn = torch.compile(decode_mlp, backend="aot_eager", fullgraph=True) if compiled else decode_mlp
+    r_op = r.clone()
+    out = fn(x, r_op, w, w1s, s1, w2s, s2, 2 * inter, hidden)
+    # step by step through the binding
+    r_b = r.clone()
+    h, sh = arn.fused_add_rmsnorm_fp8(x, r_b, w, 1e-6, dynamic=True)
+    gu = arn.fp8_gemm(h, sh, arn.fp8_weight_preshuffle(w1), s1)
+    a, sa = arn.silu_and_mul_fp8(gu, dynamic=True)
+    ref = arn.fp8_gemm(a, sa, arn.fp8_weight_preshuffle(w2), s2)
+    torch.cuda.synchronize()
+    assert torch.equal(r_op, r_b)
+    assert torch.equal(out, ref)
+    assert torch.isfinite(out.float()).all()
