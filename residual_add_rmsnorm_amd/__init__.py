@@ -1,4 +1,5 @@
-"""Fused residual-add + RMSNorm (+ OCP e4m3) for AMD Instinct MI355X (gfx950).
+"""Fused residual-add + RMSNorm (+ OCP e4m3) for AMD Instinct MI355X (gfx950),
+with the SwiGLU + e4m3 activation and the e4m3 GEMM that consume its codes.
 
 A thin binding over the C ABI of libarn.so (include/arn.h): each function
 checks and marshals torch tensors into (device pointer, row stride) pairs and
@@ -20,8 +21,10 @@ from . import _lib
 from ._lib import ArnError  # noqa: F401
 
 __all__ = [
-    "rmsnorm", "fused_add_rmsnorm", "rmsnorm_fp8", "fused_add_rmsnorm_fp8",
-    "silu_and_mul", "silu_and_mul_fp8", "norm", "fp8_gemm", "fp8_weight_preshuffle", "PreshuffledWeight", "set_tile", "set_gemm_config", "last_plan", "ArnError",
+    "rmsnorm", "fused_add_rmsnorm", "rmsnorm_fp8", "fused_add_rmsnorm_fp8", "norm",
+    "silu_and_mul", "silu_and_mul_fp8",
+    "fp8_gemm", "fp8_weight_preshuffle", "PreshuffledWeight",
+    "set_tile", "set_gemm_config", "last_plan", "ArnError",
 ]
 
 _DTYPES = {torch.bfloat16: _lib.BF16, torch.float16: _lib.FP16}

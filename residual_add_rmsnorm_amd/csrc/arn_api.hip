@@ -1,11 +1,13 @@
 // arn_api.hip -- the C ABI declared in include/arn.h: argument checks, the
-// choice of kernel shape, and the launch.  Host code only.
+// choice of kernel shape, and the launch, for the norm, SwiGLU and GEMM
+// kernels.  Host code only.
 //
-// Argument rules follow the vLLM API page "vllm.kernels.aiter_ops"
+// Norm argument rules follow the vLLM API page "vllm.kernels.aiter_ops"
 // (rms_add_no_var_16bit_only, rms_no_var_16bit_only, flatten_to_2d_is_free):
-// 16-bit activations, a weight of the same dtype or none, no variance-size
-// override, unit element stride.  Anything else is refused before any HIP
-// call, and nothing is ever copied to make an input acceptable.
+// 16-bit activations, a weight of the same dtype or none, unit element
+// stride; the named entry points take no variance-size override (arn_norm
+// adds one).  Anything else is refused before any HIP call, and nothing is
+// ever copied to make an input acceptable.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
