@@ -46,7 +46,11 @@
  *  - Return value: ARN_OK, or
  *      ARN_EINVAL       an argument is invalid (nothing is launched);
  *      ARN_EUNSUPPORTED valid but not served, e.g. hidden above the largest
- *                       compiled row size (nothing is launched);
+ *                       compiled row size (nothing is launched): rows up to
+ *                       65536 elements when hidden and every row stride are
+ *                       multiples of 4 and the 16-bit bases are 8-byte
+ *                       aligned (e4m3 out: 4-byte), else 32768 when they are
+ *                       multiples of 2 (4-byte / 2-byte aligned), else 16384;
  *      ARN_ELAUNCH      the HIP runtime refused the launch.
  *    No C++ exception crosses this interface.
  */

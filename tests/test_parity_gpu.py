@@ -450,3 +450,41 @@ def test_norm_descriptor_matches_entry_points(orc):
     b = arn.norm(xd, None, 1e-5, residual=r2)
     torch.cuda.synchronize()
     assert np.array_equal(bits(a), bits(b)) and np.array_equal(bits(r1), bits(r2))
+
+
+# ---------------------------------------------------------------------------
+# The largest rows each access width serves, and the first size beyond
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("hidden,served", [
+    (65536, True), (65544, False),   # 128-bit accesses: 16 waves x 8 vectors x 8 elements
+    (65532, True), (65540, False),   # hidden % 8 == 4: 64-bit accesses, 16 x 16 x 4
+    (32766, True), (32770, False),   # hidden % 4 == 2: 32-bit accesses, 16 x 16 x 2
+    (16383, True), (16385, False),   # odd hidden: 16-bit accesses, 16 x 16 x 1
+])
+def test_largest_rows(orc, hidden, served):
+    arn = _arn()
+    rows = 2
+    x = _random("bf16", rows, hidden, hidden, 11)
+    r = _random("bf16", rows, hidden, hidden, 12)
+    w = _random("bf16", 1, hidden, hidden, 13)[0]
+    if served:
+        run_case(orc, dtype="bf16", x=x, res=r, w=w, eps=1e-6, hidden=hidden)
+        run_case(orc, dtype="bf16", x=x, res=r, w=w, eps=1e-6, hidden=hidden, fp8="dynamic")
+        return
+    xd, rd, wd = dev(x, "bf16"), dev(r, "bf16"), dev(w, "bf16")
+    out = torch.full((rows, hidden), 7.0, dtype=torch.bfloat16, device="cuda")
+    for call in (lambda: arn.fused_add_rmsnorm(xd, rd, wd, 1e-6, out=out),
+                 lambda: arn.rmsnorm(xd, wd, 1e-6, out=out),
+                 lambda: arn.fused_add_rmsnorm_fp8(xd, rd, wd, 1e-6, dynamic=True),
+                 lambda: arn.silu_and_mul(torch.cat([xd, rd], dim=1))):
+        with pytest.raises(arn.ArnError) as e:
+            call()
+        assert e.value.status == 2
+    torch.cuda.synchronize()
+    assert torch.equal(bits_t(rd), bits_t(dev(r, "bf16"))), "residual changed by a refused call"
+    assert bool((out == 7.0).all()), "output written by a refused call"
+
+
+def bits_t(t):
+    return t.view(torch.int16)
