@@ -435,9 +435,10 @@ def bench_gemm(name: str, steps: int, warmup: int, only_m: int | None = None,
                only_layout: str | None = None) -> dict:
     """The e4m3 skinny GEMM at each activation row count, with the weight
     pre-shuffled (arn_fp8_gemm_preshuffled, the shuffle done once before the
-    timed region) and row-major (arn_fp8_gemm): device time per call,
-    weight-stream GB/s and TFLOP/s.  Weight copies rotate past the Infinity
-    Cache."""
+    timed region), pre-shuffled with a split-K workspace
+    (arn_fp8_gemm_preshuffled_ws) and row-major (arn_fp8_gemm): device time
+    per call, weight-stream GB/s and TFLOP/s.  Weight copies rotate past the
+    Infinity Cache."""
     import torch
 
     import residual_add_rmsnorm_amd as arn
@@ -452,14 +453,16 @@ def bench_gemm(name: str, steps: int, warmup: int, only_m: int | None = None,
     sb = torch.from_numpy(d["scale_b"]).cuda()
     a_all = torch.from_numpy(d["a"]).cuda()
     sa_all = torch.from_numpy(d["scale_a"]).cuda()
-    layouts = {"preshuffled": {}, "rowmajor": {}}
-    for layout in ("preshuffled", "rowmajor"):
+    layouts = {"preshuffled": {}, "preshuffled_ws": {}, "rowmajor": {}}
+    ws = arn.fp8_gemm_workspace(max(g.m_counts), g.n, g.k)
+    for layout in layouts:
         if only_layout and layout != only_layout:
             continue
-        if layout == "preshuffled":
+        if layout.startswith("preshuffled"):
             bs = [arn.fp8_weight_preshuffle(b0) for _ in range(sets)]
         else:
             bs = [b0] + [b0.clone() for _ in range(sets - 1)]
+        wsl = ws if layout == "preshuffled_ws" else None
         per_m = layouts[layout]
         for m in g.m_counts:
             if only_m and m != only_m:
@@ -469,7 +472,7 @@ def bench_gemm(name: str, steps: int, warmup: int, only_m: int | None = None,
 
             class _B:
                 def call(self, i):
-                    arn.fp8_gemm(a, sa, bs[i % sets], sb, out=out)
+                    arn.fp8_gemm(a, sa, bs[i % sets], sb, out=out, workspace=wsl)
 
             e_ms, wall = time_steps(_B(), steps, warmup)
             us = e_ms * 1e3 / steps
@@ -484,7 +487,8 @@ def bench_gemm(name: str, steps: int, warmup: int, only_m: int | None = None,
     best = max([v for lay in layouts.values() for v in lay.values()],
                key=lambda v: v["GB_per_s"])
     return {"workload": name, "n": g.n, "k": g.k, "weight_copies": sets,
-            "per_m": layouts["preshuffled"], "per_m_rowmajor": layouts["rowmajor"],
+            "per_m": layouts["preshuffled"], "per_m_splitk": layouts["preshuffled_ws"],
+            "per_m_rowmajor": layouts["rowmajor"],
             "roofline": {"bound": "hbm", "achieved": best["GB_per_s"], "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(best["GB_per_s"] / PEAK_HBM_GBS, 4),
                          "traffic": best["traffic"], "plan": best["plan"]}}
@@ -513,7 +517,8 @@ def main() -> int:
                          "recorded with the summary)")
     ap.add_argument("--gemm-m", type=int, default=None,
                     help="GEMM workloads: time only this activation row count")
-    ap.add_argument("--gemm-layout", choices=("preshuffled", "rowmajor"), default=None,
+    ap.add_argument("--gemm-layout", choices=("preshuffled", "preshuffled_ws", "rowmajor"),
+                    default=None,
                     help="GEMM workloads: time only this weight layout")
     args = ap.parse_args()
 
@@ -601,7 +606,8 @@ def summarize_pmc(name: str, fetch_csv: str, write_csv: str, command: str = "",
         with open(bench_output) as f:
             line = json.loads(f.readline())
         if "per_m" in line:
-            lay = line["per_m"] if gemm_layout == "preshuffled" else line["per_m_rowmajor"]
+            lay = {"preshuffled": line["per_m"], "preshuffled_ws": line["per_m_splitk"],
+                   "rowmajor": line["per_m_rowmajor"]}[gemm_layout]
             plan = lay[str(gemm_m)]["plan"]
         else:
             plan = line["config"]["kernel_plan"]

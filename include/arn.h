@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define ARN_ABI_VERSION 4
+#define ARN_ABI_VERSION 5
 
 enum arn_dtype { ARN_BF16 = 0, ARN_FP16 = 1 };
 enum arn_fp8_mode { ARN_FP8_STATIC = 0, ARN_FP8_DYNAMIC = 1 };
@@ -234,6 +234,37 @@ int arn_fp8_gemm_preshuffled(void *c, int64_t ldc, int out_dtype,
                              const float *scale_b, int b_per_row,
                              int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
+/*
+ * Split-K variants: with a workspace, K is also divided across several
+ * blocks per output tile when that fills the GPU better (small N, or N not
+ * a multiple of the CU count's worth of tiles); the block that completes a
+ * tile last sums the partial tiles in a fixed order, so results are
+ * deterministic for a given shape and device.
+ *   arn_fp8_gemm_workspace_bytes: bytes the workspace needs for up to
+ *     m x n outputs (about 8 x 64 x (n rounded up to 64) x 4 for m > 32,
+ *     a half or a quarter of that for m <= 32 or 16), or -1 for m < 0,
+ *     n < 0 or k <= 0.  A workspace sized for the largest shape serves
+ *     every smaller one.
+ *   workspace: device memory of at least that size, 256-byte aligned,
+ *     ZERO-FILLED before its first use; every completed call leaves it
+ *     ready for the next one, whatever the shape.  Calls that may run at
+ *     the same time (other streams) need separate workspaces.  NULL means
+ *     no split (as the plain entry points).
+ * Other arguments and results as in arn_fp8_gemm / arn_fp8_gemm_preshuffled.
+ */
+int64_t arn_fp8_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+int arn_fp8_gemm_ws(void *c, int64_t ldc, int out_dtype,
+                    const uint8_t *a, int64_t lda, const float *scale_a, int a_per_row,
+                    const uint8_t *b, int64_t ldb, const float *scale_b, int b_per_row,
+                    int64_t m, int64_t n, int64_t k, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+int arn_fp8_gemm_preshuffled_ws(void *c, int64_t ldc, int out_dtype,
+                                const uint8_t *a, int64_t lda, const float *scale_a,
+                                int a_per_row, const uint8_t *b_shuffled,
+                                const float *scale_b, int b_per_row,
+                                int64_t m, int64_t n, int64_t k, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *arn_status_str(int status);
 
@@ -263,6 +294,10 @@ int arn_set_tile(int waves_per_row, int vec_per_lane);
  * compiled shape returns ARN_EUNSUPPORTED.  (0, 0) restores automatic
  * selection; a shape never compiled returns ARN_EINVAL. */
 int arn_set_gemm_config(int col_tiles, int waves);
+/* arn_set_gemm_splits forces the number of K splits (1..8) of later
+ * workspace GEMM calls (capped by the number of 128-wide k steps); 0
+ * restores automatic selection. */
+int arn_set_gemm_splits(int splits);
 int arn_last_plan(char *buf, size_t len);
 
 #ifdef __cplusplus

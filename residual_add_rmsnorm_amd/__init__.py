@@ -23,8 +23,8 @@ from ._lib import ArnError  # noqa: F401
 __all__ = [
     "rmsnorm", "fused_add_rmsnorm", "rmsnorm_fp8", "fused_add_rmsnorm_fp8", "norm",
     "silu_and_mul", "silu_and_mul_fp8",
-    "fp8_gemm", "fp8_weight_preshuffle", "PreshuffledWeight",
-    "set_tile", "set_gemm_config", "last_plan", "ArnError",
+    "fp8_gemm", "fp8_weight_preshuffle", "PreshuffledWeight", "fp8_gemm_workspace",
+    "set_tile", "set_gemm_config", "set_gemm_splits", "last_plan", "ArnError",
 ]
 
 _DTYPES = {torch.bfloat16: _lib.BF16, torch.float16: _lib.FP16}
@@ -329,14 +329,25 @@ def fp8_weight_preshuffle(b: torch.Tensor) -> PreshuffledWeight:
     return PreshuffledWeight(dst, n, k)
 
 
+def fp8_gemm_workspace(m: int, n: int, k: int, device="cuda") -> torch.Tensor:
+    """A zero-filled split-K workspace for GEMMs of up to m x n outputs
+    (arn_fp8_gemm_workspace_bytes); reusable by later calls on one stream."""
+    size = _lib.load().arn_fp8_gemm_workspace_bytes(m, n, k)
+    if size < 0:
+        raise ValueError("invalid GEMM shape")
+    return torch.zeros(size, dtype=torch.uint8, device=device)
+
+
 def fp8_gemm(a: torch.Tensor, scale_a: torch.Tensor, b, scale_b: torch.Tensor,
              out_dtype: torch.dtype = torch.bfloat16,
-             out: torch.Tensor | None = None) -> torch.Tensor:
+             out: torch.Tensor | None = None,
+             workspace: torch.Tensor | None = None) -> torch.Tensor:
     """out[i, j] = scale_a(i) * scale_b(j) * sum_t a[i, t] * b[j, t]
     (arn_fp8_gemm) for e4m3 codes a [M, K] (float8_e4m3fn or uint8) and b
     [N, K] (the weight, out-feature major) or its PreshuffledWeight
     (arn_fp8_gemm_preshuffled); scale_a holds M or 1 float32 values,
-    scale_b N or 1."""
+    scale_b N or 1.  With a workspace (fp8_gemm_workspace) K may also be
+    split across blocks (the _ws entry points)."""
     pre = isinstance(b, PreshuffledWeight)
     for t, nm in ((a, "a"),) if pre else ((a, "a"), (b, "b")):
         _check_device(t)
@@ -359,18 +370,36 @@ def fp8_gemm(a: torch.Tensor, scale_a: torch.Tensor, b, scale_b: torch.Tensor,
     lib = _lib.load()
     a_rows = int(scale_a.numel() > 1 or m == 1)
     b_rows = int(scale_b.numel() > 1 or n == 1)
+    if workspace is not None:
+        if workspace.device != a.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on a's device")
+        ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
     with torch.cuda.device(a.device):
-        if pre:
+        if pre and workspace is not None:
+            name = "arn_fp8_gemm_preshuffled_ws"
+            st = lib.arn_fp8_gemm_preshuffled_ws(
+                out.data_ptr(), out.stride(0), _DTYPES[out.dtype], a.data_ptr(), a.stride(0),
+                scale_a.data_ptr(), a_rows, b.data.data_ptr(), scale_b.data_ptr(), b_rows,
+                m, n, k, *ws, _stream(a))
+        elif pre:
+            name = "arn_fp8_gemm_preshuffled"
             st = lib.arn_fp8_gemm_preshuffled(out.data_ptr(), out.stride(0), _DTYPES[out.dtype],
                                               a.data_ptr(), a.stride(0), scale_a.data_ptr(),
                                               a_rows, b.data.data_ptr(), scale_b.data_ptr(),
                                               b_rows, m, n, k, _stream(a))
+        elif workspace is not None:
+            name = "arn_fp8_gemm_ws"
+            st = lib.arn_fp8_gemm_ws(out.data_ptr(), out.stride(0), _DTYPES[out.dtype],
+                                     a.data_ptr(), a.stride(0), scale_a.data_ptr(), a_rows,
+                                     b.data_ptr(), b.stride(0), scale_b.data_ptr(), b_rows,
+                                     m, n, k, *ws, _stream(a))
         else:
+            name = "arn_fp8_gemm"
             st = lib.arn_fp8_gemm(out.data_ptr(), out.stride(0), _DTYPES[out.dtype],
                                   a.data_ptr(), a.stride(0), scale_a.data_ptr(), a_rows,
                                   b.data_ptr(), b.stride(0), scale_b.data_ptr(), b_rows,
                                   m, n, k, _stream(a))
-    _lib.check(st, "arn_fp8_gemm_preshuffled" if pre else "arn_fp8_gemm")
+    _lib.check(st, name)
     return out
 
 
@@ -382,6 +411,11 @@ def set_tile(waves_per_row: int = 0, vec_per_lane: int = 0) -> None:
 def set_gemm_config(col_tiles: int = 0, waves: int = 0) -> None:
     """Force the e4m3 GEMM's block shape for later calls ((0, 0) = automatic)."""
     _lib.check(_lib.load().arn_set_gemm_config(col_tiles, waves), "arn_set_gemm_config")
+
+
+def set_gemm_splits(splits: int = 0) -> None:
+    """Force the number of K splits of later workspace GEMM calls (0 = automatic)."""
+    _lib.check(_lib.load().arn_set_gemm_splits(splits), "arn_set_gemm_splits")
 
 
 def last_plan() -> str:

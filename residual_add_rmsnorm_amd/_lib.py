@@ -46,14 +46,22 @@ SIGNATURES = {
     "arn_fp8_gemm_preshuffled": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _i64, _vp,
                                                 ctypes.c_int, _vp, _vp, ctypes.c_int, _i64, _i64,
                                                 _i64, _vp]),
+    "arn_fp8_gemm_workspace_bytes": (_i64, [_i64, _i64, _i64]),
+    "arn_fp8_gemm_ws": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _i64, _vp, ctypes.c_int, _vp,
+                                       _i64, _vp, ctypes.c_int, _i64, _i64, _i64, _vp,
+                                       ctypes.c_size_t, _vp]),
+    "arn_fp8_gemm_preshuffled_ws": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _i64, _vp,
+                                                   ctypes.c_int, _vp, _vp, ctypes.c_int, _i64,
+                                                   _i64, _i64, _vp, ctypes.c_size_t, _vp]),
     "arn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "arn_abi_version": (ctypes.c_int, []),
     "arn_set_tile": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "arn_set_gemm_config": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
+    "arn_set_gemm_splits": (ctypes.c_int, [ctypes.c_int]),
     "arn_last_plan": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_size_t]),
 }
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 OUT_16BIT, OUT_FP8_STATIC, OUT_FP8_DYNAMIC = 0, 1, 2
 

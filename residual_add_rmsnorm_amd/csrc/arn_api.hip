@@ -311,15 +311,11 @@ std::atomic<int> g_forced_gemm{0};
 // wave at four or more 128-wide k steps (up to 16); with two or four row
 // tiles the accumulators and operands of a wave fill its registers, and four
 // waves per block do best.
+const GemmCfg* find_gemm(const GemmTable* table, int mt, int nt, int waves);
+
 const GemmCfg* choose_gemm(const GemmTable* table, int mt, int64_t n, int64_t k, int cus) {
   const int forced = g_forced_gemm.load(std::memory_order_relaxed);
-  auto find = [&](int nt, int waves) -> const GemmCfg* {
-    for (int i = 0; i < table->count; ++i) {
-      const GemmCfg& g = table->cfgs[i];
-      if (g.mt == mt && g.nt == nt && g.waves == waves) return &g;
-    }
-    return nullptr;
-  };
+  auto find = [&](int nt, int waves) { return find_gemm(table, mt, nt, waves); };
   if (forced != 0) return find(forced >> 8, forced & 0xFF);
   const int64_t ksteps = (k + 127) / 128;
   const int64_t want_blocks = (3 * (int64_t)cus) / 4;
@@ -345,17 +341,77 @@ int64_t preshuffled_bytes(int64_t n, int64_t k) {
   return ((n + 15) / 16) * ((k + 127) / 128) * 2048;
 }
 
+// Split-K workspace layout, a function of the workspace size alone so that
+// calls of different shapes sharing one workspace agree on where the
+// counters live: the partial tiles from the start, the int32 counters (one
+// per column tile, zero between calls) in the last ~1/512 of it.  The size
+// for m x n outputs covers up to kMaxSplits splits of every compiled shape.
+constexpr int kMaxSplits = 8;
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+int64_t partial_bound(int64_t m, int64_t n) {
+  const int64_t mpad = m <= 16 ? 16 : (m <= 32 ? 32 : 64);
+  return (int64_t)kMaxSplits * mpad * round_up(n, 64) * 4;
+}
+int64_t workspace_bytes(int64_t m, int64_t n) {
+  const int64_t p = partial_bound(m, n);
+  return round_up(p + round_up(p / 256, 256) + 512, 256);
+}
+// Counter region of a workspace of `bytes` (both 256-byte multiples):
+// [usable - counters, usable).
+int64_t ws_usable(size_t bytes) { return (int64_t)bytes / 256 * 256; }
+int64_t ws_counter_bytes(size_t bytes) { return round_up(ws_usable(bytes) / 512 + 1, 256); }
+
+// Forced number of K splits (arn_set_gemm_splits); 0 = automatic.
+std::atomic<int> g_forced_splits{0};
+
+const GemmCfg* find_gemm(const GemmTable* table, int mt, int nt, int waves) {
+  for (int i = 0; i < table->count; ++i) {
+    const GemmCfg& g = table->cfgs[i];
+    if (g.mt == mt && g.nt == nt && g.waves == waves) return &g;
+  }
+  return nullptr;
+}
+
+// With a workspace: when N is too small for one column tile per CU (the
+// shape choice fell back to 16-column tiles, e.g. a QKV projection shard)
+// and M >= 8, use 32-column tiles of 8 waves and split K so that the grid
+// holds about one block per CU.  From sweeps on MI355X: 2304 x 16384 at
+// M = 16 / 32 / 64 runs 14-38% faster this way; at M = 1 the split costs
+// more than it gains, and shapes with enough columns gain nothing from a
+// split and keep their shape.
+const GemmCfg* choose_split(const GemmTable* table, const GemmCfg* cfg, int64_t m, int64_t n,
+                            int cus, int* splits) {
+  const int forced = g_forced_splits.load(std::memory_order_relaxed);
+  if (forced > 0) {
+    *splits = forced;
+    return cfg;
+  }
+  *splits = 1;
+  if (g_forced_gemm.load(std::memory_order_relaxed) != 0 || cfg->nt != 1 || m < 8) return cfg;
+  const GemmCfg* wide = find_gemm(table, cfg->mt, 2, 8);
+  const int64_t blocks = (n + 31) / 32;
+  const int64_t sp = blocks > 0 ? cus / blocks : 1;
+  if (!wide || sp < 2) return cfg;
+  *splits = (int)(sp < kMaxSplits ? sp : kMaxSplits);
+  return wide;
+}
+
 // pre: b is the pre-shuffled copy (ldb ignored), else N x K row-major.
+// workspace (may be null: no split) holds workspace_bytes(m, n) bytes whose
+// counters are zero.
 int run_gemm(bool pre, void* c, int64_t ldc, int out_dtype, const uint8_t* a, int64_t lda,
              const float* scale_a, int a_per_row, const uint8_t* b, int64_t ldb,
              const float* scale_b, int b_per_row, int64_t m, int64_t n, int64_t k,
-             hipStream_t stream) {
+             void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (out_dtype != ARN_BF16 && out_dtype != ARN_FP16) return ARN_EINVAL;
   if (m < 0 || n < 0 || k <= 0) return ARN_EINVAL;
   if (lda < k || (!pre && ldb < k) || ldc < n) return ARN_EINVAL;
   if (m == 0 || n == 0) return ARN_OK;
   if (!c || !a || !b || !scale_a || !scale_b) return ARN_EINVAL;
   if (!aligned(c, 2) || !aligned(scale_a, 4) || !aligned(scale_b, 4)) return ARN_EINVAL;
+  if (workspace && (!aligned(workspace, 256) || (int64_t)ws_bytes < workspace_bytes(m, n))) {
+    return ARN_EINVAL;
+  }
   // Served shapes: up to 64 activation rows, K a multiple of 16, 16-byte
   // aligned operand rows.
   if (m > 64 || k % 16 != 0 || lda % 16 != 0 || !aligned(a, 16) || !aligned(b, 16) ||
@@ -368,20 +424,47 @@ int run_gemm(bool pre, void* c, int64_t ldc, int out_dtype, const uint8_t* a, in
   const int mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
   const GemmTable* table = &ARN_GEMM_TABLE_NAME(0);
   if (out_dtype == ARN_FP16) table = &ARN_GEMM_TABLE_NAME(1);
-  const GemmCfg* cfg = choose_gemm(table, mt, n, k, cu_count());
+  const int cus = cu_count();
+  const GemmCfg* cfg = choose_gemm(table, mt, n, k, cus);
   if (!cfg) return ARN_EUNSUPPORTED;
-  const int nt = cfg->nt;
   const int64_t nsteps = (k + 127) / 128;
+
+  int splits = 1;
+  if (workspace) {
+    cfg = choose_split(table, cfg, m, n, cus, &splits);
+    if (splits > kMaxSplits) splits = kMaxSplits;
+    if (splits > nsteps) splits = (int)nsteps;
+    if (splits < 1) splits = 1;
+  }
+  const int nt = cfg->nt;
+  const int64_t tile_cols = 16 * nt;
+  const int64_t k_tile = (int64_t)cfg->mt * nt * 256;  // outputs per block
+  const int steps_per_split = (int)((nsteps + splits - 1) / splits);
+  splits = (int)((nsteps + steps_per_split - 1) / steps_per_split);  // no empty split
+  if (splits > 1) {
+    // Guaranteed by the size check above; kept as a guard on the layout.
+    const int64_t tiles = (n + tile_cols - 1) / tile_cols;
+    if (tiles * splits * k_tile * 4 > ws_usable(ws_bytes) - ws_counter_bytes(ws_bytes) ||
+        tiles * 4 > ws_counter_bytes(ws_bytes)) {
+      return ARN_EINVAL;
+    }
+  }
+  float* partial = static_cast<float*>(workspace);
+  int32_t* counters =
+      workspace ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                             ws_usable(ws_bytes) - ws_counter_bytes(ws_bytes))
+                : nullptr;
 
   // Split N so that each launch's weight slice stays under 2 GiB (row-major)
   // and the grid stays well inside the launch limit.
   int64_t rows_per_launch = pre ? (int64_t(1) << 30) : (kMaxGemmBBytes / ldb);
-  rows_per_launch = rows_per_launch / (16 * nt) * (16 * nt);
+  rows_per_launch = rows_per_launch / tile_cols * tile_cols;
   if (rows_per_launch <= 0) return ARN_EUNSUPPORTED;
   int64_t done = 0;
   int64_t grid = 0;
   while (done < n) {
     const int64_t cols = (n - done < rows_per_launch) ? n - done : rows_per_launch;
+    const int64_t tile0 = done / tile_cols;
     GemmArgs g;
     g.c = static_cast<char*>(c) + done * 2;
     g.ldc = ldc;
@@ -396,18 +479,23 @@ int run_gemm(bool pre, void* c, int64_t ldc, int out_dtype, const uint8_t* a, in
     g.k = k;
     g.a_per_row = a_per_row ? 1 : 0;
     g.b_per_row = b_per_row ? 1 : 0;
-    grid = (cols + 16 * nt - 1) / (16 * nt);
+    g.splits = splits;
+    g.steps_per_split = steps_per_split;
+    g.partial = splits > 1 ? partial + tile0 * splits * k_tile : nullptr;
+    g.counters = splits > 1 ? counters + tile0 : nullptr;
+    grid = (cols + tile_cols - 1) / tile_cols;
     void* params[] = {&g};
-    const hipError_t e = hipLaunchKernel(pre ? cfg->fn_pre : cfg->fn, dim3((unsigned)grid),
+    const hipError_t e = hipLaunchKernel(pre ? cfg->fn_pre : cfg->fn,
+                                         dim3((unsigned)grid, (unsigned)splits),
                                          dim3(64u * cfg->waves), params, 0, stream);
     if (e != hipSuccess) return ARN_ELAUNCH;
     done += cols;
   }
   g_last_plan_len = std::snprintf(g_last_plan, sizeof(g_last_plan),
-                                  "fp8_gemm%s/%s/mt%d/nt%d/waves%d/grid%lld",
+                                  "fp8_gemm%s/%s/mt%d/nt%d/waves%d/splits%d/grid%lld",
                                   pre ? "_preshuffled" : "",
                                   out_dtype == ARN_BF16 ? "bf16" : "fp16", cfg->mt, cfg->nt,
-                                  cfg->waves, (long long)grid);
+                                  cfg->waves, splits, (long long)grid);
   return ARN_OK;
 }
 
@@ -444,7 +532,20 @@ int arn_fp8_gemm(void* c, int64_t ldc, int out_dtype, const uint8_t* a, int64_t 
                  const float* scale_b, int b_per_row, int64_t m, int64_t n, int64_t k,
                  hipStream_t stream) {
   return run_gemm(false, c, ldc, out_dtype, a, lda, scale_a, a_per_row, b, ldb, scale_b,
-                  b_per_row, m, n, k, stream);
+                  b_per_row, m, n, k, nullptr, 0, stream);
+}
+
+int arn_fp8_gemm_ws(void* c, int64_t ldc, int out_dtype, const uint8_t* a, int64_t lda,
+                    const float* scale_a, int a_per_row, const uint8_t* b, int64_t ldb,
+                    const float* scale_b, int b_per_row, int64_t m, int64_t n, int64_t k,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run_gemm(false, c, ldc, out_dtype, a, lda, scale_a, a_per_row, b, ldb, scale_b,
+                  b_per_row, m, n, k, workspace, workspace_bytes, stream);
+}
+
+int64_t arn_fp8_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0 || k <= 0) return -1;
+  return workspace_bytes(m, n);
 }
 
 int64_t arn_fp8_weight_preshuffled_bytes(int64_t n, int64_t k) {
@@ -462,7 +563,16 @@ int arn_fp8_gemm_preshuffled(void* c, int64_t ldc, int out_dtype, const uint8_t*
                              const float* scale_b, int b_per_row, int64_t m, int64_t n, int64_t k,
                              hipStream_t stream) {
   return run_gemm(true, c, ldc, out_dtype, a, lda, scale_a, a_per_row, b_shuffled, 0, scale_b,
-                  b_per_row, m, n, k, stream);
+                  b_per_row, m, n, k, nullptr, 0, stream);
+}
+
+int arn_fp8_gemm_preshuffled_ws(void* c, int64_t ldc, int out_dtype, const uint8_t* a,
+                                int64_t lda, const float* scale_a, int a_per_row,
+                                const uint8_t* b_shuffled, const float* scale_b, int b_per_row,
+                                int64_t m, int64_t n, int64_t k, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return run_gemm(true, c, ldc, out_dtype, a, lda, scale_a, a_per_row, b_shuffled, 0, scale_b,
+                  b_per_row, m, n, k, workspace, workspace_bytes, stream);
 }
 
 
@@ -588,6 +698,12 @@ int arn_set_gemm_config(int col_tiles, int waves) {
     }
   }
   return ARN_EINVAL;
+}
+
+int arn_set_gemm_splits(int splits) {
+  if (splits < 0 || splits > kMaxSplits) return ARN_EINVAL;
+  g_forced_splits.store(splits);
+  return ARN_OK;
 }
 
 int arn_last_plan(char* buf, size_t len) {

@@ -81,6 +81,9 @@ void gemm_fp8_kernel(const GemmArgs g) {
   const int64_t n0 = (int64_t)blockIdx.x * 16 * NT;
   const int64_t n_here = (g.n - n0) < 16 * NT ? (g.n - n0) : 16 * NT;
   const int nsteps = (int)((g.k + 127) / 128);
+  // This block's k steps: all of them, or one split's share.
+  const int s_begin = (int)blockIdx.y * g.steps_per_split;
+  const int s_end = min(nsteps, s_begin + g.steps_per_split);
   const __amdgpu_buffer_rsrc_t ars = row_rsrc(g.a, (uint32_t)(g.m * g.lda));
   // Row-major weight: this block's rows.  Pre-shuffled weight: this block's
   // column tiles, each nsteps consecutive 2 KiB MFMA tiles.
@@ -109,18 +112,18 @@ void gemm_fp8_kernel(const GemmArgs g) {
   // K steps of 128 are dealt to the waves round-robin.  Two register sets
   // ping-pong: the loads of a wave's next step are in flight while the MFMAs
   // of its current step run, and no register copy forces an early wait.  A
-  // step past K reads zeros through out-of-range offsets (no memory
-  // traffic), so the loop always runs whole pairs.
+  // step outside this block's range reads zeros through out-of-range
+  // offsets (no memory traffic), so the loop always runs whole pairs.
   auto load_step = [&](int s, i32x8 (&bq)[NT], i32x8 (&aq)[MT]) {
     const uint32_t kb = (uint32_t)s * 128u;
+    const bool in_s = s < s_end;
     if constexpr (PRE) {
       // Pre-shuffled: a 2 KiB tile per (column tile, k step), read as two
       // 1 KiB contiguous halves; lane l gets bytes [32 q, 32 q + 32) of
       // k step s for row l % 16 (q = l / 16).  K is padded with zero codes
       // to whole steps in the shuffled copy; A pieces past K read zeros.
-      const bool in_s = s < nsteps;
-      const bool a_lo = kb + 32u * kq < (uint32_t)g.k;
-      const bool a_hi = kb + 32u * kq + 16u < (uint32_t)g.k;
+      const bool a_lo = in_s && kb + 32u * kq < (uint32_t)g.k;
+      const bool a_hi = in_s && kb + 32u * kq + 16u < (uint32_t)g.k;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const uint32_t o = boff[t] + (uint32_t)s * 2048u;
@@ -133,8 +136,8 @@ void gemm_fp8_kernel(const GemmArgs g) {
       }
     } else {
       // K % 16 == 0: every 16-byte piece is wholly inside or outside K
-      const bool lo_in = kb + 16u * kq < (uint32_t)g.k;
-      const bool hi_in = kb + 64u + 16u * kq < (uint32_t)g.k;
+      const bool lo_in = in_s && kb + 16u * kq < (uint32_t)g.k;
+      const bool hi_in = in_s && kb + 64u + 16u * kq < (uint32_t)g.k;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         bq[t] = load32<kCacheStream>(brs, lo_in ? boff[t] + kb : kOutOfRange,
@@ -158,8 +161,8 @@ void gemm_fp8_kernel(const GemmArgs g) {
   // The scheduling barriers keep the compiler from sinking each load next
   // to its use (which would serialise load and MFMA again).
   i32x8 b0[NT], a0[MT], b1[NT], a1[MT];
-  load_step(wave, b0, a0);
-  for (int s = wave; s < nsteps; s += 2 * WAVES) {
+  load_step(s_begin + wave, b0, a0);
+  for (int s = s_begin + wave; s < s_end; s += 2 * WAVES) {
     load_step(s + WAVES, b1, a1);
     __builtin_amdgcn_sched_barrier(0);
     mma(b0, a0);
@@ -173,6 +176,7 @@ void gemm_fp8_kernel(const GemmArgs g) {
   // Sum the WAVES partial tiles.  In a 16x16 MFMA result, lane l holds
   // rows 4*(l/16) .. 4*(l/16)+3 of column l%16.
   __shared__ float part[WAVES * kTile];
+  __shared__ int last_split;
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -182,10 +186,71 @@ void gemm_fp8_kernel(const GemmArgs g) {
         part[wave * kTile + ((i * NT + t) * 16 + 4 * kq + j) * 16 + r16] = acc[i][t][j];
   __syncthreads();
 
-  for (int e = threadIdx.x; e < kTile; e += 64 * WAVES) {
-    float sum = 0.0f;
+  // Each thread owns the same tile elements e = threadIdx.x + 64 WAVES i in
+  // every phase below.
+  constexpr int kPer = (kTile + 64 * WAVES - 1) / (64 * WAVES);
+  float sum[kPer];
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) sum += part[w * kTile + e];
+  for (int i = 0; i < kPer; ++i) {
+    const int e = threadIdx.x + 64 * WAVES * i;
+    sum[i] = 0.0f;
+    if (e < kTile) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) sum[i] += part[w * kTile + e];
+    }
+  }
+
+  if (g.splits > 1) {
+    // Publish this split's partial tile; the block that completes the
+    // tile's count sums all splits in split order (so the result does not
+    // depend on which block finishes last).  The blocks of one tile may run
+    // on different XCDs, whose L2 caches are not coherent with each other,
+    // so the partials move with agent-scope (sc1) stores and loads, which
+    // are coherent across XCDs, rather than plain accesses made visible by
+    // agent-scope fences (each such fence writes back or invalidates a
+    // whole L2, which costs far more than the split saves).  Every thread
+    // waits for its stores to complete before the barrier that precedes the
+    // count, so a block that sees the count complete reads finished tiles.
+    float* tile_part = g.partial + (size_t)blockIdx.x * g.splits * kTile;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = threadIdx.x + 64 * WAVES * i;
+      if (e < kTile) {
+        __hip_atomic_store(tile_part + (size_t)blockIdx.y * kTile + e, sum[i], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int done = __hip_atomic_fetch_add(g.counters + blockIdx.x, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      last_split = done == g.splits - 1;
+    }
+    __syncthreads();
+    if (!last_split) return;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = threadIdx.x + 64 * WAVES * i;
+      sum[i] = 0.0f;
+      if (e < kTile) {
+        for (int sp = 0; sp < g.splits; ++sp) {
+          sum[i] += __hip_atomic_load(tile_part + (size_t)sp * kTile + e, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    // Leave the counter at zero for the next call (ordered before the next
+    // kernel on the stream by the kernel boundary).
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(g.counters + blockIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = threadIdx.x + 64 * WAVES * i;
+    if (e >= kTile) continue;
     const int tile = e >> 8;
     const int row = (e >> 4) & 15;
     const int col = e & 15;
@@ -194,7 +259,7 @@ void gemm_fp8_kernel(const GemmArgs g) {
     if (gm < g.m && gn < g.n) {
       const float sa = g.a_per_row ? g.scale_a[gm] : g.scale_a[0];
       const float sb = g.b_per_row ? g.scale_b[gn] : g.scale_b[0];
-      const float v = sum * sa * sb;
+      const float v = sum[i] * sa * sb;
       static_cast<uint16_t*>(g.c)[gm * g.ldc + gn] = (uint16_t)(pack2<DT>(v, 0.0f) & 0xFFFFu);
     }
   }

@@ -71,6 +71,15 @@ struct GemmArgs {
   int64_t k;
   int32_t a_per_row;
   int32_t b_per_row;
+  // Split K across gridDim.y blocks per column tile (1: no split).  Each
+  // split covers k steps [y * steps_per_split, (y + 1) * steps_per_split);
+  // partial tiles go to `partial` (tile-major, splits inner) and the block
+  // that finishes a tile last (counted in `counters`, one per column tile,
+  // zero on entry and left zero) sums them in split order.
+  int32_t splits;
+  int32_t steps_per_split;
+  float* partial;
+  int32_t* counters;
 };
 
 // One compiled GEMM shape: MT x NT tiles of 16 x 16 outputs per block, K

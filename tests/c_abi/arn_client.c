@@ -10,7 +10,7 @@
  *       out.bin: residual after the call (fused only), out (rows*stride u16,
  *                or rows*stride e4m3 bytes), scales (rows f32, dynamic only)
  *       variance_size 0 calls the named entry point; > 0 goes through arn_norm.
- *   arn_client gemm <rowmajor|preshuffled> m n k in.bin out.bin
+ *   arn_client gemm <rowmajor|preshuffled|preshuffled_ws> m n k in.bin out.bin
  *       in.bin : a (m*k bytes), b (n*k bytes), scale_a (m f32), scale_b (n f32)
  *       out.bin: c (m*n bf16)
  *
@@ -157,7 +157,8 @@ static int run_norm(char **argv) {
 }
 
 static int run_gemm(char **argv) {
-  const int pre = strcmp(argv[0], "preshuffled") == 0;
+  const int with_ws = strcmp(argv[0], "preshuffled_ws") == 0;
+  const int pre = with_ws || strcmp(argv[0], "preshuffled") == 0;
   const int64_t m = atoll(argv[1]), n = atoll(argv[2]), k = atoll(argv[3]);
   const size_t sa_bytes = (size_t)m * 4, sb_bytes = (size_t)n * 4;
   const size_t in_size = (size_t)(m * k + n * k) + sa_bytes + sb_bytes;
@@ -179,8 +180,23 @@ static int run_gemm(char **argv) {
     void *bs = NULL;
     HIP_OK(hipMalloc(&bs, (size_t)bytes));
     ARN_OK_(arn_fp8_weight_preshuffle((uint8_t *)bs, (const uint8_t *)b, k, n, k, stream));
-    ARN_OK_(arn_fp8_gemm_preshuffled(c, n, ARN_BF16, (const uint8_t *)a, k, sa, 1,
-                                     (const uint8_t *)bs, sb, 1, m, n, k, stream));
+    if (with_ws) {
+      /* split-K workspace: zero-filled once, reusable afterwards */
+      const int64_t ws_bytes = arn_fp8_gemm_workspace_bytes(m, n, k);
+      void *ws = NULL;
+      HIP_OK(hipMalloc(&ws, (size_t)ws_bytes));
+      HIP_OK(hipMemset(ws, 0, (size_t)ws_bytes));
+      for (int rep = 0; rep < 2; ++rep) {
+        ARN_OK_(arn_fp8_gemm_preshuffled_ws(c, n, ARN_BF16, (const uint8_t *)a, k, sa, 1,
+                                            (const uint8_t *)bs, sb, 1, m, n, k, ws,
+                                            (size_t)ws_bytes, stream));
+      }
+      HIP_OK(hipStreamSynchronize(stream));
+      HIP_OK(hipFree(ws));
+    } else {
+      ARN_OK_(arn_fp8_gemm_preshuffled(c, n, ARN_BF16, (const uint8_t *)a, k, sa, 1,
+                                       (const uint8_t *)bs, sb, 1, m, n, k, stream));
+    }
     HIP_OK(hipStreamSynchronize(stream));
     HIP_OK(hipFree(bs));
   } else {

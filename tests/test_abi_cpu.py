@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function(lib):
     for name in header_functions():
         assert name in exported, name
         assert getattr(lib, name) is not None
-    assert lib.arn_abi_version() == _lib.ABI_VERSION == 4
+    assert lib.arn_abi_version() == _lib.ABI_VERSION == 5
 
 
 def test_probe_library_exports_its_header():

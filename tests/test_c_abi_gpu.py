@@ -101,10 +101,10 @@ def test_norm_from_c(client, orc, tmp_path, form, fp8, dtype, rows, hidden, stri
         assert_scales_close(scales, ref["scales"], dtype)
 
 
-@pytest.mark.parametrize("layout", ["rowmajor", "preshuffled"])
+@pytest.mark.parametrize("layout", ["rowmajor", "preshuffled", "preshuffled_ws"])
 def test_gemm_from_c(client, orc, tmp_path, layout):
     rng = np.random.default_rng(17)
-    m, n, k = 5, 300, 1040
+    m, n, k = 9, 300, 1040   # few columns, M >= 8: with a workspace, K is split
     f = lambda rows, std: torch.from_numpy((rng.standard_normal((rows, k)) * std)
                                            .astype(np.float32)).clamp(-448, 448) \
         .to(torch.float8_e4m3fn).view(torch.uint8).numpy()

@@ -28,7 +28,7 @@ def _codes(rng, rows, cols, std):
 
 
 def check(orc, m, n, k, out="bf16", per_row=(True, True), seed=0, lda=None, ldb=None,
-          pre=False):
+          pre=False, workspace=None, repeat=1):
     import residual_add_rmsnorm_amd as arn
 
     rng = np.random.default_rng(seed)
@@ -45,7 +45,12 @@ def check(orc, m, n, k, out="bf16", per_row=(True, True), seed=0, lda=None, ldb=
     c = torch.full((m + 1, n), float("nan"), dtype=dt, device="cuda")
     if pre:
         bd = arn.fp8_weight_preshuffle(bd)
-    arn.fp8_gemm(ad, torch.from_numpy(sa).cuda(), bd, torch.from_numpy(sb).cuda(), out=c[:m])
+    sad, sbd = torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda()
+    arn.fp8_gemm(ad, sad, bd, sbd, out=c[:m], workspace=workspace)
+    first = c[:m].clone()
+    for _ in range(repeat - 1):   # the workspace is left ready for the next call
+        arn.fp8_gemm(ad, sad, bd, sbd, out=c[:m], workspace=workspace)
+        assert torch.equal(c[:m], first), "repeated call differs"
     torch.cuda.synchronize()
     ref = orc.fp8_gemm(a, sa if per_row[0] else sa[0], b, sb if per_row[1] else sb[0], k=k,
                        out_dtype=out)
@@ -236,3 +241,99 @@ def test_full_size(orc, name):
             err = np.abs(got - ref["c"])
             assert np.all(err <= tol), (m, layout, arn.last_plan(), float(np.max(err / tol)))
             assert torch.isfinite(c.float()).all(), (m, layout)
+
+
+
+# ---------------------------------------------------------------------------
+# Split K across blocks (workspace entry points)
+# ---------------------------------------------------------------------------
+
+def _counters_zero(ws, n):
+    """The counter region is the tail of the workspace (its last
+    ceil((size/512 + 1) / 256) * 256 bytes of the 256-byte-rounded size)."""
+    usable = ws.numel() // 256 * 256
+    cbytes = -(-(usable // 512 + 1) // 256) * 256
+    return bool((ws[usable - cbytes:usable] == 0).all())
+
+
+@LAYOUTS
+@pytest.mark.parametrize("splits", [2, 3, 4, 8])
+@pytest.mark.parametrize("m,n,k", [(1, 2304, 16384), (5, 300, 1040), (17, 130, 4096),
+                                   (64, 1000, 2048), (3, 70, 256), (2, 64, 128)])
+def test_split_k(orc, m, n, k, splits, pre):
+    """Forced splits (capped by the k steps: k = 128 has one), each call
+    checked against the oracle; the workspace is reused three times and its
+    counters are zero afterwards."""
+    import residual_add_rmsnorm_amd as arn
+
+    ws = arn.fp8_gemm_workspace(m, n, k)
+    arn.set_gemm_splits(splits)
+    try:
+        plan = check(orc, m, n, k, seed=m + n + splits, pre=pre, workspace=ws, repeat=3)
+    finally:
+        arn.set_gemm_splits(0)
+    nsteps = (k + 127) // 128
+    per = -(-nsteps // min(splits, nsteps))
+    assert f"/splits{-(-nsteps // per)}/" in plan, plan
+    torch.cuda.synchronize()
+    assert _counters_zero(ws, n), "counters not reset"
+
+
+@LAYOUTS
+def test_split_k_auto_matches_oracle(orc, pre):
+    import residual_add_rmsnorm_amd as arn
+
+    for m, n, k in ((1, 2304, 16384), (16, 16384, 2048), (40, 520, 6656)):
+        ws = arn.fp8_gemm_workspace(m, n, k)
+        check(orc, m, n, k, seed=m, pre=pre, workspace=ws, repeat=2)
+        assert _counters_zero(ws, n)
+
+
+def test_split_k_many_calls_one_workspace(orc):
+    """Back-to-back calls on one workspace, shapes alternating, each result
+    equal to the first call of its shape (a counter left non-zero, or a
+    partial read before it was written, would show up as a difference)."""
+    import residual_add_rmsnorm_amd as arn
+
+    rng = np.random.default_rng(21)
+    shapes = [(1, 2304, 16384), (4, 4096, 2048), (33, 700, 1024)]
+    ws = arn.fp8_gemm_workspace(64, 4096, 16384)
+    data = []
+    for m, n, k in shapes:
+        a = torch.from_numpy(_codes(rng, m, k, 24.0)).cuda()
+        b = arn.fp8_weight_preshuffle(torch.from_numpy(_codes(rng, n, k, 6.0)).cuda())
+        sa = torch.full((m,), 0.05, device="cuda")
+        sb = torch.full((n,), 0.004, device="cuda")
+        data.append((a, sa, b, sb))
+    arn.set_gemm_splits(4)
+    try:
+        firsts = [arn.fp8_gemm(*d, workspace=ws).clone() for d in data]
+        for it in range(40):
+            i = it % len(data)
+            assert torch.equal(arn.fp8_gemm(*data[i], workspace=ws), firsts[i]), (it, shapes[i])
+    finally:
+        arn.set_gemm_splits(0)
+    torch.cuda.synchronize()
+    assert _counters_zero(ws, 4096)
+    # and the split results agree with the unsplit kernel within the bound
+    for (a, sa, b, sb), f in zip(data, firsts):
+        ref = arn.fp8_gemm(a, sa, b, sb)
+        assert torch.allclose(f.float(), ref.float(), rtol=2**-6, atol=1e-3)
+
+
+def test_split_k_workspace_checks():
+    import residual_add_rmsnorm_amd as arn
+    from residual_add_rmsnorm_amd import _lib
+
+    a = torch.zeros(4, 256, dtype=torch.uint8, device="cuda")
+    b = torch.zeros(64, 256, dtype=torch.uint8, device="cuda")
+    s = torch.ones(1, device="cuda")
+    small = torch.zeros(_lib.load().arn_fp8_gemm_workspace_bytes(4, 64, 256) - 4,
+                        dtype=torch.uint8, device="cuda")
+    with pytest.raises(arn.ArnError) as e:
+        arn.fp8_gemm(a, s, b, s, workspace=small)          # too small
+    assert e.value.status == 1
+    big = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    with pytest.raises(arn.ArnError) as e:
+        arn.fp8_gemm(a, s, b, s, workspace=big[16:])       # not 256-byte aligned
+    assert e.value.status == 1
