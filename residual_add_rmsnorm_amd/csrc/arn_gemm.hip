@@ -24,6 +24,9 @@
 //    result is deterministic; the dequant scales are applied at the store.
 //  * operands are read with bounded buffer loads: rows past M or N read as
 //    zero, and a k step past K is given an out-of-range offset.
+//  * weights may come pre-shuffled into MFMA tile order (every load then
+//    reads 1 KiB contiguous), and K may be split across blocks through a
+//    caller workspace when N alone gives too few blocks for the CUs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
