@@ -275,6 +275,54 @@ MIXES = {"read": (1, 0, 0), "write": (0, 1, 0), "copy": (1, 1, 0), "2r2w": (2, 2
 PROBE_STREAM_BYTES = 256 * 1024 * 1024
 
 
+def launch_floor(calls: int = 64, replays: int = 20) -> dict:
+    """Time per call of an empty one-block kernel: from HIP-graph replay (as
+    the decode rows are timed) and from eager back-to-back launches."""
+    import ctypes
+
+    import torch
+
+    from residual_add_rmsnorm_amd import build as _build
+
+    lib = ctypes.CDLL(_build.PROBE_LIB_PATH)
+    lib.arn_probe_empty.restype = ctypes.c_int
+    lib.arn_probe_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+
+    def go():
+        st = lib.arn_probe_empty(1, 64, torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"arn_probe_empty status {st}")
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        go()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            go()
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    t1.synchronize()
+    graph_us = t0.elapsed_time(t1) * 1e3 / (calls * replays)
+    for _ in range(10):
+        go()
+    t0.record()
+    for _ in range(200):
+        go()
+    t1.record()
+    t1.synchronize()
+    eager_us = t0.elapsed_time(t1) * 1e3 / 200
+    return {"graph_us_per_call": round(graph_us, 3), "eager_us_per_call": round(eager_us, 3)}
+
+
 def workload_mix(w):
     """The probe mix with the same read:write byte ratio as the workload."""
     if w.is_glu:
@@ -422,6 +470,7 @@ def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool,
                                 "plan": arn.last_plan()}
             log(f"[bench] rows={r}: {per_rows[str(r)]}")
         line["config"]["decode_us_per_call"] = per_rows
+        line["config"]["empty_kernel_launch"] = launch_floor()
     del batch
     torch.cuda.empty_cache()
     if with_cpu:
@@ -487,6 +536,7 @@ def bench_gemm(name: str, steps: int, warmup: int, only_m: int | None = None,
     best = max([v for lay in layouts.values() for v in lay.values()],
                key=lambda v: v["GB_per_s"])
     return {"workload": name, "n": g.n, "k": g.k, "weight_copies": sets,
+            "empty_kernel_launch": launch_floor(),
             "per_m": layouts["preshuffled"], "per_m_splitk": layouts["preshuffled_ws"],
             "per_m_rowmajor": layouts["rowmajor"],
             "roofline": {"bound": "hbm", "achieved": best["GB_per_s"], "peak": PEAK_HBM_GBS,

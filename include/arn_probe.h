@@ -30,6 +30,13 @@ extern "C" {
 int arn_probe_stream(int reads, int writes16, int writes8, const void *a, const void *b,
                      void *c, void *d, int64_t n, int grid, int block, hipStream_t stream);
 
+/*
+ * One launch of an empty kernel (grid 1..2^24 blocks of 1..1024 threads) on
+ * `stream`: the launch cost that bounds the time per call of small kernels
+ * from below.  Returns 0, 1 (invalid argument) or 3 (launch failed).
+ */
+int arn_probe_empty(int grid, int block, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,6 +60,10 @@ __global__ __launch_bounds__(B) void stream_kernel(const void* a, const void* b,
   }
 }
 
+// Does nothing: the cost of a launch itself, the floor under any small
+// kernel's time per call.
+__global__ __launch_bounds__(1024) void empty_kernel() {}
+
 template <int R, int W16, int W8>
 hipError_t launch(int block, const void* a, const void* b, void* c, void* d, int64_t n,
                   int grid, hipStream_t stream) {
@@ -97,4 +101,12 @@ extern "C" int arn_probe_stream(int reads, int writes16, int writes8, const void
     return 2;
   }
   return e == hipSuccess ? 0 : 3;
+}
+
+extern "C" int arn_probe_empty(int grid, int block, hipStream_t stream) {
+  if (grid <= 0 || grid > (1 << 24) || block <= 0 || block > 1024) return 1;
+  return hipLaunchKernel((const void*)&empty_kernel, dim3((unsigned)grid), dim3((unsigned)block),
+                         nullptr, 0, stream) == hipSuccess
+             ? 0
+             : 3;
 }

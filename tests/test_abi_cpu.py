@@ -51,8 +51,8 @@ def test_probe_library_exports_its_header():
     out = subprocess.run(["nm", "-D", "--defined-only", build.PROBE_LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r" T (arn_\w+)", out))
-    assert header_functions(PROBE_HEADER) == ["arn_probe_stream"]
-    assert "arn_probe_stream" in exported
+    assert header_functions(PROBE_HEADER) == ["arn_probe_empty", "arn_probe_stream"]
+    assert {"arn_probe_stream", "arn_probe_empty"} <= exported
     probe = ctypes.CDLL(build.PROBE_LIB_PATH)
     f = probe.arn_probe_stream
     f.restype = ctypes.c_int
@@ -63,6 +63,10 @@ def test_probe_library_exports_its_header():
     assert f(1, 1, 0, 16, 16, 16, 16, 64, 1, 300, None) == 1       # block size
     assert f(2, 2, 0, 16, 16, 16, None, 64, 1, 256, None) == 1     # d missing
     assert f(2, 0, 0, 16, 16, 16, 16, 64, 1, 256, None) == 2       # mix not served
+    e = probe.arn_probe_empty
+    e.restype = ctypes.c_int
+    e.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert e(0, 64, None) == 1 and e(1, 2048, None) == 1
 
 
 def test_hip_imports_resolve_in_torch_runtime():
