@@ -81,6 +81,11 @@ def bind(lib_path: str) -> ctypes.CDLL:
     lib.orc_residual16.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16),
                                    ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(ctypes.c_uint16)]
     lib.orc_residual16.restype = ctypes.c_int
+    lib.orc_sum_parts16.argtypes = [ctypes.c_int, ctypes.c_int,
+                                    ctypes.POINTER(ctypes.POINTER(ctypes.c_uint16)),
+                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.POINTER(ctypes.c_uint16)]
+    lib.orc_sum_parts16.restype = ctypes.c_int
     lib.orc_silu.argtypes = [ctypes.c_double]
     lib.orc_silu.restype = ctypes.c_double
     lib.orc_silu_and_mul.argtypes = [
@@ -202,6 +207,32 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected its arguments")
         return out
+
+    def sum_parts(self, dtype, parts, hidden=None):
+        """The all-reduce reduction of a list of 2-D uint16 arrays of equal
+        shape (row stride = shape[1]): fp32 accumulation in list order, one
+        rounding.  Returns rows x hidden uint16 patterns."""
+        if isinstance(dtype, str):
+            dtype = DTYPES[dtype]
+        parts = [np.ascontiguousarray(p, dtype=np.uint16) for p in parts]
+        rows, stride = parts[0].shape
+        assert all(p.shape == (rows, stride) for p in parts)
+        hidden = stride if hidden is None else int(hidden)
+        out = np.empty((rows, hidden), np.uint16)
+        arr = (ctypes.POINTER(ctypes.c_uint16) * len(parts))(
+            *[_ptr(p, ctypes.c_uint16) for p in parts])
+        rc = self.c.orc_sum_parts16(dtype, len(parts), arr, stride, rows, hidden,
+                                    _ptr(out, ctypes.c_uint16))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        return out
+
+    def sum_add_rmsnorm(self, dtype, parts, residual, weight, eps, hidden=None, **kw):
+        """All-reduce of the parts, then the (fused) add + RMSNorm on the
+        reduced rows: the unfused definition of the fused kernel."""
+        x16 = self.sum_parts(dtype, parts, hidden)
+        res = None if residual is None else np.ascontiguousarray(residual)[:, :x16.shape[1]]
+        return self.add_rmsnorm(dtype, x16, res, weight, eps, **kw)
 
     def silu(self, g: float) -> float:
         return self.c.orc_silu(g)

@@ -258,6 +258,36 @@ int orc_residual16(int dtype, int64_t n, const uint16_t *x, const uint16_t *res,
     return 0;
 }
 
+/* All-reduce reduction step, per element: fp32 accumulation in rank order,
+ * then one rounding to the storage type.  (float) of a decoded 16-bit value
+ * is exact; each float addition is one IEEE single-precision add (the file
+ * is compiled without contraction or fast-math). */
+int orc_sum_parts16(int dtype, int nparts, const uint16_t *const *parts, int64_t parts_stride,
+                    int64_t rows, int64_t hidden, uint16_t *x16_out)
+{
+    int64_t i, j;
+    int g;
+    if ((dtype != ORC_BF16 && dtype != ORC_FP16) || nparts < 1 || parts == NULL ||
+        rows < 0 || hidden <= 0 || parts_stride < hidden || x16_out == NULL) {
+        return -1;
+    }
+    for (g = 0; g < nparts; g++) {
+        if (parts[g] == NULL) {
+            return -1;
+        }
+    }
+    for (i = 0; i < rows; i++) {
+        for (j = 0; j < hidden; j++) {
+            float total = (float)orc_decode16(dtype, parts[0][i * parts_stride + j]);
+            for (g = 1; g < nparts; g++) {
+                total = total + (float)orc_decode16(dtype, parts[g][i * parts_stride + j]);
+            }
+            x16_out[i * hidden + j] = orc_encode16(dtype, (double)total);
+        }
+    }
+    return 0;
+}
+
 /* Plain RMSNorm has no residual: r is x itself. */
 static void copy_row(int dtype, int64_t hidden, const uint16_t *x, uint16_t *r16,
                      double *r)

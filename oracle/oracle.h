@@ -82,6 +82,20 @@ int orc_add_rmsnorm_var(int dtype, int64_t rows, int64_t hidden, int64_t varianc
                         uint8_t *q_out, float *scale_out);
 
 /*
+ * The reduction of an all-reduce over nparts ranks, as one rank's kernel
+ * would compute it before a fused residual add + RMSNorm: for each element,
+ * the nparts 16-bit partial values are accumulated in fp32 in rank order
+ * (part 0 first), and the fp32 total is rounded once to the 16-bit type:
+ *     x16[i][j] = RNE16( fp32( ... fp32(fp32(p0) + p1) ... + p_{n-1} ) )
+ * parts[g] points at rows x hidden patterns with row stride parts_stride.
+ * x16_out is dense (row stride hidden).  Feeding x16_out as x to
+ * orc_add_rmsnorm gives the fused all-reduce + add + norm.  Returns 0, or
+ * -1 on an argument error.
+ */
+int orc_sum_parts16(int dtype, int nparts, const uint16_t *const *parts, int64_t parts_stride,
+                    int64_t rows, int64_t hidden, uint16_t *x16_out);
+
+/*
  * SwiGLU activation of a gate/up pair (Shazeer, "GLU Variants Improve
  * Transformer", 2020, the FFN_SwiGLU definition with Swish_1 = SiLU):
  *     y_j = silu(g_j) * u_j,   silu(g) = g / (1 + exp(-g)).

@@ -12,6 +12,7 @@ import pytest
 
 import oracle as O
 from tests import test_oracle_pins as pins
+from tests import test_oracle_allreduce_pins as allreduce_pins
 from tests import test_oracle_gemm_pins as gemm_pins
 from tests import test_oracle_swiglu_pins as swiglu_pins
 
@@ -44,6 +45,12 @@ MUTANTS = {
     "silu_no_sigmoid": ("return g / (1.0 + exp(-g));", "return g;"),
     "gate_up_swapped": ("y[j] = orc_silu(g) * u;", "y[j] = orc_silu(u) * g;"),
     "up_row_stride": ("up[i * up_stride + j]", "up[i * gate_stride + j + 0 * up_stride]"),
+    "sum_in_double": ("float total = (float)orc_decode16(dtype, parts[0][i * parts_stride + j]);",
+                      "double total = (float)orc_decode16(dtype, parts[0][i * parts_stride + j]);"),
+    "sum_drops_last_part": ("for (g = 1; g < nparts; g++) {\n                total",
+                            "for (g = 1; g < nparts - 1; g++) {\n                total"),
+    "sum_wrong_stride": ("total = total + (float)orc_decode16(dtype, parts[g][i * parts_stride + j]);",
+                         "total = total + (float)orc_decode16(dtype, parts[g][i * hidden + j]);"),
     "gemm_b_transposed": ("orc_e4m3_decode(b[j * ldb + t])", "orc_e4m3_decode(b[t * ldb + j])"),
     "gemm_scale_b_per_row_ignored": ("double scale_b = (double)(b_per_row ? sb[j] : sb[0]);",
                                      "double scale_b = (double)sb[0];"),
@@ -59,7 +66,8 @@ def _pin_functions():
     fns = []
     members = inspect.getmembers(pins, inspect.isfunction) + \
         inspect.getmembers(swiglu_pins, inspect.isfunction) + \
-        inspect.getmembers(gemm_pins, inspect.isfunction)
+        inspect.getmembers(gemm_pins, inspect.isfunction) + \
+        inspect.getmembers(allreduce_pins, inspect.isfunction)
     for name, fn in members:
         if not name.startswith("test_"):
             continue
