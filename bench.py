@@ -80,11 +80,18 @@ class Batch:
         H, S = w.hidden, w.stride
         OS = H if w.is_glu else S  # output row stride: dense for SwiGLU
         self.x, self.res, self.out, self.scale = [], [], [], []
-        x0 = dev(d["x"], w.dtype)
+        if w.is_sum:
+            p0 = [dev(p, w.dtype) for p in d["parts"]]
+            x0 = p0[0]
+        else:
+            x0 = dev(d["x"], w.dtype)
         r0 = dev(d["residual"], w.dtype) if w.has_residual else None
         self.weight = dev(d["weight"], w.dtype) if d["weight"] is not None else None
         for _ in range(sets):
-            self.x.append(x0.clone()[:, :w.in_width])
+            if w.is_sum:
+                self.x.append([p.clone()[:, :w.hidden] for p in p0])
+            else:
+                self.x.append(x0.clone()[:, :w.in_width])
             self.res.append(r0.clone()[:, :H] if r0 is not None else None)
             if w.fp8:
                 o = torch.empty((self.rows, OS), dtype=torch.uint8, device="cuda")
@@ -99,13 +106,23 @@ class Batch:
             else:
                 self.out.append(torch.empty((self.rows, OS), dtype=x0.dtype, device="cuda")[:, :H])
         del x0, r0
+        if w.is_sum:
+            del p0
         self.sets = sets
 
     def call(self, i: int) -> None:
         import residual_add_rmsnorm_amd as arn
 
         w, k = self.w, i % self.sets
-        if w.is_glu:
+        if w.is_sum:
+            kw = {}
+            if w.fp8 == "dynamic":
+                kw = dict(fp8="dynamic", scales_out=self.scale[k])
+            elif w.fp8 == "static":
+                kw = dict(fp8="static", scale=self.scale[k])
+            arn.sum_add_rmsnorm(self.x[k], self.weight, w.eps, residual=self.res[k],
+                                out=self.out[k], **kw)
+        elif w.is_glu:
             if w.fp8 == "dynamic":
                 arn.silu_and_mul_fp8(self.x[k], dynamic=True, out=self.out[k],
                                      scales_out=self.scale[k])
@@ -201,7 +218,11 @@ def cpu_baseline(w, target_s: float = 10.0) -> dict:
     s = static_scale(w.name) if w.fp8 == "static" else 0.0
 
     def call(d, r0, r1):
-        if w.is_glu:
+        if w.is_sum:
+            orc.sum_add_rmsnorm(w.dtype, [p[r0:r1] for p in d["parts"]], d["residual"][r0:r1],
+                                d["weight"], w.eps, hidden=w.hidden, fp8_mode=mode,
+                                static_scale=s)
+        elif w.is_glu:
             orc.silu_and_mul(w.dtype, d["x"][r0:r1], d=w.hidden, fp8_mode=mode, static_scale=s)
         else:
             res = d.get("residual")
@@ -271,7 +292,7 @@ def system_info() -> dict:
 
 # (read streams of 16 B, write streams of 16 B, write streams of 8 B) per element
 MIXES = {"read": (1, 0, 0), "write": (0, 1, 0), "copy": (1, 1, 0), "2r2w": (2, 2, 0),
-         "2r1.5w": (2, 1, 1), "2r0.5w": (2, 0, 1)}
+         "2r1.5w": (2, 1, 1), "2r0.5w": (2, 0, 1), "9r2w": (9, 2, 0), "9r1.5w": (9, 1, 1)}
 PROBE_STREAM_BYTES = 256 * 1024 * 1024
 
 
@@ -325,6 +346,10 @@ def launch_floor(calls: int = 64, replays: int = 20) -> dict:
 
 def workload_mix(w):
     """The probe mix with the same read:write byte ratio as the workload."""
+    if w.is_sum:
+        if w.nparts != 8 or not w.has_residual:
+            return None
+        return "9r1.5w" if w.fp8 else "9r2w"
     if w.is_glu:
         return "2r0.5w" if w.fp8 else None
     if not w.has_residual:
@@ -334,7 +359,8 @@ def workload_mix(w):
 
 def mix_ceilings(names, reps: int = 10) -> dict:
     """Best GB/s of the streaming probe (lib/libarn_probe.so) for each mix,
-    over block sizes and grids, on 256 MiB streams (past the MALL)."""
+    over block sizes and grids, on 256 MiB streams (64 MiB for the nine-read
+    mixes); every call moves far more than the MALL holds."""
     import ctypes
 
     import torch
@@ -345,23 +371,38 @@ def mix_ceilings(names, reps: int = 10) -> dict:
     lib.arn_probe_stream.restype = ctypes.c_int
     lib.arn_probe_stream.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 4 + [
         ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    n = PROBE_STREAM_BYTES // 16
-    bufs = [torch.empty(PROBE_STREAM_BYTES, dtype=torch.uint8, device="cuda") for _ in range(4)]
-    for b in bufs:
-        b.fill_(1)
+    lib.arn_probe_stream_many.restype = ctypes.c_int
+    lib.arn_probe_stream_many.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3 + [
+        ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     out = {}
     for name in names:
         r, w16, w8 = MIXES[name]
+        # many-read mixes use shorter streams (every call still moves far
+        # more than the MALL holds)
+        many = r > 2
+        stream_bytes = PROBE_STREAM_BYTES // 4 if many else PROBE_STREAM_BYTES
+        n = stream_bytes // 16
+        bufs = [torch.empty(stream_bytes, dtype=torch.uint8, device="cuda")
+                for _ in range(11 if many else 4)]
+        for b in bufs:
+            b.fill_(1)
         nbytes = n * (16 * r + 16 * w16 + 8 * w8)
         best = None
         for block in (256, 512, 1024):
             for grid in (256, 512, 1024, 2048, 4096, 8192, n // block):
+                srcs = (ctypes.c_void_p * r)(*[b.data_ptr() for b in bufs[:r]])
+
                 def go():
-                    st = lib.arn_probe_stream(r, w16, w8, *[b.data_ptr() for b in bufs], n,
-                                              grid, block, stream)
+                    if r > 2:
+                        st = lib.arn_probe_stream_many(r, w16, w8, srcs, bufs[-2].data_ptr(),
+                                                       bufs[-1].data_ptr(), n, grid, block,
+                                                       stream)
+                    else:
+                        st = lib.arn_probe_stream(r, w16, w8, *[b.data_ptr() for b in bufs[:4]],
+                                                  n, grid, block, stream)
                     if st != 0:
-                        raise RuntimeError(f"arn_probe_stream status {st}")
+                        raise RuntimeError(f"arn_probe status {st}")
                 for _ in range(3):
                     go()
                 t0 = torch.cuda.Event(enable_timing=True)
@@ -376,7 +417,7 @@ def mix_ceilings(names, reps: int = 10) -> dict:
                     best = {"GB_per_s": round(gbs, 1), "block": block, "grid": grid}
         out[name] = best
         log(f"[bench] ceiling {name}: {best}")
-    del bufs
+        del bufs
     torch.cuda.empty_cache()
     return out
 
@@ -442,6 +483,7 @@ def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool,
         "config": {
             "workload": name, "rows": rows, "hidden": w.hidden, "row_stride": w.stride,
             "io_dtype": w.dtype, "fp8": w.fp8, "eps": w.eps, "buffer_sets": sets,
+            **({"nparts": w.nparts} if w.is_sum else {}),
             "bytes_per_step": bytes_step, "kernel_plan": plan,
             "us_per_call": round(per_call_ms * 1e3, 3),
             "pct_of_hbm_peak": round(100 * achieved / PEAK_HBM_GBS, 2),
@@ -599,7 +641,9 @@ def main() -> int:
 
     if args.ceilings:
         print(json.dumps({"ceilings_GB_per_s": mix_ceilings(list(MIXES)),
-                          "stream_bytes": PROBE_STREAM_BYTES}), flush=True)
+                          "stream_bytes": {"two-stream mixes": PROBE_STREAM_BYTES,
+                                           "nine-stream mixes": PROBE_STREAM_BYTES // 4}}),
+              flush=True)
         return 0
 
     if args.workload in workloads.GEMMS or args.workload == "gemms":

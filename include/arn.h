@@ -160,6 +160,49 @@ typedef struct arn_norm_args {
 int arn_norm(const arn_norm_args *args);
 
 /*
+ * The reduction of an all-reduce fused with the residual add + RMSNorm: the
+ * step that follows a tensor-parallel attention or MLP block, where each of
+ * nparts ranks holds a partial sum of the same rows.  AITER supplies such
+ * communication kernels and SGLang takes the all-reduce and the RMSNorm
+ * together (page "AITER: AMD's operator library for ROCm ...", section
+ * "Where it is actually used").  This is the kernel of one rank: for every
+ * element the nparts partial values are added in fp32 in rank order (part 0
+ * first) and rounded once to 16 bits -- what the all-reduce would return --
+ * and that row then goes through the fused add + norm exactly as x does in
+ * arn_norm.  Across GPUs the part pointers would be the peers' buffers,
+ * mapped over xGMI; here any device pointers work.
+ *   parts        : HOST array of nparts (1..8) device pointers, each rows x
+ *                  hidden of dtype with row stride parts_stride elements.
+ *   residual     : as in arn_norm (NULL: no residual add).
+ *   out, scale, out_format, weight, eps, rows, hidden, stream : as in arn_norm
+ *                  (no variance-size override).
+ *   out may equal parts[0] (same stride); no other overlap.
+ * Served rows: up to 32768 elements with 16-byte aligned rows (hidden and
+ * strides multiples of 8), 16384 / 8192 / 4096 with 8 / 4 / 2-byte
+ * alignment.  Returns as the other entry points.
+ */
+typedef struct arn_sum_norm_args {
+  size_t struct_size;           /* sizeof(arn_sum_norm_args) */
+  int dtype;
+  int out_format;               /* ARN_OUT_16BIT, ARN_OUT_FP8_STATIC, ARN_OUT_FP8_DYNAMIC */
+  void *out;
+  int64_t out_stride;
+  float *scale;
+  const void *const *parts;
+  int nparts;
+  int64_t parts_stride;
+  void *residual;
+  int64_t residual_stride;
+  const void *weight;
+  float eps;
+  int64_t rows;
+  int64_t hidden;
+  hipStream_t stream;
+} arn_sum_norm_args;
+
+int arn_sum_add_rmsnorm(const arn_sum_norm_args *args);
+
+/*
  * SwiGLU activation: out[i][j] = silu(gate[i][j]) * up[i][j], j < d, with
  * silu(g) = g / (1 + exp(-g)) (Shazeer, "GLU Variants Improve Transformer",
  * 2020, FFN_SwiGLU with Swish_1).  The usual layout is one [rows, 2d] tensor

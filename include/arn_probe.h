@@ -31,6 +31,18 @@ int arn_probe_stream(int reads, int writes16, int writes8, const void *a, const 
                      void *c, void *d, int64_t n, int grid, int block, hipStream_t stream);
 
 /*
+ * The same with many read streams: `reads` streams of 16 bytes per element
+ * from the host array srcs (device pointers), summed and written as
+ * `writes16` 16-byte streams (c, then d) and `writes8` 8-byte streams (d).
+ * Served mixes: (9, 2, 0) -- eight all-reduce parts and the residual read,
+ * residual and 16-bit output written -- and (9, 1, 1) with an e4m3 output.
+ * c and d must be valid.  Returns as arn_probe_stream.
+ */
+int arn_probe_stream_many(int reads, int writes16, int writes8, const void *const *srcs,
+                          void *c, void *d, int64_t n, int grid, int block,
+                          hipStream_t stream);
+
+/*
  * One launch of an empty kernel (grid 1..2^24 blocks of 1..1024 threads) on
  * `stream`: the launch cost that bounds the time per call of small kernels
  * from below.  Returns 0, 1 (invalid argument) or 3 (launch failed).

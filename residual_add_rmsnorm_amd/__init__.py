@@ -22,6 +22,7 @@ from ._lib import ArnError  # noqa: F401
 
 __all__ = [
     "rmsnorm", "fused_add_rmsnorm", "rmsnorm_fp8", "fused_add_rmsnorm_fp8", "norm",
+    "sum_add_rmsnorm",
     "silu_and_mul", "silu_and_mul_fp8",
     "fp8_gemm", "fp8_weight_preshuffle", "PreshuffledWeight", "fp8_gemm_workspace",
     "set_tile", "set_gemm_config", "set_gemm_splits", "last_plan", "ArnError",
@@ -241,6 +242,59 @@ def norm(x: torch.Tensor, weight: torch.Tensor | None, eps: float,
     with torch.cuda.device(x.device):
         st = lib.arn_norm(ctypes.byref(args))
     _lib.check(st, "arn_norm")
+    return (out, sc) if fp8 else out
+
+
+def sum_add_rmsnorm(parts, weight: torch.Tensor | None, eps: float,
+                    residual: torch.Tensor | None = None, fp8: str | None = None,
+                    scale: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                    scales_out: torch.Tensor | None = None):
+    """The all-reduce reduction fused with the residual add + RMSNorm
+    (arn_sum_add_rmsnorm): x = the fp32 rank-order sum of the tensors in
+    ``parts`` (1..8, same shape, dtype and row layout), rounded once to 16
+    bits; then residual += x (when given) and out = norm(residual or x).
+    ``fp8`` as in norm().  Returns out, or (codes, scale tensor) for FP8."""
+    import ctypes
+
+    parts = list(parts)
+    if not 1 <= len(parts) <= 8:
+        raise ValueError("parts must hold 1 to 8 tensors")
+    x = parts[0]
+    _check_device(x)
+    dt = _dtype_code(x)
+    rows, hidden, xs = _rows(x, "parts[0]")
+    for i, p in enumerate(parts[1:], 1):
+        if p.dtype != x.dtype or p.shape != x.shape or p.device != x.device:
+            raise ValueError(f"parts[{i}] must match parts[0] in shape, dtype and device")
+        if _rows(p, f"parts[{i}]")[2] != xs:
+            raise ValueError(f"parts[{i}] must have the row stride of parts[0]")
+    rs = 0
+    if residual is not None:
+        if residual.dtype != x.dtype or residual.shape != x.shape or residual.device != x.device:
+            raise ValueError("residual must match the parts in shape, dtype and device")
+        _, _, rs = _rows(residual, "residual")
+    out = _out_like(x, out, FP8_DTYPE if fp8 else x.dtype)
+    _, _, os_ = _rows(out, "out")
+    wp = _check_weight(weight, x, hidden)
+    sc = None
+    fmt = _lib.OUT_16BIT
+    if fp8:
+        if fp8 not in ("static", "dynamic"):
+            raise ValueError("fp8 must be None, 'static' or 'dynamic'")
+        sc, _ = _fp8_scale(x, rows, scale, fp8 == "dynamic", scales_out)
+        fmt = _lib.OUT_FP8_DYNAMIC if fp8 == "dynamic" else _lib.OUT_FP8_STATIC
+    ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+    args = _lib.SumNormArgs(
+        struct_size=ctypes.sizeof(_lib.SumNormArgs), dtype=dt, out_format=fmt,
+        out=out.data_ptr(), out_stride=os_, scale=sc.data_ptr() if sc is not None else None,
+        parts=ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), nparts=len(parts),
+        parts_stride=xs, residual=residual.data_ptr() if residual is not None else None,
+        residual_stride=rs, weight=wp, eps=float(eps), rows=rows, hidden=hidden,
+        stream=_stream(x))
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        st = lib.arn_sum_add_rmsnorm(ctypes.byref(args))
+    _lib.check(st, "arn_sum_add_rmsnorm")
     return (out, sc) if fp8 else out
 
 

@@ -39,6 +39,7 @@ SIGNATURES = {
     "arn_silu_and_mul_fp8": (ctypes.c_int, [_vp, _i64, _vp, ctypes.c_int, _vp, _i64, _vp, _i64,
                                             _i64, _i64, ctypes.c_int, _vp]),
     "arn_norm": (ctypes.c_int, [_vp]),
+    "arn_sum_add_rmsnorm": (ctypes.c_int, [_vp]),
     "arn_fp8_gemm": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _i64, _vp, ctypes.c_int, _vp,
                                     _i64, _vp, ctypes.c_int, _i64, _i64, _i64, _vp]),
     "arn_fp8_weight_preshuffled_bytes": (_i64, [_i64, _i64]),
@@ -84,6 +85,28 @@ class NormArgs(ctypes.Structure):
         ("rows", ctypes.c_int64),
         ("hidden", ctypes.c_int64),
         ("variance_size", ctypes.c_int64),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+class SumNormArgs(ctypes.Structure):
+    """struct arn_sum_norm_args of include/arn.h."""
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("dtype", ctypes.c_int),
+        ("out_format", ctypes.c_int),
+        ("out", ctypes.c_void_p),
+        ("out_stride", ctypes.c_int64),
+        ("scale", ctypes.c_void_p),
+        ("parts", ctypes.POINTER(ctypes.c_void_p)),
+        ("nparts", ctypes.c_int),
+        ("parts_stride", ctypes.c_int64),
+        ("residual", ctypes.c_void_p),
+        ("residual_stride", ctypes.c_int64),
+        ("weight", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+        ("rows", ctypes.c_int64),
+        ("hidden", ctypes.c_int64),
         ("stream", ctypes.c_void_p),
     ]
 

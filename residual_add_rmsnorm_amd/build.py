@@ -72,6 +72,11 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
             units.append((os.path.join(CSRC, "arn_kernels.hip"),
                           os.path.join(OBJ_DIR, f"arn_kernels_k{k}_d{d}.o"),
                           [f"-DARN_KIND={k}", f"-DARN_DT={d}"]))
+    for k in KINDS:
+        for d in DTYPES:
+            units.append((os.path.join(CSRC, "arn_kernels.hip"),
+                          os.path.join(OBJ_DIR, f"arn_sum_k{k}_d{d}.o"),
+                          [f"-DARN_KIND={k}", f"-DARN_DT={d}", "-DARN_SUM=1"]))
     for m in GLU_MODES:
         for d in DTYPES:
             units.append((os.path.join(CSRC, "arn_glu.hip"),

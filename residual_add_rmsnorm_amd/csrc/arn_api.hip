@@ -39,6 +39,18 @@ const TileTable* table_for(int kind, int dtype) {
   return tables[kind][dtype];
 }
 
+const TileTable* sum_table_for(int kind, int dtype) {
+  static const TileTable* const tables[arn::kNumKinds][arn::kNumDtypes] = {
+      {&ARN_SUM_TABLE_NAME(0, 0), &ARN_SUM_TABLE_NAME(0, 1)},
+      {&ARN_SUM_TABLE_NAME(1, 0), &ARN_SUM_TABLE_NAME(1, 1)},
+      {&ARN_SUM_TABLE_NAME(2, 0), &ARN_SUM_TABLE_NAME(2, 1)},
+      {&ARN_SUM_TABLE_NAME(3, 0), &ARN_SUM_TABLE_NAME(3, 1)},
+      {&ARN_SUM_TABLE_NAME(4, 0), &ARN_SUM_TABLE_NAME(4, 1)},
+      {&ARN_SUM_TABLE_NAME(5, 0), &ARN_SUM_TABLE_NAME(5, 1)},
+  };
+  return tables[kind][dtype];
+}
+
 const TileTable* glu_table_for(int mode, int dtype) {
   static const TileTable* const tables[arn::kNumGluModes][arn::kNumDtypes] = {
       {&ARN_GLU_TABLE_NAME(0, 0), &ARN_GLU_TABLE_NAME(0, 1)},
@@ -91,6 +103,9 @@ struct Request {
   int64_t hidden;
   hipStream_t stream;
   int64_t var_cols = 0;  // 0: hidden
+  // All-reduce form: x is the rank-order sum of nparts parts (x unused).
+  const void* const* parts = nullptr;
+  int nparts = 0;
 };
 
 bool aligned(const void* p, uintptr_t bytes) {
@@ -104,6 +119,7 @@ int choose_vec(const Request& r) {
   for (int vec = 8; vec > 1; vec /= 2) {
     const uintptr_t b16 = 2u * vec;
     bool ok = r.hidden % vec == 0 && r.x_stride % vec == 0 && aligned(r.x, b16);
+    for (int g = 0; g < r.nparts; ++g) ok = ok && aligned(r.parts[g], b16);
     if (r.res) ok = ok && r.res_stride % vec == 0 && aligned(r.res, b16);
     if (r.w) ok = ok && aligned(r.w, b16);
     if (fp8) {
@@ -131,7 +147,8 @@ int pow2_ceil(int64_t v) {
 // row soonest.  Among the compiled tiles of the chosen wave count, the one
 // with the fewest per-lane vectors that covers the row (and at least
 // `min_nv`) is taken; failing that, any tile that covers the row.
-const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t rows, int cus) {
+const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t rows, int cus,
+                        bool lean = false) {
   const int forced = g_forced_tile.load(std::memory_order_relaxed);
   if (forced != 0) {
     const int fw = forced >> 8, fn = forced & 0xFF;
@@ -143,9 +160,11 @@ const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t r
     }
     return nullptr;
   }
+  // lean: each vector brings several inputs (the all-reduce form), so one
+  // vector per lane with more waves per row streams best.
   const bool many_rows = rows >= (int64_t)4 * cus;
-  const int64_t target_nv = many_rows ? 2 : 4;
-  const int64_t min_nv = many_rows ? 2 : 1;
+  const int64_t target_nv = lean ? 1 : (many_rows ? 2 : 4);
+  const int64_t min_nv = lean || !many_rows ? 1 : 2;
   const int wpr_floor = 8;
   int wpr = pow2_ceil((nvec + 64 * target_nv - 1) / (64 * target_nv));
   const int need1 = pow2_ceil((nvec + 63) / 64);  // waves if each lane held one vector
@@ -185,8 +204,14 @@ int run(const Request& r) {
   if ((r.kind & 1) && r.res_stride < r.hidden) return ARN_EINVAL;
   if (!(r.eps >= 0.0f) || !std::isfinite(r.eps)) return ARN_EINVAL;
   if (r.var_cols < 0 || r.var_cols > r.hidden) return ARN_EINVAL;
+  if (r.parts && (r.nparts < 1 || r.nparts > arn::kMaxParts)) return ARN_EINVAL;
   if (r.rows == 0) return ARN_OK;
   if (!r.out || !r.x) return ARN_EINVAL;
+  for (int g = 0; g < r.nparts; ++g) {
+    if (!r.parts[g] || !aligned(r.parts[g], 2)) return ARN_EINVAL;
+    if (g > 0 && r.parts[g] == r.out) return ARN_EINVAL;
+    if (r.res && r.parts[g] == r.res) return ARN_EINVAL;
+  }
   if ((r.kind & 1) && !r.res) return ARN_EINVAL;
   if (fp8 && (!r.scale || !aligned(r.scale, 4))) return ARN_EINVAL;
   if (!aligned(r.x, 2) || (r.res && !aligned(r.res, 2)) || (r.w && !aligned(r.w, 2)) ||
@@ -201,7 +226,8 @@ int run(const Request& r) {
 
   const int vec = choose_vec(r);
   const int64_t nvec = r.hidden / vec;
-  const Tile* tile = choose_tile(table_for(r.kind, r.dtype), vec, nvec, r.rows, cu_count());
+  const TileTable* table = r.parts ? sum_table_for(r.kind, r.dtype) : table_for(r.kind, r.dtype);
+  const Tile* tile = choose_tile(table, vec, nvec, r.rows, cu_count(), r.nparts >= 4);
   if (!tile) return ARN_EUNSUPPORTED;
 
   const int esize_out = fp8 ? 1 : 2;
@@ -224,6 +250,11 @@ int run(const Request& r) {
     a.eps = r.eps;
     a.var_cols = (int32_t)(r.var_cols > 0 ? r.var_cols : r.hidden);
     a.inv_var = 1.0f / (float)a.var_cols;
+    a.nparts = r.nparts;
+    for (int g = 0; g < arn::kMaxParts; ++g) {
+      a.parts[g] = g < r.nparts ? static_cast<const char*>(r.parts[g]) + done * r.x_stride * 2
+                                : nullptr;
+    }
 
     grid = (n + tile->rpb - 1) / tile->rpb;
     void* params[] = {&a};
@@ -234,7 +265,8 @@ int run(const Request& r) {
   }
 
   g_last_plan_len = std::snprintf(g_last_plan, sizeof(g_last_plan),
-                                  "%s/%s/vec%d/wpr%d/nv%d/rpb%d/grid%lld", kKindNames[r.kind],
+                                  "%s%s/%s/vec%d/wpr%d/nv%d/rpb%d/grid%lld",
+                                  r.parts ? "sum_" : "", kKindNames[r.kind],
                                   r.dtype == ARN_BF16 ? "bf16" : "fp16", vec, tile->wpr, tile->nv,
                                   tile->rpb, (long long)grid);
   return ARN_OK;
@@ -649,6 +681,31 @@ int arn_norm(const arn_norm_args* p) {
   Request r{kind,      p->dtype,  p->out,    p->out_stride, p->x,      p->x_stride,
             p->residual, p->residual_stride, p->weight, kind & 6 ? p->scale : nullptr, p->eps,
             p->rows,   p->hidden, p->stream, p->variance_size};
+  return run(r);
+}
+
+int arn_sum_add_rmsnorm(const arn_sum_norm_args* p) {
+  if (!p || p->struct_size < sizeof(arn_sum_norm_args)) return ARN_EINVAL;
+  if (!p->parts) return ARN_EINVAL;
+  int kind;
+  switch (p->out_format) {
+    case ARN_OUT_16BIT:
+      kind = arn::kPlain;
+      break;
+    case ARN_OUT_FP8_STATIC:
+      kind = arn::kPlainFp8Static;
+      break;
+    case ARN_OUT_FP8_DYNAMIC:
+      kind = arn::kPlainFp8Dynamic;
+      break;
+    default:
+      return ARN_EINVAL;
+  }
+  if (p->residual) kind |= arn::kFused;
+  Request r{kind,      p->dtype,  p->out,    p->out_stride, p->nparts > 0 ? p->parts[0] : nullptr,
+            p->parts_stride, p->residual, p->residual_stride, p->weight,
+            kind & 6 ? p->scale : nullptr, p->eps, p->rows, p->hidden, p->stream, 0,
+            p->parts, p->nparts};
   return run(r);
 }
 

@@ -22,6 +22,9 @@ enum Kind : int {
 
 enum Dtype : int { kBF16 = 0, kFP16 = 1, kNumDtypes = 2 };
 
+// Largest number of partial inputs of the all-reduce form.
+constexpr int kMaxParts = 8;
+
 // Kernel arguments, passed by value.  Strides are in elements of each
 // tensor; `out` holds 16-bit elements or e4m3 bytes depending on the kind.
 struct Args {
@@ -38,6 +41,11 @@ struct Args {
   int32_t var_cols;   // channels in the mean of squares (== hidden unless overridden)
   float eps;
   float inv_var;      // 1.0f / var_cols
+  // All-reduce form only (kernels built with ARN_SUM=1): x is the fp32
+  // rank-order sum of the nparts parts (row stride x_stride), rounded once
+  // to 16 bits.
+  const void* parts[kMaxParts];
+  int32_t nparts;
 };
 
 // SwiGLU output modes.
@@ -144,6 +152,23 @@ ARN_DECLARE_TABLE(4, 0)
 ARN_DECLARE_TABLE(4, 1)
 ARN_DECLARE_TABLE(5, 0)
 ARN_DECLARE_TABLE(5, 1)
+
+#define ARN_SUM_TABLE_NAME_(KIND, DT) arn_sum_tiles_k##KIND##_d##DT
+#define ARN_SUM_TABLE_NAME(KIND, DT) ARN_SUM_TABLE_NAME_(KIND, DT)
+#define ARN_DECLARE_SUM_TABLE(KIND, DT) extern const arn::TileTable ARN_SUM_TABLE_NAME(KIND, DT);
+
+ARN_DECLARE_SUM_TABLE(0, 0)
+ARN_DECLARE_SUM_TABLE(0, 1)
+ARN_DECLARE_SUM_TABLE(1, 0)
+ARN_DECLARE_SUM_TABLE(1, 1)
+ARN_DECLARE_SUM_TABLE(2, 0)
+ARN_DECLARE_SUM_TABLE(2, 1)
+ARN_DECLARE_SUM_TABLE(3, 0)
+ARN_DECLARE_SUM_TABLE(3, 1)
+ARN_DECLARE_SUM_TABLE(4, 0)
+ARN_DECLARE_SUM_TABLE(4, 1)
+ARN_DECLARE_SUM_TABLE(5, 0)
+ARN_DECLARE_SUM_TABLE(5, 1)
 
 #define ARN_GLU_TABLE_NAME_(MODE, DT) arn_glu_tiles_m##MODE##_d##DT
 #define ARN_GLU_TABLE_NAME(MODE, DT) ARN_GLU_TABLE_NAME_(MODE, DT)

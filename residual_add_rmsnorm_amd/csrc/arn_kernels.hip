@@ -32,7 +32,10 @@
 #include "arn_internal.h"
 
 #if !defined(ARN_KIND) || !defined(ARN_DT)
-#error "compile with -DARN_KIND=<0..5> -DARN_DT=<0|1>"
+#error "compile with -DARN_KIND=<0..5> -DARN_DT=<0|1> [-DARN_SUM=1]"
+#endif
+#if !defined(ARN_SUM)
+#define ARN_SUM 0
 #endif
 
 namespace arn {
@@ -43,7 +46,7 @@ using namespace dev;
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-template <int DT, int KIND, int VEC, int NV, int WPR, int RPB>
+template <int DT, int KIND, int VEC, int NV, int WPR, int RPB, bool SUM>
 __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
   constexpr bool kRes = (KIND & 1) != 0;
   constexpr bool kStatic = (KIND & 2) != 0;
@@ -87,10 +90,44 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
     //    row end read as zero.
     Raw<VEC> xr[NV];
     Raw<VEC> rr[NV];
+    if constexpr (SUM) {
+      // All-reduce form: every part's vectors are loaded, then x is the
+      // fp32 sum in rank order (part 0 first), rounded once to 16 bits --
+      // the value an all-reduce would hand to the unfused norm.
+      Raw<VEC> pr[kMaxParts][NV];
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      xr[k] = load16<VEC, kCacheStream>(xrs, off16 + k * kStep16);
-      if constexpr (kRes) rr[k] = load16<VEC, kCacheStream>(rrs, off16 + k * kStep16);
+      for (int g = 0; g < kMaxParts; ++g) {
+        if (g < a.nparts) {
+          const __amdgpu_buffer_rsrc_t prs =
+              row_rsrc(static_cast<const uint16_t*>(a.parts[g]) + arow * a.x_stride, n16);
+#pragma unroll
+          for (int k = 0; k < NV; ++k) pr[g][k] = load16<VEC, kCacheStream>(prs, off16 + k * kStep16);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        if constexpr (kRes) rr[k] = load16<VEC, kCacheStream>(rrs, off16 + k * kStep16);
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        float acc[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = elem<DT, VEC>(pr[0][k], e);
+#pragma unroll
+        for (int g = 1; g < kMaxParts; ++g) {
+          if (g < a.nparts) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + elem<DT, VEC>(pr[g][k], e);
+          }
+        }
+        xr[k] = pack<DT, VEC>(acc);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        xr[k] = load16<VEC, kCacheStream>(xrs, off16 + k * kStep16);
+        if constexpr (kRes) rr[k] = load16<VEC, kCacheStream>(rrs, off16 + k * kStep16);
+      }
     }
     // The weight (shared by all rows; an L2 hit after the first blocks).
     Raw<VEC> wr[NV];
@@ -211,10 +248,23 @@ constexpr int rows_per_block(int wpr) { return wpr >= 4 ? 1 : 4 / wpr; }
 }  // namespace
 }  // namespace arn
 
-#define ARN_TILE(VEC, WPR, NV)                                                          \
-  {VEC, WPR, NV, arn::rows_per_block(WPR),                                             \
-   (const void*)&arn::row_kernel<ARN_DT, ARN_KIND, VEC, NV, WPR, arn::rows_per_block(WPR)>}
+#define ARN_TILE(VEC, WPR, NV)                                                              \
+  {VEC, WPR, NV, arn::rows_per_block(WPR),                                                 \
+   (const void*)&arn::row_kernel<ARN_DT, ARN_KIND, VEC, NV, WPR, arn::rows_per_block(WPR), \
+                                 ARN_SUM != 0>}
 
+#if ARN_SUM
+// All-reduce form: up to kMaxParts inputs held per vector, so at most four
+// vectors per lane.
+static const arn::Tile kTiles[] = {
+    ARN_TILE(8, 4, 1), ARN_TILE(8, 4, 2), ARN_TILE(8, 8, 1), ARN_TILE(8, 8, 2),
+    ARN_TILE(8, 16, 1), ARN_TILE(8, 16, 2), ARN_TILE(8, 16, 4),
+    ARN_TILE(4, 16, 2), ARN_TILE(4, 16, 4), ARN_TILE(2, 16, 4), ARN_TILE(1, 16, 4),
+};
+
+extern const arn::TileTable ARN_SUM_TABLE_NAME(ARN_KIND, ARN_DT) = {
+    kTiles, (int)(sizeof(kTiles) / sizeof(kTiles[0]))};
+#else
 static const arn::Tile kTiles[] = {
     // 128-bit accesses (hidden % 8 == 0, 16-byte aligned rows)
     ARN_TILE(8, 1, 2), ARN_TILE(8, 1, 4), ARN_TILE(8, 1, 8), ARN_TILE(8, 1, 16),
@@ -230,3 +280,4 @@ static const arn::Tile kTiles[] = {
 
 extern const arn::TileTable ARN_TABLE_NAME(ARN_KIND, ARN_DT) = {
     kTiles, (int)(sizeof(kTiles) / sizeof(kTiles[0]))};
+#endif

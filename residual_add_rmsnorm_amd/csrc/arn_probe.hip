@@ -60,6 +60,51 @@ __global__ __launch_bounds__(B) void stream_kernel(const void* a, const void* b,
   }
 }
 
+// Many read streams (the all-reduce form reads every rank's part and the
+// residual): R streams of 16 bytes per element summed, written to c (16
+// bytes) and d (16 or 8 bytes per element).
+struct ManyArgs {
+  const void* src[16];
+  void* c;
+  void* d;
+  int64_t n;
+};
+
+template <int B, int R, int W16, int W8>
+__global__ __launch_bounds__(B) void many_kernel(const ManyArgs p) {
+  __amdgpu_buffer_rsrc_t rs[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rs[r] = rsrc(p.src[r], (uint32_t)(p.n * 16));
+  const auto rc = rsrc(p.c, (uint32_t)(p.n * 16));
+  const auto rd = rsrc(p.d, (uint32_t)(p.n * (W16 == 2 ? 16 : 8)));
+  const int64_t stride = (int64_t)gridDim.x * B;
+  for (int64_t i = (int64_t)blockIdx.x * B + threadIdx.x; i < p.n; i += stride) {
+    const uint32_t off = (uint32_t)i * 16u;
+    u32x4 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = __builtin_amdgcn_raw_buffer_load_b128(rs[r], (int)off, 0, kNt);
+    u32x4 s = v[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) s += v[r];
+    if constexpr (W16 >= 1) __builtin_amdgcn_raw_buffer_store_b128(s, rc, (int)off, 0, kNt);
+    if constexpr (W16 >= 2) __builtin_amdgcn_raw_buffer_store_b128(s ^ v[0], rd, (int)off, 0, kNt);
+    if constexpr (W8 >= 1) {
+      const u32x2 h = {s.x ^ s.z, s.y ^ s.w};
+      __builtin_amdgcn_raw_buffer_store_b64(h, rd, (int)(off / 2u), 0, kNt);
+    }
+  }
+}
+
+template <int R, int W16, int W8>
+hipError_t launch_many(int block, const ManyArgs& a, int grid, hipStream_t stream) {
+  void* params[] = {const_cast<ManyArgs*>(&a)};
+  const void* fn = nullptr;
+  if (block == 256) fn = (const void*)&many_kernel<256, R, W16, W8>;
+  if (block == 512) fn = (const void*)&many_kernel<512, R, W16, W8>;
+  if (block == 1024) fn = (const void*)&many_kernel<1024, R, W16, W8>;
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)block), params, 0, stream);
+}
+
 // Does nothing: the cost of a launch itself, the floor under any small
 // kernel's time per call.
 __global__ __launch_bounds__(1024) void empty_kernel() {}
@@ -109,4 +154,29 @@ extern "C" int arn_probe_empty(int grid, int block, hipStream_t stream) {
                          nullptr, 0, stream) == hipSuccess
              ? 0
              : 3;
+}
+
+extern "C" int arn_probe_stream_many(int reads, int writes16, int writes8,
+                                     const void* const* srcs, void* c, void* d, int64_t n,
+                                     int grid, int block, hipStream_t stream) {
+  if (n <= 0 || n > (int64_t(1) << 27) || grid <= 0 || grid > (1 << 24)) return 1;
+  if (block != 256 && block != 512 && block != 1024) return 1;
+  if (!srcs || !c || !d || reads < 1 || reads > 16) return 1;
+  ManyArgs a;
+  for (int r = 0; r < 16; ++r) a.src[r] = r < reads ? srcs[r] : nullptr;
+  for (int r = 0; r < reads; ++r) {
+    if (!a.src[r]) return 1;
+  }
+  a.c = c;
+  a.d = d;
+  a.n = n;
+  hipError_t e;
+  if (reads == 9 && writes16 == 2 && writes8 == 0) {
+    e = launch_many<9, 2, 0>(block, a, grid, stream);
+  } else if (reads == 9 && writes16 == 1 && writes8 == 1) {
+    e = launch_many<9, 1, 1>(block, a, grid, stream);
+  } else {
+    return 2;
+  }
+  return e == hipSuccess ? 0 : 3;
 }

@@ -51,8 +51,9 @@ def test_probe_library_exports_its_header():
     out = subprocess.run(["nm", "-D", "--defined-only", build.PROBE_LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r" T (arn_\w+)", out))
-    assert header_functions(PROBE_HEADER) == ["arn_probe_empty", "arn_probe_stream"]
-    assert {"arn_probe_stream", "arn_probe_empty"} <= exported
+    assert header_functions(PROBE_HEADER) == ["arn_probe_empty", "arn_probe_stream",
+                                              "arn_probe_stream_many"]
+    assert {"arn_probe_stream", "arn_probe_empty", "arn_probe_stream_many"} <= exported
     probe = ctypes.CDLL(build.PROBE_LIB_PATH)
     f = probe.arn_probe_stream
     f.restype = ctypes.c_int
@@ -199,15 +200,17 @@ def test_norm_descriptor_zero_rows(lib):
     assert lib.arn_norm(ctypes.byref(a)) == _lib.OK
 
 
-def test_norm_struct_layout_matches_header():
+@pytest.mark.parametrize("mirror,ctype", [(_lib.NormArgs, "arn_norm_args"),
+                                          (_lib.SumNormArgs, "arn_sum_norm_args")])
+def test_norm_struct_layout_matches_header(mirror, ctype):
     """Field offsets of the ctypes mirror equal those of the C struct,
     measured by compiling a probe against include/arn.h with the host
     compiler (no GPU code)."""
     import tempfile
     src = "#include <stdio.h>\n#include <stddef.h>\n#include \"arn.h\"\nint main(void){\n"
-    for name, _ in _lib.NormArgs._fields_:
-        src += f'  printf("{name} %zu\\n", offsetof(arn_norm_args, {name}));\n'
-    src += '  printf("size %zu\\n", sizeof(arn_norm_args));\n  return 0;\n}\n'
+    for name, _ in mirror._fields_:
+        src += f'  printf("{name} %zu\\n", offsetof({ctype}, {name}));\n'
+    src += f'  printf("size %zu\\n", sizeof({ctype}));\n  return 0;\n}}\n'
     with tempfile.TemporaryDirectory() as d:
         c = os.path.join(d, "probe.c")
         open(c, "w").write(src)
@@ -216,6 +219,35 @@ def test_norm_struct_layout_matches_header():
                         "-I", "/opt/rocm/include", c, "-o", exe], check=True)
         out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()
     got = dict(zip(out[0::2], map(int, out[1::2])))
-    for name, _ in _lib.NormArgs._fields_:
-        assert got[name] == getattr(_lib.NormArgs, name).offset, name
-    assert got["size"] == ctypes.sizeof(_lib.NormArgs)
+    for name, _ in mirror._fields_:
+        assert got[name] == getattr(mirror, name).offset, name
+    assert got["size"] == ctypes.sizeof(mirror)
+
+
+def _sum_args(**kw):
+    ptrs = (ctypes.c_void_p * 8)(*([Q] * 8))
+    a = _lib.SumNormArgs(struct_size=ctypes.sizeof(_lib.SumNormArgs), dtype=0, out_format=0,
+                         out=P, out_stride=64, scale=None,
+                         parts=ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), nparts=2,
+                         parts_stride=64, residual=R, residual_stride=64, weight=None, eps=1e-6,
+                         rows=4, hidden=64, stream=None)
+    a._keep = ptrs
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("case", [
+    dict(struct_size=8), dict(out_format=3), dict(nparts=0), dict(nparts=9),
+    dict(parts=None), dict(out_format=1, scale=None), dict(parts_stride=10), dict(dtype=3),
+])
+def test_sum_descriptor_rejects(lib, case):
+    a = _sum_args(**case)
+    assert lib.arn_sum_add_rmsnorm(ctypes.byref(a)) == _lib.EINVAL
+    assert lib.arn_sum_add_rmsnorm(None) == _lib.EINVAL
+
+
+def test_sum_descriptor_residual_aliasing_a_part(lib):
+    ptrs = (ctypes.c_void_p * 2)(Q, R)
+    a = _sum_args(parts=ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)))
+    assert lib.arn_sum_add_rmsnorm(ctypes.byref(a)) == _lib.EINVAL

@@ -8,7 +8,8 @@ Generator: numpy's counter-based Philox (Salmon et al., "Parallel random
 numbers: as easy as 1, 2, 3", SC'11), keyed by (seed, tensor stream, block of
 256 rows).  Keying per row block makes any row range reproducible on its own,
 which lets a parity test regenerate sampled rows of a full-size workload
-cheaply.  Streams: x = 1, residual = 2, weight = 3, outlier columns = 4.
+cheaply.  Streams: x = 1, residual = 2, weight = 3, outlier columns = 4;
+the partial sums of the all-reduce form use streams 8 + rank.
 
 float32 draws are rounded to bf16 by torch's CPU conversion and to fp16 by
 numpy's -- both round to nearest even.
@@ -28,6 +29,7 @@ import numpy as np
 
 BLOCK_ROWS = 256
 STREAM_X, STREAM_RES, STREAM_W, STREAM_OUTLIER = 1, 2, 3, 4
+STREAM_PART0 = 8
 
 # bf16 NaN pattern written into row padding; a kernel that reads it into a
 # row's sum of squares turns that row's output into NaN.
@@ -37,7 +39,7 @@ PAD_SENTINEL = 0x7FA5
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str            # rmsnorm | fused_add_rmsnorm | *_fp8
+    op: str            # rmsnorm | fused_add_rmsnorm | *_fp8 | silu_and_mul* | sum_add_rmsnorm*
     dtype: str         # bf16 | fp16
     rows: int
     hidden: int
@@ -50,10 +52,15 @@ class Workload:
     outliers: int = 0               # columns of x multiplied by outlier_gain
     outlier_gain: float = 50.0
     row_counts: tuple = field(default=())  # decode sweeps: prefixes of `rows`
+    nparts: int = 0                 # all-reduce form: ranks whose partial rows are summed
 
     @property
     def has_residual(self) -> bool:
-        return self.op.startswith("fused_add")
+        return self.op.startswith("fused_add") or self.op.startswith("sum_add")
+
+    @property
+    def is_sum(self) -> bool:
+        return self.nparts > 0
 
     @property
     def is_glu(self) -> bool:
@@ -68,11 +75,11 @@ class Workload:
         """Minimum HBM bytes one call must move: 16-bit x read (gate and up
         for SwiGLU), residual read and written, output written (16-bit or
         e4m3), the norm weight once, the static scale read once or the
-        dynamic scales written."""
+        dynamic scales written.  The all-reduce form reads every part."""
         r = self.rows if rows is None else rows
         h = self.hidden
         elem = 2
-        per_row = self.in_width * elem          # x (or gate | up)
+        per_row = self.in_width * elem * max(1, self.nparts)  # x (gate | up; every part)
         if self.has_residual:
             per_row += 2 * h * elem             # residual read + write
         per_row += h * (1 if self.fp8 else elem)  # output
@@ -112,6 +119,13 @@ WORKLOADS = {
                  256, 6656, 13312, 0.0, fp8="static", row_counts=(1, 8, 64, 256)),
     ]
 }
+
+# The all-reduce form, one rank's kernel: 8 tensor-parallel ranks' partial
+# sums of a 4096 x 8192 bf16 block output (each partial N(0, 1/8), so the
+# total is N(0, 1) like the other workloads' x), then add + norm.
+WORKLOADS["sum_add_rmsnorm_bf16_8x4096x8192"] = Workload(
+    "sum_add_rmsnorm_bf16_8x4096x8192", "sum_add_rmsnorm", "bf16", 4096, 8192, 8192, 1e-5,
+    x_std=float(np.float32(8 ** -0.5)), nparts=8)
 
 # The benchmark's headline workload.
 HEADLINE = "fused_add_rmsnorm_bf16_4096x8192"
@@ -183,12 +197,18 @@ def padded(bits: np.ndarray, stride: int, fill: int = PAD_SENTINEL) -> np.ndarra
 def make_rows(w: Workload, row0: int, row1: int, seed: int = 0) -> dict:
     """Inputs for rows [row0, row1) of a workload, rows laid out at the
     workload's stride with padding filled by PAD_SENTINEL.  For SwiGLU, x
-    holds gate | up (2 * hidden columns) and there is no weight."""
-    xf = _normal_rows(seed, STREAM_X, row0, row1, w.in_width, w.x_std)
-    if w.outliers:
-        xf[:, outlier_columns(w, seed)] *= np.float32(w.outlier_gain)
-    out = {"x": padded(to_bits(xf, w.dtype), w.stride)}
-    del xf
+    holds gate | up (2 * hidden columns) and there is no weight; the
+    all-reduce form has "parts" (one array per rank) instead of x."""
+    if w.is_sum:
+        out = {"parts": [padded(to_bits(_normal_rows(seed, STREAM_PART0 + g, row0, row1,
+                                                     w.hidden, w.x_std), w.dtype), w.stride)
+                         for g in range(w.nparts)]}
+    else:
+        xf = _normal_rows(seed, STREAM_X, row0, row1, w.in_width, w.x_std)
+        if w.outliers:
+            xf[:, outlier_columns(w, seed)] *= np.float32(w.outlier_gain)
+        out = {"x": padded(to_bits(xf, w.dtype), w.stride)}
+        del xf
     if w.has_residual:
         rf = _normal_rows(seed, STREAM_RES, row0, row1, w.hidden, w.res_std)
         out["residual"] = padded(to_bits(rf, w.dtype), w.stride)
