@@ -11,6 +11,8 @@ Importing this module registers, in the ``arn`` namespace:
     arn::silu_and_mul(x) -> y
     arn::silu_and_mul_fp8_static(x, scale) -> codes
     arn::silu_and_mul_fp8_dynamic(x) -> (codes, scales)
+    arn::sum_add_rmsnorm(parts[], residual!, weight, eps) -> y           (residual updated)
+    arn::sum_add_rmsnorm_fp8_dynamic(parts[], residual!, weight, eps) -> (codes, scales)
     arn::fp8_weight_preshuffle(b) -> shuffled weight bytes
     arn::fp8_gemm(a, scale_a, b, scale_b, out_dtype) -> c
     arn::fp8_gemm_preshuffled(a, scale_a, b_shuffled, n, k, scale_b, out_dtype) -> c
@@ -27,7 +29,8 @@ from typing import Optional
 import torch
 
 from . import (FP8_DTYPE, PreshuffledWeight, fp8_gemm, fp8_weight_preshuffle, fused_add_rmsnorm,
-               fused_add_rmsnorm_fp8, rmsnorm, rmsnorm_fp8, silu_and_mul, silu_and_mul_fp8)
+               fused_add_rmsnorm_fp8, rmsnorm, rmsnorm_fp8, silu_and_mul, silu_and_mul_fp8,
+               sum_add_rmsnorm)
 
 Tensor = torch.Tensor
 
@@ -178,3 +181,27 @@ def fp8_gemm_preshuffled_op(a: Tensor, scale_a: Tensor, b_shuffled: Tensor, n: i
 @fp8_gemm_preshuffled_op.register_fake
 def _(a, scale_a, b_shuffled, n, k, scale_b, out_dtype=torch.bfloat16):
     return torch.empty((a.shape[0], n), dtype=out_dtype, device=a.device)
+
+
+@torch.library.custom_op("arn::sum_add_rmsnorm", mutates_args=("residual",))
+def sum_add_rmsnorm_op(parts: list[Tensor], residual: Tensor, weight: Optional[Tensor],
+                       eps: float) -> Tensor:
+    return sum_add_rmsnorm(parts, weight, eps, residual=residual)
+
+
+@sum_add_rmsnorm_op.register_fake
+def _(parts, residual, weight, eps):
+    return torch.empty_like(parts[0])
+
+
+@torch.library.custom_op("arn::sum_add_rmsnorm_fp8_dynamic", mutates_args=("residual",))
+def sum_add_rmsnorm_fp8_dynamic_op(parts: list[Tensor], residual: Tensor,
+                                   weight: Optional[Tensor], eps: float) -> tuple[Tensor, Tensor]:
+    q, s = sum_add_rmsnorm(parts, weight, eps, residual=residual, fp8="dynamic")
+    return q, s
+
+
+@sum_add_rmsnorm_fp8_dynamic_op.register_fake
+def _(parts, residual, weight, eps):
+    x = parts[0]
+    return torch.empty(x.shape, dtype=FP8_DTYPE, device=x.device), _scales_like(x)

@@ -8,7 +8,7 @@ import residual_add_rmsnorm_amd.torch_ops  # noqa: F401  (registers arn::*)
 OPS = ["rmsnorm", "fused_add_rmsnorm", "rmsnorm_fp8_static", "rmsnorm_fp8_dynamic",
        "fused_add_rmsnorm_fp8_static", "fused_add_rmsnorm_fp8_dynamic", "silu_and_mul",
        "silu_and_mul_fp8_static", "silu_and_mul_fp8_dynamic", "fp8_weight_preshuffle",
-       "fp8_gemm", "fp8_gemm_preshuffled"]
+       "fp8_gemm", "fp8_gemm_preshuffled", "sum_add_rmsnorm", "sum_add_rmsnorm_fp8_dynamic"]
 
 
 def test_ops_registered():
@@ -40,3 +40,7 @@ def test_fake_shapes():
         assert bs.shape == (3 * 1 * 2048,) and bs.dtype == torch.uint8
         c = torch.ops.arn.fp8_gemm_preshuffled(q, sc, bs, 40, 48, sb, torch.float16)
         assert c.shape == (5, 40) and c.dtype == torch.float16
+        y = torch.ops.arn.sum_add_rmsnorm([x, x, x], r, w, 1e-6)
+        assert y.shape == x.shape and y.dtype == x.dtype
+        q, sc = torch.ops.arn.sum_add_rmsnorm_fp8_dynamic([x, x], r, w, 1e-6)
+        assert q.dtype == torch.float8_e4m3fn and sc.shape == (4, 7)

@@ -108,3 +108,27 @@ def test_decode_mlp(compiled):
     assert torch.equal(r_op, r_b)
     assert torch.equal(out, ref)
     assert torch.isfinite(out.float()).all()
+
+
+def tp_block_tail(parts, residual, weight):
+    """The step after a tensor-parallel block: all-reduce reduction of the
+    ranks' partial outputs, residual add, norm to dynamic e4m3."""
+    return torch.ops.arn.sum_add_rmsnorm_fp8_dynamic(parts, residual, weight, 1e-6)
+
+
+@pytest.mark.parametrize("compiled", [False, True])
+def test_tp_block_tail(orc, compiled):
+    rng = np.random.default_rng(73)
+    rows, hidden, g = 12, 2048, 4
+    ph = [W.to_bits((rng.standard_normal((rows, hidden)) * 0.5).astype(np.float32), "bf16")
+          for _ in range(g)]
+    r = W.to_bits(rng.standard_normal((rows, hidden)).astype(np.float32), "bf16")
+    w = W.to_bits((1 + 0.1 * rng.standard_normal(hidden)).astype(np.float32), "bf16")
+    pd, rd, wd = [dev(p, "bf16") for p in ph], dev(r, "bf16"), dev(w, "bf16")
+    fn = torch.compile(tp_block_tail, backend="aot_eager", fullgraph=True) if compiled \
+        else tp_block_tail
+    q, s = fn(pd, rd, wd)
+    torch.cuda.synchronize()
+    ref = orc.sum_add_rmsnorm("bf16", ph, r, w, 1e-6, fp8_mode=O.FP8_DYNAMIC)
+    assert np.array_equal(bits(rd), ref["r16"])
+    assert_codes_close(codes(q), ref["q"])
