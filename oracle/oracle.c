@@ -563,3 +563,42 @@ int orc_fp8_gemm(int64_t m, int64_t n, int64_t k,
     }
     return 0;
 }
+
+/* Error-bound helper for the GEMM tests (not part of the operation): for
+ * each output, the sum over 128-wide k steps (t = 128 s ... 128 s + 127) of
+ * the largest |product| in the step, times |sa sb|.  A matrix unit that
+ * aligns the 128 products of one step to the largest of them and keeps a
+ * fixed number of bits below it loses at most a fixed fraction of this. */
+int orc_fp8_gemm_stepmax(int64_t m, int64_t n, int64_t k,
+                         const uint8_t *a, int64_t lda, const float *sa, int a_per_row,
+                         const uint8_t *b, int64_t ldb, const float *sb, int b_per_row,
+                         double *stepmax_out)
+{
+    int64_t row, col, kk;
+
+    if (m < 0 || n < 0 || k <= 0 || a == NULL || b == NULL || sa == NULL || sb == NULL ||
+        lda < k || ldb < k || stepmax_out == NULL) {
+        return -1;
+    }
+    for (row = 0; row < m; row++) {
+        const double row_scale = (double)(a_per_row ? sa[row] : sa[0]);
+        for (col = 0; col < n; col++) {
+            const double col_scale = (double)(b_per_row ? sb[col] : sb[0]);
+            double total = 0.0;
+            double largest = 0.0;
+            for (kk = 0; kk < k; kk++) {
+                const double mag = fabs(orc_e4m3_decode(a[row * lda + kk]) *
+                                        orc_e4m3_decode(b[col * ldb + kk]));
+                if (mag > largest) {
+                    largest = mag;
+                }
+                if (kk % 128 == 127 || kk == k - 1) {   /* end of a 128-wide step */
+                    total += largest;
+                    largest = 0.0;
+                }
+            }
+            stepmax_out[row * n + col] = fabs(row_scale * col_scale) * total;
+        }
+    }
+    return 0;
+}

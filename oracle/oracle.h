@@ -127,6 +127,13 @@ int orc_fp8_gemm(int64_t m, int64_t n, int64_t k,
                  const uint8_t *b, int64_t ldb, const float *sb, int b_per_row,
                  int out_dtype, double *c_out, uint16_t *c16_out, double *abs_out);
 
+/* Error-bound helper for the GEMM tests: per output, the sum over 128-wide
+ * k steps of the largest |product| in the step, times |sa sb|. */
+int orc_fp8_gemm_stepmax(int64_t m, int64_t n, int64_t k,
+                         const uint8_t *a, int64_t lda, const float *sa, int a_per_row,
+                         const uint8_t *b, int64_t ldb, const float *sb, int b_per_row,
+                         double *stepmax_out);
+
 #ifdef __cplusplus
 }
 #endif

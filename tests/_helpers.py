@@ -8,7 +8,8 @@ Comparison rules (the stated tolerances of the operator):
     with p = 8, emin = -126 (bf16) or p = 11, emin = -14 (fp16); NaN matches NaN;
   * e4m3 codes: within one step, |ord(q_gpu) - ord(q_ref)| <= 1 with
     ord(c) = +-(c & 0x7f) by the sign bit (so +0 and -0 are equal);
-  * dynamic scales: relative error <= rho.
+  * dynamic scales: relative error <= rho;
+  * e4m3 GEMM outputs: see gemm_tol.
 """
 import json
 import os
@@ -100,3 +101,17 @@ def static_scale(workload: str = "fused_add_rmsnorm_fp8_static_fp16_decode_x1638
             }[workload]
     with open(os.path.join(HERE, "golden", name)) as f:
         return json.load(f)["dequant_scale"]
+
+
+def gemm_tol(ref: dict, k: int, out: str = "bf16") -> np.ndarray:
+    """Tolerance of an e4m3 GEMM output against the oracle's fp64 value:
+    one rounding to the 16-bit output (rho |c| + ulp16(c)); the matrix unit
+    (gfx950's v_mfma_*_f8f6f4) aligning the 128 products of each k step to
+    the largest of them and keeping about 13 bits below it -- measured on
+    MI355X: at most 11 units of 2^(E-13) lost per step over 3072
+    adversarial dot products, E the exponent of the step's largest product
+    -- allowed as 2^-8 of that product per step (32 units); and fp32
+    accumulation across steps and waves, (k/128 + 256) 2^-24 of the sum of
+    |products|."""
+    return (RHO[out] * np.abs(ref["c"]) + ulp16(ref["c"], out) + 2.0**-8 * ref["stepmax"]
+            + (k / 128 + 256) * 2.0**-24 * ref["abs"])

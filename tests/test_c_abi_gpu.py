@@ -12,8 +12,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from tests._helpers import (RHO, assert_codes_close, assert_scales_close, assert_y_close,
-                            static_scale, ulp16, values16)
+from tests._helpers import (assert_codes_close, assert_scales_close, assert_y_close, gemm_tol,
+                            static_scale, values16)
 from tests.c_abi import build as client_build
 
 pytestmark = pytest.mark.gpu
@@ -119,8 +119,7 @@ def test_gemm_from_c(client, orc, tmp_path, layout):
     c = np.frombuffer(open(fout, "rb").read(), np.uint16).reshape(m, n)
     ref = orc.fp8_gemm(a, sa, b, sb)
     got = values16(c, "bf16")
-    tol = RHO["bf16"] * np.abs(ref["c"]) + ulp16(ref["c"], "bf16") + \
-        (k / 128 + 256) * 2.0**-24 * ref["abs"]
+    tol = gemm_tol(ref, k)
     assert np.all(np.abs(got - ref["c"]) <= tol)
 
 

@@ -96,10 +96,9 @@ def _gemm_inputs(m, n, k, seed):
 
 
 def _gemm_tol(ref, k):
-    from tests._helpers import RHO, ulp16
+    from tests._helpers import gemm_tol
 
-    return RHO["bf16"] * np.abs(ref["c"]) + ulp16(ref["c"], "bf16") + \
-        (k / 128 + 256) * 2.0**-24 * ref["abs"]
+    return gemm_tol(ref, k)
 
 
 @pytest.mark.parametrize("split", [False, True])
