@@ -24,6 +24,7 @@ using arn::Args;
 using arn::GemmArgs;
 using arn::GemmCfg;
 using arn::GemmTable;
+using arn::panel_tiles_for;
 using arn::Tile;
 using arn::TileTable;
 
@@ -488,8 +489,8 @@ int run_gemm(bool pre, void* c, int64_t ldc, int out_dtype, const uint8_t* a, in
                 : nullptr;
 
   // Split N so that each launch's weight slice stays under 2 GiB (row-major)
-  // and the grid stays well inside the launch limit.
-  int64_t rows_per_launch = pre ? (int64_t(1) << 30) : (kMaxGemmBBytes / ldb);
+  // or covers one panel of the pre-shuffled copy.
+  int64_t rows_per_launch = pre ? panel_tiles_for(nsteps) * 16 : (kMaxGemmBBytes / ldb);
   rows_per_launch = rows_per_launch / tile_cols * tile_cols;
   if (rows_per_launch <= 0) return ARN_EUNSUPPORTED;
   int64_t done = 0;
@@ -503,7 +504,7 @@ int run_gemm(bool pre, void* c, int64_t ldc, int out_dtype, const uint8_t* a, in
     g.a = a;
     g.lda = lda;
     g.scale_a = scale_a;
-    g.b = pre ? b + (done / 16) * nsteps * 2048 : b + done * ldb;
+    g.b = pre ? b + (done / 16) * nsteps * 2048 : b + done * ldb;  // a panel starts there
     g.ldb = pre ? 0 : ldb;
     g.scale_b = b_per_row ? scale_b + done : scale_b;
     g.m = m;
@@ -548,6 +549,7 @@ int run_preshuffle(uint8_t* dst, const uint8_t* b, int64_t ldb, int64_t n, int64
   p.k = k;
   p.ntiles = (n + 15) / 16;
   p.nsteps = (k + 127) / 128;
+  p.panel_tiles = panel_tiles_for(p.nsteps);
   p.aligned = (ldb % 16 == 0 && aligned(b, 16)) ? 1 : 0;
   void* params[] = {&p};
   const hipError_t e =

@@ -90,19 +90,27 @@ void gemm_fp8_kernel(const GemmArgs g) {
   const __amdgpu_buffer_rsrc_t ars = row_rsrc(g.a, (uint32_t)(g.m * g.lda));
   // Row-major weight: this block's rows.  Pre-shuffled weight: this block's
   // column tiles, each nsteps consecutive 2 KiB MFMA tiles.
+  // Row-major weight: this block's rows.  Pre-shuffled weight: the launch's
+  // panel, k-step major -- step s of column tile T at (s * ntiles + T) * 2 KiB,
+  // so the blocks of a launch, moving through K at about the same pace,
+  // read one compact region of the weight at a time rather than one
+  // stream each.
+  const int64_t ntiles = (g.n + 15) / 16;
+  const uint32_t step_bytes = (uint32_t)(ntiles * 2048);
   const __amdgpu_buffer_rsrc_t brs =
-      PRE ? row_rsrc(static_cast<const uint8_t*>(g.b) + (n0 / 16) * nsteps * 2048,
-                     (uint32_t)(((n_here + 15) / 16) * nsteps * 2048))
+      PRE ? row_rsrc(g.b, (uint32_t)(ntiles * nsteps * 2048))
           : row_rsrc(static_cast<const uint8_t*>(g.b) + n0 * g.ldb, (uint32_t)(n_here * g.ldb));
 
   uint32_t aoff[MT], boff[NT];
+  bool b_in[NT];  // pre-shuffled: the column tile exists (the last group may be ragged)
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     aoff[i] = (uint32_t)((i * 16 + r16) * g.lda) + (PRE ? 32u : 16u) * kq;
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    boff[t] = PRE ? (uint32_t)(t * nsteps * 2048) + 16u * lane
+    b_in[t] = !PRE || n0 / 16 + t < ntiles;
+    boff[t] = PRE ? (uint32_t)((n0 / 16 + t) * 2048) + 16u * lane
                   : (uint32_t)((t * 16 + r16) * g.ldb) + 16u * kq;
   }
 
@@ -129,8 +137,9 @@ void gemm_fp8_kernel(const GemmArgs g) {
       const bool a_hi = in_s && kb + 32u * kq + 16u < (uint32_t)g.k;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const uint32_t o = boff[t] + (uint32_t)s * 2048u;
-        bq[t] = load32<kCacheStream>(brs, in_s ? o : kOutOfRange, in_s ? o + 1024u : kOutOfRange);
+        const bool in = in_s && b_in[t];
+        const uint32_t o = boff[t] + (uint32_t)s * step_bytes;
+        bq[t] = load32<kCacheStream>(brs, in ? o : kOutOfRange, in ? o + 1024u : kOutOfRange);
       }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
@@ -270,8 +279,9 @@ void gemm_fp8_kernel(const GemmArgs g) {
 
 // Pre-shuffle: one thread per 16-byte piece of the shuffled weight.  The
 // shuffled copy holds ceil(n/16) column tiles x ceil(k/128) k steps of
-// 2 KiB; in a tile, piece p (16 bytes) holds, for row r = p % 16 of the
-// column tile and lane group q = (p % 64) / 16, k bytes
+// 2 KiB, in panels of p.panel_tiles column tiles, k-step major inside a
+// panel (arn_internal.h).  In a tile, piece p (16 bytes) holds, for row
+// r = p % 16 of the column tile and lane group q = (p % 64) / 16, k bytes
 // [32 q + 16 (p / 64), +16) of the step -- so that lane l of a load of
 // bytes [16 l, 16 l + 16) and of [1024 + 16 l, +16) receives the 32 bytes
 // [32 q, 32 q + 32) of row l % 16 that the MFMA operand layout wants.
@@ -281,10 +291,14 @@ __global__ __launch_bounds__(256) void preshuffle_kernel(const PreshuffleArgs p)
   const int64_t piece = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = p.ntiles * p.nsteps * 128;
   if (piece >= total) return;
-  const int64_t tile = piece / 128;
+  const int64_t tile = piece / 128;  // position of the 2 KiB tile in the copy
   const int pp = (int)(piece % 128);
-  const int64_t nt = tile / p.nsteps;
-  const int64_t s = tile % p.nsteps;
+  const int64_t panel = tile / (p.panel_tiles * p.nsteps);
+  const int64_t first = panel * p.panel_tiles;  // first column tile of the panel
+  const int64_t width = p.ntiles - first < p.panel_tiles ? p.ntiles - first : p.panel_tiles;
+  const int64_t in_panel = tile - first * p.nsteps;
+  const int64_t s = in_panel / width;
+  const int64_t nt = first + in_panel % width;
   const int64_t row = nt * 16 + (pp % 16);
   const int64_t k0 = s * 128 + 32 * ((pp % 64) / 16) + 16 * (pp / 64);
   u32x4 v = {0u, 0u, 0u, 0u};

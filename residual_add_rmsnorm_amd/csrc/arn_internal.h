@@ -107,10 +107,22 @@ struct PreshuffleArgs {
   int64_t ldb;
   int64_t n;
   int64_t k;
-  int64_t ntiles;  // ceil(n / 16)
-  int64_t nsteps;  // ceil(k / 128)
-  int aligned;     // src and ldb are multiples of 16 bytes
+  int64_t ntiles;       // ceil(n / 16)
+  int64_t nsteps;       // ceil(k / 128)
+  int64_t panel_tiles;  // column tiles per panel (panel_tiles_for(nsteps))
+  int aligned;          // src and ldb are multiples of 16 bytes
 };
+
+// The pre-shuffled weight is a sequence of panels of `panel_tiles` column
+// tiles (the last one may hold fewer); inside a panel the 2 KiB MFMA tiles
+// are stored k-step major: all of the panel's tiles for step 0, then step 1,
+// and so on.  A panel is at most 1 GiB, so every offset a GEMM launch uses
+// fits the 32-bit buffer offsets, and the tile count is a multiple of 4 so
+// that no column group of a GEMM block straddles two panels.
+inline int64_t panel_tiles_for(int64_t nsteps) {
+  const int64_t t = (int64_t(1) << 30) / (nsteps * 2048) / 4 * 4;
+  return t < 4 ? 4 : t;
+}
 
 struct GemmTable {
   const GemmCfg* cfgs;

@@ -242,6 +242,45 @@ def test_full_size(orc, name):
 
 
 
+def test_preshuffled_panels(orc):
+    """A weight whose pre-shuffled copy spans two panels: at K = 131072 a
+    1 GiB panel holds 512 column tiles (8192 columns), and N = 8236 leaves
+    a second panel of 4 tiles, the last one ragged.  Columns on both sides
+    of the panel boundary and at the ragged end against the oracle, without
+    and with a split-K workspace (3 splits forced)."""
+    import residual_add_rmsnorm_amd as arn
+
+    m, n, k = 3, 8236, 131072
+    print(f"\n[panels] m {m} n {n} k {k}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    b = torch.randint(0, 256, (n, k), dtype=torch.uint8, device="cuda", generator=gen)
+    b[(b & 0x7F) == 0x7F] = 0  # no NaN codes
+    rng = np.random.default_rng(31)
+    a = rng.integers(0, 256, (m, k)).astype(np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0
+    sa = rng.uniform(0.01, 0.1, m).astype(np.float32)
+    sb = rng.uniform(0.001, 0.01, n).astype(np.float32)
+    cols = np.unique(np.concatenate([np.linspace(0, n - 1, 24).astype(np.int64),
+                                     [0, 15, 16, 4095, 8175, 8176, 8191, 8192, 8207, 8208,
+                                      8223, 8224, 8235]]))
+    ref = orc.fp8_gemm(a, sa, b[torch.from_numpy(cols).cuda()].cpu().numpy(), sb[cols])
+    tol = gemm_tol(ref, k)
+    pre = arn.fp8_weight_preshuffle(b)
+    del b
+    ad, sad, sbd = (torch.from_numpy(v).cuda() for v in (a, sa, sb))
+    ws = arn.fp8_gemm_workspace(m, n, k)
+    try:
+        for splits, w in ((0, None), (3, ws)):
+            arn.set_gemm_splits(splits)
+            c = arn.fp8_gemm(ad, sad, pre, sbd, workspace=w)
+            torch.cuda.synchronize()
+            got = values16(bits(c[:, torch.from_numpy(cols).cuda()]), "bf16")
+            err = np.abs(got - ref["c"])
+            assert np.all(err <= tol), (splits, arn.last_plan(), float(np.max(err / tol)))
+    finally:
+        arn.set_gemm_splits(0)
+
+
 # ---------------------------------------------------------------------------
 # Split K across blocks (workspace entry points)
 # ---------------------------------------------------------------------------
