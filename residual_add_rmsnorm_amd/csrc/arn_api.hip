@@ -366,8 +366,8 @@ const GemmCfg* choose_gemm(const GemmTable* table, int mt, int64_t n, int64_t k,
 
 // Largest weight slice one GEMM launch addresses (buffer records are 32-bit).
 constexpr int64_t kMaxGemmBBytes = int64_t(1) << 31;
-// Largest K of a pre-shuffled weight: a block's slice (up to 16 column tiles
-// of ceil(K/128) 2 KiB tiles) stays under 2 GiB.
+// Largest K of a pre-shuffled weight: a panel of at least 4 column tiles
+// (ceil(K/128) 2 KiB tiles each) stays within 1 GiB.
 constexpr int64_t kMaxPreshuffleK = int64_t(1) << 23;
 
 int64_t preshuffled_bytes(int64_t n, int64_t k) {
@@ -451,7 +451,8 @@ int run_gemm(bool pre, void* c, int64_t ldc, int out_dtype, const uint8_t* a, in
       m * lda > kMaxGemmBBytes) {
     return ARN_EUNSUPPORTED;
   }
-  if (pre ? k > kMaxPreshuffleK : (ldb % 16 != 0 || ldb > kMaxGemmBBytes / 16)) {
+  // (A block addresses up to 64 weight rows through one buffer record.)
+  if (pre ? k > kMaxPreshuffleK : (ldb % 16 != 0 || ldb > kMaxGemmBBytes / 64)) {
     return ARN_EUNSUPPORTED;
   }
   const int mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);

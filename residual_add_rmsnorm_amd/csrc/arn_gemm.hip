@@ -88,8 +88,6 @@ void gemm_fp8_kernel(const GemmArgs g) {
   const int s_begin = (int)blockIdx.y * g.steps_per_split;
   const int s_end = min(nsteps, s_begin + g.steps_per_split);
   const __amdgpu_buffer_rsrc_t ars = row_rsrc(g.a, (uint32_t)(g.m * g.lda));
-  // Row-major weight: this block's rows.  Pre-shuffled weight: this block's
-  // column tiles, each nsteps consecutive 2 KiB MFMA tiles.
   // Row-major weight: this block's rows.  Pre-shuffled weight: the launch's
   // panel, k-step major -- step s of column tile T at (s * ntiles + T) * 2 KiB,
   // so the blocks of a launch, moving through K at about the same pace,
