@@ -13,6 +13,15 @@
  *   arn_client gemm <rowmajor|preshuffled|preshuffled_ws> m n k in.bin out.bin
  *       in.bin : a (m*k bytes), b (n*k bytes), scale_a (m f32), scale_b (n f32)
  *       out.bin: c (m*n bf16)
+ *   arn_client sum <none|dynamic> <bf16|fp16> nparts rows hidden stride eps in.bin out.bin
+ *       in.bin : nparts parts (rows*stride u16 each, each copied to its own
+ *                buffer), residual (rows*stride u16), weight (hidden u16)
+ *       out.bin: residual after the call, out (rows*stride u16, or
+ *                rows*stride e4m3 bytes), scales (rows f32, dynamic only)
+ *   arn_client glu <none|dynamic> <bf16|fp16> rows d in.bin out.bin
+ *       in.bin : gate_up (rows*2d u16: gate in columns [0, d), up in [d, 2d))
+ *       out.bin: out (rows*d u16, or rows*d e4m3 bytes), scales (rows f32,
+ *                dynamic only)
  *
  * Exit status 0 on success; on any failure a message on stderr and 1.
  */
@@ -216,6 +225,102 @@ static int run_gemm(char **argv) {
   return 0;
 }
 
+static int run_sum(char **argv) {
+  const int dynamic = strcmp(argv[0], "dynamic") == 0;
+  const int dtype = strcmp(argv[1], "fp16") == 0 ? ARN_FP16 : ARN_BF16;
+  const int nparts = atoi(argv[2]);
+  const int64_t rows = atoll(argv[3]), hidden = atoll(argv[4]), stride = atoll(argv[5]);
+  const float eps = (float)atof(argv[6]);
+  if (nparts < 1 || nparts > 8) {
+    fprintf(stderr, "nparts must be 1..8\n");
+    return 1;
+  }
+  const size_t mat16 = (size_t)(rows * stride * 2);
+  const size_t in_size = mat16 * (size_t)(nparts + 1) + (size_t)hidden * 2;
+  uint8_t *in = read_file(argv[7], in_size);
+  const void *parts[8];
+  for (int p = 0; p < nparts; ++p) parts[p] = to_device(in + mat16 * p, mat16);
+  void *res = to_device(in + mat16 * nparts, mat16);
+  void *w = to_device(in + mat16 * (nparts + 1), (size_t)hidden * 2);
+  const size_t out_size = dynamic ? (size_t)(rows * stride) : mat16;
+  void *out = NULL;
+  HIP_OK(hipMalloc(&out, out_size ? out_size : 1));
+  HIP_OK(hipMemset(out, 0, out_size ? out_size : 1));
+  float *scale = NULL;
+  if (dynamic) HIP_OK(hipMalloc((void **)&scale, (size_t)rows * sizeof(float) + 4));
+  hipStream_t stream;
+  HIP_OK(hipStreamCreate(&stream));
+
+  arn_sum_norm_args a;
+  memset(&a, 0, sizeof(a));
+  a.struct_size = sizeof(a);
+  a.dtype = dtype;
+  a.out_format = dynamic ? ARN_OUT_FP8_DYNAMIC : ARN_OUT_16BIT;
+  a.out = out;
+  a.out_stride = stride;
+  a.scale = scale;
+  a.parts = parts;
+  a.nparts = nparts;
+  a.parts_stride = stride;
+  a.residual = res;
+  a.residual_stride = stride;
+  a.weight = w;
+  a.eps = eps;
+  a.rows = rows;
+  a.hidden = hidden;
+  a.stream = stream;
+  ARN_OK_(arn_sum_add_rmsnorm(&a));
+  HIP_OK(hipStreamSynchronize(stream));
+  HIP_OK(hipGetLastError());
+
+  FILE *f = fopen(argv[8], "wb");
+  if (!f) {
+    fprintf(stderr, "cannot open %s\n", argv[8]);
+    return 1;
+  }
+  append(f, res, mat16);
+  append(f, out, out_size);
+  if (dynamic) append(f, scale, (size_t)rows * sizeof(float));
+  fclose(f);
+  HIP_OK(hipStreamDestroy(stream));
+  return 0;
+}
+
+static int run_glu(char **argv) {
+  const int dynamic = strcmp(argv[0], "dynamic") == 0;
+  const int dtype = strcmp(argv[1], "fp16") == 0 ? ARN_FP16 : ARN_BF16;
+  const int64_t rows = atoll(argv[2]), d = atoll(argv[3]);
+  const size_t in_size = (size_t)(rows * 2 * d * 2);
+  uint8_t *in = read_file(argv[4], in_size);
+  uint8_t *gu = to_device(in, in_size);
+  const size_t out_size = (size_t)(rows * d) * (dynamic ? 1 : 2);
+  void *out = NULL;
+  HIP_OK(hipMalloc(&out, out_size ? out_size : 1));
+  float *scale = NULL;
+  if (dynamic) HIP_OK(hipMalloc((void **)&scale, (size_t)rows * sizeof(float) + 4));
+  hipStream_t stream;
+  HIP_OK(hipStreamCreate(&stream));
+  /* gate = the first d columns of each row, up = the next d */
+  if (dynamic) {
+    ARN_OK_(arn_silu_and_mul_fp8((uint8_t *)out, d, scale, ARN_FP8_DYNAMIC, gu, 2 * d,
+                                 gu + d * 2, 2 * d, rows, d, dtype, stream));
+  } else {
+    ARN_OK_(arn_silu_and_mul(out, d, gu, 2 * d, gu + d * 2, 2 * d, rows, d, dtype, stream));
+  }
+  HIP_OK(hipStreamSynchronize(stream));
+  HIP_OK(hipGetLastError());
+  FILE *f = fopen(argv[5], "wb");
+  if (!f) {
+    fprintf(stderr, "cannot open %s\n", argv[5]);
+    return 1;
+  }
+  append(f, out, out_size);
+  if (dynamic) append(f, scale, (size_t)rows * sizeof(float));
+  fclose(f);
+  HIP_OK(hipStreamDestroy(stream));
+  return 0;
+}
+
 int main(int argc, char **argv) {
   if (arn_abi_version() != ARN_ABI_VERSION) {
     fprintf(stderr, "libarn ABI %d, header %d\n", arn_abi_version(), ARN_ABI_VERSION);
@@ -223,6 +328,8 @@ int main(int argc, char **argv) {
   }
   if (argc == 13 && strcmp(argv[1], "norm") == 0) return run_norm(argv + 2);
   if (argc == 8 && strcmp(argv[1], "gemm") == 0) return run_gemm(argv + 2);
+  if (argc == 11 && strcmp(argv[1], "sum") == 0) return run_sum(argv + 2);
+  if (argc == 8 && strcmp(argv[1], "glu") == 0) return run_glu(argv + 2);
   fprintf(stderr, "usage: see the comment at the top of arn_client.c\n");
   return 1;
 }

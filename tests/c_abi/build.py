@@ -2,7 +2,7 @@
 
 The client lives next to the tests that run it; build() of the repository
 compiles it with everything else, and the test compiles it only if it is
-missing or older than its source.
+missing or older than its source or the header.
 """
 import os
 import subprocess
@@ -27,6 +27,8 @@ def build() -> str:
 
 
 def ensure() -> str:
-    if not os.path.exists(EXE) or os.path.getmtime(EXE) < os.path.getmtime(SRC):
+    header = os.path.join(ROOT, "include", "arn.h")
+    if not os.path.exists(EXE) or os.path.getmtime(EXE) < max(os.path.getmtime(SRC),
+                                                               os.path.getmtime(header)):
         build()
     return EXE

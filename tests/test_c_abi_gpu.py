@@ -1,8 +1,10 @@
 """The C boundary by itself: a plain C program (tests/c_abi/arn_client.c,
 host code built with gcc against include/arn.h, no Python or torch in its
 process) allocates device memory with hipMalloc, calls the library's entry
-points on a HIP stream it created, and writes the results to a file; they
-must match the oracle by the same rules as the Python-driven tests."""
+points (the norm in every output mode, the all-reduce form, SwiGLU, the
+e4m3 GEMM in both weight layouts and with a split-K workspace) on a HIP
+stream it created, and writes the results to a file; they must match the
+oracle by the same rules as the Python-driven tests."""
 import os
 import subprocess
 
@@ -121,6 +123,69 @@ def test_gemm_from_c(client, orc, tmp_path, layout):
     got = values16(c, "bf16")
     tol = gemm_tol(ref, k)
     assert np.all(np.abs(got - ref["c"]) <= tol)
+
+
+@pytest.mark.parametrize("fp8,dtype,nparts,rows,hidden,stride",
+                         [("none", "bf16", 8, 6, 8192, 8192), ("dynamic", "bf16", 2, 9, 7168, 7176),
+                          ("none", "fp16", 3, 5, 4096, 4104), ("dynamic", "fp16", 8, 4, 2880, 2880)])
+def test_sum_from_c(client, orc, tmp_path, fp8, dtype, nparts, rows, hidden, stride):
+    """arn_sum_add_rmsnorm from C: nparts partial rows (each in its own
+    buffer) summed in rank order, added to the residual, normalised."""
+    rng = np.random.default_rng(nparts * 1000 + hidden)
+    std = nparts ** -0.5
+    parts = []
+    for _ in range(nparts):
+        p = np.full((rows, stride), W.PAD_SENTINEL, np.uint16)
+        p[:, :hidden] = W.to_bits((rng.standard_normal((rows, hidden)) * std).astype(np.float32),
+                                  dtype)
+        parts.append(p)
+    _, r, w = _inputs(rng, rows, hidden, stride, dtype)
+    eps = 1e-6
+    fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(fin, "wb") as f:
+        for p in parts:
+            f.write(p.tobytes())
+        f.write(r.tobytes())
+        f.write(w.tobytes())
+    _run(client, ["sum", fp8, dtype, nparts, rows, hidden, stride, repr(eps), fin, fout],
+         tmp_path)
+    raw = open(fout, "rb").read()
+    n16 = rows * stride * 2
+    r_after = np.frombuffer(raw[:n16], np.uint16).reshape(rows, stride)
+    mode = O.FP8_DYNAMIC if fp8 == "dynamic" else O.FP8_NONE
+    ref = orc.sum_add_rmsnorm(dtype, parts, r, w, eps, hidden=hidden, fp8_mode=mode)
+    assert np.array_equal(r_after[:, :hidden], ref["r16"]), "stored residual"
+    assert np.all(r_after[:, hidden:] == W.PAD_SENTINEL), "residual padding touched"
+    if fp8 == "none":
+        out = np.frombuffer(raw[n16:2 * n16], np.uint16).reshape(rows, stride)
+        assert_y_close(out[:, :hidden], ref["y"], dtype)
+    else:
+        out = np.frombuffer(raw[n16:n16 + rows * stride], np.uint8).reshape(rows, stride)
+        assert_codes_close(out[:, :hidden], ref["q"])
+        scales = np.frombuffer(raw[n16 + rows * stride:], np.float32)
+        assert_scales_close(scales, ref["scales"], dtype)
+    assert np.all(out[:, hidden:] == 0), "output padding touched"
+
+
+@pytest.mark.parametrize("fp8,dtype,rows,d", [("none", "bf16", 7, 6656), ("dynamic", "bf16", 5, 6656),
+                                              ("dynamic", "fp16", 3, 2048)])
+def test_glu_from_c(client, orc, tmp_path, fp8, dtype, rows, d):
+    """arn_silu_and_mul(_fp8) from C on one [rows, 2d] gate/up tensor."""
+    rng = np.random.default_rng(rows * 7 + d)
+    gu = W.to_bits((rng.standard_normal((rows, 2 * d)) * 2).astype(np.float32), dtype)
+    fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
+    fin.write_bytes(gu.tobytes())
+    _run(client, ["glu", fp8, dtype, rows, d, fin, fout], tmp_path)
+    raw = open(fout, "rb").read()
+    mode = O.FP8_DYNAMIC if fp8 == "dynamic" else O.FP8_NONE
+    ref = orc.silu_and_mul(dtype, gu, d=d, fp8_mode=mode)
+    if fp8 == "none":
+        out = np.frombuffer(raw, np.uint16).reshape(rows, d)
+        assert_y_close(out, ref["y"], dtype)
+    else:
+        out = np.frombuffer(raw[:rows * d], np.uint8).reshape(rows, d)
+        assert_codes_close(out, ref["q"])
+        assert_scales_close(np.frombuffer(raw[rows * d:], np.float32), ref["scales"], dtype)
 
 
 def test_client_reports_status(client, tmp_path):
