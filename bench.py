@@ -37,7 +37,7 @@ _CSRC = "residual_add_rmsnorm_amd/csrc/"
 KERNEL_SOURCES = {
     "norm": [_CSRC + "arn_kernels.hip", _CSRC + "arn_device.h", _CSRC + "arn_internal.h"],
     "glu": [_CSRC + "arn_glu.hip", _CSRC + "arn_device.h", _CSRC + "arn_internal.h"],
-    "gemm": [_CSRC + "arn_gemm.hip", _CSRC + "arn_device.h", _CSRC + "arn_internal.h"],
+    "gemm": [_CSRC + "arn_gemm.hip", _CSRC + "arn_device.h", _CSRC + "arn_gemm.h"],
 }
 
 

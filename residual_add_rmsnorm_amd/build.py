@@ -45,7 +45,7 @@ DTYPES = range(2)
 
 def sources() -> list[str]:
     return [os.path.join(CSRC, f) for f in ("arn_kernels.hip", "arn_glu.hip", "arn_gemm.hip",
-                                            "arn_api.hip", "arn_internal.h", "arn_device.h",
+                                            "arn_api.hip", "arn_internal.h", "arn_gemm.h", "arn_device.h",
                                             "arn_probe.hip")] + [
         os.path.join(INCLUDE, "arn.h"), os.path.join(INCLUDE, "arn_probe.h")]
 

@@ -17,6 +17,7 @@
 
 #include "arn.h"
 #include "arn_internal.h"
+#include "arn_gemm.h"
 
 namespace {
 

@@ -31,7 +31,7 @@
 #include <stdint.h>
 
 #include "arn_device.h"
-#include "arn_internal.h"
+#include "arn_gemm.h"
 
 #if !defined(ARN_DT)
 #error "compile with -DARN_DT=<0|1>"
