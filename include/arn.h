@@ -251,9 +251,11 @@ int arn_fp8_gemm(void *c, int64_t ldc, int out_dtype,
  * "vllm/rocm/use_aiter=1 slows Gemma 4 on an AMD MI300X", section "Why the
  * fp8 Multiplies Run Slower") reads its weight in a pre-shuffled layout.
  * Here the shuffled copy is a sequence of 2 KiB tiles, one per 16 weight
- * rows and 128-wide k step (column tiles outer, k steps inner), each laid
- * out so that every load instruction of the GEMM reads 1 KiB contiguous
- * bytes.  Rows past n and k past the last whole step are zero codes.  The
+ * rows and 128-wide k step, each laid out so that every load instruction of
+ * the GEMM reads 1 KiB contiguous bytes, and stored k-step major within
+ * panels of at most 1 GiB (all column tiles of a panel for step 0, then for
+ * step 1, ...), so that the GEMM's blocks read one compact region at a
+ * time.  Rows past n and k past the last whole step are zero codes.  The
  * layout is private to this library: produce it with
  * arn_fp8_weight_preshuffle and read it only with arn_fp8_gemm_preshuffled.
  *
