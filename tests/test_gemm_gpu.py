@@ -82,6 +82,15 @@ def test_shapes(orc, n, k, pre):
 
 
 @LAYOUTS
+@pytest.mark.parametrize("m", [1, 8])
+def test_logged_decode_shape(orc, m, pre):
+    """The decode fp8 GEMM shape in the AITER log of "VLLM_ROCM_USE_AITER=1
+    slows Gemma 4 on an AMD MI300X" (section "Why the fp8 Multiplies Run
+    Slower": M 1, N 8192, K 3840, a pre-shuffled e4m3 weight), at M = 1 and 8."""
+    check(orc, m, 8192, 3840, seed=100 + m, pre=pre)
+
+
+@LAYOUTS
 @pytest.mark.parametrize("per_row", [(False, False), (True, False), (False, True)])
 def test_scale_modes(orc, per_row, pre):
     check(orc, 5, 300, 640, per_row=per_row, seed=3, pre=pre)
