@@ -12,7 +12,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from tests._helpers import (TORCH_DT, assert_codes_close, assert_scales_close, assert_y_close,
+from tests._helpers import (assert_codes_close, assert_scales_close, assert_y_close,
                             bits, codes, dev)
 
 pytestmark = pytest.mark.gpu

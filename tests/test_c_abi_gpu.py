@@ -5,7 +5,6 @@ points (the norm in every output mode, the all-reduce form, SwiGLU, the
 e4m3 GEMM in both weight layouts and with a split-K workspace) on a HIP
 stream it created, and writes the results to a file; they must match the
 oracle by the same rules as the Python-driven tests."""
-import os
 import subprocess
 
 import numpy as np

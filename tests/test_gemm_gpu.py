@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle as O
-from tests._helpers import RHO, bits, dev, gemm_tol, ulp16, values16
+from tests._helpers import bits, dev, gemm_tol, values16
 
 pytestmark = pytest.mark.gpu
 

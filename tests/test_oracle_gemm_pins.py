@@ -6,7 +6,6 @@ import numpy as np
 import pytest
 import torch
 
-import oracle as O
 
 
 def _codes(vals):

@@ -6,7 +6,6 @@ directory and run through the pin tests.  The edits live only here and only
 on the CPU; oracle.c itself is never changed.
 """
 import inspect
-import os
 
 import pytest
 

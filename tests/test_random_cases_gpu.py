@@ -13,7 +13,7 @@ from hypothesis import HealthCheck, given, settings
 from hypothesis import strategies as st
 
 import workloads as W
-from tests._helpers import bits, dev
+from tests._helpers import dev
 
 pytestmark = pytest.mark.gpu
 

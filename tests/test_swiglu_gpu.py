@@ -4,7 +4,6 @@ out = silu(gate) * up with gate | up the two halves of a [rows, 2d] row
 (the fused gate/up projection layout), or two separate tensors.  Outputs
 start as NaN canaries and a guard row follows the last row.
 """
-import ctypes
 
 import numpy as np
 import pytest
