@@ -159,6 +159,37 @@ def test_preshuffle_unaligned_weight(orc):
     assert np.all(np.abs(got - ref["c"]) <= tol)
 
 
+@LAYOUTS
+def test_nan_codes_propagate(orc, pre):
+    """A NaN code (0x7F / 0xFF) inside K makes its whole output row (in A) or
+    column (in B) NaN, as in the oracle's definition; every other output is
+    unaffected.  (The rest of the suite keeps NaN codes in row padding,
+    which must never be read.)"""
+    import residual_add_rmsnorm_amd as arn
+
+    rng = np.random.default_rng(12)
+    m, n, k = 5, 70, 640
+    a = _codes(rng, m, k, 24.0)
+    b = _codes(rng, n, k, 6.0)
+    a[2, 300] = 0x7F
+    b[41, 5] = 0xFF
+    sa = rng.uniform(0.01, 0.1, m).astype(np.float32)
+    sb = rng.uniform(0.001, 0.01, n).astype(np.float32)
+    bd = torch.from_numpy(b).cuda()
+    if pre:
+        bd = arn.fp8_weight_preshuffle(bd)
+    ad, sad, sbd = (torch.from_numpy(x).cuda() for x in (a, sa, sb))
+    c = arn.fp8_gemm(ad, sad, bd, sbd).float().cpu().numpy()
+    ref = orc.fp8_gemm(a, sa, b, sb)
+    nan_ref = np.isnan(ref["c"])
+    assert nan_ref[2].all() and nan_ref[:, 41].all() and nan_ref.sum() == n + m - 1
+    assert np.array_equal(np.isnan(c), nan_ref)
+    ok = ~nan_ref
+    tol = gemm_tol({k2: (v[ok] if isinstance(v, np.ndarray) and v.shape == ref["c"].shape else v)
+                    for k2, v in ref.items()}, k)
+    assert np.all(np.abs(c[ok] - ref["c"][ok]) <= tol)
+
+
 def test_deterministic():
     import residual_add_rmsnorm_amd as arn
 
