@@ -99,11 +99,24 @@ void gemm_fp8_kernel(const GemmArgs g) {
       PRE ? row_rsrc(g.b, (uint32_t)(ntiles * nsteps * 2048))
           : row_rsrc(static_cast<const uint8_t*>(g.b) + n0 * g.ldb, (uint32_t)(n_here * g.ldb));
 
+  // A operand.  The MFMA layout puts one A row in every 16th lane, so a
+  // load that fills operand registers directly touches 16 rows (16 cache
+  // lines, half of each) per instruction, where a weight load touches 8
+  // whole lines.  With 32 or 64 rows (MT >= 2) A costs as much per block as
+  // the weight, so there each A load instead covers 8 whole 128-byte rows
+  // (lane l: row l / 8, bytes 16 (l % 8)) and the wave permutes its tiles
+  // into the operand layout through its own LDS slice (rows padded to 144
+  // bytes, which keeps both the writes and the reads free of bank
+  // conflicts).
+  constexpr bool kAPerm = MT >= 2;
+  constexpr int kRowP = 144;
+  constexpr int kStage = kAPerm ? MT * 16 * kRowP : 0;  // LDS bytes per wave
   uint32_t aoff[MT], boff[NT];
   bool b_in[NT];  // pre-shuffled: the column tile exists (the last group may be ragged)
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    aoff[i] = (uint32_t)((i * 16 + r16) * g.lda) + (PRE ? 32u : 16u) * kq;
+    aoff[i] = kAPerm ? (uint32_t)((i * 16 + (lane >> 3)) * g.lda) + 16u * (lane & 7)
+                     : (uint32_t)((i * 16 + r16) * g.lda) + (PRE ? 32u : 16u) * kq;
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -126,6 +139,16 @@ void gemm_fp8_kernel(const GemmArgs g) {
   auto load_step = [&](int s, i32x8 (&bq)[NT], i32x8 (&aq)[MT]) {
     const uint32_t kb = (uint32_t)s * 128u;
     const bool in_s = s < s_end;
+    if constexpr (kAPerm) {
+      // rows 0-7 of each A tile in aq[i][0..3], rows 8-15 in aq[i][4..7];
+      // K % 16 == 0, so each 16-byte piece is wholly inside or outside K
+      const bool a_in = in_s && kb + 16u * (lane & 7) < (uint32_t)g.k;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        aq[i] = load32<kCacheDefault>(ars, a_in ? aoff[i] + kb : kOutOfRange,
+                                      a_in ? aoff[i] + kb + 8u * (uint32_t)g.lda : kOutOfRange);
+      }
+    }
     if constexpr (PRE) {
       // Pre-shuffled: a 2 KiB tile per (column tile, k step), read as two
       // 1 KiB contiguous halves; lane l gets bytes [32 q, 32 q + 32) of
@@ -139,10 +162,12 @@ void gemm_fp8_kernel(const GemmArgs g) {
         const uint32_t o = boff[t] + (uint32_t)s * step_bytes;
         bq[t] = load32<kCacheStream>(brs, in ? o : kOutOfRange, in ? o + 1024u : kOutOfRange);
       }
+      if constexpr (!kAPerm) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        aq[i] = load32<kCacheDefault>(ars, a_lo ? aoff[i] + kb : kOutOfRange,
-                                      a_hi ? aoff[i] + kb + 16u : kOutOfRange);
+        for (int i = 0; i < MT; ++i) {
+          aq[i] = load32<kCacheDefault>(ars, a_lo ? aoff[i] + kb : kOutOfRange,
+                                        a_hi ? aoff[i] + kb + 16u : kOutOfRange);
+        }
       }
     } else {
       // K % 16 == 0: every 16-byte piece is wholly inside or outside K
@@ -153,14 +178,54 @@ void gemm_fp8_kernel(const GemmArgs g) {
         bq[t] = load32<kCacheStream>(brs, lo_in ? boff[t] + kb : kOutOfRange,
                                      hi_in ? boff[t] + kb + 64u : kOutOfRange);
       }
+      if constexpr (!kAPerm) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        aq[i] = load32<kCacheDefault>(ars, lo_in ? aoff[i] + kb : kOutOfRange,
-                                      hi_in ? aoff[i] + kb + 64u : kOutOfRange);
+        for (int i = 0; i < MT; ++i) {
+          aq[i] = load32<kCacheDefault>(ars, lo_in ? aoff[i] + kb : kOutOfRange,
+                                        hi_in ? aoff[i] + kb + 64u : kOutOfRange);
+        }
       }
     }
   };
-  auto mma = [&](const i32x8 (&bq)[NT], const i32x8 (&aq)[MT]) {
+  // The LDS of the block: the waves' A staging slices during the k loop,
+  // then the partial tiles of the cross-wave sum.
+  constexpr int kLdsBytes =
+      WAVES * kStage > WAVES * kTile * 4 ? WAVES * kStage : WAVES * kTile * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  uint8_t* const stage = lds + wave * kStage;
+  // A tiles into the MFMA operand layout: lane l = r + 16 q gets row r's
+  // bytes [32 q, 32 q + 32) of the step (pre-shuffled weight) or
+  // [16 q, +16) and [64 + 16 q, +16) (row-major weight), the same in-lane k
+  // order as the weight operand.  Only this wave touches its slice, and its
+  // LDS accesses complete in order, so no barrier is needed.
+  auto permute_a = [&](const i32x8 (&raw)[MT], i32x8 (&aq)[MT]) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const u32x4 lo = {(uint32_t)raw[i][0], (uint32_t)raw[i][1], (uint32_t)raw[i][2],
+                        (uint32_t)raw[i][3]};
+      const u32x4 hi = {(uint32_t)raw[i][4], (uint32_t)raw[i][5], (uint32_t)raw[i][6],
+                        (uint32_t)raw[i][7]};
+      uint8_t* dst = stage + (i * 16 + (lane >> 3)) * kRowP + 16 * (lane & 7);
+      *reinterpret_cast<u32x4*>(dst) = lo;
+      *reinterpret_cast<u32x4*>(dst + 8 * kRowP) = hi;
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const uint8_t* src = stage + (i * 16 + r16) * kRowP;
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(src + (PRE ? 32 * kq : 16 * kq));
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(src + (PRE ? 32 * kq + 16 : 64 + 16 * kq));
+      aq[i] = (i32x8){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    }
+  };
+  auto mma = [&](const i32x8 (&bq)[NT], const i32x8 (&a_in)[MT]) {
+    i32x8 aq[MT];
+    if constexpr (kAPerm) {
+      permute_a(a_in, aq);
+    } else {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) aq[i] = a_in[i];
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -185,7 +250,8 @@ void gemm_fp8_kernel(const GemmArgs g) {
 
   // Sum the WAVES partial tiles.  In a 16x16 MFMA result, lane l holds
   // rows 4*(l/16) .. 4*(l/16)+3 of column l%16.
-  __shared__ float part[WAVES * kTile];
+  if constexpr (kAPerm) __syncthreads();  // every wave is done with its A slice
+  float* const part = reinterpret_cast<float*>(lds);
   __shared__ int last_split;
 #pragma unroll
   for (int i = 0; i < MT; ++i)
