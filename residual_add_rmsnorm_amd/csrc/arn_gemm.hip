@@ -106,8 +106,8 @@ void gemm_fp8_kernel(const GemmArgs g) {
   // the weight, so there each A load instead covers 8 whole 128-byte rows
   // (lane l: row l / 8, bytes 16 (l % 8)) and the wave permutes its tiles
   // into the operand layout through its own LDS slice (rows padded to 144
-  // bytes, which keeps both the writes and the reads free of bank
-  // conflicts).
+  // bytes, so that the operand reads -- 16 rows at one column -- fall in
+  // distinct banks).
   constexpr bool kAPerm = MT >= 2;
   constexpr int kRowP = 144;
   constexpr int kStage = kAPerm ? MT * 16 * kRowP : 0;  // LDS bytes per wave
