@@ -14,9 +14,10 @@
 //  * v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3 -> fp32): each lane brings 32
 //    bytes of one row of A and of B for a 128-wide k step, as two 16-byte
 //    pieces laid out so that one load instruction reads 64 contiguous bytes
-//    of each of 16 weight rows.  The k order inside an MFMA is the same for
-//    both operands, and a dot product does not depend on it, so the pieces
-//    need no shuffling.
+//    of each of 16 weight rows (row-major weight).  The k order inside an
+//    MFMA is the same for both operands, and a dot product does not depend
+//    on it, so the pieces need no shuffling.  A is loaded as whole 128-byte
+//    rows and put in operand order through LDS (see aoff below).
 //  * a block owns a (16 MT) x (16 NT) output tile and splits K over WAVES
 //    waves in interleaved 128-wide steps (the block reads each weight row
 //    front to back); A tiles are reused across the NT weight tiles of a
@@ -102,21 +103,18 @@ void gemm_fp8_kernel(const GemmArgs g) {
   // A operand.  The MFMA layout puts one A row in every 16th lane, so a
   // load that fills operand registers directly touches 16 rows (16 cache
   // lines, half of each) per instruction, where a weight load touches 8
-  // whole lines.  With 32 or 64 rows (MT >= 2) A costs as much per block as
-  // the weight, so there each A load instead covers 8 whole 128-byte rows
-  // (lane l: row l / 8, bytes 16 (l % 8)) and the wave permutes its tiles
-  // into the operand layout through its own LDS slice (rows padded to 144
-  // bytes, so that the operand reads -- 16 rows at one column -- fall in
-  // distinct banks).
-  constexpr bool kAPerm = MT >= 2;
+  // whole lines; with 64 rows A costs a block as many bytes as its weight.
+  // So each A load covers 8 whole 128-byte rows (lane l: row l / 8, bytes
+  // 16 (l % 8)) and the wave permutes its tiles into the operand layout
+  // through its own LDS slice (rows padded to 144 bytes, so that the
+  // operand reads -- 16 rows at one column -- fall in distinct banks).
   constexpr int kRowP = 144;
-  constexpr int kStage = kAPerm ? MT * 16 * kRowP : 0;  // LDS bytes per wave
+  constexpr int kStage = MT * 16 * kRowP;  // LDS bytes per wave
   uint32_t aoff[MT], boff[NT];
   bool b_in[NT];  // pre-shuffled: the column tile exists (the last group may be ragged)
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    aoff[i] = kAPerm ? (uint32_t)((i * 16 + (lane >> 3)) * g.lda) + 16u * (lane & 7)
-                     : (uint32_t)((i * 16 + r16) * g.lda) + (PRE ? 32u : 16u) * kq;
+    aoff[i] = (uint32_t)((i * 16 + (lane >> 3)) * g.lda) + 16u * (lane & 7);
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -139,35 +137,25 @@ void gemm_fp8_kernel(const GemmArgs g) {
   auto load_step = [&](int s, i32x8 (&bq)[NT], i32x8 (&aq)[MT]) {
     const uint32_t kb = (uint32_t)s * 128u;
     const bool in_s = s < s_end;
-    if constexpr (kAPerm) {
-      // rows 0-7 of each A tile in aq[i][0..3], rows 8-15 in aq[i][4..7];
-      // K % 16 == 0, so each 16-byte piece is wholly inside or outside K
-      const bool a_in = in_s && kb + 16u * (lane & 7) < (uint32_t)g.k;
+    // A, as whole rows: rows 0-7 of each tile in aq[i][0..3], rows 8-15 in
+    // aq[i][4..7] (permute_a reorders them); K % 16 == 0, so each 16-byte
+    // piece is wholly inside or outside K.
+    const bool a_in = in_s && kb + 16u * (lane & 7) < (uint32_t)g.k;
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        aq[i] = load32<kCacheDefault>(ars, a_in ? aoff[i] + kb : kOutOfRange,
-                                      a_in ? aoff[i] + kb + 8u * (uint32_t)g.lda : kOutOfRange);
-      }
+    for (int i = 0; i < MT; ++i) {
+      aq[i] = load32<kCacheDefault>(ars, a_in ? aoff[i] + kb : kOutOfRange,
+                                    a_in ? aoff[i] + kb + 8u * (uint32_t)g.lda : kOutOfRange);
     }
     if constexpr (PRE) {
       // Pre-shuffled: a 2 KiB tile per (column tile, k step), read as two
       // 1 KiB contiguous halves; lane l gets bytes [32 q, 32 q + 32) of
       // k step s for row l % 16 (q = l / 16).  K is padded with zero codes
-      // to whole steps in the shuffled copy; A pieces past K read zeros.
-      const bool a_lo = in_s && kb + 32u * kq < (uint32_t)g.k;
-      const bool a_hi = in_s && kb + 32u * kq + 16u < (uint32_t)g.k;
+      // to whole steps in the shuffled copy.
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const bool in = in_s && b_in[t];
         const uint32_t o = boff[t] + (uint32_t)s * step_bytes;
         bq[t] = load32<kCacheStream>(brs, in ? o : kOutOfRange, in ? o + 1024u : kOutOfRange);
-      }
-      if constexpr (!kAPerm) {
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          aq[i] = load32<kCacheDefault>(ars, a_lo ? aoff[i] + kb : kOutOfRange,
-                                        a_hi ? aoff[i] + kb + 16u : kOutOfRange);
-        }
       }
     } else {
       // K % 16 == 0: every 16-byte piece is wholly inside or outside K
@@ -177,13 +165,6 @@ void gemm_fp8_kernel(const GemmArgs g) {
       for (int t = 0; t < NT; ++t) {
         bq[t] = load32<kCacheStream>(brs, lo_in ? boff[t] + kb : kOutOfRange,
                                      hi_in ? boff[t] + kb + 64u : kOutOfRange);
-      }
-      if constexpr (!kAPerm) {
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          aq[i] = load32<kCacheDefault>(ars, lo_in ? aoff[i] + kb : kOutOfRange,
-                                        hi_in ? aoff[i] + kb + 64u : kOutOfRange);
-        }
       }
     }
   };
@@ -218,14 +199,9 @@ void gemm_fp8_kernel(const GemmArgs g) {
                       (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     }
   };
-  auto mma = [&](const i32x8 (&bq)[NT], const i32x8 (&a_in)[MT]) {
+  auto mma = [&](const i32x8 (&bq)[NT], const i32x8 (&a_raw)[MT]) {
     i32x8 aq[MT];
-    if constexpr (kAPerm) {
-      permute_a(a_in, aq);
-    } else {
-#pragma unroll
-      for (int i = 0; i < MT; ++i) aq[i] = a_in[i];
-    }
+    permute_a(a_raw, aq);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -250,7 +226,7 @@ void gemm_fp8_kernel(const GemmArgs g) {
 
   // Sum the WAVES partial tiles.  In a 16x16 MFMA result, lane l holds
   // rows 4*(l/16) .. 4*(l/16)+3 of column l%16.
-  if constexpr (kAPerm) __syncthreads();  // every wave is done with its A slice
+  __syncthreads();  // every wave is done with its A slice
   float* const part = reinterpret_cast<float*>(lds);
   __shared__ int last_split;
 #pragma unroll
