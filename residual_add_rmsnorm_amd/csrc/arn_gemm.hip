@@ -12,12 +12,11 @@
 // bytes of B dominate and the kernel is HBM-bound, so the layout serves the
 // weight stream:
 //  * v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3 -> fp32): each lane brings 32
-//    bytes of one row of A and of B for a 128-wide k step, as two 16-byte
-//    pieces laid out so that one load instruction reads 64 contiguous bytes
-//    of each of 16 weight rows (row-major weight).  The k order inside an
-//    MFMA is the same for both operands, and a dot product does not depend
-//    on it, so the pieces need no shuffling.  A is loaded as whole 128-byte
-//    rows and put in operand order through LDS (see aoff below).
+//    bytes of one row of A and of B for a 128-wide k step.  Row-major
+//    operands are loaded as whole 128-byte rows and put into operand order
+//    through LDS (see aoff below); the pre-shuffled weight arrives in
+//    operand order.  The k order inside an MFMA is the same for both
+//    operands, and a dot product does not depend on it.
 //  * a block owns a (16 MT) x (16 NT) output tile and splits K over WAVES
 //    waves in interleaved 128-wide steps (the block reads each weight row
 //    front to back); A tiles are reused across the NT weight tiles of a
@@ -100,16 +99,17 @@ void gemm_fp8_kernel(const GemmArgs g) {
       PRE ? row_rsrc(g.b, (uint32_t)(ntiles * nsteps * 2048))
           : row_rsrc(static_cast<const uint8_t*>(g.b) + n0 * g.ldb, (uint32_t)(n_here * g.ldb));
 
-  // A operand.  The MFMA layout puts one A row in every 16th lane, so a
-  // load that fills operand registers directly touches 16 rows (16 cache
-  // lines, half of each) per instruction, where a weight load touches 8
-  // whole lines; with 64 rows A costs a block as many bytes as its weight.
-  // So each A load covers 8 whole 128-byte rows (lane l: row l / 8, bytes
-  // 16 (l % 8)) and the wave permutes its tiles into the operand layout
-  // through its own LDS slice (rows padded to 144 bytes, so that the
-  // operand reads -- 16 rows at one column -- fall in distinct banks).
+  // Row-major operands.  The MFMA layout puts one operand row in every 16th
+  // lane, so a load that fills operand registers directly touches 16 rows
+  // (16 cache lines, half of each) per instruction, where a load of the
+  // pre-shuffled weight touches 8 whole lines.  So every row-major tile --
+  // A always, the weight unless pre-shuffled -- is loaded as whole 128-byte
+  // rows (lane l: row l / 8, bytes 16 (l % 8); two loads per 16-row tile)
+  // and put into operand order through the wave's own LDS slice (rows
+  // padded to 144 bytes, so that the operand reads -- 16 rows at one column
+  // -- fall in distinct banks).
   constexpr int kRowP = 144;
-  constexpr int kStage = MT * 16 * kRowP;  // LDS bytes per wave
+  constexpr int kStage = 16 * kRowP;  // LDS bytes per wave: one tile at a time
   uint32_t aoff[MT], boff[NT];
   bool b_in[NT];  // pre-shuffled: the column tile exists (the last group may be ragged)
 #pragma unroll
@@ -120,7 +120,7 @@ void gemm_fp8_kernel(const GemmArgs g) {
   for (int t = 0; t < NT; ++t) {
     b_in[t] = !PRE || n0 / 16 + t < ntiles;
     boff[t] = PRE ? (uint32_t)((n0 / 16 + t) * 2048) + 16u * lane
-                  : (uint32_t)((t * 16 + r16) * g.ldb) + 16u * kq;
+                  : (uint32_t)((t * 16 + (lane >> 3)) * g.ldb) + 16u * (lane & 7);
   }
 
   f32x4 acc[MT][NT];
@@ -137,14 +137,14 @@ void gemm_fp8_kernel(const GemmArgs g) {
   auto load_step = [&](int s, i32x8 (&bq)[NT], i32x8 (&aq)[MT]) {
     const uint32_t kb = (uint32_t)s * 128u;
     const bool in_s = s < s_end;
-    // A, as whole rows: rows 0-7 of each tile in aq[i][0..3], rows 8-15 in
-    // aq[i][4..7] (permute_a reorders them); K % 16 == 0, so each 16-byte
-    // piece is wholly inside or outside K.
-    const bool a_in = in_s && kb + 16u * (lane & 7) < (uint32_t)g.k;
+    // Whole rows: rows 0-7 of each tile in [0..3], rows 8-15 in [4..7]
+    // (permute reorders them); K % 16 == 0, so each 16-byte piece is wholly
+    // inside or outside K.
+    const bool row_in = in_s && kb + 16u * (lane & 7) < (uint32_t)g.k;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      aq[i] = load32<kCacheDefault>(ars, a_in ? aoff[i] + kb : kOutOfRange,
-                                    a_in ? aoff[i] + kb + 8u * (uint32_t)g.lda : kOutOfRange);
+      aq[i] = load32<kCacheDefault>(ars, row_in ? aoff[i] + kb : kOutOfRange,
+                                    row_in ? aoff[i] + kb + 8u * (uint32_t)g.lda : kOutOfRange);
     }
     if constexpr (PRE) {
       // Pre-shuffled: a 2 KiB tile per (column tile, k step), read as two
@@ -158,50 +158,49 @@ void gemm_fp8_kernel(const GemmArgs g) {
         bq[t] = load32<kCacheStream>(brs, in ? o : kOutOfRange, in ? o + 1024u : kOutOfRange);
       }
     } else {
-      // K % 16 == 0: every 16-byte piece is wholly inside or outside K
-      const bool lo_in = in_s && kb + 16u * kq < (uint32_t)g.k;
-      const bool hi_in = in_s && kb + 64u + 16u * kq < (uint32_t)g.k;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        bq[t] = load32<kCacheStream>(brs, lo_in ? boff[t] + kb : kOutOfRange,
-                                     hi_in ? boff[t] + kb + 64u : kOutOfRange);
+        bq[t] = load32<kCacheStream>(brs, row_in ? boff[t] + kb : kOutOfRange,
+                                     row_in ? boff[t] + kb + 8u * (uint32_t)g.ldb : kOutOfRange);
       }
     }
   };
-  // The LDS of the block: the waves' A staging slices during the k loop,
-  // then the partial tiles of the cross-wave sum.
+  // The LDS of the block: the waves' staging slices during the k loop, then
+  // the partial tiles of the cross-wave sum.
   constexpr int kLdsBytes =
       WAVES * kStage > WAVES * kTile * 4 ? WAVES * kStage : WAVES * kTile * 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   uint8_t* const stage = lds + wave * kStage;
-  // A tiles into the MFMA operand layout: lane l = r + 16 q gets row r's
-  // bytes [32 q, 32 q + 32) of the step (pre-shuffled weight) or
-  // [16 q, +16) and [64 + 16 q, +16) (row-major weight), the same in-lane k
-  // order as the weight operand.  Only this wave touches its slice, and its
-  // LDS accesses complete in order, so no barrier is needed.
-  auto permute_a = [&](const i32x8 (&raw)[MT], i32x8 (&aq)[MT]) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const u32x4 lo = {(uint32_t)raw[i][0], (uint32_t)raw[i][1], (uint32_t)raw[i][2],
-                        (uint32_t)raw[i][3]};
-      const u32x4 hi = {(uint32_t)raw[i][4], (uint32_t)raw[i][5], (uint32_t)raw[i][6],
-                        (uint32_t)raw[i][7]};
-      uint8_t* dst = stage + (i * 16 + (lane >> 3)) * kRowP + 16 * (lane & 7);
-      *reinterpret_cast<u32x4*>(dst) = lo;
-      *reinterpret_cast<u32x4*>(dst + 8 * kRowP) = hi;
-    }
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const uint8_t* src = stage + (i * 16 + r16) * kRowP;
-      const u32x4 x0 = *reinterpret_cast<const u32x4*>(src + (PRE ? 32 * kq : 16 * kq));
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(src + (PRE ? 32 * kq + 16 : 64 + 16 * kq));
-      aq[i] = (i32x8){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-    }
+  // One tile into the MFMA operand layout: lane l = r + 16 q gets row r's
+  // bytes [32 q, 32 q + 32) of the step (pre-shuffled weight) or [16 q, +16)
+  // and [64 + 16 q, +16) (row-major weight), the in-lane k order of the
+  // weight operand.  Only this wave touches its slice, and the LDS executes
+  // a wave's accesses in order, so the next tile may overwrite the slice
+  // right behind the reads, and no barrier is needed.
+  auto permute = [&](const i32x8& raw, i32x8& out) {
+    const u32x4 lo = {(uint32_t)raw[0], (uint32_t)raw[1], (uint32_t)raw[2], (uint32_t)raw[3]};
+    const u32x4 hi = {(uint32_t)raw[4], (uint32_t)raw[5], (uint32_t)raw[6], (uint32_t)raw[7]};
+    uint8_t* dst = stage + (lane >> 3) * kRowP + 16 * (lane & 7);
+    *reinterpret_cast<u32x4*>(dst) = lo;
+    *reinterpret_cast<u32x4*>(dst + 8 * kRowP) = hi;
+    const uint8_t* src = stage + r16 * kRowP;
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(src + (PRE ? 32 * kq : 16 * kq));
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(src + (PRE ? 32 * kq + 16 : 64 + 16 * kq));
+    out = (i32x8){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                  (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
   };
-  auto mma = [&](const i32x8 (&bq)[NT], const i32x8 (&a_raw)[MT]) {
-    i32x8 aq[MT];
-    permute_a(a_raw, aq);
+  auto mma = [&](const i32x8 (&b_raw)[NT], const i32x8 (&a_raw)[MT]) {
+    i32x8 aq[MT], bq[NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) permute(a_raw[i], aq[i]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (PRE) {
+        bq[t] = b_raw[t];
+      } else {
+        permute(b_raw[t], bq[t]);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -226,7 +225,7 @@ void gemm_fp8_kernel(const GemmArgs g) {
 
   // Sum the WAVES partial tiles.  In a 16x16 MFMA result, lane l holds
   // rows 4*(l/16) .. 4*(l/16)+3 of column l%16.
-  __syncthreads();  // every wave is done with its A slice
+  __syncthreads();  // every wave is done with its staging slice
   float* const part = reinterpret_cast<float*>(lds);
   __shared__ int last_split;
 #pragma unroll
