@@ -15,6 +15,8 @@ would need a copy raises ValueError instead of copying.
 """
 from __future__ import annotations
 
+import contextlib
+
 import torch
 
 from . import _lib
@@ -37,6 +39,8 @@ def _rows(t: torch.Tensor, name: str):
     if t.dim() == 0:
         raise ValueError(f"{name}: needs at least one dimension")
     hidden = t.shape[-1]
+    if hidden > 0 and t.is_contiguous():
+        return t.numel() // hidden, hidden, hidden
     if hidden > 1 and t.stride(-1) != 1:
         raise ValueError(f"{name}: last dimension must have unit stride")
     rows = 1
@@ -86,8 +90,21 @@ def _check_device(x: torch.Tensor):
         raise ValueError("tensors must live on a GPU device")
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_SAME_DEVICE = contextlib.nullcontext()
+
+
 def _stream(x: torch.Tensor) -> int:
+    """The current HIP stream of x's device (a raw handle)."""
+    if _raw_stream is not None:
+        return _raw_stream(x.device.index)
     return torch.cuda.current_stream(x.device).cuda_stream
+
+
+def _on(x: torch.Tensor):
+    """Make x's device current for the call (a no-op when it already is)."""
+    idx = x.device.index
+    return _SAME_DEVICE if idx == torch.cuda.current_device() else torch.cuda.device(idx)
 
 
 def _out_like(x, out, dtype, name="out"):
@@ -108,7 +125,7 @@ def rmsnorm(x: torch.Tensor, weight: torch.Tensor | None, eps: float,
     _, _, os_ = _rows(out, "out")
     wp = _check_weight(weight, x, hidden)
     lib = _lib.load()
-    with torch.cuda.device(x.device):
+    with _on(x):
         st = lib.arn_rmsnorm(out.data_ptr(), os_, x.data_ptr(), xs, wp, float(eps),
                              rows, hidden, dt, _stream(x))
     _lib.check(st, "arn_rmsnorm")
@@ -129,7 +146,7 @@ def fused_add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, weight: torch.Ten
     _, _, os_ = _rows(out, "out")
     wp = _check_weight(weight, x, hidden)
     lib = _lib.load()
-    with torch.cuda.device(x.device):
+    with _on(x):
         st = lib.arn_fused_add_rmsnorm(out.data_ptr(), os_, x.data_ptr(), xs,
                                        residual.data_ptr(), rs, wp, float(eps),
                                        rows, hidden, dt, _stream(x))
@@ -169,7 +186,7 @@ def rmsnorm_fp8(x: torch.Tensor, weight: torch.Tensor | None, eps: float,
     wp = _check_weight(weight, x, hidden)
     sc, mode = _fp8_scale(x, rows, scale, dynamic, scales_out)
     lib = _lib.load()
-    with torch.cuda.device(x.device):
+    with _on(x):
         st = lib.arn_rmsnorm_fp8(out.data_ptr(), os_, sc.data_ptr(), mode, x.data_ptr(), xs,
                                  wp, float(eps), rows, hidden, dt, _stream(x))
     _lib.check(st, "arn_rmsnorm_fp8")
@@ -194,7 +211,7 @@ def fused_add_rmsnorm_fp8(x: torch.Tensor, residual: torch.Tensor,
     wp = _check_weight(weight, x, hidden)
     sc, mode = _fp8_scale(x, rows, scale, dynamic, scales_out)
     lib = _lib.load()
-    with torch.cuda.device(x.device):
+    with _on(x):
         st = lib.arn_fused_add_rmsnorm_fp8(out.data_ptr(), os_, sc.data_ptr(), mode,
                                            x.data_ptr(), xs, residual.data_ptr(), rs, wp,
                                            float(eps), rows, hidden, dt, _stream(x))
@@ -239,7 +256,7 @@ def norm(x: torch.Tensor, weight: torch.Tensor | None, eps: float,
         variance_size=0 if variance_size is None else int(variance_size),
         stream=_stream(x))
     lib = _lib.load()
-    with torch.cuda.device(x.device):
+    with _on(x):
         st = lib.arn_norm(ctypes.byref(args))
     _lib.check(st, "arn_norm")
     return (out, sc) if fp8 else out
@@ -292,7 +309,7 @@ def sum_add_rmsnorm(parts, weight: torch.Tensor | None, eps: float,
         residual_stride=rs, weight=wp, eps=float(eps), rows=rows, hidden=hidden,
         stream=_stream(x))
     lib = _lib.load()
-    with torch.cuda.device(x.device):
+    with _on(x):
         st = lib.arn_sum_add_rmsnorm(ctypes.byref(args))
     _lib.check(st, "arn_sum_add_rmsnorm")
     return (out, sc) if fp8 else out
@@ -325,7 +342,7 @@ def silu_and_mul(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tens
     _, _, os_ = _rows(out, "out")
     lib = _lib.load()
     base = x.data_ptr()
-    with torch.cuda.device(x.device):
+    with _on(x):
         st = lib.arn_silu_and_mul(out.data_ptr(), os_, base, xs, base + 2 * d, xs, rows, d,
                                   _DTYPES[x.dtype], _stream(x))
     _lib.check(st, "arn_silu_and_mul")
@@ -342,7 +359,7 @@ def silu_and_mul_fp8(x: torch.Tensor, scale: torch.Tensor | None = None, dynamic
     sc, mode = _fp8_scale(x, rows, scale, dynamic, scales_out)
     lib = _lib.load()
     base = x.data_ptr()
-    with torch.cuda.device(x.device):
+    with _on(x):
         st = lib.arn_silu_and_mul_fp8(out.data_ptr(), os_, sc.data_ptr(), mode, base, xs,
                                       base + 2 * d, xs, rows, d, _DTYPES[x.dtype], _stream(x))
     _lib.check(st, "arn_silu_and_mul_fp8")
@@ -376,7 +393,7 @@ def fp8_weight_preshuffle(b: torch.Tensor) -> PreshuffledWeight:
     if size < 0:
         raise ValueError("b must have K >= 1")
     dst = torch.empty(max(size, 16), dtype=torch.uint8, device=b.device)
-    with torch.cuda.device(b.device):
+    with _on(b):
         st = lib.arn_fp8_weight_preshuffle(dst.data_ptr(), b.data_ptr(), b.stride(0), n, k,
                                            _stream(b))
     _lib.check(st, "arn_fp8_weight_preshuffle")
@@ -428,7 +445,7 @@ def fp8_gemm(a: torch.Tensor, scale_a: torch.Tensor, b, scale_b: torch.Tensor,
         if workspace.device != a.device or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on a's device")
         ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
-    with torch.cuda.device(a.device):
+    with _on(a):
         if pre and workspace is not None:
             name = "arn_fp8_gemm_preshuffled_ws"
             st = lib.arn_fp8_gemm_preshuffled_ws(

@@ -124,6 +124,8 @@ _lib = None
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libarn.so, building it first only if it is not there at all."""
     global _lib
+    if _lib is not None:  # loaded: no lock on the per-call path
+        return _lib
     with _lock:
         if _lib is not None:
             return _lib
