@@ -208,6 +208,26 @@ void gemm_fp8_kernel(const GemmArgs g) {
         acc[i][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[i], bq[t], acc[i][t], 0,
                                                                      0, 0, 0, 0, 0);
   };
+  // Each thread stores the same tile elements e = threadIdx.x + 64 WAVES i
+  // at the end.  With few of them per thread their dequant scales are
+  // fetched now, so that the latency of those loads hides behind the k loop
+  // instead of adding to the end of the block.
+  constexpr int kPer = (kTile + 64 * WAVES - 1) / (64 * WAVES);
+  constexpr bool kEarlyScales = kPer <= 4;
+  float pre_sa[kEarlyScales ? kPer : 1], pre_sb[kEarlyScales ? kPer : 1];
+  if constexpr (kEarlyScales) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = threadIdx.x + 64 * WAVES * i;
+      const int tile = e >> 8;
+      const int64_t gm = (int64_t)(tile / NT) * 16 + ((e >> 4) & 15);
+      const int64_t gn = n0 + (int64_t)(tile % NT) * 16 + (e & 15);
+      const bool out = e < kTile && gm < g.m && gn < g.n;
+      pre_sa[i] = out ? (g.a_per_row ? g.scale_a[gm] : g.scale_a[0]) : 0.0f;
+      pre_sb[i] = out ? (g.b_per_row ? g.scale_b[gn] : g.scale_b[0]) : 0.0f;
+    }
+  }
+
   // The scheduling barriers keep the compiler from sinking each load next
   // to its use (which would serialise load and MFMA again).
   i32x8 b0[NT], a0[MT], b1[NT], a1[MT];
@@ -239,7 +259,6 @@ void gemm_fp8_kernel(const GemmArgs g) {
 
   // Each thread owns the same tile elements e = threadIdx.x + 64 WAVES i in
   // every phase below.
-  constexpr int kPer = (kTile + 64 * WAVES - 1) / (64 * WAVES);
   float sum[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -308,8 +327,14 @@ void gemm_fp8_kernel(const GemmArgs g) {
     const int64_t gm = (int64_t)(tile / NT) * 16 + row;
     const int64_t gn = n0 + (int64_t)(tile % NT) * 16 + col;
     if (gm < g.m && gn < g.n) {
-      const float sa = g.a_per_row ? g.scale_a[gm] : g.scale_a[0];
-      const float sb = g.b_per_row ? g.scale_b[gn] : g.scale_b[0];
+      float sa, sb;
+      if constexpr (kEarlyScales) {
+        sa = pre_sa[i];
+        sb = pre_sb[i];
+      } else {
+        sa = g.a_per_row ? g.scale_a[gm] : g.scale_a[0];
+        sb = g.b_per_row ? g.scale_b[gn] : g.scale_b[0];
+      }
       const float v = sum[i] * sa * sb;
       static_cast<uint16_t*>(g.c)[gm * g.ldc + gn] = (uint16_t)(pack2<DT>(v, 0.0f) & 0xFFFFu);
     }
