@@ -115,3 +115,14 @@ def gemm_tol(ref: dict, k: int, out: str = "bf16") -> np.ndarray:
     |products|."""
     return (RHO[out] * np.abs(ref["c"]) + ulp16(ref["c"], out) + 2.0**-8 * ref["stepmax"]
             + (k / 128 + 256) * 2.0**-24 * ref["abs"])
+
+
+def device_normal(rows: int, cols: int, std: float, gen: torch.Generator,
+                  dtype=torch.bfloat16, chunk: int = 1 << 20) -> torch.Tensor:
+    """Seeded N(0, std^2) values rounded to `dtype`, drawn on the device in
+    chunks of rows (inputs of several GiB never pass through the host)."""
+    t = torch.empty((rows, cols), dtype=dtype, device="cuda")
+    for i in range(0, rows, chunk):
+        j = min(rows, i + chunk)
+        t[i:j] = (torch.randn((j - i, cols), generator=gen, device="cuda") * std).to(dtype)
+    return t

@@ -13,7 +13,7 @@ import torch
 import oracle as O
 import workloads as W
 from tests._helpers import (assert_codes_close, assert_scales_close, assert_y_close,
-                            bits, codes, dev)
+                            bits, codes, dev, device_normal)
 
 pytestmark = pytest.mark.gpu
 
@@ -215,3 +215,42 @@ def test_full_size(orc):
     r0 = torch.from_numpy(d["residual"].view(np.int16)).view(torch.bfloat16).float()
     expect = (xf + r0).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(rb, expect)
+
+
+def test_rows_past_4gib_and_launch_split(orc):
+    """Parts, residual and output of 4 GiB and more, and more rows than one
+    launch takes (the one-row-per-block tile forced: 2^22 rows per launch),
+    so every part's pointer of the second launch starts 4 GiB in.  Two parts,
+    fused residual, 16-bit output; sampled rows on both sides of the launch
+    boundary against the oracle."""
+    import residual_add_rmsnorm_amd as arn
+
+    rows, H, eps = (1 << 22) + 1000, 512, 1e-6
+    print(f"\n[past-4GiB] sum_add_rmsnorm 2 parts rows {rows} hidden {H}", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4444)
+    parts = [device_normal(rows, H, 0.7, gen) for _ in range(2)]
+    res = device_normal(rows, H, 1.0, gen)
+    w = (1 + 0.1 * torch.randn(H, generator=gen, device="cuda")).to(torch.bfloat16)
+    b = 1 << 22
+    idx = np.unique(np.concatenate([np.linspace(0, rows - 1, 64).astype(np.int64),
+                                    np.arange(b - 3, b + 3), np.arange(rows - 3, rows)]))
+    sel = torch.from_numpy(idx).cuda()
+    ps = [bits(p.index_select(0, sel)) for p in parts]
+    rs = bits(res.index_select(0, sel))
+    out = torch.full((rows, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    arn.set_tile(8, 1)
+    try:
+        arn.sum_add_rmsnorm(parts, w, eps, residual=res, out=out)
+        plan = arn.last_plan()
+    finally:
+        arn.set_tile(0, 0)
+    torch.cuda.synchronize()
+    print(f"[past-4GiB] plan {plan}", flush=True)
+    assert plan.endswith("wpr8/nv1/rpb1/grid1000")
+    ref = orc.sum_add_rmsnorm("bf16", ps, rs, bits(w), eps)
+    assert np.array_equal(bits(res.index_select(0, sel)), ref["r16"])
+    assert_y_close(bits(out.index_select(0, sel)), ref["y"], "bf16")
+    for i in range(0, rows, 1 << 20):
+        j = min(rows, i + (1 << 20))
+        assert not bool(torch.isnan(out[i:j].float()).any()), f"unwritten output in rows {i}..{j}"

@@ -321,6 +321,47 @@ def test_preshuffled_panels(orc):
         arn.set_gemm_splits(0)
 
 
+def test_rowmajor_weight_past_2gib(orc):
+    """A row-major weight over 2 GiB: a launch addresses at most 2 GiB of it
+    (32-bit buffer offsets), so at K = 131072 the first launch takes 16384
+    weight rows and a second one the last 116.  Columns on both sides of the
+    launch boundary and at the end against the oracle, without and with a
+    split-K workspace (3 splits forced: the second launch's partial tiles and
+    counters start past the first launch's)."""
+    import residual_add_rmsnorm_amd as arn
+
+    m, n, k = 3, 16500, 131072
+    assert n * k > 1 << 31
+    print(f"\n[row-major past 2 GiB] m {m} n {n} k {k}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(6)
+    b = torch.randint(0, 256, (n, k), dtype=torch.uint8, device="cuda", generator=gen)
+    b[(b & 0x7F) == 0x7F] = 0  # no NaN codes
+    rng = np.random.default_rng(32)
+    a = rng.integers(0, 256, (m, k)).astype(np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0
+    sa = rng.uniform(0.01, 0.1, m).astype(np.float32)
+    sb = rng.uniform(0.001, 0.01, n).astype(np.float32)
+    cols = np.unique(np.concatenate([np.linspace(0, n - 1, 24).astype(np.int64),
+                                     [0, 15, 16, 16367, 16368, 16383, 16384, 16385, 16399,
+                                      16400, 16495, 16496, 16499]]))
+    ref = orc.fp8_gemm(a, sa, b[torch.from_numpy(cols).cuda()].cpu().numpy(), sb[cols])
+    tol = gemm_tol(ref, k)
+    ad, sad, sbd = (torch.from_numpy(v).cuda() for v in (a, sa, sb))
+    ws = arn.fp8_gemm_workspace(m, n, k)
+    try:
+        for splits, w in ((0, None), (3, ws)):
+            arn.set_gemm_splits(splits)
+            c = arn.fp8_gemm(ad, sad, b, sbd, workspace=w)
+            torch.cuda.synchronize()
+            got = values16(bits(c[:, torch.from_numpy(cols).cuda()]), "bf16")
+            err = np.abs(got - ref["c"])
+            assert np.all(err <= tol), (splits, arn.last_plan(), float(np.max(err / tol)))
+            assert "grid" in arn.last_plan()
+    finally:
+        arn.set_gemm_splits(0)
+    assert _counters_zero(ws, n)
+
+
 # ---------------------------------------------------------------------------
 # Split K across blocks (workspace entry points)
 # ---------------------------------------------------------------------------

@@ -12,7 +12,7 @@ import torch
 import oracle as O
 import workloads as W
 from tests._helpers import (assert_codes_close, assert_scales_close, assert_y_close, bits, codes,
-                            dev, static_scale)
+                            dev, device_normal, static_scale)
 
 pytestmark = pytest.mark.gpu
 
@@ -179,3 +179,41 @@ def test_workloads_sampled(orc, name):
     assert_codes_close(codes(out)[idx], ref["q"])
     if w.fp8 == "dynamic":
         assert_scales_close(sc.cpu().numpy()[idx], ref["scales"], w.dtype)
+
+
+def test_rows_past_4gib_and_launch_split(orc):
+    """A gate|up tensor of 8 GiB and more rows than one launch takes: with
+    the one-row-per-block tile forced, 2^22 rows fill a launch, so 2^22 +
+    1000 rows of d = 512 take two, the second starting 8 GiB into the input
+    and 2 GiB into the codes; dynamic e4m3, so the per-row scales are offset
+    too.  Sampled rows on both sides of the boundary against the oracle."""
+    import residual_add_rmsnorm_amd as arn
+
+    rows, d = (1 << 22) + 1000, 512
+    print(f"\n[past-4GiB] silu_and_mul_fp8 rows {rows} d {d}", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4343)
+    x = device_normal(rows, 2 * d, 2.0, gen)
+    b = 1 << 22
+    idx = np.unique(np.concatenate([np.linspace(0, rows - 1, 64).astype(np.int64),
+                                    np.arange(b - 3, b + 3), np.arange(rows - 3, rows)]))
+    sel = torch.from_numpy(idx).cuda()
+    xs = bits(x.index_select(0, sel))
+    out = torch.full((rows, d), 0x7F, dtype=torch.uint8, device="cuda")
+    sc = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+    arn.set_tile(8, 1)
+    try:
+        arn.silu_and_mul_fp8(x, dynamic=True, out=out.view(torch.float8_e4m3fn), scales_out=sc)
+        plan = arn.last_plan()
+    finally:
+        arn.set_tile(0, 0)
+    torch.cuda.synchronize()
+    print(f"[past-4GiB] plan {plan}", flush=True)
+    assert plan.endswith("wpr8/nv1/rpb1/grid1000")
+    ref = orc.silu_and_mul("bf16", xs, d=d, fp8_mode=O.FP8_DYNAMIC)
+    assert_codes_close(codes(out.index_select(0, sel)), ref["q"])
+    assert_scales_close(sc.index_select(0, sel).cpu().numpy(), ref["scales"], "bf16")
+    assert not bool(torch.isnan(sc).any()), "a row's scale was not written"
+    for i in range(0, rows, 1 << 20):
+        j = min(rows, i + (1 << 20))
+        assert not bool(((out[i:j] & 0x7F) == 0x7F).any()), f"unwritten codes in rows {i}..{j}"
