@@ -49,6 +49,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // under 2 GiB): a 16-byte load there reads zeros.
 constexpr uint32_t kOutOfRange = 0xFFFFFF00u;
 
+// Cache policy sc1: a load coherent across the XCDs (agent scope), the
+// policy a relaxed agent-scope atomic load compiles to.
+constexpr int kCacheDeviceScope = 16;
+
 // A lane's 32 bytes of one 128-byte k step come from two 16-byte pieces:
 // bytes [16 q, 16 q + 16) and [64 + 16 q, 64 + 16 q + 16) for lane group q.
 // Each load instruction then reads 64 contiguous bytes of every row it
@@ -209,24 +213,33 @@ void gemm_fp8_kernel(const GemmArgs g) {
                                                                      0, 0, 0, 0, 0);
   };
   // Each thread stores the same tile elements e = threadIdx.x + 64 WAVES i
-  // at the end.  With few of them per thread their dequant scales are
-  // fetched now, so that the latency of those loads hides behind the k loop
-  // instead of adding to the end of the block.
+  // at the end.  Their dequant scales are all requested before any is used,
+  // so the block waits for one round trip rather than one per element: with
+  // few elements per thread before the k loop (the latency hides behind it),
+  // otherwise right after the loop (it overlaps the cross-wave sum), where
+  // holding them does not cost loop registers.
   constexpr int kPer = (kTile + 64 * WAVES - 1) / (64 * WAVES);
   constexpr bool kEarlyScales = kPer <= 4;
-  float pre_sa[kEarlyScales ? kPer : 1], pre_sb[kEarlyScales ? kPer : 1];
-  if constexpr (kEarlyScales) {
+  float pre_sa[kPer], pre_sb[kPer];
+  auto fetch_scales = [&]() {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = threadIdx.x + 64 * WAVES * i;
       const int tile = e >> 8;
       const int64_t gm = (int64_t)(tile / NT) * 16 + ((e >> 4) & 15);
       const int64_t gn = n0 + (int64_t)(tile % NT) * 16 + (e & 15);
+      // Unconditional loads from clamped (always valid) indices, then a
+      // select: no branch, so no wait between the loads.
       const bool out = e < kTile && gm < g.m && gn < g.n;
-      pre_sa[i] = out ? (g.a_per_row ? g.scale_a[gm] : g.scale_a[0]) : 0.0f;
-      pre_sb[i] = out ? (g.b_per_row ? g.scale_b[gn] : g.scale_b[0]) : 0.0f;
+      const int64_t ia = (g.a_per_row && out) ? gm : 0;
+      const int64_t ib = (g.b_per_row && out) ? gn : 0;
+      const float sa = g.scale_a[ia];
+      const float sb = g.scale_b[ib];
+      pre_sa[i] = out ? sa : 0.0f;
+      pre_sb[i] = out ? sb : 0.0f;
     }
-  }
+  };
+  if constexpr (kEarlyScales) fetch_scales();
 
   // The scheduling barriers keep the compiler from sinking each load next
   // to its use (which would serialise load and MFMA again).
@@ -245,6 +258,7 @@ void gemm_fp8_kernel(const GemmArgs g) {
 
   // Sum the WAVES partial tiles.  In a 16x16 MFMA result, lane l holds
   // rows 4*(l/16) .. 4*(l/16)+3 of column l%16.
+  if constexpr (!kEarlyScales) fetch_scales();
   __syncthreads();  // every wave is done with its staging slice
   float* const part = reinterpret_cast<float*>(lds);
   __shared__ int last_split;
@@ -299,16 +313,25 @@ void gemm_fp8_kernel(const GemmArgs g) {
     }
     __syncthreads();
     if (!last_split) return;
+    // The same agent-scope (sc1) loads as relaxed atomic loads, written as
+    // buffer loads so that the kPer loads of a split are all in flight
+    // before the first is used; each element still adds the splits in
+    // split order.
+    const __amdgpu_buffer_rsrc_t prs =
+        row_rsrc(tile_part, (uint32_t)(g.splits * kTile * (int)sizeof(float)));
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = threadIdx.x + 64 * WAVES * i;
-      sum[i] = 0.0f;
-      if (e < kTile) {
-        for (int sp = 0; sp < g.splits; ++sp) {
-          sum[i] += __hip_atomic_load(tile_part + (size_t)sp * kTile + e, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-        }
+    for (int i = 0; i < kPer; ++i) sum[i] = 0.0f;
+    for (int sp = 0; sp < g.splits; ++sp) {
+      float v[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int e = threadIdx.x + 64 * WAVES * i;
+        const uint32_t off = e < kTile ? (uint32_t)((sp * kTile + e) * 4) : kOutOfRange;
+        v[i] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(prs, (int)off, 0, kCacheDeviceScope));
       }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) sum[i] += v[i];
     }
     // Leave the counter at zero for the next call (ordered before the next
     // kernel on the stream by the kernel boundary).
@@ -327,14 +350,8 @@ void gemm_fp8_kernel(const GemmArgs g) {
     const int64_t gm = (int64_t)(tile / NT) * 16 + row;
     const int64_t gn = n0 + (int64_t)(tile % NT) * 16 + col;
     if (gm < g.m && gn < g.n) {
-      float sa, sb;
-      if constexpr (kEarlyScales) {
-        sa = pre_sa[i];
-        sb = pre_sb[i];
-      } else {
-        sa = g.a_per_row ? g.scale_a[gm] : g.scale_a[0];
-        sb = g.b_per_row ? g.scale_b[gn] : g.scale_b[0];
-      }
+      const float sa = pre_sa[i];
+      const float sb = pre_sb[i];
       const float v = sum[i] * sa * sb;
       static_cast<uint16_t*>(g.c)[gm * g.ldc + gn] = (uint16_t)(pack2<DT>(v, 0.0f) & 0xFFFFu);
     }
