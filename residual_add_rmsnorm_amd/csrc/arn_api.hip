@@ -143,14 +143,21 @@ int pow2_ceil(int64_t v) {
 // Kernel shape.  A row is split over `wpr` waves so that each lane holds
 // only a few vectors.  Measured on MI355X: with many rows, rows of eight
 // waves (512-thread blocks) holding at most two 128-bit vectors per lane
-// stream best (about 40 VGPRs, eight waves per SIMD); one-wave rows that
-// keep a whole 8192-wide row in registers run 20-25% slower.  With few rows
-// (decode) eight waves per row with up to four vectors per lane finish each
-// row soonest.  Among the compiled tiles of the chosen wave count, the one
+// stream best for the fused kinds (about 40 VGPRs, eight waves per SIMD);
+// one-wave rows that keep a whole 8192-wide row in registers run 20-25%
+// slower.  The plain kinds (no residual) move fewer bytes per element, so
+// a row's fixed costs (its barrier and reductions) weigh more and more
+// rows per CU pay: rows of at most four waves with up to four vectors per
+// lane, the fewest waves whose lanes still hold two vectors when the row
+// is narrow, so that no lane slot is wasted where it can be avoided
+// (65536 rows of dynamic e4m3: 2048 wide 35% faster than before, 2880 and
+// 4096 wide 33-40%, 5120 and 6144 wide 16-26%).  With few rows (decode)
+// eight waves per row with up to four vectors per lane finish each row
+// soonest.  Among the compiled tiles of the chosen wave count, the one
 // with the fewest per-lane vectors that covers the row (and at least
 // `min_nv`) is taken; failing that, any tile that covers the row.
 const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t rows, int cus,
-                        bool lean = false) {
+                        bool lean = false, bool plain = false) {
   const int forced = g_forced_tile.load(std::memory_order_relaxed);
   if (forced != 0) {
     const int fw = forced >> 8, fn = forced & 0xFF;
@@ -162,9 +169,23 @@ const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t r
     }
     return nullptr;
   }
+  const bool many_rows = rows >= (int64_t)4 * cus;
+  if (plain && many_rows) {
+    int w = 4;
+    while (w > 1 && (int64_t)64 * (w / 2) * 2 >= nvec) w /= 2;
+    const int64_t per_lane = (nvec + 64 * w - 1) / (64 * w);
+    const Tile* pick = nullptr;
+    for (int i = 0; per_lane <= 4 && i < table->count; ++i) {
+      const Tile& t = table->tiles[i];
+      if (t.vec == vec && t.wpr == w && t.nv >= per_lane && t.nv <= 4 &&
+          (!pick || t.nv < pick->nv)) {
+        pick = &t;
+      }
+    }
+    if (pick) return pick;
+  }
   // lean: each vector brings several inputs (the all-reduce form), so one
   // vector per lane with more waves per row streams best.
-  const bool many_rows = rows >= (int64_t)4 * cus;
   const int64_t target_nv = lean ? 1 : (many_rows ? 2 : 4);
   const int64_t min_nv = lean || !many_rows ? 1 : 2;
   const int wpr_floor = 8;
@@ -229,7 +250,8 @@ int run(const Request& r) {
   const int vec = choose_vec(r);
   const int64_t nvec = r.hidden / vec;
   const TileTable* table = r.parts ? sum_table_for(r.kind, r.dtype) : table_for(r.kind, r.dtype);
-  const Tile* tile = choose_tile(table, vec, nvec, r.rows, cu_count(), r.nparts >= 4);
+  const Tile* tile = choose_tile(table, vec, nvec, r.rows, cu_count(), r.nparts >= 4,
+                                 !(r.kind & arn::kFused) && !r.parts);
   if (!tile) return ARN_EUNSUPPORTED;
 
   const int esize_out = fp8 ? 1 : 2;

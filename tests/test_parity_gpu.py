@@ -192,6 +192,26 @@ def test_hidden_sweep_fp8(orc, hidden, fp8, fused):
              s=0.01 if fp8 == "static" else None)
 
 
+@pytest.mark.parametrize("hidden,tile", [(1024, "wpr1/nv2/rpb4"), (2048, "wpr2/nv2/rpb2"),
+                                         (2880, "wpr4/nv2/rpb1"), (5120, "wpr4/nv3/rpb1"),
+                                         (7168, "wpr4/nv4/rpb1"), (12288, "wpr16/nv2/rpb1")])
+@pytest.mark.parametrize("fp8", [None, "dynamic", "static"])
+def test_plain_many_rows_automatic_tiles(orc, hidden, tile, fp8):
+    """The plain kinds with many rows (at least 4 per CU) take rows of at
+    most four waves with up to four vectors per lane, fewer waves for
+    narrow rows; wider rows fall back to the general rule.  1030 rows
+    (several rows per block where the tile holds more than one, and a
+    ragged last block), every row against the oracle."""
+    arn = _arn()
+    rows = 4 * torch.cuda.get_device_properties(0).multi_processor_count + 6
+    dtype = "bf16"
+    x = _random(dtype, rows, hidden, hidden, 40 + hidden % 97)
+    w = _random(dtype, 1, hidden, hidden, 41)[0]
+    run_case(orc, dtype=dtype, x=x, res=None, w=w, eps=1e-6, hidden=hidden, fp8=fp8,
+             s=0.01 if fp8 == "static" else None)
+    assert f"/vec8/{tile}/" in arn.last_plan(), arn.last_plan()
+
+
 @pytest.mark.parametrize("rows", [1, 2, 255, 256, 257, 1025, 4099])
 def test_row_counts(orc, rows):
     x = _random("bf16", rows, 1024, 1024, 7)
