@@ -153,11 +153,15 @@ int pow2_ceil(int64_t v) {
 // (65536 rows of dynamic e4m3: 2048 wide 35% faster than before, 2880 and
 // 4096 wide 33-40%, 5120 and 6144 wide 16-26%).  With few rows (decode)
 // eight waves per row with up to four vectors per lane finish each row
-// soonest.  Among the compiled tiles of the chosen wave count, the one
+// soonest.  SwiGLU (5 bytes per output element with e4m3) follows the plain
+// rule while two vectors per lane cover the row (d <= 4096; 65536 rows of
+// dynamic e4m3: d = 1792 33% less time, 2048 24%, 3584 31%); wider rows,
+// such as one GPU's 6656-wide shard, stream best with eight-wave rows.
+// Among the compiled tiles of the chosen wave count, the one
 // with the fewest per-lane vectors that covers the row (and at least
 // `min_nv`) is taken; failing that, any tile that covers the row.
 const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t rows, int cus,
-                        bool lean = false, bool plain = false) {
+                        bool lean = false, int compact_nv = 0) {
   const int forced = g_forced_tile.load(std::memory_order_relaxed);
   if (forced != 0) {
     const int fw = forced >> 8, fn = forced & 0xFF;
@@ -170,14 +174,14 @@ const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t r
     return nullptr;
   }
   const bool many_rows = rows >= (int64_t)4 * cus;
-  if (plain && many_rows) {
+  if (compact_nv > 0 && many_rows) {
     int w = 4;
     while (w > 1 && (int64_t)64 * (w / 2) * 2 >= nvec) w /= 2;
     const int64_t per_lane = (nvec + 64 * w - 1) / (64 * w);
     const Tile* pick = nullptr;
-    for (int i = 0; per_lane <= 4 && i < table->count; ++i) {
+    for (int i = 0; per_lane <= compact_nv && i < table->count; ++i) {
       const Tile& t = table->tiles[i];
-      if (t.vec == vec && t.wpr == w && t.nv >= per_lane && t.nv <= 4 &&
+      if (t.vec == vec && t.wpr == w && t.nv >= per_lane && t.nv <= compact_nv &&
           (!pick || t.nv < pick->nv)) {
         pick = &t;
       }
@@ -251,7 +255,7 @@ int run(const Request& r) {
   const int64_t nvec = r.hidden / vec;
   const TileTable* table = r.parts ? sum_table_for(r.kind, r.dtype) : table_for(r.kind, r.dtype);
   const Tile* tile = choose_tile(table, vec, nvec, r.rows, cu_count(), r.nparts >= 4,
-                                 !(r.kind & arn::kFused) && !r.parts);
+                                 (r.kind & arn::kFused) || r.parts ? 0 : 4);
   if (!tile) return ARN_EUNSUPPORTED;
 
   const int esize_out = fp8 ? 1 : 2;
@@ -322,7 +326,7 @@ int run_glu(int mode, int dtype, void* out, int64_t out_stride, float* scale, co
     }
   }
   const int64_t nvec = d / vec;
-  const Tile* tile = choose_tile(glu_table_for(mode, dtype), vec, nvec, rows, cu_count());
+  const Tile* tile = choose_tile(glu_table_for(mode, dtype), vec, nvec, rows, cu_count(), false, 2);
   if (!tile) return ARN_EUNSUPPORTED;
 
   const int esize_out = fp8 ? 1 : 2;

@@ -152,6 +152,22 @@ def test_forced_tiles(orc, wpr, nv):
         arn.set_tile(0, 0)
 
 
+@pytest.mark.parametrize("d,tile", [(1024, "wpr1/nv2/rpb4"), (1792, "wpr2/nv2/rpb2"),
+                                    (3584, "wpr4/nv2/rpb1"), (4096, "wpr4/nv2/rpb1"),
+                                    (6656, "wpr8/nv2/rpb1")])
+@pytest.mark.parametrize("fp8", [None, "dynamic", "static"])
+def test_many_rows_automatic_tiles(orc, d, tile, fp8):
+    """With many rows (at least 4 per CU) rows up to 4096 wide take the
+    fewest waves whose lanes hold at most two vectors; wider rows keep
+    eight-wave rows.  Every row of 4 x CUs + 3 rows against the oracle."""
+    import residual_add_rmsnorm_amd as arn
+
+    rows = 4 * torch.cuda.get_device_properties(0).multi_processor_count + 3
+    run_glu(orc, "bf16", _x("bf16", rows, d, seed=60 + d % 89), d, fp8=fp8,
+            s=0.05 if fp8 == "static" else None)
+    assert f"/vec8/{tile}/" in arn.last_plan(), arn.last_plan()
+
+
 @pytest.mark.parametrize("name", ["silu_and_mul_fp8_dynamic_bf16_32768x6656",
                                   "silu_and_mul_fp8_static_bf16_decode_x6656"])
 def test_workloads_sampled(orc, name):
