@@ -367,13 +367,16 @@ std::atomic<int> g_forced_gemm{0};
 // or more: the widest column tile that still gives at least 3/4 of a block
 // per CU.  Wide tiles matter more as M grows: every block reads all of A
 // (M x K), so A's share of the load traffic per block is M / (16 NT) of the
-// weight's.  With one row tile, K is split over as many waves as keep each
-// wave at four or more 128-wide k steps (up to 16); with two or four row
-// tiles the accumulators and operands of a wave fill its registers, and four
-// waves per block do best.
+// weight's.  With one row tile, K is split over eight waves once each keeps
+// four or more 128-wide k steps, else over four (16 waves measured 1-12%
+// slower at K = 8192-16384, most with one column tile: the QKV shard
+// 2304 x 16384 at M = 1 takes 9.1 us with 8 waves, 10.3 with 16); with two
+// or four row tiles the accumulators and operands of a wave fill its
+// registers, and four waves per block do best.
 const GemmCfg* find_gemm(const GemmTable* table, int mt, int nt, int waves);
 
-const GemmCfg* choose_gemm(const GemmTable* table, int mt, int64_t n, int64_t k, int cus) {
+const GemmCfg* choose_gemm(const GemmTable* table, bool pre, int mt, int64_t n, int64_t k,
+                           int cus) {
   const int forced = g_forced_gemm.load(std::memory_order_relaxed);
   auto find = [&](int nt, int waves) { return find_gemm(table, mt, nt, waves); };
   if (forced != 0) return find(forced >> 8, forced & 0xFF);
@@ -387,7 +390,11 @@ const GemmCfg* choose_gemm(const GemmTable* table, int mt, int64_t n, int64_t k,
     nt = 2;
   }
   int waves = 4;
-  if (mt == 1) waves = ksteps >= 64 ? 16 : (ksteps >= 32 ? 8 : 4);
+  if (mt == 1 && ksteps >= 32) waves = 8;
+  // A row-major weight goes through LDS on its way to the operands: with
+  // several column tiles and a long K, more waves hide that (gate_up at
+  // M = 1: 38.2 us with 16 waves, 40.4 with 8).
+  if (mt == 1 && !pre && nt >= 2 && ksteps >= 64) waves = 16;
   return find(nt, waves);
 }
 
@@ -486,7 +493,7 @@ int run_gemm(bool pre, void* c, int64_t ldc, int out_dtype, const uint8_t* a, in
   const GemmTable* table = &ARN_GEMM_TABLE_NAME(0);
   if (out_dtype == ARN_FP16) table = &ARN_GEMM_TABLE_NAME(1);
   const int cus = cu_count();
-  const GemmCfg* cfg = choose_gemm(table, mt, n, k, cus);
+  const GemmCfg* cfg = choose_gemm(table, pre, mt, n, k, cus);
   if (!cfg) return ARN_EUNSUPPORTED;
   const int64_t nsteps = (k + 127) / 128;
 
