@@ -254,8 +254,20 @@ int run(const Request& r) {
   const int vec = choose_vec(r);
   const int64_t nvec = r.hidden / vec;
   const TileTable* table = r.parts ? sum_table_for(r.kind, r.dtype) : table_for(r.kind, r.dtype);
-  const Tile* tile = choose_tile(table, vec, nvec, r.rows, cu_count(), r.nparts >= 4,
-                                 (r.kind & arn::kFused) || r.parts ? 0 : 4);
+  // Compact tiles (see choose_tile): the plain kinds up to four vectors per
+  // lane; the fused dynamic-e4m3 kind, whose second reduction and scale
+  // store add to each row's fixed cost, up to two (65536 rows: 1536, 2560,
+  // 2880 and 3072 wide 12%, 21%, 15% and 11% less time, 3584 5%).
+  int compact = 0;
+  if (!r.parts) {
+    if (!(r.kind & arn::kFused)) {
+      compact = 4;
+    } else if (r.kind == arn::kFusedFp8Dynamic) {
+      compact = 2;
+    }
+  }
+  const Tile* tile =
+      choose_tile(table, vec, nvec, r.rows, cu_count(), r.nparts >= 4, compact);
   if (!tile) return ARN_EUNSUPPORTED;
 
   const int esize_out = fp8 ? 1 : 2;

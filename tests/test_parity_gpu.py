@@ -212,6 +212,22 @@ def test_plain_many_rows_automatic_tiles(orc, hidden, tile, fp8):
     assert f"/vec8/{tile}/" in arn.last_plan(), arn.last_plan()
 
 
+@pytest.mark.parametrize("hidden,tile", [(1024, "wpr1/nv2/rpb4"), (2048, "wpr2/nv2/rpb2"),
+                                         (2880, "wpr4/nv2/rpb1"), (4096, "wpr4/nv2/rpb1"),
+                                         (7168, "wpr8/nv2/rpb1")])
+def test_fused_dynamic_many_rows_automatic_tiles(orc, hidden, tile):
+    """The fused dynamic-e4m3 kind with many rows takes the compact tile up
+    to two vectors per lane (rows up to 4096 wide) and the general rule
+    beyond; every row of 4 x CUs + 5 rows against the oracle."""
+    arn = _arn()
+    rows = 4 * torch.cuda.get_device_properties(0).multi_processor_count + 5
+    x = _random("bf16", rows, hidden, hidden, 70 + hidden % 83)
+    r = _random("bf16", rows, hidden, hidden, 71)
+    w = _random("bf16", 1, hidden, hidden, 72)[0]
+    run_case(orc, dtype="bf16", x=x, res=r, w=w, eps=1e-6, hidden=hidden, fp8="dynamic")
+    assert f"/vec8/{tile}/" in arn.last_plan(), arn.last_plan()
+
+
 @pytest.mark.parametrize("rows", [1, 2, 255, 256, 257, 1025, 4099])
 def test_row_counts(orc, rows):
     x = _random("bf16", rows, 1024, 1024, 7)
