@@ -257,14 +257,15 @@ int run(const Request& r) {
   // Compact tiles (see choose_tile): the plain kinds up to four vectors per
   // lane; the fused dynamic-e4m3 kind, whose second reduction and scale
   // store add to each row's fixed cost, up to two (65536 rows: 1536, 2560,
-  // 2880 and 3072 wide 12%, 21%, 15% and 11% less time, 3584 5%).
+  // 2880 and 3072 wide 12%, 21%, 15% and 11% less time, 3584 5%); the
+  // all-reduce form over two or three parts up to two (4096 wide: 7-8%).
   int compact = 0;
-  if (!r.parts) {
-    if (!(r.kind & arn::kFused)) {
-      compact = 4;
-    } else if (r.kind == arn::kFusedFp8Dynamic) {
-      compact = 2;
-    }
+  if (r.parts) {
+    if (r.nparts < 4) compact = 2;
+  } else if (!(r.kind & arn::kFused)) {
+    compact = 4;
+  } else if (r.kind == arn::kFusedFp8Dynamic) {
+    compact = 2;
   }
   const Tile* tile =
       choose_tile(table, vec, nvec, r.rows, cu_count(), r.nparts >= 4, compact);

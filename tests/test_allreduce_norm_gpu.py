@@ -121,6 +121,21 @@ def test_hidden_sweep(orc, hidden, stride):
     run_case(orc, dtype="bf16", parts=parts, res=res, w=w, eps=1e-5, hidden=hidden)
 
 
+@pytest.mark.parametrize("nparts,hidden,tile", [(2, 4096, "wpr4/nv2/"), (3, 4096, "wpr4/nv2/"),
+                                                (2, 6144, "wpr8/nv2/"), (8, 4096, "wpr8/nv1/")])
+def test_many_rows_automatic_tiles(orc, nparts, hidden, tile):
+    """With many rows, two or three parts take the compact tile up to two
+    vectors per lane; four or more parts keep one vector per lane with more
+    waves.  4 x CUs + 2 rows, every row against the oracle."""
+    rows = 4 * torch.cuda.get_device_properties(0).multi_processor_count + 2
+    parts = [_random("bf16", rows, hidden, hidden, 50 + g, std=nparts ** -0.5)
+             for g in range(nparts)]
+    res = _random("bf16", rows, hidden, hidden, 49)
+    w = _random("bf16", 1, hidden, hidden, 48)[0]
+    plan = run_case(orc, dtype="bf16", parts=parts, res=res, w=w, eps=1e-6, hidden=hidden)
+    assert f"/vec8/{tile}" in plan, plan
+
+
 @pytest.mark.parametrize("rows", [1, 255, 1029])
 def test_row_counts(orc, rows):
     parts = [_random("fp16", rows, 1024, 1024, 30 + g) for g in range(3)]
