@@ -141,25 +141,26 @@ int pow2_ceil(int64_t v) {
 }
 
 // Kernel shape.  A row is split over `wpr` waves so that each lane holds
-// only a few vectors.  Measured on MI355X: with many rows, rows of eight
-// waves (512-thread blocks) holding at most two 128-bit vectors per lane
-// stream best for the fused kinds (about 40 VGPRs, eight waves per SIMD);
-// one-wave rows that keep a whole 8192-wide row in registers run 20-25%
-// slower.  The plain kinds (no residual) move fewer bytes per element, so
-// a row's fixed costs (its barrier and reductions) weigh more and more
-// rows per CU pay: rows of at most four waves with up to four vectors per
-// lane, the fewest waves whose lanes still hold two vectors when the row
-// is narrow, so that no lane slot is wasted where it can be avoided
-// (65536 rows of dynamic e4m3: 2048 wide 35% faster than before, 2880 and
-// 4096 wide 33-40%, 5120 and 6144 wide 16-26%).  With few rows (decode)
-// eight waves per row with up to four vectors per lane finish each row
-// soonest.  SwiGLU (5 bytes per output element with e4m3) follows the plain
-// rule while two vectors per lane cover the row (d <= 4096; 65536 rows of
-// dynamic e4m3: d = 1792 33% less time, 2048 24%, 3584 31%); wider rows,
-// such as one GPU's 6656-wide shard, stream best with eight-wave rows.
-// Among the compiled tiles of the chosen wave count, the one
-// with the fewest per-lane vectors that covers the row (and at least
-// `min_nv`) is taken; failing that, any tile that covers the row.
+// only a few vectors.  Measured on MI355X:
+//  * fused kinds, many rows (at least 4 per CU): rows of eight waves
+//    (512-thread blocks), at most two 128-bit vectors per lane (about 40
+//    VGPRs, eight waves per SIMD); one-wave rows holding a whole 8192-wide
+//    row run 20-25% slower.
+//  * compact tiles (`compact_nv` > 0), many rows: the fewest waves, at most
+//    four, whose lanes hold at most two vectors, then up to `compact_nv`
+//    vectors per lane.  Kinds that move few bytes per element or carry a
+//    large fixed cost per row (barrier, reductions, scale store) gain from
+//    more rows per CU and fewer idle lane slots: the plain kinds (up to
+//    four vectors: 65536 rows of dynamic e4m3 2048-6144 wide take 14-41%
+//    less time than with eight-wave rows), SwiGLU (d <= 4096: 22-31%), the
+//    fused dynamic-e4m3 kind (1536-3584 wide: 5-21%) and the all-reduce
+//    form over two or three parts (4096 wide: 7-8%), up to two vectors.
+//    Rows too wide for that take the rule above.
+//  * few rows (decode): eight waves per row, up to four vectors per lane,
+//    finish each row soonest.
+// Among the compiled tiles of the chosen wave count, the one with the
+// fewest per-lane vectors that covers the row (and at least `min_nv`) is
+// taken; failing that, any tile that covers the row.
 const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t rows, int cus,
                         bool lean = false, int compact_nv = 0) {
   const int forced = g_forced_tile.load(std::memory_order_relaxed);
@@ -254,11 +255,9 @@ int run(const Request& r) {
   const int vec = choose_vec(r);
   const int64_t nvec = r.hidden / vec;
   const TileTable* table = r.parts ? sum_table_for(r.kind, r.dtype) : table_for(r.kind, r.dtype);
-  // Compact tiles (see choose_tile): the plain kinds up to four vectors per
-  // lane; the fused dynamic-e4m3 kind, whose second reduction and scale
-  // store add to each row's fixed cost, up to two (65536 rows: 1536, 2560,
-  // 2880 and 3072 wide 12%, 21%, 15% and 11% less time, 3584 5%); the
-  // all-reduce form over two or three parts up to two (4096 wide: 7-8%).
+  // Compact tiles (choose_tile): plain kinds up to four vectors per lane;
+  // the fused dynamic-e4m3 kind and the all-reduce form over two or three
+  // parts up to two.
   int compact = 0;
   if (r.parts) {
     if (r.nparts < 4) compact = 2;
@@ -339,6 +338,7 @@ int run_glu(int mode, int dtype, void* out, int64_t out_stride, float* scale, co
     }
   }
   const int64_t nvec = d / vec;
+  // Compact tiles up to two vectors per lane (choose_tile).
   const Tile* tile = choose_tile(glu_table_for(mode, dtype), vec, nvec, rows, cu_count(), false, 2);
   if (!tile) return ARN_EUNSUPPORTED;
 
