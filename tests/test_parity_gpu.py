@@ -477,6 +477,35 @@ def test_norm_variance_size(orc, hidden, k, fused, fp8):
         assert_y_close(bits(out), ref["y"], dtype)
 
 
+@pytest.mark.parametrize("hidden,k,fused,fp8,tile", [
+    (5120, 1000, False, None, "wpr4/nv3/rpb1"), (2048, 2047, False, "dynamic", "wpr2/nv2/rpb2"),
+    (2880, 2000, True, "dynamic", "wpr4/nv2/rpb1"), (7168, 4096, True, None, "wpr8/nv2/rpb1")])
+def test_norm_variance_size_many_rows(orc, hidden, k, fused, fp8, tile):
+    """The variance-size override on the tiles many rows get (compact and
+    eight-wave), every row of 4 x CUs + 1 rows against the oracle."""
+    arn = _arn()
+    dtype = "bf16"
+    rows = 4 * torch.cuda.get_device_properties(0).multi_processor_count + 1
+    x = _random(dtype, rows, hidden, hidden, 63)
+    r = _random(dtype, rows, hidden, hidden, 64)
+    w = _random(dtype, 1, hidden, hidden, 65)[0]
+    xd, rd, wd = dev(x, dtype), dev(r, dtype), dev(w, dtype)
+    out = arn.norm(xd, wd, 1e-6, residual=rd if fused else None, variance_size=k, fp8=fp8)
+    torch.cuda.synchronize()
+    assert f"/vec8/{tile}/" in arn.last_plan(), arn.last_plan()
+    mode = O.FP8_DYNAMIC if fp8 else O.FP8_NONE
+    ref = orc.add_rmsnorm(dtype, x, r if fused else None, w, 1e-6, fp8_mode=mode,
+                          variance_size=k)
+    if fused:
+        assert np.array_equal(bits(rd), ref["r16"])
+    if fp8:
+        q, sc = out
+        assert_codes_close(codes(q), ref["q"])
+        assert_scales_close(sc.cpu().numpy(), ref["scales"], dtype)
+    else:
+        assert_y_close(bits(out), ref["y"], dtype)
+
+
 def test_norm_descriptor_matches_entry_points(orc):
     arn = _arn()
     x = _random("fp16", 33, 2048, 2048, 63)
