@@ -212,6 +212,19 @@ def test_plain_many_rows_automatic_tiles(orc, hidden, tile, fp8):
     assert f"/vec8/{tile}/" in arn.last_plan(), arn.last_plan()
 
 
+@pytest.mark.parametrize("hidden,fused,fp8", [(1030, False, "dynamic"), (1028, True, "dynamic"),
+                                              (2050, False, None), (3076, True, None)])
+def test_many_rows_narrow_accesses(orc, hidden, fused, fp8):
+    """Many rows whose width allows only 4- or 2-element accesses (the
+    compact rule looks among those tiles, else the general rule); every row
+    against the oracle."""
+    rows = 4 * torch.cuda.get_device_properties(0).multi_processor_count + 7
+    x = _random("bf16", rows, hidden, hidden, 80)
+    r = _random("bf16", rows, hidden, hidden, 81) if fused else None
+    w = _random("bf16", 1, hidden, hidden, 82)[0]
+    run_case(orc, dtype="bf16", x=x, res=r, w=w, eps=1e-6, hidden=hidden, fp8=fp8)
+
+
 @pytest.mark.parametrize("hidden,tile", [(1024, "wpr1/nv2/rpb4"), (2048, "wpr2/nv2/rpb2"),
                                          (2880, "wpr4/nv2/rpb1"), (4096, "wpr4/nv2/rpb1"),
                                          (7168, "wpr8/nv2/rpb1")])
