@@ -577,13 +577,18 @@ def bench_gemm(name: str, steps: int, warmup: int, only_m: int | None = None,
         torch.cuda.empty_cache()
     best = max([v for lay in layouts.values() for v in lay.values()],
                key=lambda v: v["GB_per_s"])
+    # The roofline entry is the decode case: one activation row, pre-shuffled
+    # weight (the configuration the committed counters cover); the best line
+    # over every row count and layout is reported beside it.
+    head = layouts["preshuffled"].get("1", best)
     return {"workload": name, "n": g.n, "k": g.k, "weight_copies": sets,
             "empty_kernel_launch": launch_floor(),
             "per_m": layouts["preshuffled"], "per_m_splitk": layouts["preshuffled_ws"],
             "per_m_rowmajor": layouts["rowmajor"],
-            "roofline": {"bound": "hbm", "achieved": best["GB_per_s"], "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(best["GB_per_s"] / PEAK_HBM_GBS, 4),
-                         "traffic": best["traffic"], "plan": best["plan"]}}
+            "roofline": {"bound": "hbm", "achieved": head["GB_per_s"], "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(head["GB_per_s"] / PEAK_HBM_GBS, 4),
+                         "traffic": head["traffic"], "plan": head["plan"],
+                         "best_GB_per_s": best["GB_per_s"], "best_plan": best["plan"]}}
 
 
 def main() -> int:
