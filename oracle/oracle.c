@@ -38,11 +38,8 @@
  *   - Static FP8: the caller passes the dequant scale s; q = E(y / s).
  *   - Dynamic FP8: amax = max_j |y_j|, scale = fp32(amax / 448) stored,
  *     q = E(y / scale); a row with amax == 0 gets scale 0 and zero codes.
- *   - The FP8 rounding decision is taken on the quotient rounded to fp32,
- *     the precision the GPU kernel decides in.  Because fp32 carries at
- *     least 2*4+2 bits, rounding first to fp32 and then to e4m3 gives the
- *     same code as rounding the exact quotient (the double-rounding
- *     theorem), so this costs the definition nothing.
+ *   - The e4m3 code is chosen from the quotient y / s as fp64 computes it,
+ *     with no narrower rounding in between: E rounds that value itself.
  */
 #include "oracle.h"
 
@@ -330,8 +327,7 @@ static void quant_static_row(int64_t hidden, const double *y, float s, uint8_t *
 {
     int64_t j;
     for (j = 0; j < hidden; j++) {
-        float quotient = (float)(y[j] / (double)s);
-        q[j] = orc_e4m3_encode((double)quotient);
+        q[j] = orc_e4m3_encode(y[j] / (double)s);
     }
 }
 
@@ -358,8 +354,7 @@ static float quant_dynamic_row(int64_t hidden, const double *y, uint8_t *q)
         if (amax == 0.0) {
             q[j] = 0x00;
         } else {
-            float quotient = (float)(y[j] / (double)scale);
-            q[j] = orc_e4m3_encode((double)quotient);
+            q[j] = orc_e4m3_encode(y[j] / (double)scale);
         }
     }
     return scale;
@@ -531,7 +526,7 @@ int orc_silu_and_mul(int dtype, int64_t rows, int64_t d,
 int orc_fp8_gemm(int64_t m, int64_t n, int64_t k,
                  const uint8_t *a, int64_t lda, const float *sa, int a_per_row,
                  const uint8_t *b, int64_t ldb, const float *sb, int b_per_row,
-                 int out_dtype, double *c_out, uint16_t *c16_out, double *abs_out)
+                 int out_dtype, double *c_out, uint16_t *c16_out)
 {
     int64_t i, j, t;
 
@@ -544,11 +539,9 @@ int orc_fp8_gemm(int64_t m, int64_t n, int64_t k,
         for (j = 0; j < n; j++) {
             double scale_b = (double)(b_per_row ? sb[j] : sb[0]);
             double sum = 0.0;
-            double sum_abs = 0.0;
             for (t = 0; t < k; t++) {
                 double p = orc_e4m3_decode(a[i * lda + t]) * orc_e4m3_decode(b[j * ldb + t]);
                 sum += p;
-                sum_abs += fabs(p);
             }
             if (c_out) {
                 c_out[i * n + j] = scale_a * scale_b * sum;
@@ -556,48 +549,6 @@ int orc_fp8_gemm(int64_t m, int64_t n, int64_t k,
             if (c16_out) {
                 c16_out[i * n + j] = orc_encode16(out_dtype, scale_a * scale_b * sum);
             }
-            if (abs_out) {
-                abs_out[i * n + j] = fabs(scale_a * scale_b) * sum_abs;
-            }
-        }
-    }
-    return 0;
-}
-
-/* Error-bound helper for the GEMM tests (not part of the operation): for
- * each output, the sum over 128-wide k steps (t = 128 s ... 128 s + 127) of
- * the largest |product| in the step, times |sa sb|.  A matrix unit that
- * aligns the 128 products of one step to the largest of them and keeps a
- * fixed number of bits below it loses at most a fixed fraction of this. */
-int orc_fp8_gemm_stepmax(int64_t m, int64_t n, int64_t k,
-                         const uint8_t *a, int64_t lda, const float *sa, int a_per_row,
-                         const uint8_t *b, int64_t ldb, const float *sb, int b_per_row,
-                         double *stepmax_out)
-{
-    int64_t row, col, kk;
-
-    if (m < 0 || n < 0 || k <= 0 || a == NULL || b == NULL || sa == NULL || sb == NULL ||
-        lda < k || ldb < k || stepmax_out == NULL) {
-        return -1;
-    }
-    for (row = 0; row < m; row++) {
-        const double row_scale = (double)(a_per_row ? sa[row] : sa[0]);
-        for (col = 0; col < n; col++) {
-            const double col_scale = (double)(b_per_row ? sb[col] : sb[0]);
-            double total = 0.0;
-            double largest = 0.0;
-            for (kk = 0; kk < k; kk++) {
-                const double mag = fabs(orc_e4m3_decode(a[row * lda + kk]) *
-                                        orc_e4m3_decode(b[col * ldb + kk]));
-                if (mag > largest) {
-                    largest = mag;
-                }
-                if (kk % 128 == 127 || kk == k - 1) {   /* end of a 128-wide step */
-                    total += largest;
-                    largest = 0.0;
-                }
-            }
-            stepmax_out[row * n + col] = fabs(row_scale * col_scale) * total;
         }
     }
     return 0;

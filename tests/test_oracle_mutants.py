@@ -31,7 +31,12 @@ MUTANTS = {
     "no_fp8_saturation": ("if (a >= 448.0) {", "if (a >= 480.0) {"),
     "fp8_subnormal_edge": ("if (e < -6) {", "if (e < -7) {"),
     "fnuz_dynamic_max": ("scale = (float)(amax / 448.0);", "scale = (float)(amax / 240.0);"),
-    "static_scale_multiplied": ("(float)(y[j] / (double)s)", "(float)(y[j] * (double)s)"),
+    "static_scale_multiplied": ("orc_e4m3_encode(y[j] / (double)s)",
+                                "orc_e4m3_encode(y[j] * (double)s)"),
+    "static_quotient_rounded_to_fp32": ("orc_e4m3_encode(y[j] / (double)s)",
+                                        "orc_e4m3_encode((double)(float)(y[j] / (double)s))"),
+    "dynamic_quotient_rounded_to_fp32": ("orc_e4m3_encode(y[j] / (double)scale)",
+                                         "orc_e4m3_encode((double)(float)(y[j] / (double)scale))"),
     "row_stride_ignored": ("const uint16_t *xi = x + i * x_stride;",
                            "const uint16_t *xi = x + i * hidden;"),
     "fp16_bias": ("f.bias = 15;", "f.bias = 16;"),

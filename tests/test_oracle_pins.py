@@ -7,8 +7,9 @@ torch float8_e4m3fn), the e4m3 bit identity printed in "MI210 LLM Stack"
 (Zhang & Sennrich 2019, eq. 4), or invariants that definition implies.
 """
 import math
-
 import os
+from decimal import Decimal, localcontext
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -453,12 +454,52 @@ def test_fp8_dynamic_invariants(orc):
         assert r["scales"][i] == np.float32(amax / 448)
         k = int(np.argmax(np.abs(y)))
         assert r["q"][i, k] & 0x7F == 0x7E  # the largest |y| maps to 448
-        # RNE: |q*scale - y| <= half the e4m3 spacing at |y/scale|, plus the
-        # fp32 rounding of the quotient.
+        # RNE: |q*scale - y| <= half the e4m3 spacing at |y/scale| (the
+        # slack covers only the fp64 rounding of the quotient itself).
         v = y / r["scales"][i]
         spacing = np.where(np.abs(v) < 2.0**-6, 2.0**-9,
                            np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(v), 1e-300))).astype(int) - 3))
-        assert np.all(np.abs(dec[i] - v) <= spacing / 2 * (1 + 2.0**-20))
+        assert np.all(np.abs(dec[i] - v) <= spacing / 2 * (1 + 2.0**-40))
+
+
+def test_fp8_static_code_decided_on_the_exact_quotient(orc):
+    """x = 1, w = 1 and eps = 0 give y = 1 exactly, so the code is E(1 / s).
+    With the fp32 scale s = 0.84210527, 1 / s = 1.18749999115..., just below
+    the e4m3 tie 1.1875 between 1.125 (0x39) and 1.25 (0x3A): the nearest
+    code is 0x39.  The same quotient rounded to fp32 first is the tie itself
+    and would go to the even code 0x3A, so this pins the decision to the
+    unrounded quotient."""
+    s = np.float32(0.84210527)
+    q = Fraction(1) / Fraction(float(s))
+    tie = Fraction(19, 16)
+    assert tie - Fraction(1, 2**24) < q < tie          # inside an fp32 half-ulp
+    assert np.float32(1.0) / s == np.float32(1.1875)   # fp32 lands on the tie
+    for dtype in ("bf16", "fp16"):
+        r = orc.add_rmsnorm(dtype, _bits(np.ones((2, 8)), dtype), None,
+                            _bits(np.ones(8), dtype), 0.0,
+                            fp8_mode=O.FP8_STATIC, static_scale=float(s))
+        assert np.all(r["y"] == 1.0)
+        assert np.all(r["q"] == 0x39), r["q"]
+
+
+def test_fp8_dynamic_code_decided_on_the_exact_quotient(orc):
+    """Row (448, 17), eps = 0: y = r / rms, amax = 448 / rms and the stored
+    scale is fp32(amax / 448) = fp32(1 / rms).  The second code is
+    E(17 (1 / rms) / scale): computed to 60 digits the quotient lies 1.9e-7
+    above the tie 17 between 16 (0x58) and 18 (0x59), so the nearest code
+    is 0x59.  Rounded to fp32 first it would be 17 itself and go to the
+    even 0x58."""
+    with localcontext() as ctx:
+        ctx.prec = 60
+        rms = ((Decimal(448) ** 2 + Decimal(17) ** 2) / 2).sqrt()
+        scale = np.float32(float(1 / rms))
+        q = Decimal(17) / rms / Decimal(float(scale))
+        assert Decimal(0) < q - 17 < Decimal(2.0**-20)  # above the tie, inside an fp32 half-ulp
+        assert np.float32(float(q)) == np.float32(17.0)
+    r = orc.add_rmsnorm("bf16", _bits([[448.0, 17.0]]), None, None, 0.0,
+                        fp8_mode=O.FP8_DYNAMIC)
+    assert r["scales"][0] == scale
+    assert r["q"][0, 0] == 0x7E and r["q"][0, 1] == 0x59, r["q"]
 
 
 def test_fp8_dynamic_zero_row_only(orc):
