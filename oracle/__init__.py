@@ -103,15 +103,9 @@ def bind(lib_path: str) -> ctypes.CDLL:
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         u8p, ctypes.c_int64, f32p, ctypes.c_int,
         u8p, ctypes.c_int64, f32p, ctypes.c_int,
-        ctypes.c_int, f64p, u16p, f64p,
+        ctypes.c_int, f64p, u16p,
     ]
     lib.orc_fp8_gemm.restype = ctypes.c_int
-    lib.orc_fp8_gemm_stepmax.argtypes = [
-        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-        u8p, ctypes.c_int64, f32p, ctypes.c_int,
-        u8p, ctypes.c_int64, f32p, ctypes.c_int, f64p,
-    ]
-    lib.orc_fp8_gemm_stepmax.restype = ctypes.c_int
     return lib
 
 
@@ -299,10 +293,7 @@ class Oracle:
     def fp8_gemm(self, a, sa, b, sb, k=None, out_dtype="bf16"):
         """C = diag(sa) dec(A) dec(B)^T diag(sb) for uint8 code arrays
         A (M x lda) and B (N x ldb); sa / sb hold M / N per-row scales or one
-        per-tensor scale.  Returns dict c (float64), c16, abs (sum of
-        |products| times |scales|) and stepmax (sum over 128-wide k steps of
-        the largest |product|, times |scales|), the last two for error
-        bounds."""
+        per-tensor scale.  Returns dict c (float64) and c16."""
         a = np.ascontiguousarray(a, dtype=np.uint8)
         b = np.ascontiguousarray(b, dtype=np.uint8)
         sa = np.ascontiguousarray(np.atleast_1d(sa), dtype=np.float32)
@@ -312,23 +303,14 @@ class Oracle:
         k = min(lda, ldb) if k is None else int(k)
         c = np.empty((m, n), np.float64)
         c16 = np.empty((m, n), np.uint16)
-        ab = np.empty((m, n), np.float64)
         rc = self.c.orc_fp8_gemm(m, n, k, _ptr(a, ctypes.c_uint8), lda, _ptr(sa, ctypes.c_float),
                                  int(sa.size > 1),
                                  _ptr(b, ctypes.c_uint8), ldb, _ptr(sb, ctypes.c_float),
                                  int(sb.size > 1), DTYPES[out_dtype],
-                                 _ptr(c, ctypes.c_double), _ptr(c16, ctypes.c_uint16),
-                                 _ptr(ab, ctypes.c_double))
+                                 _ptr(c, ctypes.c_double), _ptr(c16, ctypes.c_uint16))
         if rc != 0:
             raise ValueError("oracle rejected its arguments")
-        sm = np.empty((m, n), np.float64)
-        rc = self.c.orc_fp8_gemm_stepmax(m, n, k, _ptr(a, ctypes.c_uint8), lda,
-                                         _ptr(sa, ctypes.c_float), int(sa.size > 1),
-                                         _ptr(b, ctypes.c_uint8), ldb, _ptr(sb, ctypes.c_float),
-                                         int(sb.size > 1), _ptr(sm, ctypes.c_double))
-        if rc != 0:
-            raise ValueError("oracle rejected its arguments")
-        return {"c": c, "c16": c16, "abs": ab, "stepmax": sm}
+        return {"c": c, "c16": c16}
 
 
 def oracle() -> Oracle:

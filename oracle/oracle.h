@@ -119,20 +119,12 @@ int orc_silu_and_mul(int dtype, int64_t rows, int64_t d,
  * weight of a linear layer stored out-feature major), sa: M per-row scales
  * or 1 per-tensor scale (a_per_row = 0), sb likewise over N.  The sum runs
  * k = 0..K-1 in fp64.  Outputs (dense, row stride N; may be NULL): c_out in
- * fp64, c16_out rounded to the 16-bit dtype, and abs_out = the same sum of
- * |products| (for error bounds).
+ * fp64 and c16_out rounded to the 16-bit dtype.
  */
 int orc_fp8_gemm(int64_t m, int64_t n, int64_t k,
                  const uint8_t *a, int64_t lda, const float *sa, int a_per_row,
                  const uint8_t *b, int64_t ldb, const float *sb, int b_per_row,
-                 int out_dtype, double *c_out, uint16_t *c16_out, double *abs_out);
-
-/* Error-bound helper for the GEMM tests: per output, the sum over 128-wide
- * k steps of the largest |product| in the step, times |sa sb|. */
-int orc_fp8_gemm_stepmax(int64_t m, int64_t n, int64_t k,
-                         const uint8_t *a, int64_t lda, const float *sa, int a_per_row,
-                         const uint8_t *b, int64_t ldb, const float *sb, int b_per_row,
-                         double *stepmax_out);
+                 int out_dtype, double *c_out, uint16_t *c16_out);
 
 #ifdef __cplusplus
 }

@@ -143,7 +143,7 @@ int main(void) {
   }
   EXPECT(fabs(orc_silu(0.0)) == 0.0, "silu(0)");
 
-  /* GEMM and its error-bound helper: ragged K, padded strides, scale modes */
+  /* GEMM: ragged K, padded strides, scale modes */
   const int64_t gshapes[][3] = {{1, 1, 16}, {3, 17, 48}, {5, 40, 300}, {2, 9, 1040}};
   for (int s = 0; s < 4; ++s) {
     const int64_t m = gshapes[s][0], n = gshapes[s][1], k = gshapes[s][2];
@@ -152,19 +152,15 @@ int main(void) {
     float *sa = malloc((size_t)m * sizeof(float)), *sb = malloc((size_t)n * sizeof(float));
     for (int64_t i = 0; i < m; ++i) sa[i] = (float)(0.01 + uniform());
     for (int64_t j = 0; j < n; ++j) sb[j] = (float)(0.01 + uniform());
-    double *c = malloc((size_t)(m * n) * sizeof(double)), *ab = malloc((size_t)(m * n) * sizeof(double));
-    double *sm = malloc((size_t)(m * n) * sizeof(double));
+    double *c = malloc((size_t)(m * n) * sizeof(double));
     uint16_t *c16 = malloc((size_t)(m * n) * 2);
     for (int per = 0; per < 2; ++per) {
-      EXPECT(orc_fp8_gemm(m, n, k, a, lda, sa, per, b, ldb, sb, per, s & 1, c, c16, ab) == 0,
+      EXPECT(orc_fp8_gemm(m, n, k, a, lda, sa, per, b, ldb, sb, per, s & 1, c, c16) == 0,
              "orc_fp8_gemm");
-      EXPECT(orc_fp8_gemm_stepmax(m, n, k, a, lda, sa, per, b, ldb, sb, per, sm) == 0,
-             "orc_fp8_gemm_stepmax");
-      for (int64_t i = 0; i < m * n; ++i) EXPECT(sm[i] <= ab[i] + 1e-300, "stepmax <= sum |a b|");
     }
-    EXPECT(orc_fp8_gemm(m, n, k, a, k - 1, sa, 1, b, ldb, sb, 1, 0, c, c16, ab) == -1,
+    EXPECT(orc_fp8_gemm(m, n, k, a, k - 1, sa, 1, b, ldb, sb, 1, 0, c, c16) == -1,
            "lda < k refused");
-    free(a); free(b); free(sa); free(sb); free(c); free(ab); free(sm); free(c16);
+    free(a); free(b); free(sa); free(sb); free(c); free(c16);
   }
 
   if (failures) {

@@ -13,7 +13,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from tests._helpers import (assert_codes_close, assert_scales_close, assert_y_close, gemm_tol,
+from tests._helpers import (assert_codes_close, assert_scales_close, assert_y_close, gemm_ref, gemm_tol,
                             static_scale, values16)
 from tests.c_abi import build as client_build
 
@@ -118,7 +118,7 @@ def test_gemm_from_c(client, orc, tmp_path, layout):
             fh.write(np.ascontiguousarray(arr).tobytes())
     _run(client, ["gemm", layout, m, n, k, fin, fout], tmp_path)
     c = np.frombuffer(open(fout, "rb").read(), np.uint16).reshape(m, n)
-    ref = orc.fp8_gemm(a, sa, b, sb)
+    ref = gemm_ref(orc, a, sa, b, sb)
     got = values16(c, "bf16")
     tol = gemm_tol(ref, k)
     assert np.all(np.abs(got - ref["c"]) <= tol)

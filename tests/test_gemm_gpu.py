@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle as O
-from tests._helpers import bits, dev, gemm_tol, values16
+from tests._helpers import bits, dev, gemm_ref, gemm_tol, values16
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +54,7 @@ def check(orc, m, n, k, out="bf16", per_row=(True, True), seed=0, lda=None, ldb=
         arn.fp8_gemm(ad, sad, bd, sbd, out=c[:m], workspace=workspace)
         assert torch.equal(c[:m], first), "repeated call differs"
     torch.cuda.synchronize()
-    ref = orc.fp8_gemm(a, sa if per_row[0] else sa[0], b, sb if per_row[1] else sb[0], k=k,
+    ref = gemm_ref(orc, a, sa if per_row[0] else sa[0], b, sb if per_row[1] else sb[0], k=k,
                        out_dtype=out)
     got = values16(bits(c[:m]), out)
     tol = gemm_tol(ref, k, out)
@@ -153,7 +153,7 @@ def test_preshuffle_unaligned_weight(orc):
     with pytest.raises(arn.ArnError):
         arn.fp8_gemm(ad, sad, bd, sbd)
     c = arn.fp8_gemm(ad, sad, arn.fp8_weight_preshuffle(bd), sbd)
-    ref = orc.fp8_gemm(a, sa, np.ascontiguousarray(bv[:, :k]), sb)
+    ref = gemm_ref(orc, a, sa, np.ascontiguousarray(bv[:, :k]), sb)
     got = values16(bits(c), "bf16")
     tol = gemm_tol(ref, k)
     assert np.all(np.abs(got - ref["c"]) <= tol)
@@ -180,7 +180,7 @@ def test_nan_codes_propagate(orc, pre):
         bd = arn.fp8_weight_preshuffle(bd)
     ad, sad, sbd = (torch.from_numpy(x).cuda() for x in (a, sa, sb))
     c = arn.fp8_gemm(ad, sad, bd, sbd).float().cpu().numpy()
-    ref = orc.fp8_gemm(a, sa, b, sb)
+    ref = gemm_ref(orc, a, sa, b, sb)
     nan_ref = np.isnan(ref["c"])
     assert nan_ref[2].all() and nan_ref[:, 41].all() and nan_ref.sum() == n + m - 1
     assert np.array_equal(np.isnan(c), nan_ref)
@@ -242,7 +242,7 @@ def test_swiglu_codes_feed_gemm(orc):
     # the GEMM is checked on the codes the GPU produced (those match the
     # oracle's within one step, checked by the SwiGLU tests)
     assert np.mean(qa == ref_g["q"]) > 0.99
-    ref = orc.fp8_gemm(qa, sqa, b, sb)
+    ref = gemm_ref(orc, qa, sqa, b, sb)
     got = values16(bits(c), "bf16")
     tol = gemm_tol(ref, d)
     assert np.all(np.abs(got - ref["c"]) <= tol)
@@ -269,7 +269,7 @@ def test_full_size(orc, name):
     layouts = {"rowmajor": bd, "preshuffled": arn.fp8_weight_preshuffle(bd)}
     for m in (1, 64):
         a, sa = d["a"][:m], d["scale_a"][:m]
-        ref = orc.fp8_gemm(a, sa, np.ascontiguousarray(d["b"][cols]), d["scale_b"][cols])
+        ref = gemm_ref(orc, a, sa, np.ascontiguousarray(d["b"][cols]), d["scale_b"][cols])
         tol = gemm_tol(ref, g.k)
         ad, sad = torch.from_numpy(a).cuda(), torch.from_numpy(sa).cuda()
         for layout, b in layouts.items():
@@ -303,7 +303,7 @@ def test_preshuffled_panels(orc):
     cols = np.unique(np.concatenate([np.linspace(0, n - 1, 24).astype(np.int64),
                                      [0, 15, 16, 4095, 8175, 8176, 8191, 8192, 8207, 8208,
                                       8223, 8224, 8235]]))
-    ref = orc.fp8_gemm(a, sa, b[torch.from_numpy(cols).cuda()].cpu().numpy(), sb[cols])
+    ref = gemm_ref(orc, a, sa, b[torch.from_numpy(cols).cuda()].cpu().numpy(), sb[cols])
     tol = gemm_tol(ref, k)
     pre = arn.fp8_weight_preshuffle(b)
     del b
@@ -344,7 +344,7 @@ def test_rowmajor_weight_past_2gib(orc):
     cols = np.unique(np.concatenate([np.linspace(0, n - 1, 24).astype(np.int64),
                                      [0, 15, 16, 16367, 16368, 16383, 16384, 16385, 16399,
                                       16400, 16495, 16496, 16499]]))
-    ref = orc.fp8_gemm(a, sa, b[torch.from_numpy(cols).cuda()].cpu().numpy(), sb[cols])
+    ref = gemm_ref(orc, a, sa, b[torch.from_numpy(cols).cuda()].cpu().numpy(), sb[cols])
     tol = gemm_tol(ref, k)
     ad, sad, sbd = (torch.from_numpy(v).cuda() for v in (a, sa, sb))
     ws = arn.fp8_gemm_workspace(m, n, k)
@@ -455,3 +455,135 @@ def test_split_k_workspace_checks():
     with pytest.raises(arn.ArnError) as e:
         arn.fp8_gemm(a, s, b, s, workspace=big[16:])       # not 256-byte aligned
     assert e.value.status == 1
+
+
+# ---------------------------------------------------------------------------
+# Exact cases: zero tolerance
+# ---------------------------------------------------------------------------
+
+def _exact_codes(rng, rows, cols):
+    """Codes of the values k/4 with |k| <= 16, all exact e4m3.  Products are
+    multiples of 2^-4 no larger than 16, so the sum of any 128-wide k step
+    needs 8 bits below its largest product, and a whole row of K <= 16384
+    stays within 2^18 on a 2^-4 grid (22 bits): every partial sum the matrix
+    unit, the waves and the splits form is exact in fp32."""
+    v = rng.integers(-16, 17, (rows, cols)).astype(np.float32) / 4
+    return torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def exact_data(m, n, k, per_row=(True, True), seed=0):
+    rng = np.random.default_rng(1000 + seed)
+    a = _exact_codes(rng, m, k)
+    b = _exact_codes(rng, n, k)
+    sa = np.ldexp(1.0, rng.integers(-3, 4, m if per_row[0] else 1)).astype(np.float32)
+    sb = np.ldexp(1.0, rng.integers(-3, 4, n if per_row[1] else 1)).astype(np.float32)
+    return a, sa, b, sb
+
+
+def check_exact(orc, m, n, k, pre, out="bf16", per_row=(True, True), seed=0, workspace=None,
+                cols=None, data=None):
+    """c16 of the GPU equal to the oracle's bit for bit (power-of-two scales
+    keep the scaled result exact too, so both sides round the same value
+    once).  `cols` limits the comparison to sampled output columns."""
+    import residual_add_rmsnorm_amd as arn
+
+    assert k <= 16384
+    a, sa, b, sb = data if data is not None else exact_data(m, n, k, per_row, seed)
+    a = a[:m]
+    sa = sa[:m] if sa.size > 1 else sa
+    bd = torch.from_numpy(b).cuda()
+    if pre:
+        bd = arn.fp8_weight_preshuffle(bd)
+    ad, sad, sbd = (torch.from_numpy(np.ascontiguousarray(v)).cuda() for v in (a, sa, sb))
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[out]
+    c = torch.empty((m, n), dtype=dt, device="cuda")
+    arn.fp8_gemm(ad, sad, bd, sbd, out=c, workspace=workspace)
+    torch.cuda.synchronize()
+    del bd
+    got = bits(c)
+    if cols is not None:
+        b = np.ascontiguousarray(b[cols])
+        sb = sb[cols] if sb.size > 1 else sb
+        got = got[:, cols]
+    ref = orc.fp8_gemm(a, sa if sa.size > 1 else sa[0], b, sb if sb.size > 1 else sb[0], k=k,
+                       out_dtype=out)
+    bad = np.flatnonzero(got != ref["c16"])
+    assert bad.size == 0, (f"{bad.size} outputs differ; first at {np.unravel_index(bad[0], got.shape)}: "
+                           f"gpu {got.ravel()[bad[0]]:#06x} ref {ref['c16'].ravel()[bad[0]]:#06x} "
+                           f"({arn.last_plan()})")
+    return arn.last_plan()
+
+
+@LAYOUTS
+@pytest.mark.parametrize("m,n,k", [(1, 200, 1024), (2, 70, 208), (8, 2304, 16384),
+                                   (16, 517, 2048), (17, 1000, 4096), (33, 300, 640),
+                                   (64, 2304, 2064), (1, 13312, 512)])
+def test_gemm_exact_auto(orc, m, n, k, pre):
+    check_exact(orc, m, n, k, pre, seed=m + n + k)
+
+
+@LAYOUTS
+@pytest.mark.parametrize("per_row", [(False, False), (True, False), (False, True)])
+def test_gemm_exact_scale_modes_fp16(orc, per_row, pre):
+    check_exact(orc, 5, 300, 640, pre, out="fp16", per_row=per_row, seed=7)
+
+
+@pytest.mark.parametrize("cfg", [(1, 4), (1, 8), (1, 16), (2, 4), (2, 8), (2, 16), (4, 4),
+                                 (4, 8), (4, 16)])
+@pytest.mark.parametrize("m", [3, 20, 40])
+def test_gemm_exact_forced_configs(orc, m, cfg):
+    """Every compiled block shape of each row tiling, both layouts."""
+    import residual_add_rmsnorm_amd as arn
+
+    mt = 1 if m <= 16 else (2 if m <= 32 else 4)
+    arn.set_gemm_config(*cfg)
+    try:
+        for pre in (False, True):
+            try:
+                plan = check_exact(orc, m, 330, 1296, pre, seed=m + cfg[0] + cfg[1])
+            except arn.ArnError as e:
+                assert e.status == 2   # shape not compiled for this row tiling
+                continue
+            assert f"mt{mt}/nt{cfg[0]}/waves{cfg[1]}/" in plan
+    finally:
+        arn.set_gemm_config(0, 0)
+
+
+@LAYOUTS
+@pytest.mark.parametrize("splits", [2, 3, 4, 8])
+@pytest.mark.parametrize("m,n,k", [(1, 2304, 16384), (5, 300, 1040), (17, 130, 4096),
+                                   (64, 1000, 2048)])
+def test_gemm_exact_split_k(orc, m, n, k, splits, pre):
+    import residual_add_rmsnorm_amd as arn
+
+    ws = arn.fp8_gemm_workspace(m, n, k)
+    arn.set_gemm_splits(splits)
+    try:
+        plan = check_exact(orc, m, n, k, pre, seed=splits + m, workspace=ws)
+    finally:
+        arn.set_gemm_splits(0)
+    assert "/splits1/" not in plan, plan
+
+
+@pytest.mark.parametrize("name", ["fp8_gemm_gate_up_13312x16384", "fp8_gemm_down_16384x6656",
+                                  "fp8_gemm_qkv_2304x16384", "fp8_gemm_o_16384x2048"])
+def test_gemm_exact_full_size(orc, name):
+    """The benchmark's shapes in its launch configuration (automatic block
+    shape; the QKV shard also with a split-K workspace), both layouts, at
+    M = 1 and 64, sampled output columns compared bit for bit."""
+    import residual_add_rmsnorm_amd as arn
+    import workloads as W
+
+    g = W.GEMMS[name]
+    print(f"\n[exact full-size] {name}", flush=True)
+    cols = np.unique(np.concatenate([np.linspace(0, g.n - 1, 96).astype(np.int64),
+                                     [0, 15, 16, 63, 64, g.n // 2, g.n - 17, g.n - 16,
+                                      g.n - 1]]))
+    data = exact_data(64, g.n, g.k, seed=len(name))
+    for m in (1, 64):
+        for pre in (False, True):
+            check_exact(orc, m, g.n, g.k, pre, cols=cols, data=data)
+    if name == "fp8_gemm_qkv_2304x16384":
+        ws = arn.fp8_gemm_workspace(64, g.n, g.k)
+        plan = check_exact(orc, 64, g.n, g.k, True, cols=cols, workspace=ws, data=data)
+        assert "/splits1/" not in plan, plan

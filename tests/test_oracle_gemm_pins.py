@@ -26,7 +26,6 @@ def test_small_integers_exact(orc):
     b_int = rng.integers(-8, 9, (7, 64))
     r = orc.fp8_gemm(_codes(a_int), 1.0, _codes(b_int), 1.0)
     assert np.array_equal(r["c"], (a_int @ b_int.T).astype(np.float64))
-    assert np.array_equal(r["abs"], (np.abs(a_int) @ np.abs(b_int).T).astype(np.float64))
 
 
 def test_random_codes_match_numpy(orc):
@@ -74,21 +73,3 @@ def test_c16_is_rne_of_c(orc):
     back = torch.from_numpy(r["c16"].view(np.int16).copy()).view(torch.bfloat16).double().numpy()
     assert np.all(np.abs(back - r["c"]) <= np.abs(r["c"]) * 2.0**-8)
     assert np.mean(r["c16"] == ref) > 0.99
-
-
-def test_stepmax_matches_numpy(orc):
-    """The error-bound helper: per output, the sum over 128-wide k steps of
-    the largest |product| (the last step may be partial), times |sa sb|."""
-    rng = np.random.default_rng(12)
-    m, n, k = 3, 5, 300
-    a = _codes(np.clip(rng.standard_normal((m, k)) * 8, -448, 448))
-    b = _codes(np.clip(rng.standard_normal((n, k)) * 2, -448, 448))
-    sa = rng.uniform(0.5, 2, m).astype(np.float32)
-    sb = np.array([0.25], np.float32)
-    got = orc.fp8_gemm(a, sa, b, sb)["stepmax"]
-    da, db = _dec(a), _dec(b)
-    for i in range(m):
-        for j in range(n):
-            p = np.abs(da[i] * db[j])
-            want = sum(p[s:s + 128].max() for s in range(0, k, 128)) * sa[i] * 0.25
-            assert got[i, j] == pytest.approx(want, rel=1e-15)

@@ -12,7 +12,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from tests._helpers import assert_codes_close, assert_y_close, bits, codes, dev
+from tests._helpers import assert_codes_close, assert_y_close, bits, codes, dev, gemm_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -117,7 +117,7 @@ def test_gemm_non_default_stream(orc, split):
         c = arn.fp8_gemm(ad, sad, bw, sbd, workspace=ws)
     s.synchronize()
     assert ("splits1" not in arn.last_plan()) == split
-    ref = orc.fp8_gemm(a, sa, b, sb)
+    ref = gemm_ref(orc, a, sa, b, sb)
     assert np.all(np.abs(values16(bits(c), "bf16") - ref["c"]) <= _gemm_tol(ref, k))
 
 
