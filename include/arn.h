@@ -28,8 +28,9 @@
  * ---------------------------------------
  *  - Pointers are DEVICE pointers owned by the caller (hipMalloc, or a
  *    framework's allocator).  The library allocates nothing and keeps no
- *    state across calls other than a per-device cache of the CU count and
- *    the settings of the tuning aids at the end of this file.
+ *    state across calls other than a lazily filled, thread-safe per-device
+ *    cache of the CU count.  (The test and tuning aids of arn_tuning.h keep
+ *    per-thread settings that change only the calling thread's own calls.)
  *  - Layout: row-major, element stride 1, row stride given per tensor in
  *    ELEMENTS of that tensor (one e4m3 code = one element).  stride >= hidden.
  *    Elements [hidden, stride) of a row are neither read nor written.
@@ -315,35 +316,6 @@ const char *arn_status_str(int status);
 
 /* ARN_ABI_VERSION of the loaded library. */
 int arn_abi_version(void);
-
-/*
- * Tuning and test aids (not needed for normal use).
- *
- * arn_set_tile forces the kernel shape of later calls from any thread:
- * waves_per_row (1, 2, 4, 8, 16) 64-lane waves share one row, and each lane
- * keeps up to vec_per_lane vectors of the row in registers.  A call whose
- * shape the forced tile cannot serve returns ARN_EUNSUPPORTED.  (0, 0)
- * restores automatic selection.  Returns ARN_EINVAL for a tile that is not
- * compiled.
- *
- * arn_last_plan copies into buf (size len, always NUL-terminated when
- * len > 0) a description of the kernel the calling thread's last successful
- * launch used, e.g. "fused_add/bf16/vec8/wpr1/nv16/rpb4/grid1024".
- * Returns the full length of the description.
- */
-int arn_set_tile(int waves_per_row, int vec_per_lane);
-
-/* arn_set_gemm_config forces the shape of later GEMM calls: each
- * block computes col_tiles x 16 output columns (1, 2 or 4) with K split
- * over `waves` waves (4, 8 or 16).  A call whose row tiling has no such
- * compiled shape returns ARN_EUNSUPPORTED.  (0, 0) restores automatic
- * selection; a shape never compiled returns ARN_EINVAL. */
-int arn_set_gemm_config(int col_tiles, int waves);
-/* arn_set_gemm_splits forces the number of K splits (1..8) of later
- * workspace GEMM calls (capped by the number of 128-wide k steps); 0
- * restores automatic selection. */
-int arn_set_gemm_splits(int splits);
-int arn_last_plan(char *buf, size_t len);
 
 #ifdef __cplusplus
 }

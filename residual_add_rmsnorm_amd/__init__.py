@@ -475,17 +475,20 @@ def fp8_gemm(a: torch.Tensor, scale_a: torch.Tensor, b, scale_b: torch.Tensor,
 
 
 def set_tile(waves_per_row: int = 0, vec_per_lane: int = 0) -> None:
-    """Force a kernel shape for later calls ((0, 0) = automatic)."""
+    """Force a kernel shape for this thread's later calls ((0, 0) = automatic;
+    other threads are not affected)."""
     _lib.check(_lib.load().arn_set_tile(waves_per_row, vec_per_lane), "arn_set_tile")
 
 
 def set_gemm_config(col_tiles: int = 0, waves: int = 0) -> None:
-    """Force the e4m3 GEMM's block shape for later calls ((0, 0) = automatic)."""
+    """Force the e4m3 GEMM's block shape for this thread's later calls
+    ((0, 0) = automatic; other threads are not affected)."""
     _lib.check(_lib.load().arn_set_gemm_config(col_tiles, waves), "arn_set_gemm_config")
 
 
 def set_gemm_splits(splits: int = 0) -> None:
-    """Force the number of K splits of later workspace GEMM calls (0 = automatic)."""
+    """Force the number of K splits of this thread's later workspace GEMM
+    calls (0 = automatic; other threads are not affected)."""
     _lib.check(_lib.load().arn_set_gemm_splits(splits), "arn_set_gemm_splits")
 
 

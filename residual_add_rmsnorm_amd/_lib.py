@@ -21,7 +21,8 @@ OK, EINVAL, EUNSUPPORTED, ELAUNCH = 0, 1, 2, 3
 BF16, FP16 = 0, 1
 FP8_STATIC, FP8_DYNAMIC = 0, 1
 
-# Every function include/arn.h declares, with its ctypes signature.
+# Every function include/arn.h and include/arn_tuning.h declare, with its
+# ctypes signature.
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
 SIGNATURES = {

@@ -47,7 +47,8 @@ def sources() -> list[str]:
     return [os.path.join(CSRC, f) for f in ("arn_kernels.hip", "arn_glu.hip", "arn_gemm.hip",
                                             "arn_api.hip", "arn_internal.h", "arn_gemm.h", "arn_device.h",
                                             "arn_probe.hip")] + [
-        os.path.join(INCLUDE, "arn.h"), os.path.join(INCLUDE, "arn_probe.h")]
+        os.path.join(INCLUDE, "arn.h"), os.path.join(INCLUDE, "arn_tuning.h"),
+        os.path.join(INCLUDE, "arn_probe.h")]
 
 
 def _compile(src: str, obj: str, defines: list[str]) -> None:

@@ -16,6 +16,7 @@
 #include <cstring>
 
 #include "arn.h"
+#include "arn_tuning.h"
 #include "arn_internal.h"
 #include "arn_gemm.h"
 
@@ -67,8 +68,11 @@ const char* const kGluNames[arn::kNumGluModes] = {"silu_mul", "silu_mul_fp8s", "
 const char* const kKindNames[arn::kNumKinds] = {"plain",      "fused_add",      "plain_fp8s",
                                                 "fused_add_fp8s", "plain_fp8d", "fused_add_fp8d"};
 
+// Settings of the tuning aids (arn_tuning.h), one copy per calling
+// thread, so that forcing a shape on one thread never changes or refuses
+// another thread's calls.
 // Forced tile (arn_set_tile); 0 = automatic.  Packed as wpr << 8 | nv.
-std::atomic<int> g_forced_tile{0};
+thread_local int g_forced_tile = 0;
 
 thread_local char g_last_plan[160] = "";
 thread_local int g_last_plan_len = 0;
@@ -163,7 +167,7 @@ int pow2_ceil(int64_t v) {
 // taken; failing that, any tile that covers the row.
 const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t rows, int cus,
                         bool lean = false, int compact_nv = 0) {
-  const int forced = g_forced_tile.load(std::memory_order_relaxed);
+  const int forced = g_forced_tile;
   if (forced != 0) {
     const int fw = forced >> 8, fn = forced & 0xFF;
     for (int i = 0; i < table->count; ++i) {
@@ -373,7 +377,7 @@ int run_glu(int mode, int dtype, void* out, int64_t out_stride, float* scale, co
 }
 
 // Forced GEMM shape (arn_set_gemm_config); 0 = automatic.  nt << 8 | waves.
-std::atomic<int> g_forced_gemm{0};
+thread_local int g_forced_gemm = 0;
 
 // GEMM shape, from sweeps of decode projections on MI355X (N 2304..16384,
 // K 2048..16384, M 1..64).  The weight stream wants about one block per CU
@@ -390,7 +394,7 @@ const GemmCfg* find_gemm(const GemmTable* table, int mt, int nt, int waves);
 
 const GemmCfg* choose_gemm(const GemmTable* table, bool pre, int mt, int64_t n, int64_t k,
                            int cus) {
-  const int forced = g_forced_gemm.load(std::memory_order_relaxed);
+  const int forced = g_forced_gemm;
   auto find = [&](int nt, int waves) { return find_gemm(table, mt, nt, waves); };
   if (forced != 0) return find(forced >> 8, forced & 0xFF);
   const int64_t ksteps = (k + 127) / 128;
@@ -447,7 +451,7 @@ int64_t ws_usable(size_t bytes) { return (int64_t)bytes / 256 * 256; }
 int64_t ws_counter_bytes(size_t bytes) { return round_up(ws_usable(bytes) / 512 + 1, 256); }
 
 // Forced number of K splits (arn_set_gemm_splits); 0 = automatic.
-std::atomic<int> g_forced_splits{0};
+thread_local int g_forced_splits = 0;
 
 const GemmCfg* find_gemm(const GemmTable* table, int mt, int nt, int waves) {
   for (int i = 0; i < table->count; ++i) {
@@ -466,13 +470,13 @@ const GemmCfg* find_gemm(const GemmTable* table, int mt, int nt, int waves) {
 // split and keep their shape.
 const GemmCfg* choose_split(const GemmTable* table, const GemmCfg* cfg, int64_t m, int64_t n,
                             int cus, int* splits) {
-  const int forced = g_forced_splits.load(std::memory_order_relaxed);
+  const int forced = g_forced_splits;
   if (forced > 0) {
     *splits = forced;
     return cfg;
   }
   *splits = 1;
-  if (g_forced_gemm.load(std::memory_order_relaxed) != 0 || cfg->nt != 1 || m < 8) return cfg;
+  if (g_forced_gemm != 0 || cfg->nt != 1 || m < 8) return cfg;
   const GemmCfg* wide = find_gemm(table, cfg->mt, 2, 8);
   const int64_t blocks = (n + 31) / 32;
   const int64_t sp = blocks > 0 ? cus / blocks : 1;
@@ -783,14 +787,14 @@ int arn_abi_version(void) { return ARN_ABI_VERSION; }
 
 int arn_set_tile(int waves_per_row, int vec_per_lane) {
   if (waves_per_row == 0 && vec_per_lane == 0) {
-    g_forced_tile.store(0);
+    g_forced_tile = 0;
     return ARN_OK;
   }
   // The tile must exist in the tables (all tables list the same shapes).
   const TileTable* t = table_for(arn::kPlain, ARN_BF16);
   for (int i = 0; i < t->count; ++i) {
     if (t->tiles[i].wpr == waves_per_row && t->tiles[i].nv == vec_per_lane) {
-      g_forced_tile.store((waves_per_row << 8) | vec_per_lane);
+      g_forced_tile = (waves_per_row << 8) | vec_per_lane;
       return ARN_OK;
     }
   }
@@ -799,13 +803,13 @@ int arn_set_tile(int waves_per_row, int vec_per_lane) {
 
 int arn_set_gemm_config(int col_tiles, int waves) {
   if (col_tiles == 0 && waves == 0) {
-    g_forced_gemm.store(0);
+    g_forced_gemm = 0;
     return ARN_OK;
   }
   const GemmTable* t = &ARN_GEMM_TABLE_NAME(0);
   for (int i = 0; i < t->count; ++i) {
     if (t->cfgs[i].nt == col_tiles && t->cfgs[i].waves == waves) {
-      g_forced_gemm.store((col_tiles << 8) | waves);
+      g_forced_gemm = (col_tiles << 8) | waves;
       return ARN_OK;
     }
   }
@@ -814,7 +818,7 @@ int arn_set_gemm_config(int col_tiles, int waves) {
 
 int arn_set_gemm_splits(int splits) {
   if (splits < 0 || splits > kMaxSplits) return ARN_EINVAL;
-  g_forced_splits.store(splits);
+  g_forced_splits = splits;
   return ARN_OK;
 }
 

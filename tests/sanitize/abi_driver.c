@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include "arn.h"
+#include "arn_tuning.h"
 
 static int failures = 0;
 #define EXPECT_EQ(got, want, what)                                                  \

@@ -13,6 +13,7 @@ from residual_add_rmsnorm_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "arn.h")
+TUNING_HEADER = os.path.join(ROOT, "include", "arn_tuning.h")
 
 
 PROBE_HEADER = os.path.join(ROOT, "include", "arn_probe.h")
@@ -30,14 +31,20 @@ def lib():
 
 
 def test_header_declares_the_bound_functions():
-    assert header_functions() == sorted(_lib.SIGNATURES)
+    product, tuning = header_functions(), header_functions(TUNING_HEADER)
+    assert not set(product) & set(tuning)
+    assert sorted(product + tuning) == sorted(_lib.SIGNATURES)
+    # the product header declares nothing that sets state
+    assert not any(n.startswith("arn_set_") for n in product)
+    assert tuning == ["arn_last_plan", "arn_set_gemm_config", "arn_set_gemm_splits",
+                      "arn_set_tile"]
 
 
 def test_library_exports_every_declared_function(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r" T (arn_\w+)", out))
-    for name in header_functions():
+    for name in header_functions() + header_functions(TUNING_HEADER):
         assert name in exported, name
         assert getattr(lib, name) is not None
     assert lib.arn_abi_version() == _lib.ABI_VERSION == 5
