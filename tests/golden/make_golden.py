@@ -13,7 +13,14 @@ batch; the library takes the dequant scale s with code = e4m3(y / s), so the
 stored value is s = fp32(4 * max|y| / 448), with max|y| taken from the
 oracle's unrounded fp64 y over the 256-row seed-0 batch (the decode row
 counts 1, 8, 64, 256 are prefixes of that batch).
+
+workload_digests.json -- SHA-256 of the generator's output for the first
+rows (up to 256) of every norm, SwiGLU and all-reduce-form workload: x (or
+the parts), residual and weight as stored 16-bit patterns, row padding
+included.  It pins the draw itself, which the stored static scales above
+depend on.  Calls only the generator.
 """
+import hashlib
 import json
 import os
 import sys
@@ -59,9 +66,32 @@ def glu_static_scale():
     }
 
 
+def digest(d: dict) -> str:
+    """SHA-256 over the generator's arrays of one call, in a fixed order."""
+    h = hashlib.sha256()
+    for key in ("parts", "x", "residual", "weight"):
+        v = d.get(key)
+        arrays = v if isinstance(v, list) else [v]
+        for a in arrays:
+            if a is not None:
+                h.update(key.encode())
+                h.update(str(a.shape).encode())
+                h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
+def workload_digests():
+    out = {}
+    for name, w in workloads.WORKLOADS.items():
+        rows = min(256, w.rows)
+        out[name] = {"rows": rows, "sha256": digest(workloads.make(w, rows=rows, seed=0))}
+    return {"generator": "workloads.make(w, rows=min(256, w.rows), seed=0)", "workloads": out}
+
+
 if __name__ == "__main__":
     for name, fn in (("fp16_16384_static_scale.json", static_scale),
-                     ("bf16_6656_swiglu_static_scale.json", glu_static_scale)):
+                     ("bf16_6656_swiglu_static_scale.json", glu_static_scale),
+                     ("workload_digests.json", workload_digests)):
         out = os.path.join(HERE, name)
         with open(out, "w") as f:
             json.dump(fn(), f, indent=1)

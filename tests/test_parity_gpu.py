@@ -447,6 +447,58 @@ def test_e4m3_conversion_every_16bit_weight(orc, dtype, log2s):
     assert np.all((qg[inf] & 0x7F) == 0x7E)
 
 
+def _fp32_with_reciprocal(q32):
+    """An fp32 s whose correctly rounded fp32 reciprocal 1.0f / s is q32."""
+    s = np.float32(1.0 / np.float64(q32))
+    for _ in range(8):
+        r = np.float32(1.0) / s
+        if r == q32:
+            return s
+        s = np.nextafter(s, np.float32(np.inf) if r > q32 else np.float32(0))
+    raise AssertionError(f"no fp32 scale with reciprocal {q32!r}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_e4m3_convert_near_ties_at_fp32_resolution(orc, dtype):
+    """The packed convert rounds fp32 values, not only 16-bit ones.  x = 1,
+    eps = 0 and a power-of-two width make the normaliser exactly 1, so the
+    static kernel converts fp32(w * q) with q = 1.0f / s.  With q = 1 + j 2^-23
+    (j = -3..3) and w every e4m3 rounding tie, every e4m3 value and the
+    saturation edge, both signs, the converted values sit on a tie or a few
+    fp32 ulps to either side of it.  Each code must be the nearest e4m3
+    (ties to even, saturating at 448) of the fp32 value the kernel forms,
+    which the host computes with numpy's float32 product."""
+    arn = _arn()
+    pos = sorted({orc.e4m3_decode(c) for c in range(0x7F)})         # 0 .. 448
+    mids = [(lo + hi) / 2 for lo, hi in zip(pos[:-1], pos[1:])] + [464.0]
+    vals = np.array(pos[1:] + mids, np.float64)
+    vals = np.concatenate([vals, -vals])
+    hidden = 1024
+    assert vals.size <= hidden
+    w16 = np.zeros(hidden, np.uint16)
+    if dtype == "fp16":
+        w16[:vals.size] = vals.astype(np.float16).view(np.uint16)
+        wv = w16.view(np.float16).astype(np.float32)
+    else:
+        w16[:vals.size] = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        wv = torch.from_numpy(w16.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(wv[:vals.size].astype(np.float64), vals)  # every tie is a 16-bit value
+    one = 0x3F80 if dtype == "bf16" else 0x3C00
+    xd = dev(np.full((1, hidden), one, np.uint16), dtype)
+    wd = dev(w16, dtype)
+    enc = np.vectorize(lambda v: orc.e4m3_encode(float(v)), otypes=[np.uint8])
+    for j in range(-3, 4):
+        q32 = np.float32(1.0 + j * 2.0**-23)
+        s = _fp32_with_reciprocal(q32)
+        y32 = wv * q32                                              # fp32 products, RNE
+        want = enc(y32.astype(np.float64))
+        q, _ = arn.rmsnorm_fp8(xd, wd, 0.0, scale=torch.tensor([float(s)], device="cuda"))
+        got = codes(q)[0]
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, (f"j={j}: {bad.size} codes differ; first y={float(y32[bad[0]])!r} "
+                               f"gpu={got[bad[0]]:#04x} want={want[bad[0]]:#04x}")
+
+
 def test_e4m3_dynamic_every_finite_bf16_weight(orc):
     arn = _arn()
     w = np.arange(65536, dtype=np.uint32).astype(np.uint16)
