@@ -21,12 +21,18 @@
 //    max |r*w| travel together, so dynamic FP8 costs no extra barrier:
 //    max |y| = max |r*w| * inv because inv > 0.
 //  * Reductions use a fixed order, so results are bitwise reproducible.
+//  * Every finite input is served to the stated tolerance: a bf16 row whose
+//    fp32 sum of squares underflows or overflows is detected after the
+//    reduction and recomputed from the row scaled by 2^+-76 (exact), in a
+//    branch the other rows skip.
 //  * e4m3 codes come from the packed gfx950 v_cvt_pk_fp8_f32 (OCP format
 //    on this target) after an explicit fmed3 clamp to +-448.
 //  * x and out may alias: every element is loaded before the reduction and
 //    stored after it by the same lane, so nothing is marked __restrict__.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "arn_device.h"
 #include "arn_internal.h"
@@ -84,6 +90,8 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
 
   __shared__ float red_sum[WPR * RPB];  // one slot per wave
   __shared__ float red_max[WPR * RPB];
+  __shared__ float red_scaled[WPR * RPB];  // rescaled sums (rows out of fp32 range)
+  __shared__ float red_scaled_max[WPR * RPB];
 
   {
     // 1. Load the row: x (and residual) into registers.  Vectors past the
@@ -140,7 +148,12 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
       for (int k = 0; k < NV; ++k) wr[k] = ones<DT, VEC>();
     }
     float qmul = 0.0f;
-    if constexpr (kStatic) qmul = 1.0f / *a.scale;
+    if constexpr (kStatic) {
+      qmul = 1.0f / *a.scale;
+      // Keep the divide here, beside the loads, rather than after the row
+      // reduction where it would lengthen each row's critical path.
+      asm volatile("" ::"v"(qmul));
+    }
 
     // 2. r = x + residual in fp32, rounded to 16 bits and stored back;
     //    sum of squares of the rounded r over the first var_cols channels
@@ -206,39 +219,122 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
         if constexpr (kDynamic) mx = fmaxf(mx, red_max[rib * WPR + i]);
       }
     }
-    const float inv = rsqrtf(__builtin_fmaf(ss, a.inv_var, a.eps));
+    float inv = rsqrtf(__builtin_fmaf(ss, a.inv_var, a.eps));
+    float rmul = 1.0f;  // rescaled rows: y = ((r * rmul) * inv) * w
+
+    // 3b. Rows outside fp32's range.  A bf16 row whose squares underflow
+    //     (every |r| below about 2^-75, with eps as small) or whose sum of
+    //     squares overflows (|r| near bf16's largest values) gets its sum of
+    //     squares again from r * 2^76 or r * 2^-76 -- powers of two, so the
+    //     scaled values are exact -- and y = (r * 2^+-76) / sqrt(ms 2^+-152
+    //     + eps 2^+-152) * w, the same quantity with no intermediate out of
+    //     range.  Other rows never enter this branch, so their results are
+    //     the plain formula's, bit for bit.  The branch is uniform over every
+    //     row that shares a barrier: with several multi-wave rows per block,
+    //     all of them enter when one needs it (their own rescaled sums are
+    //     then unused).
+    const float total = __builtin_fmaf(ss, a.inv_var, a.eps);
+    const bool rescue = !(total >= 0x1p-96f) || !(ss <= 3.4028234e38f);
+    bool enter = rescue;
+    if constexpr (WPR > 1 && RPB > 1) {
+      enter = false;
+#pragma unroll
+      for (int rr = 0; rr < RPB; ++rr) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < WPR; ++i) s += red_sum[rr * WPR + i];
+        const float tt = __builtin_fmaf(s, a.inv_var, a.eps);
+        enter = enter || !(tt >= 0x1p-96f) || !(s <= 3.4028234e38f);
+      }
+    }
+    if (enter) {
+      const float sc = ss < 1.0f ? 0x1p76f : 0x1p-76f;
+      float s2 = 0.0f;
+      float m2 = 0.0f;  // dynamic e4m3: max |(r * sc) * w|, which cannot overflow
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        // The packed row passes through an empty asm the compiler cannot
+        // see through, so no unpacked copy of it is kept live across this
+        // branch for the output step.
+        asm volatile("" : "+v"(xr[k]));
+        const int col0 = (t + k * kTPR) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float rf = elem<DT, VEC>(xr[k], e) * sc;
+          s2 = __builtin_fmaf(rf, col0 + e < a.var_cols ? rf : 0.0f, s2);
+          if constexpr (kDynamic) m2 = fmaxf(m2, fabsf(rf * elem<DT, VEC>(wr[k], e)));
+        }
+      }
+      s2 = wave_sum(s2);
+      if constexpr (kDynamic) m2 = wave_max(m2);
+      if constexpr (WPR > 1) {
+        if (lane == 0) {
+          red_scaled[wave] = s2;
+          if constexpr (kDynamic) red_scaled_max[wave] = m2;
+        }
+        __syncthreads();
+        s2 = 0.0f;
+        m2 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < WPR; ++i) {
+          s2 += red_scaled[rib * WPR + i];
+          if constexpr (kDynamic) m2 = fmaxf(m2, red_scaled_max[rib * WPR + i]);
+        }
+      }
+      if (rescue) {
+        rmul = sc;
+        inv = rsqrtf(__builtin_fmaf(s2, a.inv_var, a.eps * sc * sc));
+        mx = m2;
+      }
+    }
 
     if constexpr (kDynamic) {
-      const float amax = mx * inv;
+      const float amax = mx * inv;  // mx already carries rmul
       qmul = amax > 0.0f ? 448.0f / amax : 0.0f;
       if (active && t == 0) a.scale[row] = amax / 448.0f;
     }
 
-    // 4. y = r * inv * w, stored as 16 bits or as e4m3 codes.
-    if constexpr (kFp8) {
-      const __amdgpu_buffer_rsrc_t ors = row_rsrc(
-          static_cast<uint8_t*>(a.out) + arow * a.out_stride, active ? row_bytes8 : 0u);
+    // 4. y = r * inv * w, stored as 16 bits or as e4m3 codes.  A rescaled
+    //    row takes its own copy of the loop (y = ((r * rmul) * inv) * w), so
+    //    the other rows pay no extra multiply per element.
+    auto emit = [&](auto scaled) {
+      constexpr bool kScaled = decltype(scaled)::value;
+      if constexpr (kFp8) {
+        const __amdgpu_buffer_rsrc_t ors = row_rsrc(
+            static_cast<uint8_t*>(a.out) + arow * a.out_stride, active ? row_bytes8 : 0u);
 #pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        float y[VEC];
+        for (int k = 0; k < NV; ++k) {
+          float y[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          y[e] = elem<DT, VEC>(xr[k], e) * inv * elem<DT, VEC>(wr[k], e) * qmul;
+          for (int e = 0; e < VEC; ++e) {
+            const float rv = kScaled ? elem<DT, VEC>(xr[k], e) * rmul : elem<DT, VEC>(xr[k], e);
+            y[e] = rv * inv * elem<DT, VEC>(wr[k], e) * qmul;
+          }
+          store8<VEC>(pack_fp8<VEC>(y), ors, off8 + k * kStep8);
         }
-        store8<VEC>(pack_fp8<VEC>(y), ors, off8 + k * kStep8);
+      } else {
+        const __amdgpu_buffer_rsrc_t ors =
+            row_rsrc(static_cast<uint16_t*>(a.out) + arow * a.out_stride, n16);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          float y[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float rv = kScaled ? elem<DT, VEC>(xr[k], e) * rmul : elem<DT, VEC>(xr[k], e);
+            y[e] = rv * inv * elem<DT, VEC>(wr[k], e);
+          }
+          store16<VEC>(pack<DT, VEC>(y), ors, off16 + k * kStep16);
+        }
       }
+    };
+    if (rescue) {
+      // (Laundered as above, so the two loops share no unpacked values that
+      // the compiler would hoist above the branch and keep live.)
+#pragma unroll
+      for (int k = 0; k < NV; ++k) asm volatile("" : "+v"(xr[k]));
+      emit(std::true_type{});
     } else {
-      const __amdgpu_buffer_rsrc_t ors =
-          row_rsrc(static_cast<uint16_t*>(a.out) + arow * a.out_stride, n16);
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        float y[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          y[e] = elem<DT, VEC>(xr[k], e) * inv * elem<DT, VEC>(wr[k], e);
-        }
-        store16<VEC>(pack<DT, VEC>(y), ors, off16 + k * kStep16);
-      }
+      emit(std::false_type{});
     }
   }
 }

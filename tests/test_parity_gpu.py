@@ -299,21 +299,61 @@ def test_fp16_subnormal_inputs(orc):
     run_case(orc, dtype="fp16", x=x, res=r, w=None, eps=0.0, hidden=hidden)
 
 
-@pytest.mark.parametrize("eps,scales", [
-    (1e-6, [2.0**-130, 2.0**-100, 1e-20, 1e-3]),   # subnormal and tiny rows: eps dominates
-    (0.0, [1e-10, 1e10, 1e15, 1.0]),                # squares stay in fp32 range
-])
-def test_bf16_tiny_and_huge_inputs(orc, eps, scales):
-    """fp32 accumulation: rows whose squares underflow fp32 (|r| below about
-    1e-23) are only meaningful with eps > 0, and rows whose sum of squares
-    overflows fp32 are outside the supported range; both ends are probed
-    inside those limits."""
-    rng = np.random.default_rng(19)
-    hidden = 2048
-    f = (rng.standard_normal((len(scales), hidden)) * np.array(scales)[:, None]).astype(np.float32)
+# Rows at both ends of bf16's range, interleaved with ordinary ones so that
+# blocks holding several rows mix them.  With a small eps the fp32 sum of
+# squares of such rows underflows (every |r| below about 2^-75: squares
+# under fp32's smallest values) or overflows (|r| of 2^60 and more over a
+# 2048-wide row); the kernel recomputes it from r scaled by 2^+-76, so these
+# rows meet the same tolerance as any other.
+OUT_OF_RANGE_SCALES = [2.0**-131, 1.0, 2.0**-128, 2.0**-100, 1e-3, 1e-30, 2.0**-80,
+                       2.0**-70, 2.0**60, 1.0, 2.0**100, 2.0**124, 2.0**-40, 3.0]
+
+
+def _out_of_range_rows(hidden=2048, seed=19):
+    rng = np.random.default_rng(seed)
+    sc = np.array(OUT_OF_RANGE_SCALES, np.float64)
+    f = rng.standard_normal((sc.size, hidden)) * sc[:, None]
+    f = np.clip(f, -2.0**126, 2.0**126).astype(np.float32)
     x = W.to_bits(f, "bf16")
     r = W.to_bits(f * np.float32(0.25), "bf16")
-    run_case(orc, dtype="bf16", x=x, res=r, w=None, eps=eps, hidden=hidden)
+    w = W.to_bits(rng.uniform(0.5, 1.5, hidden).astype(np.float32), "bf16")
+    return x, r, w
+
+
+@pytest.mark.parametrize("tile", [None, (1, 4), (2, 2), (8, 1), (16, 1)],
+                         ids=["auto", "wpr1", "wpr2", "wpr8", "wpr16"])
+@pytest.mark.parametrize("fp8", [None, "static", "dynamic"])
+@pytest.mark.parametrize("eps", [0.0, 1e-38, 1e-6])
+def test_bf16_rows_out_of_fp32_range(orc, eps, fp8, tile):
+    """Subnormal, tiny and huge bf16 rows (their squares or sums of squares
+    out of fp32's range) match the fp64 definition, with eps = 0, an eps far
+    below them, or an ordinary eps; every output format; one-row-per-wave,
+    two-rows-per-block and multi-wave tiles forced."""
+    arn = _arn()
+    x, r, w = _out_of_range_rows()
+    hidden = x.shape[1]
+    if tile:
+        arn.set_tile(*tile)
+    try:
+        run_case(orc, dtype="bf16", x=x, res=r, w=w, eps=eps, hidden=hidden, fp8=fp8,
+                 s=2.0**-6 if fp8 == "static" else None)
+        if tile:
+            assert f"/wpr{tile[0]}/nv{tile[1]}/" in arn.last_plan()
+    finally:
+        arn.set_tile(0, 0)
+
+
+@pytest.mark.parametrize("k", [2048, 700])
+def test_bf16_rows_out_of_fp32_range_variance_size(orc, k):
+    arn = _arn()
+    x, r, w = _out_of_range_rows(seed=23)
+    H = x.shape[1]
+    xd, rd, wd = dev(x, "bf16"), dev(r, "bf16"), dev(w, "bf16")
+    y = arn.norm(xd, wd, 0.0, residual=rd, variance_size=k)
+    torch.cuda.synchronize()
+    ref = orc.add_rmsnorm("bf16", x, r, w, 0.0, variance_size=k)
+    assert np.array_equal(bits(rd), ref["r16"])
+    assert_y_close(bits(y), ref["y"], "bf16")
 
 
 def test_zero_rows_eps0_give_nan(orc):
