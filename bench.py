@@ -3,16 +3,23 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
 
 A step is one call of the operator over one batch of the workload, inputs
-already resident in device memory.  The headline workload is fused add +
-RMSNorm, bf16, 4096 rows x 8192.  Its 192 MiB working set is under the
-256 MB Infinity Cache, so steps rotate over several buffer sets whose total
-exceeds that cache: every step streams from HBM.
+already resident in device memory.  With no --workload the run measures
+every configuration of the operator and prints ONE JSON line: the headline
+is the largest, fused add + RMSNorm, bf16, 65536 rows x 3840 at row stride
+4096 (2.01 GB per call), and `config.per_workload` holds the others -- plain
+RMSNorm 64 x 4096, fused 4096 x 8192, the decode rows 1/8/64/256 x 16384
+with static e4m3 (device time per call from HIP-graph replay and host wall
+time per call, beside the launch floor of an empty kernel), dynamic e4m3
+32768 x 7168 and the strided 65536 x 2880.  Working sets under four times
+the 256 MB Infinity Cache rotate over several buffer sets, so every step
+streams from HBM.
 
-The printed JSON line carries the throughput (algorithmic bytes / time), the
-roofline entry of the kernel (average launch duration from HIP events on the
+Each entry carries the throughput (algorithmic bytes / time), the roofline
+fraction of its kernel (average launch duration from HIP events on the
 launch stream), the HBM traffic measured by rocprofv3 counters when it was
-taken on the current kernel source, and the plain CPU oracle timed on a
-bounded sample of the same workload.
+taken on the current kernel source and launch shape, and the ceiling of a
+plain streaming kernel moving the same byte mix.  The headline also carries
+the plain CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -443,8 +450,14 @@ def traffic_for(name: str, plan: str):
     return t.get("traffic_bytes_per_launch")
 
 
-def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool,
-                   with_ceiling: bool = True) -> dict:
+def measure_workload(name: str, steps: int, warmup: int, ceilings: dict | None) -> dict:
+    """Time `steps` calls of one workload after `warmup` untimed ones (HIP
+    events on the launch stream) and return its entry: per-call time,
+    algorithmic GB/s, fraction of the 8 TB/s peak, the launch plan, the
+    stored HBM traffic for that plan, and the mix ceiling.  Decode workloads
+    add each row count's device time per call from HIP-graph replay and its
+    host wall time per call; latency-bound ones (few rows) add their graph
+    replay time too."""
     import torch
 
     import residual_add_rmsnorm_amd as arn
@@ -465,41 +478,26 @@ def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool,
     log(f"[bench] plan {plan}: {per_call_ms * 1e3:.2f} us/call, {achieved:.1f} GB/s "
         f"({100 * achieved / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
     traffic = traffic_for(name, plan)
-    mix = workload_mix(w)
-    ceiling = mix_ceilings([mix])[mix] if mix and with_ceiling else None
-    line = {
-        "metric": METRIC,
-        "value": round(achieved, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": round(per_call_ms, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": name, "rows": rows, "hidden": w.hidden, "row_stride": w.stride,
-            "io_dtype": w.dtype, "fp8": w.fp8, "eps": w.eps, "buffer_sets": sets,
-            **({"nparts": w.nparts} if w.is_sum else {}),
-            "bytes_per_step": bytes_step, "kernel_plan": plan,
-            "us_per_call": round(per_call_ms * 1e3, 3),
-            "pct_of_hbm_peak": round(100 * achieved / PEAK_HBM_GBS, 2),
-            "host_wall_ms_per_step": round(wall_ms / steps, 6),
-        },
-        "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": traffic,
-        },
+    entry = {
+        "op": w.op, "rows": rows, "hidden": w.hidden, "row_stride": w.stride,
+        "io_dtype": w.dtype, "fp8": w.fp8, "eps": w.eps, "buffer_sets": sets,
+        **({"nparts": w.nparts} if w.is_sum else {}),
+        "bytes_per_call": bytes_step, "kernel_plan": plan,
+        "us_per_call": round(per_call_ms * 1e3, 3),
+        "GB_per_s": round(achieved, 2),
+        "frac_of_hbm_peak": round(achieved / PEAK_HBM_GBS, 4),
+        "host_wall_us_per_call": round(wall_ms * 1e3 / steps, 3),
+        "traffic_bytes_per_launch": traffic,
+        "traffic_over_algorithmic": round(traffic / bytes_step, 5) if traffic else None,
     }
-    if ceiling:
-        line["roofline"]["mix_ceiling"] = {
-            "mix": mix, "GB_per_s": ceiling["GB_per_s"],
-            "frac": round(achieved / ceiling["GB_per_s"], 4),
-            "probe": f"plain streaming kernel, block {ceiling['block']}, grid {ceiling['grid']}"}
+    mix = workload_mix(w)
+    if ceilings is not None and mix:
+        if mix not in ceilings:
+            ceilings.update(mix_ceilings([mix]))
+        c = ceilings[mix]
+        entry["mix_ceiling"] = {
+            "mix": mix, "GB_per_s": c["GB_per_s"], "frac": round(achieved / c["GB_per_s"], 4),
+            "probe": f"plain streaming kernel, block {c['block']}, grid {c['grid']}"}
     if w.row_counts:
         per_rows = {}
         for r in w.row_counts:
@@ -509,15 +507,67 @@ def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool,
             per_rows[str(r)] = {"device_us_per_call_graph": round(dev_us, 3),
                                 "event_us_per_call": round(e_ms * 1e3 / 200, 3),
                                 "host_wall_us_per_call": round(wall * 1e3 / 200, 3),
+                                "bytes_per_call": w.algorithmic_bytes(r),
                                 "plan": arn.last_plan()}
             log(f"[bench] rows={r}: {per_rows[str(r)]}")
-        line["config"]["decode_us_per_call"] = per_rows
-        line["config"]["empty_kernel_launch"] = launch_floor()
+            del b
+        entry["decode_us_per_call"] = per_rows
+        entry["empty_kernel_launch"] = launch_floor()
+    elif rows < 1024:
+        b = Batch(w, 8)
+        entry["device_us_per_call_graph"] = round(time_graph(b, calls=64, replays=20), 3)
+        entry["empty_kernel_launch"] = launch_floor()
+        del b
     del batch
     torch.cuda.empty_cache()
+    return entry
+
+
+def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool,
+                   with_ceiling: bool = True, others: tuple = ()) -> dict:
+    """The JSON line of one workload (`name`), optionally with entries for
+    `others` under config.per_workload."""
+    ceilings = {} if with_ceiling else None
+    head = measure_workload(name, steps, warmup, ceilings)
+    per = {}
+    for other in others:
+        per[other] = measure_workload(other, steps, warmup, ceilings)
+    achieved = head["GB_per_s"]
+    config = {"workload": name}
+    config.update({k: v for k, v in head.items()
+                   if k not in ("GB_per_s", "frac_of_hbm_peak", "traffic_bytes_per_launch",
+                                "traffic_over_algorithmic", "mix_ceiling")})
+    config["bytes_per_step"] = config.pop("bytes_per_call")
+    config["pct_of_hbm_peak"] = round(100 * achieved / PEAK_HBM_GBS, 2)
+    if per:
+        config["per_workload"] = per
+    line = {
+        "metric": METRIC,
+        "value": achieved,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(head["us_per_call"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": config,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": head["frac_of_hbm_peak"],
+            "traffic": head["traffic_bytes_per_launch"],
+        },
+    }
+    if "mix_ceiling" in head:
+        line["roofline"]["mix_ceiling"] = head["mix_ceiling"]
     if with_cpu:
+        import workloads
+
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline"] = cpu_baseline(workloads.WORKLOADS[name])
         line["system"] = system_info()
     return line
 
@@ -597,7 +647,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None,
-                    help="workload name, or 'all' (default: the headline workload)")
+                    help="one workload name (one line), 'all' (one line each), 'gemms'; "
+                         "default: the headline with every configuration in one line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-probe ceiling of the workload's byte mix")
@@ -609,6 +660,12 @@ def main() -> int:
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --calibrate-copy` into profiles/traffic_<workload>.json")
     ap.add_argument("--pmc-command", default="", help="command line recorded with the summary")
+    ap.add_argument("--launch-traffic", action="store_true",
+                    help="only run the plain norm at a few row counts with and without a weight "
+                         "(run it under rocprofv3 --pmc to separate fixed bytes per launch)")
+    ap.add_argument("--summarize-launch-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="fit the two counter runs of --launch-traffic into "
+                         "profiles/launch_traffic_rmsnorm_bf16_x4096.json")
     ap.add_argument("--pmc-bench-output", default=None,
                     help="the JSON line the profiled bench run printed (its kernel plan is "
                          "recorded with the summary)")
@@ -625,6 +682,10 @@ def main() -> int:
         summarize_pmc(args.workload or workloads.HEADLINE, *args.summarize_pmc,
                       command=args.pmc_command, bench_output=args.pmc_bench_output,
                       gemm_m=args.gemm_m, gemm_layout=args.gemm_layout)
+        return 0
+
+    if args.summarize_launch_traffic:
+        summarize_launch_traffic(*args.summarize_launch_traffic, command=args.pmc_command)
         return 0
 
     if args.gpus != 1:
@@ -644,6 +705,10 @@ def main() -> int:
 
     _lib.load()  # fails loudly if the HIP library is missing
 
+    if args.launch_traffic:
+        launch_traffic_sweep()
+        return 0
+
     if args.ceilings:
         print(json.dumps({"ceilings_GB_per_s": mix_ceilings(list(MIXES)),
                           "stream_bytes": {"two-stream mixes": PROBE_STREAM_BYTES,
@@ -659,8 +724,18 @@ def main() -> int:
         if args.calibrate_copy:
             copy_calibration()
         return 0
-    names = list(workloads.WORKLOADS) if args.workload == "all" else \
-        [args.workload or workloads.HEADLINE]
+    if args.workload is None:
+        # the default run: the headline with every other configuration in
+        # config.per_workload, one JSON line
+        others = tuple(n for n in workloads.BENCH_WORKLOADS if n != workloads.HEADLINE)
+        line = bench_workload(workloads.HEADLINE, args.steps, args.warmup,
+                              with_cpu=not args.no_cpu_baseline,
+                              with_ceiling=not args.no_ceiling, others=others)
+        print(json.dumps(line), flush=True)
+        if args.calibrate_copy:
+            copy_calibration()
+        return 0
+    names = list(workloads.WORKLOADS) if args.workload == "all" else [args.workload]
     for n in names:
         line = bench_workload(n, args.steps, args.warmup,
                               with_cpu=not args.no_cpu_baseline and n == names[0],
@@ -712,11 +787,14 @@ def summarize_pmc(name: str, fetch_csv: str, write_csv: str, command: str = "",
             plan = line["config"]["kernel_plan"]
     out = {"workload": key, "kernel_source_sha": kernel_source_sha(kernel_family(key)),
            "kernel_plan": plan, "algorithmic_bytes_per_launch": alg, "command": command}
+    want_items = plan_work_items(plan) if plan else None
     for counter, path, kind in (("FETCH_SIZE", fetch_csv, "read"), ("WRITE_SIZE", write_csv, "write")):
         rows = _pmc_rows(path, counter)
         kern = [float(r["Counter_Value"]) for r in rows
                 if r["Kernel_Name"].startswith("void arn::")
-                and "preshuffle_kernel" not in r["Kernel_Name"]]
+                and "preshuffle_kernel" not in r["Kernel_Name"]
+                and (want_items is None or "Grid_Size" not in r
+                     or int(r["Grid_Size"]) == want_items)]
         copies = [float(r["Counter_Value"]) for r in rows
                   if "copyBuffer" in r["Kernel_Name"]][-COPY_REPS:]
         kib = sum(kern) / len(kern)
@@ -730,6 +808,85 @@ def summarize_pmc(name: str, fetch_csv: str, write_csv: str, command: str = "",
     out["traffic_bytes_per_launch"] = out["read_bytes_per_launch"] + out["write_bytes_per_launch"]
     out["traffic_over_algorithmic"] = round(out["traffic_bytes_per_launch"] / alg, 5)
     with open(traffic_file(key), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    log(json.dumps(out, indent=1))
+    return out
+
+
+def plan_work_items(plan: str):
+    """Work-items of one launch of a norm-family plan string
+    (".../wpr8/nv2/rpb1/grid4096": 4096 blocks of 64 * 8 * 1 threads), the
+    Grid_Size rocprofv3 records per dispatch; None for other plans.  A run
+    that also launches other row counts (the decode sweep) is summarised
+    over the dispatches of the recorded plan only."""
+    import re
+
+    m = re.search(r"/wpr(\d+)/nv\d+/rpb(\d+)/grid(\d+)$", plan)
+    if not m:
+        return None
+    wpr, rpb, grid = (int(g) for g in m.groups())
+    return grid * 64 * wpr * rpb
+
+
+# Fixed traffic per launch: the plain norm 4096 wide (the rmsnorm workload's
+# width) at two row counts with the weight and two without, 20 launches each
+# over 8 rotating buffer sets, then the calibration copies.  Under two
+# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) this separates the bytes per
+# row, the weight's bytes per launch and a fixed remainder per launch.
+SWEEP_HIDDEN = 4096
+SWEEP_CASES = ((64, True), (65, False), (256, True), (257, False))
+SWEEP_LAUNCHES = 20
+
+
+def launch_traffic_sweep() -> None:
+    import torch
+
+    import residual_add_rmsnorm_amd as arn
+
+    rmax = max(r for r, _ in SWEEP_CASES)
+    xs = [torch.randn(rmax, SWEEP_HIDDEN, device="cuda").to(torch.bfloat16) for _ in range(8)]
+    outs = [torch.empty_like(xs[0]) for _ in range(8)]
+    w = torch.full((SWEEP_HIDDEN,), 1.5, dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    for rows, with_w in SWEEP_CASES:
+        for i in range(SWEEP_LAUNCHES):
+            arn.rmsnorm(xs[i % 8][:rows], w if with_w else None, 1e-6, out=outs[i % 8][:rows])
+        torch.cuda.synchronize()
+        log(f"[bench] launch-traffic sweep: {rows} rows, weight {with_w}, plan {arn.last_plan()}")
+    copy_calibration()
+
+
+def summarize_launch_traffic(fetch_csv: str, write_csv: str, command: str = "") -> dict:
+    """Per case of SWEEP_CASES (told apart by their grids: one block of 512
+    threads per row), the mean FETCH_SIZE and WRITE_SIZE bytes per launch
+    (scaled by the calibration copies), and the fit: bytes per row from the
+    two weightless cases, the fixed remainder per launch, and the weight's
+    bytes per launch."""
+    out = {"hidden": SWEEP_HIDDEN, "cases": [], "command": command}
+    per = {}
+    for counter, path, kind in (("FETCH_SIZE", fetch_csv, "read"), ("WRITE_SIZE", write_csv, "write")):
+        rows = _pmc_rows(path, counter)
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-COPY_REPS:]
+        factor = COPY_BYTES / (sum(copies) / len(copies) * 1024.0)
+        for nrows, with_w in SWEEP_CASES:
+            vals = [float(r["Counter_Value"]) for r in rows
+                    if r["Kernel_Name"].startswith("void arn::") and int(r["Grid_Size"]) == nrows * 512]
+            per[(nrows, with_w, kind)] = sum(vals) / len(vals) * 1024.0 * factor
+    for nrows, with_w in SWEEP_CASES:
+        out["cases"].append({"rows": nrows, "weight": with_w,
+                             "read_bytes_per_launch": round(per[(nrows, with_w, "read")]),
+                             "write_bytes_per_launch": round(per[(nrows, with_w, "write")])})
+    (r0, _), (r1, _) = [c for c in SWEEP_CASES if not c[1]]
+    row_bytes = (per[(r1, False, "read")] - per[(r0, False, "read")]) / (r1 - r0)
+    fixed = per[(r0, False, "read")] - r0 * row_bytes
+    weight = [per[(r, True, "read")] - fixed - r * row_bytes for r, w in SWEEP_CASES if w]
+    out["fit"] = {"read_bytes_per_row": round(row_bytes, 1),
+                  "read_fixed_bytes_per_launch": round(fixed),
+                  "read_weight_bytes_per_launch": [round(v) for v in weight],
+                  "weight_bytes": SWEEP_HIDDEN * 2}
+    path = os.path.join(ROOT, "profiles", "launch_traffic_rmsnorm_bf16_x4096.json")
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     log(json.dumps(out, indent=1))

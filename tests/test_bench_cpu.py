@@ -60,22 +60,30 @@ def test_workload_mix():
         assert m is None or m in bench.MIXES
 
 
-def _counter_csv(path, counter, kernel_kib, copy_kib, copies=bench.COPY_REPS):
+def _counter_csv(path, counter, kernel_kib, copy_kib, copies=bench.COPY_REPS, grid=None,
+                 other_grid_kib=()):
     with open(path, "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
-                                          "Counter_Value"])
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Grid_Size", "Kernel_Name",
+                                          "Counter_Name", "Counter_Value"])
         w.writeheader()
         i = 0
         for v in kernel_kib:
             i += 1
-            w.writerow({"Dispatch_Id": i, "Kernel_Name": "void arn::row_kernel<0>(arn::Args)",
+            w.writerow({"Dispatch_Id": i, "Grid_Size": grid or 1,
+                        "Kernel_Name": "void arn::row_kernel<0>(arn::Args)",
+                        "Counter_Name": counter, "Counter_Value": v})
+        for v in other_grid_kib:   # the same kernel at another row count
+            i += 1
+            w.writerow({"Dispatch_Id": i, "Grid_Size": 512,
+                        "Kernel_Name": "void arn::row_kernel<0>(arn::Args)",
                         "Counter_Name": counter, "Counter_Value": v})
         i += 1
-        w.writerow({"Dispatch_Id": i, "Kernel_Name": "void some_other_kernel()",
+        w.writerow({"Dispatch_Id": i, "Grid_Size": 64, "Kernel_Name": "void some_other_kernel()",
                     "Counter_Name": counter, "Counter_Value": 1e9})
         for _ in range(copies):
             i += 1
-            w.writerow({"Dispatch_Id": i, "Kernel_Name": "__amd_rocclr_copyBuffer",
+            w.writerow({"Dispatch_Id": i, "Grid_Size": 1 << 20,
+                        "Kernel_Name": "__amd_rocclr_copyBuffer",
                         "Counter_Name": counter, "Counter_Value": copy_kib})
 
 
@@ -131,3 +139,76 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert res.returncode == 2
     assert "one GPU" in res.stdout + res.stderr
+
+
+def test_default_run_covers_every_configuration_with_the_largest_as_headline():
+    """The default bench line measures all five configurations (the strided
+    one at both widths); its headline is the one that moves the most bytes."""
+    names = W.BENCH_WORKLOADS
+    assert len(names) == len(set(names)) == 6
+    assert W.HEADLINE in names
+    assert W.HEADLINE == max(names, key=lambda n: W.WORKLOADS[n].algorithmic_bytes())
+    assert W.WORKLOADS[W.HEADLINE].algorithmic_bytes() == 65536 * 3840 * 8 + 3840 * 2
+    ops = {W.WORKLOADS[n].op for n in names}
+    assert ops == {"rmsnorm", "fused_add_rmsnorm", "fused_add_rmsnorm_fp8"}
+    decode = [n for n in names if W.WORKLOADS[n].row_counts]
+    assert decode == ["fused_add_rmsnorm_fp8_static_fp16_decode_x16384"]
+    assert W.WORKLOADS[decode[0]].row_counts == (1, 8, 64, 256)
+
+
+def test_summarize_pmc_keeps_the_recorded_plans_dispatches(tmp_path, monkeypatch):
+    """A run that also launches other row counts (the decode sweep) is
+    summarised over the dispatches whose grid matches the recorded plan."""
+    name = "fused_add_rmsnorm_fp8_static_fp16_decode_x16384"
+    plan = "fused_add_fp8s/fp16/vec8/wpr8/nv4/rpb1/grid256"
+    assert bench.plan_work_items(plan) == 256 * 512
+    assert bench.plan_work_items("fp8_gemm/bf16/mt1/nt1/waves8/splits1/grid144") is None
+    alg = W.WORKLOADS[name].algorithmic_bytes()
+    copy_kib = bench.COPY_BYTES / 1024
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [alg * 4 / 7 / 1024] * 3, copy_kib, grid=256 * 512,
+                 other_grid_kib=[1.0, 2.0])
+    _counter_csv(write, "WRITE_SIZE", [alg * 3 / 7 / 1024] * 3, copy_kib, grid=256 * 512,
+                 other_grid_kib=[3.0])
+    line = tmp_path / "line.json"
+    line.write_text(json.dumps({"config": {"kernel_plan": plan}}) + "\n")
+    monkeypatch.setattr(bench, "traffic_file", lambda key: str(tmp_path / "t.json"))
+    out = bench.summarize_pmc(name, str(fetch), str(write), bench_output=str(line))
+    assert out["read_dispatches"] == 3 and out["write_dispatches"] == 3
+    assert out["traffic_over_algorithmic"] == pytest.approx(1.0, abs=1e-6)
+
+
+def test_launch_traffic_fit(tmp_path, monkeypatch):
+    """The sweep's fit recovers bytes per row, a fixed remainder per launch
+    and the weight's bytes from synthetic counter files built with them."""
+    per_row, fixed, weight = 8192, 48000, 8 * 8192
+    rows = []
+    i = 0
+    for nrows, with_w in bench.SWEEP_CASES:
+        for _ in range(3):
+            i += 1
+            read = fixed + nrows * per_row + (weight if with_w else 0)
+            rows.append((i, nrows * 512, "void arn::row_kernel<0>(arn::Args)", read, nrows * 8192))
+    for _ in range(bench.COPY_REPS):
+        i += 1
+        rows.append((i, 1 << 20, "__amd_rocclr_copyBuffer", bench.COPY_BYTES, bench.COPY_BYTES))
+    paths = {}
+    for k, counter in ((3, "FETCH_SIZE"), (4, "WRITE_SIZE")):
+        p = tmp_path / f"{counter}.csv"
+        with open(p, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Grid_Size", "Kernel_Name",
+                                              "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for r in rows:
+                # the read counter reads half of the true bytes, in KiB
+                v = r[k] / 1024 / (2 if k == 3 else 1)
+                w.writerow({"Dispatch_Id": r[0], "Grid_Size": r[1], "Kernel_Name": r[2],
+                            "Counter_Name": counter, "Counter_Value": v})
+        paths[counter] = str(p)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    out = bench.summarize_launch_traffic(paths["FETCH_SIZE"], paths["WRITE_SIZE"])
+    assert out["fit"]["read_bytes_per_row"] == pytest.approx(per_row)
+    assert out["fit"]["read_fixed_bytes_per_launch"] == pytest.approx(fixed, abs=1)
+    assert out["fit"]["read_weight_bytes_per_launch"] == [weight, weight]
+    assert out["cases"][1]["write_bytes_per_launch"] == 65 * 8192

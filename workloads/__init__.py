@@ -127,8 +127,18 @@ WORKLOADS["sum_add_rmsnorm_bf16_8x4096x8192"] = Workload(
     "sum_add_rmsnorm_bf16_8x4096x8192", "sum_add_rmsnorm", "bf16", 4096, 8192, 8192, 1e-5,
     x_std=float(np.float32(8 ** -0.5)), nparts=8)
 
-# The benchmark's headline workload.
-HEADLINE = "fused_add_rmsnorm_bf16_4096x8192"
+# The benchmark's workloads: the five configurations of the operator (the
+# strided one at two widths), and the headline among them, the largest
+# (65536 x 3840 at row stride 4096: 2.01 GB moved per call).
+BENCH_WORKLOADS = (
+    "rmsnorm_bf16_64x4096",
+    "fused_add_rmsnorm_bf16_4096x8192",
+    "fused_add_rmsnorm_fp8_static_fp16_decode_x16384",
+    "fused_add_rmsnorm_fp8_dynamic_bf16_32768x7168",
+    "fused_add_rmsnorm_bf16_65536x3840_stride4096",
+    "fused_add_rmsnorm_bf16_65536x2880_stride4096",
+)
+HEADLINE = "fused_add_rmsnorm_bf16_65536x3840_stride4096"
 
 
 def _rng(seed: int, stream: int, block: int) -> np.random.Generator:
