@@ -660,6 +660,9 @@ def main() -> int:
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --calibrate-copy` into profiles/traffic_<workload>.json")
     ap.add_argument("--pmc-command", default="", help="command line recorded with the summary")
+    ap.add_argument("--row-probe", action="store_true",
+                    help="only time the row-ordered 2R2W probe in every access order beside "
+                         "the fused kernel")
     ap.add_argument("--launch-traffic", action="store_true",
                     help="only run the plain norm at a few row counts with and without a weight "
                          "(run it under rocprofv3 --pmc to separate fixed bytes per launch)")
@@ -707,6 +710,10 @@ def main() -> int:
 
     if args.launch_traffic:
         launch_traffic_sweep()
+        return 0
+
+    if args.row_probe:
+        print(json.dumps({"row_order_probe": row_order_probe()}), flush=True)
         return 0
 
     if args.ceilings:
@@ -827,6 +834,81 @@ def plan_work_items(plan: str):
         return None
     wpr, rpb, grid = (int(g) for g in m.groups())
     return grid * 64 * wpr * rpb
+
+
+# Access order of the fused norm's row traffic: the row-ordered 2R2W probe
+# (arn_probe_rows) in every order and rows per block, next to the fused
+# kernel itself and the grid-stride 2R2W probe, at the strided 3840-wide row
+# shape (65536 rows, pitch 4096) and at a 8192-wide row (32768 rows).
+ROW_PROBE_SHAPES = (("65536x3840_stride4096", 65536, 3840, 4096),
+                    ("32768x8192", 32768, 8192, 8192))
+
+
+def row_order_probe(reps: int = 20) -> dict:
+    import ctypes
+
+    import torch
+
+    import residual_add_rmsnorm_amd as arn
+    from residual_add_rmsnorm_amd import build as _build
+
+    lib = ctypes.CDLL(_build.PROBE_LIB_PATH)
+    f = lib.arn_probe_rows
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 + [
+        ctypes.c_void_p]
+    st = torch.cuda.current_stream().cuda_stream
+
+    def timed(go):
+        for _ in range(3):
+            go()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            go()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    out = {}
+    for name, rows, hidden, stride in ROW_PROBE_SHAPES:
+        n = rows * stride
+        x = torch.randn(n, device="cuda").to(torch.bfloat16)
+        r = torch.randn(n, device="cuda").to(torch.bfloat16)
+        o = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        nbytes = rows * hidden * 2 * 4
+        res = {}
+        xv, rv, ov = (t.view(rows, stride)[:, :hidden] for t in (x, r, o))
+        w = torch.ones(hidden, dtype=torch.bfloat16, device="cuda")
+        # the kernel first and last, so a drift over the run shows
+        for tag in ("fused_kernel_first",):
+            us = timed(lambda: arn.fused_add_rmsnorm(xv, rv, w, 1e-6, out=ov))
+            res[tag] = {"us": round(us, 2), "GB_per_s": round((nbytes + 2 * hidden) / us / 1e3, 1),
+                        "plan": arn.last_plan()}
+        for g in (1, 2, 4):
+            for mode in (0, 1, 2, 3):
+                if g == 1 and mode:
+                    continue
+
+                def go():
+                    rc = f(mode, g, x.data_ptr(), r.data_ptr(), o.data_ptr(), rows, hidden * 2,
+                           stride * 2, st)
+                    if rc != 0:
+                        raise RuntimeError(f"arn_probe_rows status {rc}")
+                us = timed(go)
+                res[f"rows_per_block{g}_mode{mode}"] = {"us": round(us, 2),
+                                                        "GB_per_s": round(nbytes / us / 1e3, 1)}
+        us = timed(lambda: arn.fused_add_rmsnorm(xv, rv, w, 1e-6, out=ov))
+        res["fused_kernel_last"] = {"us": round(us, 2),
+                                    "GB_per_s": round((nbytes + 2 * hidden) / us / 1e3, 1),
+                                    "plan": arn.last_plan()}
+        log(f"[bench] row probe {name}: {res}")
+        out[name] = res
+        del x, r, o, xv, rv, ov
+        torch.cuda.empty_cache()
+    out["grid_stride_2r2w"] = mix_ceilings(["2r2w"])["2r2w"]
+    return out
 
 
 # Fixed traffic per launch: the plain norm 4096 wide (the rmsnorm workload's

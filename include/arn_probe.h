@@ -43,6 +43,21 @@ int arn_probe_stream_many(int reads, int writes16, int writes8, const void *cons
                           hipStream_t stream);
 
 /*
+ * The fused norm's row traffic without its arithmetic: for `rows` rows of
+ * row_bytes bytes (multiple of 16, at most 16384) at a pitch of
+ * stride_bytes, read x and res, write res in place and out.  Each block of
+ * 512 threads owns rows_per_block (1, 2 or 4) consecutive rows and orders
+ * its accesses by `mode`: 0 row by row (load, store, store), 1 all loads
+ * then each row's stores, 2 all loads then all residual stores then all
+ * output stores, 3 the next row's loads before the current row's stores.
+ * x, res, out: device buffers of (rows - 1) * stride_bytes + row_bytes
+ * bytes.  Returns 0, 1 (invalid argument), 2 (rows_per_block not served)
+ * or 3 (launch failed).
+ */
+int arn_probe_rows(int mode, int rows_per_block, const void *x, void *res, void *out,
+                   int64_t rows, int64_t row_bytes, int64_t stride_bytes, hipStream_t stream);
+
+/*
  * One launch of an empty kernel (grid 1..2^24 blocks of 1..1024 threads) on
  * `stream`: the launch cost that bounds the time per call of small kernels
  * from below.  Returns 0, 1 (invalid argument) or 3 (launch failed).

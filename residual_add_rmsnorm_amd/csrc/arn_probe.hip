@@ -105,6 +105,100 @@ hipError_t launch_many(int block, const ManyArgs& a, int grid, hipStream_t strea
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)block), params, 0, stream);
 }
 
+// The fused norm's traffic with the row structure kept: each block owns G
+// consecutive rows (row pitch `stride` bytes, `len` bytes used, len <= 16
+// KiB), and for every row reads x and the residual and writes the residual
+// back in place and the output.  512 threads, two 16-byte vectors per
+// thread per row and stream; buffer records end at `len`, so a shorter row
+// drops the excess loads and stores.  The order of a block's accesses is
+// the variable:
+//   MODE 0  row by row: load x_g, r_g, store r_g, o_g (the operator's order)
+//   MODE 1  all loads of the G rows, then each row's two stores
+//   MODE 2  all loads, then every residual store, then every output store
+//   MODE 3  one row ahead: load row g+1 before storing row g
+struct RowsArgs {
+  const char* x;
+  char* res;
+  char* out;
+  int64_t rows;
+  int64_t stride;
+  uint32_t len;
+};
+
+template <int G, int MODE>
+__global__ __launch_bounds__(512) void rows_kernel(const RowsArgs p) {
+  constexpr int kNv = 2;
+  const uint32_t off = threadIdx.x * 16u;
+  auto rs = [&](const char* base, int64_t row) {
+    return rsrc(base + row * p.stride, row < p.rows ? p.len : 0u);
+  };
+  const int64_t row0 = (int64_t)blockIdx.x * G;
+  u32x4 xv[G][kNv], rv[G][kNv];
+  auto load_row = [&](int g) {
+#pragma unroll
+    for (int k = 0; k < kNv; ++k) {
+      xv[g][k] = __builtin_amdgcn_raw_buffer_load_b128(rs(p.x, row0 + g), (int)(off + k * 8192u), 0, kNt);
+      rv[g][k] = __builtin_amdgcn_raw_buffer_load_b128(rs(p.res, row0 + g), (int)(off + k * 8192u), 0, kNt);
+    }
+  };
+  auto store_res = [&](int g) {
+#pragma unroll
+    for (int k = 0; k < kNv; ++k) {
+      __builtin_amdgcn_raw_buffer_store_b128(xv[g][k] + rv[g][k], rs(p.res, row0 + g),
+                                             (int)(off + k * 8192u), 0, kNt);
+    }
+  };
+  auto store_out = [&](int g) {
+#pragma unroll
+    for (int k = 0; k < kNv; ++k) {
+      __builtin_amdgcn_raw_buffer_store_b128(xv[g][k] ^ rv[g][k], rs(p.out, row0 + g),
+                                             (int)(off + k * 8192u), 0, kNt);
+    }
+  };
+  if constexpr (MODE == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      load_row(g);
+      store_res(g);
+      store_out(g);
+    }
+  } else if constexpr (MODE == 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) load_row(g);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      store_res(g);
+      store_out(g);
+    }
+  } else if constexpr (MODE == 2) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) load_row(g);
+#pragma unroll
+    for (int g = 0; g < G; ++g) store_res(g);
+#pragma unroll
+    for (int g = 0; g < G; ++g) store_out(g);
+  } else {
+    load_row(0);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (g + 1 < G) load_row(g + 1);
+      store_res(g);
+      store_out(g);
+    }
+  }
+}
+
+template <int G>
+const void* rows_fn(int mode) {
+  switch (mode) {
+    case 0: return (const void*)&rows_kernel<G, 0>;
+    case 1: return (const void*)&rows_kernel<G, 1>;
+    case 2: return (const void*)&rows_kernel<G, 2>;
+    case 3: return (const void*)&rows_kernel<G, 3>;
+    default: return nullptr;
+  }
+}
+
 // Does nothing: the cost of a launch itself, the floor under any small
 // kernel's time per call.
 __global__ __launch_bounds__(1024) void empty_kernel() {}
@@ -179,4 +273,33 @@ extern "C" int arn_probe_stream_many(int reads, int writes16, int writes8,
     return 2;
   }
   return e == hipSuccess ? 0 : 3;
+}
+
+extern "C" int arn_probe_rows(int mode, int rows_per_block, const void* x, void* res, void* out,
+                              int64_t rows, int64_t row_bytes, int64_t stride_bytes,
+                              hipStream_t stream) {
+  if (!x || !res || !out || rows <= 0 || row_bytes <= 0 || row_bytes > 16384 ||
+      row_bytes % 16 != 0 || stride_bytes < row_bytes || mode < 0 || mode > 3) {
+    return 1;
+  }
+  const void* fn = nullptr;
+  if (rows_per_block == 1) fn = rows_fn<1>(mode);
+  if (rows_per_block == 2) fn = rows_fn<2>(mode);
+  if (rows_per_block == 4) fn = rows_fn<4>(mode);
+  if (!fn) return 2;
+  const int64_t grid = (rows + rows_per_block - 1) / rows_per_block;
+  if (grid > (int64_t(1) << 24) || (rows - 1) * stride_bytes + row_bytes > (int64_t(1) << 40)) {
+    return 1;
+  }
+  RowsArgs a;
+  a.x = static_cast<const char*>(x);
+  a.res = static_cast<char*>(res);
+  a.out = static_cast<char*>(out);
+  a.rows = rows;
+  a.stride = stride_bytes;
+  a.len = (uint32_t)row_bytes;
+  void* params[] = {&a};
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(512u), params, 0, stream) == hipSuccess
+             ? 0
+             : 3;
 }

@@ -58,9 +58,9 @@ def test_probe_library_exports_its_header():
     out = subprocess.run(["nm", "-D", "--defined-only", build.PROBE_LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r" T (arn_\w+)", out))
-    assert header_functions(PROBE_HEADER) == ["arn_probe_empty", "arn_probe_stream",
-                                              "arn_probe_stream_many"]
-    assert {"arn_probe_stream", "arn_probe_empty", "arn_probe_stream_many"} <= exported
+    assert header_functions(PROBE_HEADER) == ["arn_probe_empty", "arn_probe_rows",
+                                              "arn_probe_stream", "arn_probe_stream_many"]
+    assert set(header_functions(PROBE_HEADER)) <= exported
     probe = ctypes.CDLL(build.PROBE_LIB_PATH)
     f = probe.arn_probe_stream
     f.restype = ctypes.c_int
@@ -75,6 +75,16 @@ def test_probe_library_exports_its_header():
     e.restype = ctypes.c_int
     e.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     assert e(0, 64, None) == 1 and e(1, 2048, None) == 1
+    r = probe.arn_probe_rows
+    r.restype = ctypes.c_int
+    r.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 + [
+        ctypes.c_void_p]
+    assert r(0, 1, 16, 16, 16, 4, 16384 + 16, 16400, None) == 1   # row over 16 KiB
+    assert r(0, 1, 16, 16, 16, 4, 100, 128, None) == 1            # not a multiple of 16
+    assert r(4, 1, 16, 16, 16, 4, 128, 128, None) == 1            # mode
+    assert r(0, 1, 16, 16, 16, 4, 128, 64, None) == 1             # pitch below the row
+    assert r(0, 3, 16, 16, 16, 4, 128, 128, None) == 2            # rows per block
+
 
 
 def test_hip_imports_resolve_in_torch_runtime():
