@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define ARN_ABI_VERSION 5
+#define ARN_ABI_VERSION 6
 
 enum arn_dtype { ARN_BF16 = 0, ARN_FP16 = 1 };
 enum arn_fp8_mode { ARN_FP8_STATIC = 0, ARN_FP8_DYNAMIC = 1 };
@@ -310,6 +310,33 @@ int arn_fp8_gemm_preshuffled_ws(void *c, int64_t ldc, int out_dtype,
                                 const float *scale_b, int b_per_row,
                                 int64_t m, int64_t n, int64_t k, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * arn_fp8_gemm_preshuffled_ws without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the split-K partial
+ * tiles and tile counters live in a device array inside the library, of
+ * ARN_NOALLOC_SCRATCH_BYTES (8 MiB) per GPU, held until the process ends.
+ * The call allocates nothing and calls no allocating routine.
+ *   - Served: shapes whose workspace (arn_fp8_gemm_workspace_bytes) fits
+ *     the array -- m <= 64 with n <= 4032, m <= 32 with n <= 8128, m <= 16
+ *     with n <= 16256 -- else ARN_EUNSUPPORTED, nothing launched (use
+ *     arn_fp8_gemm_preshuffled_ws with a workspace of your own).
+ *   - The array is shared by every call on one GPU: calls that may run at
+ *     the same time on that GPU (other streams, other threads) race and
+ *     give wrong results; serialise them.  Each completed call leaves the
+ *     array ready for the next one.  The first call on a device clears the
+ *     array's counters with a small kernel on `stream`.
+ *   - Other arguments, results and status codes as in
+ *     arn_fp8_gemm_preshuffled_ws (bit-identical results for the same
+ *     shape and device); ARN_ELAUNCH if the array cannot be located.
+ */
+#define ARN_NOALLOC_SCRATCH_BYTES (8u << 20)
+int arn_fp8_gemm_preshuffled_noalloc(void *c, int64_t ldc, int out_dtype,
+                                     const uint8_t *a, int64_t lda, const float *scale_a,
+                                     int a_per_row, const uint8_t *b_shuffled,
+                                     const float *scale_b, int b_per_row,
+                                     int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *arn_status_str(int status);

@@ -27,6 +27,7 @@ __all__ = [
     "sum_add_rmsnorm",
     "silu_and_mul", "silu_and_mul_fp8",
     "fp8_gemm", "fp8_weight_preshuffle", "PreshuffledWeight", "fp8_gemm_workspace",
+    "fp8_gemm_preshuffled_noalloc",
     "set_tile", "set_gemm_config", "set_gemm_splits", "last_plan", "ArnError",
 ]
 
@@ -471,6 +472,41 @@ def fp8_gemm(a: torch.Tensor, scale_a: torch.Tensor, b, scale_b: torch.Tensor,
                                   b.data_ptr(), b.stride(0), scale_b.data_ptr(), b_rows,
                                   m, n, k, _stream(a))
     _lib.check(st, name)
+    return out
+
+
+def fp8_gemm_preshuffled_noalloc(a: torch.Tensor, scale_a: torch.Tensor, b: "PreshuffledWeight",
+                                 scale_b: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp8_gemm with a pre-shuffled weight and K split across blocks as with a
+    workspace, the partial tiles held in the library's own device array
+    (arn_fp8_gemm_preshuffled_noalloc): no device memory is allocated when
+    `out` is given.  Calls on one GPU must not overlap."""
+    if not isinstance(b, PreshuffledWeight):
+        raise ValueError("b must be a PreshuffledWeight")
+    _check_device(a)
+    if a.dtype not in (FP8_DTYPE, torch.uint8) or a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("a must be a 2-D e4m3 (or uint8) tensor with unit column stride")
+    if b.device != a.device:
+        raise ValueError("a and b must be on the same device")
+    m, k = a.shape
+    n, kb = b.shape
+    if kb != k:
+        raise ValueError("a and b must have the same K")
+    for sc, cnt, nm in ((scale_a, m, "scale_a"), (scale_b, n, "scale_b")):
+        if (sc.dtype != torch.float32 or not sc.is_contiguous() or sc.numel() not in (1, cnt)
+                or sc.device != a.device):
+            raise ValueError(f"{nm} must hold 1 or {cnt} contiguous float32 values")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    if out.shape != (m, n) or out.dtype not in _DTYPES or out.stride(1) != 1:
+        raise ValueError("out must be [M, N] bfloat16/float16 with unit column stride")
+    with _on(a):
+        st = _lib.load().arn_fp8_gemm_preshuffled_noalloc(
+            out.data_ptr(), out.stride(0), _DTYPES[out.dtype], a.data_ptr(), a.stride(0),
+            scale_a.data_ptr(), int(scale_a.numel() > 1 or m == 1), b.data.data_ptr(),
+            scale_b.data_ptr(), int(scale_b.numel() > 1 or n == 1), m, n, k, _stream(a))
+    _lib.check(st, "arn_fp8_gemm_preshuffled_noalloc")
     return out
 
 

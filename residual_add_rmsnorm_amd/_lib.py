@@ -55,6 +55,9 @@ SIGNATURES = {
     "arn_fp8_gemm_preshuffled_ws": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _i64, _vp,
                                                    ctypes.c_int, _vp, _vp, ctypes.c_int, _i64,
                                                    _i64, _i64, _vp, ctypes.c_size_t, _vp]),
+    "arn_fp8_gemm_preshuffled_noalloc": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _i64, _vp,
+                                                        ctypes.c_int, _vp, _vp, ctypes.c_int,
+                                                        _i64, _i64, _i64, _vp]),
     "arn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "arn_abi_version": (ctypes.c_int, []),
     "arn_set_tile": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
@@ -63,9 +66,10 @@ SIGNATURES = {
     "arn_last_plan": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_size_t]),
 }
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 OUT_16BIT, OUT_FP8_STATIC, OUT_FP8_DYNAMIC = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class NormArgs(ctypes.Structure):

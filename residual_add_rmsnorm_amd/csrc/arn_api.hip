@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "arn.h"
 #include "arn_tuning.h"
@@ -614,9 +615,78 @@ int run_preshuffle(uint8_t* dst, const uint8_t* b, int64_t ldb, int64_t n, int64
   return e == hipSuccess ? ARN_OK : ARN_ELAUNCH;
 }
 
+// ---------------------------------------------------------------------------
+// Device scratch of arn_fp8_gemm_preshuffled_noalloc: the split-K partial
+// tiles and tile counters, in a file-scope array instead of a caller's
+// workspace, for callers that cannot allocate.  Every GPU the library runs
+// on holds its own copy until the process ends; its address is taken once
+// per device with hipGetSymbolAddress (the array's name is only a host-side
+// stand-in), and that address is what the kernels receive.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[ARN_NOALLOC_SCRATCH_BYTES];
+
+__global__ void zero_words(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  int status = ARN_ELAUNCH;
+};
+ScratchSlot g_scratch[64];
+
+// The current device's scratch address.  On the first call for a device the
+// address is looked up and the counter region is cleared by a small kernel
+// on `stream` (no memset node, so a capturing caller records a kernel);
+// every completed call leaves the counters at zero again.
+int scratch_for_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ARN_ELAUNCH;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return;
+    const size_t bytes = ARN_NOALLOC_SCRATCH_BYTES;
+    const int64_t cbytes = ws_counter_bytes(bytes);
+    uint32_t* counters =
+        reinterpret_cast<uint32_t*>(static_cast<char*>(ptr) + ws_usable(bytes) - cbytes);
+    const int64_t words = cbytes / 4;
+    void* params[] = {&counters, const_cast<int64_t*>(&words)};
+    if (hipLaunchKernel((const void*)&zero_words, dim3((unsigned)((words + 255) / 256)),
+                        dim3(256u), params, 0, stream) != hipSuccess) {
+      return;
+    }
+    slot.ptr = ptr;
+    slot.status = ARN_OK;
+  });
+  *out = slot.ptr;
+  return slot.status;
+}
+
 }  // namespace
 
 extern "C" {
+
+int arn_fp8_gemm_preshuffled_noalloc(void* c, int64_t ldc, int out_dtype, const uint8_t* a,
+                                     int64_t lda, const float* scale_a, int a_per_row,
+                                     const uint8_t* b_shuffled, const float* scale_b,
+                                     int b_per_row, int64_t m, int64_t n, int64_t k,
+                                     hipStream_t stream) {
+  // The argument checks of the workspace entry point, then the size limit,
+  // all before any HIP call.
+  if (out_dtype != ARN_BF16 && out_dtype != ARN_FP16) return ARN_EINVAL;
+  if (m < 0 || n < 0 || k <= 0 || lda < k || ldc < n) return ARN_EINVAL;
+  if (m == 0 || n == 0) return ARN_OK;
+  if (!c || !a || !b_shuffled || !scale_a || !scale_b) return ARN_EINVAL;
+  if (workspace_bytes(m, n) > (int64_t)ARN_NOALLOC_SCRATCH_BYTES) return ARN_EUNSUPPORTED;
+  void* ws = nullptr;
+  const int st = scratch_for_current_device(stream, &ws);
+  if (st != ARN_OK) return st;
+  return run_gemm(true, c, ldc, out_dtype, a, lda, scale_a, a_per_row, b_shuffled, 0, scale_b,
+                  b_per_row, m, n, k, ws, ARN_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 int arn_fp8_gemm(void* c, int64_t ldc, int out_dtype, const uint8_t* a, int64_t lda,
                  const float* scale_a, int a_per_row, const uint8_t* b, int64_t ldb,

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_function(lib):
     for name in header_functions() + header_functions(TUNING_HEADER):
         assert name in exported, name
         assert getattr(lib, name) is not None
-    assert lib.arn_abi_version() == _lib.ABI_VERSION == 5
+    assert lib.arn_abi_version() == _lib.ABI_VERSION == 6
 
 
 def test_probe_library_exports_its_header():
@@ -84,7 +84,6 @@ def test_probe_library_exports_its_header():
     assert r(4, 1, 16, 16, 16, 4, 128, 128, None) == 1            # mode
     assert r(0, 1, 16, 16, 16, 4, 128, 64, None) == 1             # pitch below the row
     assert r(0, 3, 16, 16, 16, 4, 128, 128, None) == 2            # rows per block
-
 
 
 def test_hip_imports_resolve_in_torch_runtime():
@@ -268,3 +267,27 @@ def test_sum_descriptor_residual_aliasing_a_part(lib):
     ptrs = (ctypes.c_void_p * 2)(Q, R)
     a = _sum_args(parts=ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)))
     assert lib.arn_sum_add_rmsnorm(ctypes.byref(a)) == _lib.EINVAL
+
+
+def test_noalloc_gemm_limits_and_refusals(lib):
+    """The no-allocation GEMM serves exactly the shapes whose workspace fits
+    its 8 MiB device array (the limits the header states) and refuses the
+    others, and invalid arguments, before any HIP call."""
+    cap = _lib.NOALLOC_SCRATCH_BYTES
+    assert cap == 8 << 20
+    for m, nmax in ((64, 4032), (32, 8128), (16, 16256), (1, 16256)):
+        assert lib.arn_fp8_gemm_workspace_bytes(m, nmax, 4096) <= cap
+        assert lib.arn_fp8_gemm_workspace_bytes(m, nmax + 1, 4096) > cap
+    f = lib.arn_fp8_gemm_preshuffled_noalloc
+    P = 1 << 20
+    args = lambda m, n, k=256, dt=0, lda=256, ldc=None: (  # noqa: E731
+        P, ldc if ldc is not None else n, dt, P, lda, P, 1, P, P, 1, m, n, k, None)
+    assert f(*args(64, 4033)) == _lib.EUNSUPPORTED
+    assert f(*args(16, 16257)) == _lib.EUNSUPPORTED
+    assert f(*args(4, 64, dt=2)) == _lib.EINVAL
+    assert f(*args(4, 64, lda=128)) == _lib.EINVAL
+    assert f(*args(-1, 64)) == _lib.EINVAL
+    assert f(*args(0, 64)) == _lib.OK and f(*args(4, 0)) == _lib.OK
+    a = list(args(4, 64))
+    a[0] = None
+    assert f(*a) == _lib.EINVAL
