@@ -10,7 +10,8 @@
  *       out.bin: residual after the call (fused only), out (rows*stride u16,
  *                or rows*stride e4m3 bytes), scales (rows f32, dynamic only)
  *       variance_size 0 calls the named entry point; > 0 goes through arn_norm.
- *   arn_client gemm <rowmajor|preshuffled|preshuffled_ws> m n k in.bin out.bin
+ *   arn_client gemm <rowmajor|preshuffled|preshuffled_ws|preshuffled_noalloc> m n k in.bin
+ *              out.bin
  *       in.bin : a (m*k bytes), b (n*k bytes), scale_a (m f32), scale_b (n f32)
  *       out.bin: c (m*n bf16)
  *   arn_client sum <none|dynamic> <bf16|fp16> nparts rows hidden stride eps in.bin out.bin
@@ -167,7 +168,8 @@ static int run_norm(char **argv) {
 
 static int run_gemm(char **argv) {
   const int with_ws = strcmp(argv[0], "preshuffled_ws") == 0;
-  const int pre = with_ws || strcmp(argv[0], "preshuffled") == 0;
+  const int noalloc = strcmp(argv[0], "preshuffled_noalloc") == 0;
+  const int pre = with_ws || noalloc || strcmp(argv[0], "preshuffled") == 0;
   const int64_t m = atoll(argv[1]), n = atoll(argv[2]), k = atoll(argv[3]);
   const size_t sa_bytes = (size_t)m * 4, sb_bytes = (size_t)n * 4;
   const size_t in_size = (size_t)(m * k + n * k) + sa_bytes + sb_bytes;
@@ -202,6 +204,12 @@ static int run_gemm(char **argv) {
       }
       HIP_OK(hipStreamSynchronize(stream));
       HIP_OK(hipFree(ws));
+    } else if (noalloc) {
+      /* the library's own split-K array: no workspace; twice, as above */
+      for (int rep = 0; rep < 2; ++rep) {
+        ARN_OK_(arn_fp8_gemm_preshuffled_noalloc(c, n, ARN_BF16, (const uint8_t *)a, k, sa, 1,
+                                                 (const uint8_t *)bs, sb, 1, m, n, k, stream));
+      }
     } else {
       ARN_OK_(arn_fp8_gemm_preshuffled(c, n, ARN_BF16, (const uint8_t *)a, k, sa, 1,
                                        (const uint8_t *)bs, sb, 1, m, n, k, stream));

@@ -138,6 +138,17 @@ int main(void) {
   EXPECT_EQ(arn_fp8_weight_preshuffle(dev8, NULL, 128, 64, 128, 0), ARN_EINVAL, "shuffle null src");
   EXPECT_EQ(arn_fp8_weight_preshuffle(dev8, dev8, 64, 64, 128, 0), ARN_EINVAL, "shuffle ldb < k");
 
+  /* the no-allocation GEMM: argument and size refusals before any HIP call */
+  EXPECT_EQ(arn_fp8_gemm_preshuffled_noalloc(dev, 64, 7, dev8, 128, devf, 1, dev8, devf, 1, 4, 64,
+                                             128, 0), ARN_EINVAL, "noalloc bad dtype");
+  EXPECT_EQ(arn_fp8_gemm_preshuffled_noalloc(NULL, 64, ARN_BF16, dev8, 128, devf, 1, dev8, devf, 1,
+                                             4, 64, 128, 0), ARN_EINVAL, "noalloc null c");
+  EXPECT_EQ(arn_fp8_gemm_preshuffled_noalloc(dev, 4033, ARN_BF16, dev8, 128, devf, 1, dev8, devf,
+                                             1, 64, 4033, 128, 0), ARN_EUNSUPPORTED,
+            "noalloc past its array");
+  EXPECT_EQ(arn_fp8_gemm_preshuffled_noalloc(dev, 64, ARN_BF16, dev8, 128, devf, 1, dev8, devf, 1,
+                                             0, 64, 128, 0), ARN_OK, "noalloc m = 0");
+
   /* tuning knobs and the plan buffer */
   EXPECT_EQ(arn_set_tile(3, 3), ARN_EINVAL, "tile not compiled");
   EXPECT_EQ(arn_set_tile(0, 0), ARN_OK, "tile reset");

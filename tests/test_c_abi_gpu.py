@@ -102,7 +102,8 @@ def test_norm_from_c(client, orc, tmp_path, form, fp8, dtype, rows, hidden, stri
         assert_scales_close(scales, ref["scales"], dtype)
 
 
-@pytest.mark.parametrize("layout", ["rowmajor", "preshuffled", "preshuffled_ws"])
+@pytest.mark.parametrize("layout", ["rowmajor", "preshuffled", "preshuffled_ws",
+                                    "preshuffled_noalloc"])
 def test_gemm_from_c(client, orc, tmp_path, layout):
     rng = np.random.default_rng(17)
     m, n, k = 9, 300, 1040   # few columns, M >= 8: with a workspace, K is split

@@ -48,6 +48,32 @@ def test_random_norm_cases(orc, dtype, rows, hidden, pad, fp8, fused, weighted, 
              s=0.02 if fp8 == "static" else None)
 
 
+@settings(max_examples=40, deadline=None, derandomize=True, database=None,
+          suppress_health_check=list(HealthCheck))
+@given(rows=st.integers(1, 40), hidden=hidden_st, log2_scale=st.integers(-133, 120),
+       fp8=st.sampled_from([None, "static", "dynamic"]), fused=st.booleans(),
+       eps=st.sampled_from([0.0, 1e-38, 1e-30, 1e-6]), seed=st.integers(0, 2**31 - 1))
+def test_random_bf16_magnitudes(orc, rows, hidden, log2_scale, fp8, fused, eps, seed):
+    """bf16 rows of every magnitude bf16 holds (N(0,1) scaled by 2^-133 ..
+    2^120, clipped to +-2^126), so the sum of squares may underflow or
+    overflow fp32, with eps from 0 up: the same checks as every other case."""
+    from tests.test_parity_gpu import run_case
+
+    print(f"[case] magnitude bf16 rows={rows} hidden={hidden} 2^{log2_scale} fp8={fp8} "
+          f"fused={fused} eps={eps} seed={seed}", flush=True)
+    rng = np.random.default_rng(seed)
+    scale = 2.0 ** log2_scale
+
+    def draw(mult):
+        f = np.clip(rng.standard_normal((rows, hidden)) * scale * mult, -2.0**126, 2.0**126)
+        return W.to_bits(f.astype(np.float32), "bf16")
+    x = draw(1.0)
+    r = draw(0.5) if fused else None
+    w = W.to_bits(rng.uniform(0.5, 1.5, hidden).astype(np.float32), "bf16")
+    run_case(orc, dtype="bf16", x=x, res=r, w=w, eps=eps, hidden=hidden, fp8=fp8,
+             s=2.0**-6 if fp8 == "static" else None)
+
+
 @SETTINGS
 @given(m=st.integers(1, 64), n=st.integers(1, 3000), k16=st.integers(1, 512),
        layout=st.sampled_from(["rowmajor", "preshuffled", "splitk"]),
