@@ -111,6 +111,77 @@ __device__ __forceinline__ Raw<VEC> ones() {
 }
 
 // ---------------------------------------------------------------------------
+// Packed 16-bit arithmetic on whole 32-bit words (two elements each).
+// ---------------------------------------------------------------------------
+// The fp16 residual add as one packed fp16 add per word (v_pk_add_f16).  It
+// equals the fp32 add of the two values rounded to fp16: fp32 carries at
+// least 2 * 11 + 2 bits, so rounding the exact sum first to fp32 and then to
+// fp16 gives the correctly rounded fp16 sum (double-rounding theorem), which
+// is what the packed add returns.  (bf16 has no packed add on gfx950; its
+// sum goes through fp32 and v_cvt_pk_bf16_f32.)
+template <int VEC>
+__device__ __forceinline__ Raw<VEC> add_f16(const Raw<VEC>& a, const Raw<VEC>& b) {
+  if constexpr (VEC == 1) {
+    return __builtin_bit_cast(uint16_t, (_Float16)(__builtin_bit_cast(_Float16, a) +
+                                                    __builtin_bit_cast(_Float16, b)));
+  } else if constexpr (VEC == 2) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) + __builtin_bit_cast(f16x2, b));
+  } else {
+    Raw<VEC> r;
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) {
+      // Each element is copied to a plain word first: clang's
+      // __builtin_bit_cast of an ext-vector element expression (a[i])
+      // reads element 0 whatever i is.
+      const uint32_t ai = a[i], bi = b[i];
+      r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ai) + __builtin_bit_cast(f16x2, bi));
+    }
+    return r;
+  }
+}
+
+// acc + the squares of the two 16-bit values of a word, with one
+// v_dot2_f32_{f16,bf16}: the products are exact in fp32, the sums fp32.
+template <int DT>
+__device__ __forceinline__ float dot2_self(uint32_t w, float acc) {
+  if constexpr (DT == kBF16) {
+    const bf16x2 v = __builtin_bit_cast(bf16x2, w);
+    return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+  } else {
+    const f16x2 v = __builtin_bit_cast(f16x2, w);
+    return __builtin_amdgcn_fdot2(v, v, acc, false);
+  }
+}
+
+// acc + the sum of squares of the VEC values of one vector.
+template <int DT, int VEC>
+__device__ __forceinline__ float sum_squares(const Raw<VEC>& r, float acc) {
+  if constexpr (VEC == 1) {
+    const float f = lo_f32<DT>((uint32_t)r);
+    return __builtin_fmaf(f, f, acc);
+  } else if constexpr (VEC == 2) {
+    return dot2_self<DT>(r, acc);
+  } else {
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) {
+      const uint32_t w = r[i];
+      acc = dot2_self<DT>(w, acc);
+    }
+    return acc;
+  }
+}
+
+// A -0.0f the compiler cannot see through.  fma(a, b, -0) is a * b exactly
+// (signed zeros included), and with an fp16 operand and an addend the
+// compiler does not know it selects v_fma_mix_f32, which reads the fp16 half
+// of a register directly instead of converting it first.
+__device__ __forceinline__ float opaque_neg_zero() {
+  float z = -0.0f;
+  asm volatile("" : "+v"(z));
+  return z;
+}
+
+// ---------------------------------------------------------------------------
 // OCP e4m3: clamp to the finite range, then the packed gfx950 convert
 // (round to nearest even).  word_sel picks which 16-bit half of the
 // destination dword receives the two codes.

@@ -163,24 +163,24 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
     if constexpr (kRes) {
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
-        float f[VEC];
+        if constexpr (DT == kFP16) {
+          xr[k] = add_f16<VEC>(xr[k], rr[k]);  // = fp32 add rounded to fp16, two per op
+        } else {
+          float f[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) f[e] = elem<DT, VEC>(xr[k], e) + elem<DT, VEC>(rr[k], e);
-        xr[k] = pack<DT, VEC>(f);
+          for (int e = 0; e < VEC; ++e) f[e] = elem<DT, VEC>(xr[k], e) + elem<DT, VEC>(rr[k], e);
+          xr[k] = pack<DT, VEC>(f);
+        }
         store16<VEC>(xr[k], rrs, off16 + k * kStep16);
       }
     }
+    // fma(a, b, nz) is a * b; with an fp16 operand it reads the half directly.
+    const float nz = opaque_neg_zero();
     float ss = 0.0f;
     float mx = 0.0f;
     if (a.var_cols == a.hidden) {
 #pragma unroll
-      for (int k = 0; k < NV; ++k) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const float rf = elem<DT, VEC>(xr[k], e);
-          ss = __builtin_fmaf(rf, rf, ss);
-        }
-      }
+      for (int k = 0; k < NV; ++k) ss = sum_squares<DT, VEC>(xr[k], ss);
     } else {
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
       for (int k = 0; k < NV; ++k) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          mx = fmaxf(mx, fabsf(elem<DT, VEC>(xr[k], e) * elem<DT, VEC>(wr[k], e)));
+          mx = fmaxf(mx, fabsf(__builtin_fmaf(elem<DT, VEC>(xr[k], e), elem<DT, VEC>(wr[k], e), nz)));
         }
       }
     }
@@ -307,8 +307,12 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
           float y[VEC];
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
-            const float rv = kScaled ? elem<DT, VEC>(xr[k], e) * rmul : elem<DT, VEC>(xr[k], e);
-            y[e] = rv * inv * elem<DT, VEC>(wr[k], e) * qmul;
+            if constexpr (kScaled) {
+              y[e] = elem<DT, VEC>(xr[k], e) * rmul * inv * elem<DT, VEC>(wr[k], e) * qmul;
+            } else {
+              const float t = __builtin_fmaf(elem<DT, VEC>(xr[k], e), inv, nz);
+              y[e] = __builtin_fmaf(elem<DT, VEC>(wr[k], e), t, nz) * qmul;
+            }
           }
           store8<VEC>(pack_fp8<VEC>(y), ors, off8 + k * kStep8);
         }
@@ -320,8 +324,12 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
           float y[VEC];
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
-            const float rv = kScaled ? elem<DT, VEC>(xr[k], e) * rmul : elem<DT, VEC>(xr[k], e);
-            y[e] = rv * inv * elem<DT, VEC>(wr[k], e);
+            if constexpr (kScaled) {
+              y[e] = elem<DT, VEC>(xr[k], e) * rmul * inv * elem<DT, VEC>(wr[k], e);
+            } else {
+              const float t = __builtin_fmaf(elem<DT, VEC>(xr[k], e), inv, nz);
+              y[e] = __builtin_fmaf(elem<DT, VEC>(wr[k], e), t, nz);
+            }
           }
           store16<VEC>(pack<DT, VEC>(y), ors, off16 + k * kStep16);
         }
