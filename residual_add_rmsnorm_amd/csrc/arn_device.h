@@ -191,7 +191,10 @@ __device__ __forceinline__ float sat448(float v) {
 }
 
 __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+  // The first convert writes the low 16 bits and keeps the high 16 of its
+  // third operand, which the second convert then overwrites: any value
+  // already in a register serves (a literal 0 would cost a move).
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), __float_as_int(a), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
   return (uint32_t)w;
 }
