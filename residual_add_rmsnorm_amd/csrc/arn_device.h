@@ -252,6 +252,14 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
+// Max over the wave in fp64 (lane permutes; for rows whose values leave
+// fp32's range, so not on the hot path).  Every lane gets the result.
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmax(v, __shfl_xor(v, m));
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Row accesses go through buffer instructions: a descriptor in SGPRs holds
 // the row's base address and its length in bytes (num_records), and each

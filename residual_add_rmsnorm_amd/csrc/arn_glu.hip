@@ -47,6 +47,24 @@ __device__ __forceinline__ float silu(float g) {
   return g * (g >= 0.0f ? r : e * r);
 }
 
+// silu(g) * u in fp64, for rows whose outputs leave fp32's range.
+// exp(-|g|) = 2^-(n + fr) with n = floor(|g| log2 e) and fr in [0, 1): the
+// hardware exp2 of -fr, then an exact fp64 ldexp by -n, so gates far below
+// -87 (where silu() underflows in fp32) keep their value down to fp64's
+// range.  The product with u is exact up to fp64 rounding.  n - a must
+// subtract the rounded a (exact, as both are fp32 values within a factor of
+// two of each other or a < 1): contracting |g| log2 e into it as an fma
+// would leave the rounding error of a, which for |g| near 2^66 is about
+// 2^43, in the exponent.
+[[maybe_unused]] __device__ __forceinline__ double silu_mul_f64(float g, float u) {
+#pragma clang fp contract(off)
+  const float a = fabsf(g) * 1.44269504088896341f;
+  const float n = floorf(a);
+  const double e = __builtin_ldexp((double)__builtin_amdgcn_exp2f(n - a), -(int)fminf(n, 2000.0f));
+  const double r = (double)__builtin_amdgcn_rcpf(1.0f + (float)e);
+  return (double)g * (g >= 0.0f ? r : e * r) * (double)u;
+}
+
 template <int DT, int MODE, int VEC, int NV, int WPR, int RPB>
 __global__ __launch_bounds__(64 * WPR * RPB) void glu_kernel(const GluArgs a) {
   constexpr bool kStatic = MODE == kGluStatic;
@@ -104,7 +122,72 @@ __global__ __launch_bounds__(64 * WPR * RPB) void glu_kernel(const GluArgs a) {
 #pragma unroll
       for (int i = 0; i < WPR; ++i) mx = fmaxf(mx, red_max[rib * WPR + i]);
     }
-    qmul = mx > 0.0f ? 448.0f / mx : 0.0f;
+    // code = e4m3(y / scale) with scale = max|y| / 448 rounded to fp32.  A
+    // row whose max|y| is not in [2^-96, 2^128) ("wide": a product silu(g)
+    // * u overflowed, or every output is tiny or zero) forms its outputs
+    // again in fp64 from the inputs (read a second time; they are never
+    // written), one vector at a time and twice -- once for the max, once
+    // for the codes -- so the branch holds few registers.  Its codes divide
+    // by the stored scale in fp64 (infinite quotients where the scale
+    // rounded to zero, zero where it overflowed, as y / scale gives).  Rows
+    // sharing a barrier enter together; for a row that did not need it the
+    // fp64 outputs round to the same codes within the one-step rule.
+    const bool wide = !(mx >= 0x1p-96f && mx <= 3.4028234e38f);
+    bool enter_w = wide;
+    if constexpr (WPR > 1 && RPB > 1) {
+      enter_w = false;
+#pragma unroll
+      for (int rr = 0; rr < RPB; ++rr) {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < WPR; ++i) m = fmaxf(m, red_max[rr * WPR + i]);
+        enter_w = enter_w || !(m >= 0x1p-96f && m <= 3.4028234e38f);
+      }
+    }
+    if (enter_w) {
+      __shared__ double red_wide[WPR * RPB];
+      double m2 = 0.0;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        asm volatile("" ::: "memory");  // one vector's reloads at a time
+        const Raw<VEC> g2 = load16<VEC, kCacheStream>(grs, off16 + k * kStep16);
+        const Raw<VEC> u2 = load16<VEC, kCacheStream>(urs, off16 + k * kStep16);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          m2 = fmax(m2, fabs(silu_mul_f64(elem<DT, VEC>(g2, e), elem<DT, VEC>(u2, e))));
+        }
+      }
+      m2 = wave_max_f64(m2);
+      if constexpr (WPR > 1) {
+        if (lane == 0) red_wide[wave] = m2;
+        __syncthreads();
+        m2 = 0.0;
+#pragma unroll
+        for (int i = 0; i < WPR; ++i) m2 = fmax(m2, red_wide[rib * WPR + i]);
+      }
+      const float s = (float)(m2 * (1.0 / 448.0));
+      if (active && t == 0) a.scale[row] = s;
+      const double qd = m2 > 0.0 ? 1.0 / (double)s : 0.0;  // an all-zero row: codes 0
+      const __amdgpu_buffer_rsrc_t ors = row_rsrc(
+          static_cast<uint8_t*>(a.out) + arow * a.out_stride, active ? (uint32_t)a.d : 0u);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        asm volatile("" ::: "memory");
+        const Raw<VEC> g2 = load16<VEC, kCacheStream>(grs, off16 + k * kStep16);
+        const Raw<VEC> u2 = load16<VEC, kCacheStream>(urs, off16 + k * kStep16);
+        float v[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          v[e] = (float)(silu_mul_f64(elem<DT, VEC>(g2, e), elem<DT, VEC>(u2, e)) * qd);
+        }
+        store8<VEC>(pack_fp8<VEC>(v), ors, off8 + k * kStep8);
+      }
+      return;
+    }
+    // Any other row: max|y| in [2^-96, 2^128), so 448 / max|y| and the
+    // scale max|y| / 448 are normal fp32 numbers, and an output that lost
+    // low bits below 2^-126 is off by less than 2^-54 of the max.
+    qmul = 448.0f / mx;
     if (active && t == 0) a.scale[row] = mx / 448.0f;
   }
 

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
   __shared__ float red_sum[WPR * RPB];  // one slot per wave
   __shared__ float red_max[WPR * RPB];
   __shared__ float red_scaled[WPR * RPB];  // rescaled sums (rows out of fp32 range)
-  __shared__ float red_scaled_max[WPR * RPB];
+  __shared__ float red_wide[WPR * RPB];    // dynamic e4m3: rescaled maxima
 
   {
     // 1. Load the row: x (and residual) into registers.  Vectors past the
@@ -192,6 +192,9 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
         }
       }
     }
+    // Dynamic e4m3: max |p| over the products p = r * w.  For 16-bit r and w
+    // each product is exact in fp32 unless it leaves fp32's range (|p| >=
+    // 2^128, or below 2^-126 with low bits lost).
     if constexpr (kDynamic) {
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
@@ -250,7 +253,6 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
     if (enter) {
       const float sc = ss < 1.0f ? 0x1p76f : 0x1p-76f;
       float s2 = 0.0f;
-      float m2 = 0.0f;  // dynamic e4m3: max |(r * sc) * w|, which cannot overflow
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         // The packed row passes through an empty asm the compiler cannot
@@ -262,41 +264,141 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
         for (int e = 0; e < VEC; ++e) {
           const float rf = elem<DT, VEC>(xr[k], e) * sc;
           s2 = __builtin_fmaf(rf, col0 + e < a.var_cols ? rf : 0.0f, s2);
-          if constexpr (kDynamic) m2 = fmaxf(m2, fabsf(rf * elem<DT, VEC>(wr[k], e)));
         }
       }
       s2 = wave_sum(s2);
-      if constexpr (kDynamic) m2 = wave_max(m2);
       if constexpr (WPR > 1) {
-        if (lane == 0) {
-          red_scaled[wave] = s2;
-          if constexpr (kDynamic) red_scaled_max[wave] = m2;
-        }
+        if (lane == 0) red_scaled[wave] = s2;
         __syncthreads();
         s2 = 0.0f;
-        m2 = 0.0f;
 #pragma unroll
-        for (int i = 0; i < WPR; ++i) {
-          s2 += red_scaled[rib * WPR + i];
-          if constexpr (kDynamic) m2 = fmaxf(m2, red_scaled_max[rib * WPR + i]);
-        }
+        for (int i = 0; i < WPR; ++i) s2 += red_scaled[rib * WPR + i];
       }
       if (rescue) {
         rmul = sc;
         inv = rsqrtf(__builtin_fmaf(s2, a.inv_var, a.eps * sc * sc));
-        mx = m2;
       }
     }
 
+    // 4. y = r * inv * w, stored as 16 bits or as e4m3 codes.
     if constexpr (kDynamic) {
-      const float amax = mx * inv;  // mx already carries rmul
-      qmul = amax > 0.0f ? 448.0f / amax : 0.0f;
-      if (active && t == 0) a.scale[row] = amax / 448.0f;
+      // code = e4m3(y / scale) with scale = max|y| / 448.  Since y = p * inv
+      // * rmul with one positive factor for the whole row, y / scale =
+      // p * 448 / max|p|: the codes need the products and their max only.
+      // That holds in fp32 while max|p| lies in [2^-96, 2^128): then 448 /
+      // max|p| is finite and a product that lost low bits below 2^-126 is
+      // off by less than 2^-54 of the max.  A row outside that range ("wide":
+      // a product overflowed, or every product is below 2^-96 or zero) forms
+      // its products from operands scaled by f = 2^-64 each (overflow) or
+      // 2^64 each (tiny; an operand that would pass fp32's largest value is
+      // held there, which only happens when the other one is zero):
+      //  * down: the largest product's operands are >= 1, so they and it
+      //    stay exact, the max is >= 1, and what smaller operands lose in
+      //    scaling is below 2^-86 of it;
+      //  * up: every operand stays exact and so does every product (at
+      //    most 22 significant bits, none below 2^-138), and a max still
+      //    below 2^-96 (products under 2^-224) is lifted by 2^100 more
+      //    before 448 / max is formed.
+      // The scale is formed in fp64 from the max and the factors, so it is
+      // the rounded quotient whatever its magnitude.
+      const bool wide = !(mx >= 0x1p-96f && mx <= 3.4028234e38f);
+      const float f = wide ? (mx > 1.0f ? 0x1p-64f : 0x1p64f) : 1.0f;
+      bool enter_w = wide;
+      if constexpr (WPR > 1 && RPB > 1) {
+        enter_w = false;
+#pragma unroll
+        for (int rr = 0; rr < RPB; ++rr) {
+          float m = 0.0f;
+#pragma unroll
+          for (int i = 0; i < WPR; ++i) m = fmaxf(m, red_max[rr * WPR + i]);
+          enter_w = enter_w || !(m >= 0x1p-96f && m <= 3.4028234e38f);
+        }
+      }
+      // scaled product of one element (wide rows)
+      auto pscaled = [&](int k, int e) {
+        const float xs = __builtin_amdgcn_fmed3f(elem<DT, VEC>(xr[k], e) * f, -3.4028234e38f,
+                                                 3.4028234e38f);
+        const float ws = __builtin_amdgcn_fmed3f(elem<DT, VEC>(wr[k], e) * f, -3.4028234e38f,
+                                                 3.4028234e38f);
+        return xs * ws;
+      };
+      float m = mx;
+      if (enter_w) {
+        float m2 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          asm volatile("" : "+v"(xr[k]), "+v"(wr[k]));
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) m2 = fmaxf(m2, fabsf(pscaled(k, e)));
+        }
+        m2 = wave_max(m2);
+        if constexpr (WPR > 1) {
+          if (lane == 0) red_wide[wave] = m2;
+          __syncthreads();
+          m2 = 0.0f;
+#pragma unroll
+          for (int i = 0; i < WPR; ++i) m2 = fmaxf(m2, red_wide[rib * WPR + i]);
+        }
+        if (wide) m = m2;
+      }
+      // Products as formed are p / ung (ung = 1 / (f * f)); wide rows then
+      // lift them.  The scale uses only exact powers of two besides the
+      // fp64 products, so it is max|y| / 448 rounded once to fp32 up to the
+      // fp64 rounding of its factors.
+      const double ung = f == 1.0f ? 1.0 : (f < 1.0f ? 0x1p128 : 0x1p-128);
+      const float lift = m < 0x1p-96f ? 0x1p100f : 1.0f;
+      const double yscale = (double)inv * (double)rmul;  // y = p * yscale
+      const float s = (float)((double)m * ung * yscale * (1.0 / 448.0));
+      if (active && t == 0) a.scale[row] = s;
+      // code = e4m3(y / s) = e4m3(formed product * lift * c).  While s is a
+      // normal fp32 number it is max|y| / 448 to within half an fp32 ulp, so
+      // c = 448 / (lifted max).  Otherwise the stored value is coarse or not
+      // finite and the codes follow it: c = yscale / (s * lift / ung), in
+      // fp64 -- infinite when s rounded to zero under a nonzero row, zero
+      // when it overflowed, as y / s is.
+      float c;
+      if (s >= 0x1p-126f && s <= 3.4028234e38f) {
+        c = 448.0f / (m * lift);
+      } else {
+        c = m > 0.0f ? (float)(yscale * ung / ((double)s * (double)lift)) : 0.0f;
+      }
+      const __amdgpu_buffer_rsrc_t ors = row_rsrc(
+          static_cast<uint8_t*>(a.out) + arow * a.out_stride, active ? row_bytes8 : 0u);
+      if (wide) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          // (Laundered so the scaled operands are formed again here rather
+          // than kept live from the max loop.)
+          asm volatile("" : "+v"(xr[k]), "+v"(wr[k]));
+          float y[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) y[e] = (pscaled(k, e) * lift) * c;
+          store8<VEC>(pack_fp8<VEC>(y), ors, off8 + k * kStep8);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          float y[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            y[e] = __builtin_fmaf(elem<DT, VEC>(xr[k], e), elem<DT, VEC>(wr[k], e), nz) * c;
+          }
+          store8<VEC>(pack_fp8<VEC>(y), ors, off8 + k * kStep8);
+        }
+      }
+      return;
     }
 
-    // 4. y = r * inv * w, stored as 16 bits or as e4m3 codes.  A rescaled
-    //    row takes its own copy of the loop (y = ((r * rmul) * inv) * w), so
-    //    the other rows pay no extra multiply per element.
+    // Static e4m3 multiplies by 1/s.  For fp16 rows the product r * w is
+    // exact in fp32 (at most 22 significant bits, magnitude within
+    // [2^-48, 2^32] or zero), so y / s = (r * w) * (inv / s) with the row
+    // constant inv / s; held at fp32's largest value if it overflows, which
+    // still saturates every nonzero product and keeps zeros zero.  bf16
+    // products can leave fp32's range, so bf16 rows form y first.
+    const float cq = kStatic ? fminf(inv * qmul, 3.4028234e38f) : 0.0f;
+
+    // A rescaled row takes its own copy of the loop (y = ((r * rmul) * inv)
+    // * w), so the other rows pay no extra multiply per element.
     auto emit = [&](auto scaled) {
       constexpr bool kScaled = decltype(scaled)::value;
       if constexpr (kFp8) {
@@ -309,6 +411,8 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
           for (int e = 0; e < VEC; ++e) {
             if constexpr (kScaled) {
               y[e] = elem<DT, VEC>(xr[k], e) * rmul * inv * elem<DT, VEC>(wr[k], e) * qmul;
+            } else if constexpr (DT == kFP16) {
+              y[e] = __builtin_fmaf(elem<DT, VEC>(xr[k], e), elem<DT, VEC>(wr[k], e), nz) * cq;
             } else {
               const float t = __builtin_fmaf(elem<DT, VEC>(xr[k], e), inv, nz);
               y[e] = __builtin_fmaf(elem<DT, VEC>(wr[k], e), t, nz) * qmul;

@@ -8,7 +8,7 @@ Comparison rules (the stated tolerances of the operator):
     with p = 8, emin = -126 (bf16) or p = 11, emin = -14 (fp16); NaN matches NaN;
   * e4m3 codes: within one step, |ord(q_gpu) - ord(q_ref)| <= 1 with
     ord(c) = +-(c & 0x7f) by the sign bit (so +0 and -0 are equal);
-  * dynamic scales: relative error <= rho;
+  * dynamic scales: relative error <= rho; zero or overflowed ones equal;
   * e4m3 GEMM outputs: see gemm_tol.
 """
 import json
@@ -88,9 +88,10 @@ def assert_codes_close(q_gpu: np.ndarray, q_ref: np.ndarray, what="codes"):
 def assert_scales_close(s_gpu: np.ndarray, s_ref: np.ndarray, dtype: str):
     s_gpu = s_gpu.astype(np.float64)
     s_ref = s_ref.astype(np.float64)
-    zero = s_ref == 0
-    assert np.all(s_gpu[zero] == 0)
-    rel = np.abs(s_gpu[~zero] - s_ref[~zero]) / np.abs(s_ref[~zero])
+    exact = (s_ref == 0) | ~np.isfinite(s_ref)  # zero or overflowed: equal
+    assert np.array_equal(s_gpu[exact], s_ref[exact], equal_nan=True), \
+        f"scales: {s_gpu[exact]} vs {s_ref[exact]}"
+    rel = np.abs(s_gpu[~exact] - s_ref[~exact]) / np.abs(s_ref[~exact])
     assert np.all(rel <= RHO[dtype]), f"scales: max rel err {rel.max()}"
 
 

@@ -356,6 +356,64 @@ def test_bf16_rows_out_of_fp32_range_variance_size(orc, k):
     assert_y_close(bits(y), ref["y"], "bf16")
 
 
+# Dynamic e4m3 rows whose products r * w leave fp32's range although their
+# sums of squares may not: tiny weights under ordinary activations, huge
+# weights under large activations, both tiny (the scale then underflows to an
+# fp32 subnormal or to zero), and a single product past 2^128.  Each family
+# is one weight vector; the rows vary the activations' magnitude.  Values
+# are drawn away from zero (|v| = scale * U(1, 2), random sign), so no y is
+# exactly zero where the scale rounds to zero (0 / 0 there); the residual
+# takes x's signs, so x + residual does not cancel.
+WIDE_WEIGHTS = {
+    "tiny_w": (2.0**-120, [1.0, 2.0**30, 2.0**-60, 2.0**-131, 2.0**10]),
+    "denormal_w": (2.0**-130, [2.0**-131, 1.0, 2.0**40, 2.0**-100, 2.0**90]),
+    "huge_w": (2.0**80, [2.0**50, 2.0**60, 1.0, 2.0**-131, 2.0**-100]),
+    "mixed_w": (None, [1.0, 2.0**100, 2.0**-120, 2.0**40, 2.0**-131]),
+}
+
+
+def _wide_rows(family, hidden, seed):
+    """(x, residual, w) bit patterns for one family of WIDE_WEIGHTS."""
+    rng = np.random.default_rng(seed)
+    wscale, xscales = WIDE_WEIGHTS[family]
+
+    def mag(n, scale):
+        return np.minimum(scale * rng.uniform(1.0, 2.0, n), 2.0**127)
+
+    if wscale is None:  # one huge, one tiny and one subnormal column among ordinary ones
+        wf = rng.uniform(0.5, 1.5, hidden)
+        wf[[3, hidden // 2, hidden - 1]] = [2.0**100, 2.0**-125, 2.0**-132]
+    else:
+        wf = mag(hidden, wscale)
+    sign = np.where(rng.random((len(xscales), hidden)) < 0.5, -1.0, 1.0)
+    xf = sign * np.stack([mag(hidden, sc) for sc in xscales])
+    rf = sign * np.stack([mag(hidden, sc) for sc in xscales])
+    return tuple(W.to_bits(a.astype(np.float32), "bf16") for a in (xf, rf, wf))
+
+
+@pytest.mark.parametrize("tile", [None, (1, 4), (2, 2), (8, 1), (16, 1)],
+                         ids=["auto", "wpr1", "wpr2", "wpr8", "wpr16"])
+@pytest.mark.parametrize("eps", [0.0, 1e-6])
+@pytest.mark.parametrize("family", list(WIDE_WEIGHTS))
+def test_bf16_dynamic_products_out_of_fp32_range(orc, family, eps, tile):
+    """Codes and scales of rows whose products overflow fp32 or fall below
+    2^-96 (down to products under 2^-256 whose scale rounds to zero) match
+    the fp64 definition; with and without the residual, every tile shape
+    (one-row-per-wave, two rows per block sharing a barrier, multi-wave)."""
+    arn = _arn()
+    hidden = 2048
+    x, r, w = _wide_rows(family, hidden, seed=31)
+    if tile:
+        arn.set_tile(*tile)
+    try:
+        run_case(orc, dtype="bf16", x=x, res=None, w=w, eps=eps, hidden=hidden, fp8="dynamic")
+        run_case(orc, dtype="bf16", x=x, res=r, w=w, eps=eps, hidden=hidden, fp8="dynamic")
+        if tile:
+            assert f"/wpr{tile[0]}/nv{tile[1]}/" in arn.last_plan()
+    finally:
+        arn.set_tile(0, 0)
+
+
 def test_zero_rows_eps0_give_nan(orc):
     x = np.zeros((4, 256), np.uint16)
     run_case(orc, dtype="bf16", x=x, res=None, w=None, eps=0.0, hidden=256)

@@ -111,6 +111,50 @@ def test_extreme_gates(orc):
     run_glu(orc, "bf16", x, d)
 
 
+# Dynamic e4m3 rows whose outputs leave fp32's range: (gate magnitude,
+# gate sign or None for random, up magnitude), magnitudes scale * U(1, 2).
+# Values are never zero, so no y is 0 where the scale rounds to zero.
+WIDE_GLU_ROWS = [
+    (2.0**-131, None, 1.0),          # subnormal gates: outputs near 2^-132
+    (2.0**-60, None, 2.0**-60),      # outputs near 2^-121 (448 / max overflows fp32)
+    (2.0**66, 1.0, 2.0**66),         # products past 2^128, scale finite
+    (2.0**70, 1.0, 2.0**70),         # outputs near 2^141: the scale overflows, codes 0
+    (2.0**-131, None, 2.0**-131),    # outputs near 2^-263: the scale rounds to zero
+    (1.0, None, 1.0),                # an ordinary row beside them
+]
+
+
+def _wide_glu_rows(d, seed):
+    rng = np.random.default_rng(seed)
+    rows = []
+    for gs, gsign, us in WIDE_GLU_ROWS:
+        sign = gsign if gsign is not None else np.where(rng.random(d) < 0.5, -1.0, 1.0)
+        g = sign * np.minimum(gs * rng.uniform(1.0, 2.0, d), 2.0**127)
+        u = np.where(rng.random(d) < 0.5, -1.0, 1.0) * np.minimum(us * rng.uniform(1.0, 2.0, d),
+                                                                  2.0**127)
+        rows.append(np.concatenate([g, u]))
+    return W.to_bits(np.stack(rows).astype(np.float32), "bf16")
+
+
+@pytest.mark.parametrize("tile", [None, (1, 2), (2, 2), (8, 1), (16, 1)],
+                         ids=["auto", "wpr1", "wpr2", "wpr8", "wpr16"])
+def test_dynamic_outputs_out_of_fp32_range(orc, tile):
+    """Codes and scales of rows whose outputs silu(g) * u overflow fp32,
+    fall far below its normal range, or give a scale that overflows or
+    rounds to zero, against the fp64 definition; every tile shape."""
+    import residual_add_rmsnorm_amd as arn
+
+    d = 1024
+    if tile:
+        arn.set_tile(*tile)
+    try:
+        run_glu(orc, "bf16", _wide_glu_rows(d, 61), d, fp8="dynamic")
+        if tile:
+            assert f"wpr{tile[0]}/nv{tile[1]}/" in arn.last_plan(), arn.last_plan()
+    finally:
+        arn.set_tile(0, 0)
+
+
 def test_zero_row_dynamic(orc):
     x = _x("bf16", 5, 768, seed=55)
     x[2] = 0
