@@ -436,6 +436,46 @@ def test_fp8_static_saturates(orc):
              fp8="static", s=1.0 / 256)
 
 
+def _magnitude_rows(dtype, hidden, seed):
+    """Rows of one magnitude each: ordinary, the dtype's smallest normal and
+    subnormal values, its largest, and a row with exact zeros."""
+    rng = np.random.default_rng(seed)
+    big = 2.0**126 if dtype == "bf16" else 30000.0  # x + residual stays finite
+    tiny = 2.0**-126 if dtype == "bf16" else 2.0**-14
+    sub = 2.0**-131 if dtype == "bf16" else 2.0**-20
+    rows = []
+    for sc in (1.0, tiny, sub, big):
+        rows.append(np.where(rng.random(hidden) < 0.5, -1.0, 1.0) * sc * rng.uniform(0.5, 1.0, hidden))
+    z = rng.standard_normal(hidden)
+    z[::3] = 0.0
+    rows.append(z)
+    return W.to_bits(np.stack(rows).astype(np.float32), dtype)
+
+
+@pytest.mark.parametrize("s", [2.0**-126, 1e-30, 1e-6, 1.0, 1e30, 3.4e38])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_fp8_static_scale_range(orc, dtype, s):
+    """Static e4m3 over the range of normal fp32 scales, on rows of every
+    magnitude the dtype holds (zeros included): saturation at one end, codes
+    rounding to zero at the other, both signs."""
+    hidden = 1024
+    x = _magnitude_rows(dtype, hidden, 70)
+    r = _magnitude_rows(dtype, hidden, 71)
+    w = W.to_bits(np.random.default_rng(72).uniform(0.25, 2.0, hidden).astype(np.float32), dtype)
+    run_case(orc, dtype=dtype, x=x, res=None, w=w, eps=1e-6, hidden=hidden, fp8="static", s=s)
+    run_case(orc, dtype=dtype, x=x, res=r, w=w, eps=0.0, hidden=hidden, fp8="static", s=s)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_fp8_dynamic_every_magnitude(orc, dtype):
+    hidden = 1024
+    x = _magnitude_rows(dtype, hidden, 73)
+    r = _magnitude_rows(dtype, hidden, 74)
+    w = W.to_bits(np.random.default_rng(75).uniform(0.25, 2.0, hidden).astype(np.float32), dtype)
+    run_case(orc, dtype=dtype, x=x, res=None, w=w, eps=1e-6, hidden=hidden, fp8="dynamic")
+    run_case(orc, dtype=dtype, x=x, res=r, w=w, eps=0.0, hidden=hidden, fp8="dynamic")
+
+
 def test_zero_rows_launch_nothing():
     arn = _arn()
     x = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
