@@ -154,7 +154,11 @@ __global__ __launch_bounds__(64 * WPR * RPB) void glu_kernel(const GluArgs a) {
         const Raw<VEC> u2 = load16<VEC, kCacheStream>(urs, off16 + k * kStep16);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          m2 = fmax(m2, fabs(silu_mul_f64(elem<DT, VEC>(g2, e), elem<DT, VEC>(u2, e))));
+          // One element at a time: its inputs wait on the running max, so
+          // the fp64 temporaries of several elements are never live together.
+          float g = elem<DT, VEC>(g2, e), u = elem<DT, VEC>(u2, e);
+          asm volatile("" : "+v"(g), "+v"(u) : "v"(m2));
+          m2 = fmax(m2, fabs(silu_mul_f64(g, u)));
         }
       }
       m2 = wave_max_f64(m2);
@@ -178,7 +182,9 @@ __global__ __launch_bounds__(64 * WPR * RPB) void glu_kernel(const GluArgs a) {
         float v[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          v[e] = (float)(silu_mul_f64(elem<DT, VEC>(g2, e), elem<DT, VEC>(u2, e)) * qd);
+          float g = elem<DT, VEC>(g2, e), u = elem<DT, VEC>(u2, e);
+          if (e > 0) asm volatile("" : "+v"(g), "+v"(u) : "v"(v[e - 1]));
+          v[e] = (float)(silu_mul_f64(g, u) * qd);
         }
         store8<VEC>(pack_fp8<VEC>(v), ors, off8 + k * kStep8);
       }
