@@ -105,10 +105,20 @@ int arn_fused_add_rmsnorm(void *out, int64_t out_stride,
  *   out, out_stride : rows x hidden bytes of e4m3 codes, written.
  *   scale           : fp8_mode ARN_FP8_STATIC -- ONE fp32 on the device, the
  *                     dequant scale s, read: code = e4m3(y / s), y ~ code * s.
+ *                     s must be a positive normal fp32 number (2^-126 up to
+ *                     the largest finite value); it is read by the kernel,
+ *                     so it is not checked.
  *                     fp8_mode ARN_FP8_DYNAMIC -- `rows` fp32 on the device,
- *                     written: scale[i] = max_j |y_ij| / 448 and
- *                     code = e4m3(y / scale[i]); a row whose max is 0 gets
- *                     scale 0 and all-zero codes.
+ *                     written: scale[i] = max_j |y_ij| / 448 rounded to fp32
+ *                     and code = e4m3(y / scale[i]); a row whose max is 0
+ *                     gets scale 0 and all-zero codes.  Rows whose max or
+ *                     products leave fp32's range are served too: a scale
+ *                     that rounds to a subnormal, to zero or past the
+ *                     largest finite value is stored as rounded, and the
+ *                     codes follow the stored value.
+ *   Codes are within one e4m3 step of e4m3(y / scale) for exact y: the
+ *   kernel forms the quotient in fp32, so a value within about one fp32
+ *   rounding of a tie between two codes may take either.
  */
 int arn_rmsnorm_fp8(uint8_t *out, int64_t out_stride, float *scale, int fp8_mode,
                     const void *x, int64_t x_stride,
