@@ -155,6 +155,22 @@ def test_dynamic_outputs_out_of_fp32_range(orc, tile):
         arn.set_tile(0, 0)
 
 
+@pytest.mark.parametrize("s", [2.0**-126, 1e-30, 1e-6, 1.0, 1e30, 3.4e38])
+def test_static_scale_range(orc, s):
+    """Static e4m3 over the range of normal fp32 scales: saturation at one
+    end, codes rounding to zero at the other, on gates and ups of ordinary,
+    tiny and large magnitude."""
+    rng = np.random.default_rng(62)
+    d = 1024
+    rows = []
+    for sc in (1.0, 2.0**-60, 2.0**40):
+        g = np.where(rng.random(d) < 0.5, -1.0, 1.0) * sc * rng.uniform(0.5, 2.0, d)
+        u = np.where(rng.random(d) < 0.5, -1.0, 1.0) * sc * rng.uniform(0.5, 2.0, d)
+        rows.append(np.concatenate([g, u]))
+    x = W.to_bits(np.stack(rows).astype(np.float32), "bf16")
+    run_glu(orc, "bf16", x, d, fp8="static", s=s)
+
+
 def test_zero_row_dynamic(orc):
     x = _x("bf16", 5, 768, seed=55)
     x[2] = 0
