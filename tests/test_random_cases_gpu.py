@@ -74,6 +74,36 @@ def test_random_bf16_magnitudes(orc, rows, hidden, log2_scale, fp8, fused, eps, 
              s=2.0**-6 if fp8 == "static" else None)
 
 
+@settings(max_examples=50, deadline=None, derandomize=True, database=None,
+          suppress_health_check=list(HealthCheck))
+@given(rows=st.integers(1, 16), hidden=st.integers(1, 520).map(lambda v: 8 * v),
+       log2_x=st.integers(-133, 120), log2_w=st.integers(-133, 110),
+       fp8=st.sampled_from(["static", "dynamic"]), fused=st.booleans(),
+       eps=st.sampled_from([0.0, 1e-38, 1e-6]), log2_s=st.integers(-126, 127),
+       seed=st.integers(0, 2**31 - 1))
+def test_random_bf16_weight_magnitudes(orc, rows, hidden, log2_x, log2_w, fp8, fused, eps,
+                                       log2_s, seed):
+    """e4m3 outputs of bf16 rows whose activations and weights both range
+    over every magnitude bf16 holds, so the products r * w and the dynamic
+    scale may leave fp32's range in either direction; static scales over
+    the normal fp32 range.  Weights stay below 2^111 so that |y| stays below
+    2^128, which the static kind forms in fp32."""
+    from tests.test_parity_gpu import run_case
+
+    print(f"[case] weight magnitude bf16 rows={rows} hidden={hidden} x 2^{log2_x} w 2^{log2_w} "
+          f"fp8={fp8} fused={fused} eps={eps} s 2^{log2_s} seed={seed}", flush=True)
+    rng = np.random.default_rng(seed)
+
+    def draw(shape, log2_scale, mult=1.0):
+        f = np.clip(rng.standard_normal(shape) * 2.0**log2_scale * mult, -2.0**126, 2.0**126)
+        return W.to_bits(f.astype(np.float32), "bf16")
+    x = draw((rows, hidden), log2_x)
+    r = draw((rows, hidden), log2_x, 0.5) if fused else None
+    w = draw((hidden,), log2_w)
+    run_case(orc, dtype="bf16", x=x, res=r, w=w, eps=eps, hidden=hidden, fp8=fp8,
+             s=2.0**log2_s if fp8 == "static" else None)
+
+
 @SETTINGS
 @given(m=st.integers(1, 64), n=st.integers(1, 3000), k16=st.integers(1, 512),
        layout=st.sampled_from(["rowmajor", "preshuffled", "splitk"]),
