@@ -191,10 +191,11 @@ __global__ __launch_bounds__(64 * WPR * RPB) void glu_kernel(const GluArgs a) {
       return;
     }
     // Any other row: max|y| in [2^-96, 2^128), so 448 / max|y| and the
-    // scale max|y| / 448 are normal fp32 numbers, and an output that lost
-    // low bits below 2^-126 is off by less than 2^-54 of the max.
-    qmul = 448.0f / mx;
-    if (active && t == 0) a.scale[row] = mx / 448.0f;
+    // scale max|y| / 448 are normal fp32 numbers (the reciprocal of mx / 448
+    // in [2^-105, 2^120) by the hardware's 1-ulp v_rcp_f32), and an output
+    // that lost low bits below 2^-126 is off by less than 2^-54 of the max.
+    qmul = __builtin_amdgcn_rcpf(mx * (1.0f / 448.0f));
+    if (active && t == 0) a.scale[row] = mx * (1.0f / 448.0f);
   }
 
   if constexpr (kFp8) {

@@ -301,7 +301,9 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
       //    before 448 / max is formed.
       // The scale is formed in fp64 from the max and the factors, so it is
       // the rounded quotient whatever its magnitude.
-      const bool wide = !(mx >= 0x1p-96f && mx <= 3.4028234e38f);
+      // (mx >= 0, so its bits order like its value: one subtract and one
+      // unsigned compare test 2^-96 <= mx <= fp32's largest value.)
+      const bool wide = __float_as_uint(mx) - 0x0F800000u > 0x7F7FFFFFu - 0x0F800000u;
       const float f = wide ? (mx > 1.0f ? 0x1p-64f : 0x1p64f) : 1.0f;
       bool enter_w = wide;
       if constexpr (WPR > 1 && RPB > 1) {
@@ -341,26 +343,39 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
         }
         if (wide) m = m2;
       }
-      // Products as formed are p / ung (ung = 1 / (f * f)); wide rows then
-      // lift them.  The scale uses only exact powers of two besides the
-      // fp64 products, so it is max|y| / 448 rounded once to fp32 up to the
-      // fp64 rounding of its factors.
-      const double ung = f == 1.0f ? 1.0 : (f < 1.0f ? 0x1p128 : 0x1p-128);
-      const float lift = m < 0x1p-96f ? 0x1p100f : 1.0f;
-      const double yscale = (double)inv * (double)rmul;  // y = p * yscale
-      const float s = (float)((double)m * ung * yscale * (1.0 / 448.0));
-      if (active && t == 0) a.scale[row] = s;
-      // code = e4m3(y / s) = e4m3(formed product * lift * c).  While s is a
-      // normal fp32 number it is max|y| / 448 to within half an fp32 ulp, so
-      // c = 448 / (lifted max).  Otherwise the stored value is coarse or not
-      // finite and the codes follow it: c = yscale / (s * lift / ung), in
-      // fp64 -- infinite when s rounded to zero under a nonzero row, zero
-      // when it overflowed, as y / s is.
+      // code = e4m3(y / s) = e4m3(formed product * lift * c).  The usual row
+      // (products in range, no rescaling, max|y| = m * inv well inside
+      // fp32) takes s = (m * inv) / 448 and c = 448 / m in fp32 (a multiply
+      // by 1/448 and a hardware reciprocal, each within an ulp or two), the
+      // scale written by one lane.  Any other row forms s in fp64: products as
+      // formed are p / ung (ung = 1 / (f * f)), so s = m * ung * inv * rmul
+      // / 448 with only exact powers of two besides the fp64 products,
+      // rounded once to fp32.  While that s is a normal fp32 number it is
+      // max|y| / 448 to within half an fp32 ulp and c = 448 / (lifted max);
+      // otherwise the stored value is coarse or not finite and the codes
+      // follow it: c = yscale / (s * lift / ung) in fp64 -- infinite when s
+      // rounded to zero under a nonzero row, zero when it overflowed, as
+      // y / s is.
+      const float amax = m * inv;
       float c;
-      if (s >= 0x1p-126f && s <= 3.4028234e38f) {
-        c = 448.0f / (m * lift);
+      float lift = 1.0f;  // a wide row's max below 2^-96 is lifted by 2^100
+      // (amax >= 0 or NaN; NaN's bits lie above 2^100's.)
+      if (!wide && !rescue && __float_as_uint(amax) - 0x0D800000u <= 0x71800000u - 0x0D800000u) {
+        // m / 448 lies in [2^-105, 2^120), so its hardware reciprocal (1
+        // ulp) is a normal number; the codes allow the fp32 roundings.
+        if (active && t == 0) a.scale[row] = amax * (1.0f / 448.0f);
+        c = __builtin_amdgcn_rcpf(m * (1.0f / 448.0f));
       } else {
-        c = m > 0.0f ? (float)(yscale * ung / ((double)s * (double)lift)) : 0.0f;
+        const double ung = f == 1.0f ? 1.0 : (f < 1.0f ? 0x1p128 : 0x1p-128);
+        const double yscale = (double)inv * (double)rmul;  // y = p * yscale
+        const float s = (float)((double)m * ung * yscale * (1.0 / 448.0));
+        if (active && t == 0) a.scale[row] = s;
+        if (m < 0x1p-96f) lift = 0x1p100f;
+        if (s >= 0x1p-126f && s <= 3.4028234e38f) {
+          c = 448.0f / (m * lift);
+        } else {
+          c = m > 0.0f ? (float)(yscale * ung / ((double)s * (double)lift)) : 0.0f;
+        }
       }
       const __amdgpu_buffer_rsrc_t ors = row_rsrc(
           static_cast<uint8_t*>(a.out) + arow * a.out_stride, active ? row_bytes8 : 0u);
