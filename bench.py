@@ -28,6 +28,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -185,9 +186,11 @@ def time_steps(batch: Batch, steps: int, warmup: int, min_warm_ms: float = 0.0):
     return start.elapsed_time(end), wall
 
 
-def time_graph(batch: Batch, calls: int, replays: int):
+def time_graph(batch: Batch, calls: int, replays: int, per_replay: bool = False):
     """Device time per call with host overhead removed: `calls` launches
-    captured in one HIP graph, replayed `replays` times."""
+    captured in one HIP graph, replayed `replays` times.  With per_replay,
+    each replay is timed by its own pair of events and (mean, median) of
+    the per-call times over the replays is returned."""
     import torch
 
     s = torch.cuda.Stream()
@@ -203,6 +206,16 @@ def time_graph(batch: Batch, calls: int, replays: int):
             batch.call(i)
     g.replay()
     torch.cuda.synchronize()
+    if per_replay:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(replays)]
+        for a, b in evs:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        per = [a.elapsed_time(b) * 1e3 / calls for a, b in evs]
+        return sum(per) / len(per), statistics.median(per)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
@@ -523,9 +536,13 @@ def measure_workload(name: str, steps: int, warmup: int, ceilings: dict | None,
         per_rows = {}
         for r in w.row_counts:
             b = Batch(w, 8, rows=r)
-            dev_us = time_graph(b, calls=64, replays=20)
+            # 30 replays of 64 calls each, timed one by one: the mean, and the
+            # median over the 30 (the decode measurement of the MI300X write-up
+            # takes the median of 30 iterations)
+            dev_us, dev_med = time_graph(b, calls=64, replays=30, per_replay=True)
             e_ms, wall = time_steps(b, 200, 20)
             per_rows[str(r)] = {"device_us_per_call_graph": round(dev_us, 3),
+                                "device_us_per_call_graph_median30": round(dev_med, 3),
                                 "event_us_per_call": round(e_ms * 1e3 / 200, 3),
                                 "host_wall_us_per_call": round(wall * 1e3 / 200, 3),
                                 "bytes_per_call": w.algorithmic_bytes(r),
