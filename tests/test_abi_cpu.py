@@ -7,6 +7,8 @@ import subprocess
 
 import pytest
 import torch
+from hypothesis import HealthCheck, assume, given, settings
+from hypothesis import strategies as st
 
 import residual_add_rmsnorm_amd as arn
 from residual_add_rmsnorm_amd import _lib
@@ -156,6 +158,36 @@ def test_fused_rejects(lib, case):
 ])
 def test_fp8_rejects(lib, fused, case):
     assert _fp8(lib, fused, **case) == _lib.EINVAL
+
+
+# Invalid arguments drawn in combination: any set of them is refused with
+# ARN_EINVAL (before any HIP call: there is no GPU here, so a call that got
+# past validation would report a launch failure instead).
+VIOLATIONS = {
+    "dtype": dict(dt=2), "rows": dict(rows=-3), "hidden": dict(hidden=0),
+    "x_stride": dict(xs=63), "out_stride": dict(os_=32), "eps_negative": dict(eps=-1.0),
+    "eps_nan": dict(eps=float("nan")), "eps_inf": dict(eps=float("inf")),
+    "out_null": dict(out=None), "x_null": dict(x=None), "x_misaligned": dict(x=Q + 1),
+    "w_misaligned": dict(w=S + 1), "scale_null": dict(scale=None),
+    "scale_misaligned": dict(scale=S + 2), "mode": dict(mode=7),
+    "res_null": dict(res=None), "res_stride": dict(rs=10), "res_is_x": dict(res=Q),
+    "res_is_out": dict(res=P), "res_misaligned": dict(res=R + 1),
+}
+
+
+@settings(max_examples=300, deadline=None, derandomize=True, database=None,
+          suppress_health_check=list(HealthCheck))
+@given(names=st.lists(st.sampled_from(sorted(VIOLATIONS)), min_size=1, max_size=6, unique=True),
+       fused=st.booleans())
+def test_any_combination_of_invalid_arguments_is_refused(names, fused):
+    lib = _lib.load()
+    if not fused:
+        names = [n for n in names if not n.startswith("res_")]
+    assume(names)
+    kw = {}
+    for n in names:
+        kw.update(VIOLATIONS[n])
+    assert _fp8(lib, fused, **kw) == _lib.EINVAL, names
 
 
 def test_zero_rows_is_a_no_op(lib):
