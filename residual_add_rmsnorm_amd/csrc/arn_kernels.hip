@@ -223,15 +223,15 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
       }
     }
     float inv = rsqrtf(__builtin_fmaf(ss, a.inv_var, a.eps));
-    float rmul = 1.0f;  // rescaled rows: y = ((r * rmul) * inv) * w
+    float rmul = 1.0f;  // rescued rows: y = ((r * rmul) * inv) * w
 
     // 3b. Rows outside fp32's range.  A bf16 row whose squares underflow
     //     (every |r| below about 2^-75, with eps as small) or whose sum of
     //     squares overflows (|r| near bf16's largest values) gets its sum of
     //     squares again from r * 2^76 or r * 2^-76 -- powers of two, so the
-    //     scaled values are exact -- and y = (r * 2^+-76) / sqrt(ms 2^+-152
-    //     + eps 2^+-152) * w, the same quantity with no intermediate out of
-    //     range.  Other rows never enter this branch, so their results are
+    //     scaled values are exact -- and y = r * (2^+-76 / sqrt(ms 2^+-152
+    //     + eps 2^+-152)) * w, the same quantity, with no intermediate out
+    //     of range unless r times the true factor is.  Other rows never enter this branch, so their results are
     //     the plain formula's, bit for bit.  The branch is uniform over every
     //     row that shares a barrier: with several multi-wave rows per block,
     //     all of them enter when one needs it (their own rescaled sums are
@@ -262,8 +262,10 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
         const int col0 = (t + k * kTPR) * VEC;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float rf = elem<DT, VEC>(xr[k], e) * sc;
-          s2 = __builtin_fmaf(rf, col0 + e < a.var_cols ? rf : 0.0f, s2);
+          // Channels past the variance size are dropped before the scaling:
+          // scaled by 2^76 they could overflow, and inf * 0 is NaN.
+          const float rf = (col0 + e < a.var_cols ? elem<DT, VEC>(xr[k], e) : 0.0f) * sc;
+          s2 = __builtin_fmaf(rf, rf, s2);
         }
       }
       s2 = wave_sum(s2);
@@ -275,8 +277,17 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
         for (int i = 0; i < WPR; ++i) s2 += red_scaled[rib * WPR + i];
       }
       if (rescue) {
-        rmul = sc;
-        inv = rsqrtf(__builtin_fmaf(s2, a.inv_var, a.eps * sc * sc));
+        // The true row factor is is * sc, exact while it is a normal fp32
+        // number; then the row takes the plain order (r * factor) * w.  Only
+        // a factor outside the normal range keeps the scaled operand,
+        // ((r * sc) * is) * w.  (With a variance size below the row the other
+        // channels can be far larger than the ones the mean runs over, and
+        // r * 2^76 would overflow where r * factor does not.)
+        const float is = rsqrtf(__builtin_fmaf(s2, a.inv_var, a.eps * sc * sc));
+        const float g = is * sc;
+        const bool normal = __float_as_uint(g) - 0x00800000u <= 0x7F7FFFFFu - 0x00800000u;
+        rmul = normal ? g : sc;
+        inv = normal ? 1.0f : is;
       }
     }
 

@@ -508,6 +508,37 @@ def test_fp8_dynamic_zero_row_only(orc):
     assert np.all(r["scales"] == 0) and np.all(r["q"] == 0)
 
 
+def test_fp8_dynamic_scales_beyond_fp32(orc):
+    """The stored scale is fp32(amax / 448) and the codes are E(y / scale)
+    against that stored value, wherever it lands:
+      * x = w = 2^-133 (bf16's smallest subnormal), eps = 1e-6: amax is
+        about 2^-256, the scale rounds to 0, y / 0 is +-inf and saturates to
+        +-448 (0x7E / 0xFE), and an exact zero gives 0 / 0, the NaN code;
+      * x = 1, w = 2^-130, eps = 0: y = w exactly, amax / 448 = 2^-138.807
+        rounds to the fp32 subnormal 1170 * 2^-149, and y / scale =
+        2^19 / 1170 = 448.109..., which still rounds to 448;
+      * with the variance over the first channel only, r = (2^-60, 2^100,
+        -2^100, 3), eps = 0: y_1 = 2^160, amax / 448 exceeds fp32's range,
+        the scale is +inf and every code is E(y / inf) = +-0."""
+    b = lambda a: _bits(np.asarray(a, np.float64))
+    t = 2.0**-133
+    r = orc.add_rmsnorm("bf16", b([[t, -t, 0.0, t]]), None, b([t] * 4), 1e-6,
+                        fp8_mode=O.FP8_DYNAMIC)
+    assert r["scales"][0] == 0 and 0 < np.max(np.abs(r["y"][0])) < 2.0**-250
+    assert list(r["q"][0, [0, 1, 3]]) == [0x7E, 0xFE, 0x7E]
+    assert r["q"][0, 2] & 0x7F == 0x7F
+    r = orc.add_rmsnorm("bf16", b([[1.0] * 8]), None, b([2.0**-130] * 8), 0.0,
+                        fp8_mode=O.FP8_DYNAMIC)
+    assert np.all(r["y"][0] == 2.0**-130)
+    assert r["scales"][0] == np.float32(1170 * 2.0**-149)
+    assert Fraction(2**19, 1170) == Fraction(2.0**-130) / Fraction(1170 * 2.0**-149)
+    assert np.all(r["q"][0] == 0x7E)
+    r = orc.add_rmsnorm("bf16", b([[2.0**-60, 2.0**100, -2.0**100, 3.0]]), None, None, 0.0,
+                        fp8_mode=O.FP8_DYNAMIC, variance_size=1)
+    assert r["y"][0, 1] == 2.0**160 and np.isinf(r["scales"][0]) and r["scales"][0] > 0
+    assert list(r["q"][0]) == [0x00, 0x00, 0x80, 0x00]
+
+
 def test_variance_size_override_closed_form(orc):
     """variance_size = k: the mean square of the first k channels
     normalises every channel.  Row (a, .., a | b, .., b) with k a's gives

@@ -680,6 +680,62 @@ def test_norm_variance_size(orc, hidden, k, fused, fp8):
         assert_y_close(bits(out), ref["y"], dtype)
 
 
+# (mean-square channels, other channels, static scale), as powers of two.
+# The row factor 1/rms is 2^60 (a normal number after the rescaled sum),
+# 2^130 (past fp32's largest value) and about 2^-127.5 (subnormal).
+FAR_APART = {
+    "tiny_mean": (-60, 60, 115),
+    "subnormal_mean": (-130, -25, 100),
+    "huge_mean": (127, 100, -30),
+}
+
+
+@pytest.mark.parametrize("k", [1, 3])
+@pytest.mark.parametrize("fp8", [None, "static", "dynamic"])
+@pytest.mark.parametrize("regime", sorted(FAR_APART))
+def test_norm_variance_size_far_apart_channels(orc, regime, k, fp8):
+    """A variance size k below the row, with the k channels the mean runs
+    over and the other channels far apart in magnitude, so the sum of
+    squares needs the rescaled recomputation while r times the row factor
+    stays in range for the other channels: neither the scaled sum nor y may
+    pass through an out-of-range intermediate (2^60 * 2^76 overflows).
+    With tiny mean-square channels under 2^100 channels, y passes 448 times
+    fp32's largest value, so the dynamic scale is +inf and every code is
+    E(y / inf) = +-0, as in the definition."""
+    arn = _arn()
+    rng = np.random.default_rng(66)
+    lv, lo, ls = FAR_APART[regime]
+    if regime == "tiny_mean" and fp8 == "dynamic":
+        lo = 100
+    hidden, rows = 512, 3
+    sign = np.where(rng.random((rows, hidden)) < 0.5, -1.0, 1.0)
+    f = sign * 2.0**lo * rng.uniform(1, 2, (rows, hidden))
+    f[:, :k] = sign[:, :k] * 2.0**lv * rng.uniform(1, 1.9, (rows, k))
+    wf = rng.uniform(0.5, 1.5, hidden)
+    x = W.to_bits(f.astype(np.float32), "bf16")
+    w = W.to_bits(wf.astype(np.float32), "bf16")
+    xd, wd = dev(x, "bf16"), dev(w, "bf16")
+    s = 2.0**ls
+    kw = dict(fp8="dynamic") if fp8 == "dynamic" else (
+        dict(fp8="static", scale=torch.tensor([s], device="cuda")) if fp8 else {})
+    out = arn.norm(xd, wd, 0.0, variance_size=k, **kw)
+    torch.cuda.synchronize()
+    mode = {None: O.FP8_NONE, "static": O.FP8_STATIC, "dynamic": O.FP8_DYNAMIC}[fp8]
+    ref = orc.add_rmsnorm("bf16", x, None, w, 0.0, fp8_mode=mode, static_scale=s,
+                          variance_size=k)
+    if fp8 == "dynamic":
+        q, sc = out
+        if regime == "tiny_mean":
+            assert np.all(np.isinf(ref["scales"]))
+        assert_scales_close(sc.cpu().numpy(), ref["scales"], "bf16")
+        assert_codes_close(codes(q), ref["q"])
+    elif fp8 == "static":
+        assert_codes_close(codes(out[0]), ref["q"])
+    else:
+        assert np.all(np.abs(ref["y"]) < 2.0**127)
+        assert_y_close(bits(out), ref["y"], "bf16")
+
+
 @pytest.mark.parametrize("hidden,k,fused,fp8,tile", [
     (5120, 1000, False, None, "wpr4/nv3/rpb1"), (2048, 2047, False, "dynamic", "wpr2/nv2/rpb2"),
     (2880, 2000, True, "dynamic", "wpr4/nv2/rpb1"), (7168, 4096, True, None, "wpr8/nv2/rpb1")])
