@@ -104,6 +104,83 @@ def test_random_bf16_weight_magnitudes(orc, rows, hidden, log2_x, log2_w, fp8, f
              s=2.0**log2_s if fp8 == "static" else None)
 
 
+@pytest.mark.parametrize("fp8", [None, "static", "dynamic"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@settings(max_examples=25, deadline=None, derandomize=True, database=None,
+          suppress_health_check=list(HealthCheck))
+@given(rows=st.integers(1, 12),
+       hidden=st.one_of(st.integers(1, 3000), st.integers(1, 520).map(lambda v: 8 * v)),
+       kfrac=st.floats(0.0, 1.0), fused=st.booleans(), eps=st.sampled_from([0.0, 1e-38, 1e-6]),
+       seed=st.integers(0, 2**31 - 1))
+def test_random_variance_size_magnitudes(orc, dtype, fp8, rows, hidden, kfrac, fused, eps,
+                                         seed):
+    """The variance-size override with the channels inside the mean and the
+    ones outside it at independent magnitudes, each a power of two drawn from
+    the seed over bf16's whole range (fp16 rows: over fp16's), every output
+    kind, with and without the residual.  The stored
+    residual is compared on every row; y, codes and scales on the rows whose
+    y is finite (and, for 16-bit outputs and bf16 static e4m3, below 2^127,
+    where y itself is formed in fp32 and the dtype's largest value is
+    near)."""
+    import residual_add_rmsnorm_amd as arn
+    from tests._helpers import (assert_codes_close, assert_scales_close, assert_y_close,
+                                bits, codes)
+    import oracle as O
+
+    k = 1 + int(kfrac * (hidden - 1))
+    rng = np.random.default_rng(seed)
+    if dtype == "fp16":
+        top = 15
+        log2_in = int(rng.integers(-24, top + 1))
+        lo = int(rng.integers(-24, top + 1))
+    else:
+        top = 126
+        # mean-square channels tiny, ordinary or huge with equal odds (the
+        # first and last need the rescaled sum unless eps dominates)
+        band = [(-133, -49), (-48, 59), (60, 126)][int(rng.integers(0, 3))]
+        log2_in = int(rng.integers(band[0], band[1] + 1))
+        lo = int(rng.integers(-133, top + 1))
+    log2_s = int(rng.integers(-126, 128))
+    s = 2.0**log2_s
+    print(f"[case] variance size {dtype} rows={rows} hidden={hidden} k={k} in 2^{log2_in} "
+          f"out 2^{lo} fp8={fp8} fused={fused} eps={eps} s 2^{log2_s} seed={seed}", flush=True)
+    lim = 1.9 * 2.0**top
+
+    def draw(mult):
+        f = rng.standard_normal((rows, hidden)) * mult
+        f[:, :k] *= 2.0**log2_in
+        f[:, k:] *= 2.0**lo
+        return W.to_bits(np.clip(f, -lim, lim).astype(np.float32), dtype)
+    x = draw(1.0)
+    r = draw(0.5) if fused else None
+    w = W.to_bits(rng.uniform(0.5, 1.5, hidden).astype(np.float32), dtype)
+    xd, wd = dev(x, dtype), dev(w, dtype)
+    rd = dev(r, dtype) if fused else None
+    kw = dict(fp8="dynamic") if fp8 == "dynamic" else (
+        dict(fp8="static", scale=torch.tensor([s], device="cuda")) if fp8 else {})
+    out = arn.norm(xd, wd, eps, residual=rd, variance_size=k, **kw)
+    torch.cuda.synchronize()
+    mode = {None: O.FP8_NONE, "static": O.FP8_STATIC, "dynamic": O.FP8_DYNAMIC}[fp8]
+    ref = orc.add_rmsnorm(dtype, x, r, w, eps, fp8_mode=mode, static_scale=s,
+                          variance_size=k)
+    if fused:
+        assert np.array_equal(bits(rd), ref["r16"]), "stored residual not bit-exact"
+    ay = np.abs(ref["y"])
+    ok = np.all(np.isfinite(ay), axis=1)
+    if fp8 is None:
+        ok &= np.all(ay < (2.0**127 if dtype == "bf16" else 65504.0), axis=1)
+    elif fp8 == "static" and dtype == "bf16":
+        ok &= np.all(ay < 2.0**127, axis=1)
+    if fp8 == "dynamic":
+        q, sc = out
+        assert_scales_close(sc.cpu().numpy()[ok], ref["scales"][ok], dtype)
+        assert_codes_close(codes(q)[ok], ref["q"][ok])
+    elif fp8 == "static":
+        assert_codes_close(codes(out[0])[ok], ref["q"][ok])
+    else:
+        assert_y_close(bits(out)[ok], ref["y"][ok], dtype)
+
+
 @SETTINGS
 @given(m=st.integers(1, 64), n=st.integers(1, 3000), k16=st.integers(1, 512),
        layout=st.sampled_from(["rowmajor", "preshuffled", "splitk"]),
