@@ -146,6 +146,13 @@ int arn_fused_add_rmsnorm_fp8(uint8_t *out, int64_t out_stride, float *scale, in
  *   residual      : NULL selects plain RMSNorm, else the fused form
  *   scale         : as in arn_rmsnorm_fp8 (ignored for 16-bit output)
  * Other fields and the return value as in the entry points above.
+ * With variance_size below hidden a channel outside the mean can be far
+ * larger than the row's rms.  The 16-bit and bf16 static outputs form
+ * (r_j * rsqrt(ms + eps)) * w_j in fp32 in that order, so an element whose
+ * first product passes fp32's largest value (about 3.4e38) comes out
+ * infinite (static: saturated) even where a weight below one would bring
+ * y_j back into range.  At the full variance size that product stays below
+ * sqrt(hidden).
  */
 enum arn_out_format { ARN_OUT_16BIT = 0, ARN_OUT_FP8_STATIC = 1, ARN_OUT_FP8_DYNAMIC = 2 };
 

@@ -24,7 +24,10 @@
 //  * Every finite input is served to the stated tolerance: a bf16 row whose
 //    fp32 sum of squares underflows or overflows is detected after the
 //    reduction and recomputed from the row scaled by 2^+-76 (exact), in a
-//    branch the other rows skip.
+//    branch the other rows skip.  (With a variance size below the row, y =
+//    (r * factor) * w is formed in that order, and r * factor can pass
+//    fp32's range where y would not; at the full size it is below
+//    sqrt(hidden).)
 //  * e4m3 codes come from the packed gfx950 v_cvt_pk_fp8_f32 (OCP format
 //    on this target) after an explicit fmed3 clamp to +-448.
 //  * x and out may alias: every element is loaded before the reduction and
