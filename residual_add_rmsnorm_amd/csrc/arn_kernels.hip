@@ -190,8 +190,10 @@ __global__ __launch_bounds__(64 * WPR * RPB) void row_kernel(const Args a) {
         const int col0 = (t + k * kTPR) * VEC;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float rf = elem<DT, VEC>(xr[k], e);
-          ss = __builtin_fmaf(rf, col0 + e < a.var_cols ? rf : 0.0f, ss);
+          // (Selected before squaring: an infinite channel past the variance
+          // size must add nothing, and inf * 0 would add a NaN.)
+          const float rf = col0 + e < a.var_cols ? elem<DT, VEC>(xr[k], e) : 0.0f;
+          ss = __builtin_fmaf(rf, rf, ss);
         }
       }
     }

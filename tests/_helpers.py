@@ -60,7 +60,9 @@ def assert_y_close(y_bits: np.ndarray, y_ref: np.ndarray, dtype: str, what="y"):
     nan_ref = np.isnan(y_ref)
     nan_got = np.isnan(got)
     assert np.array_equal(nan_ref, nan_got), f"{what}: NaN positions differ ({nan_got.sum()} vs {nan_ref.sum()})"
-    ok = ~nan_ref
+    inf_ref = np.isinf(y_ref)
+    assert np.array_equal(got[inf_ref], y_ref[inf_ref]), f"{what}: infinite outputs differ"
+    ok = ~nan_ref & ~inf_ref
     tol = np.maximum(RHO[dtype] * np.abs(y_ref[ok]), ulp16(y_ref[ok], dtype))
     err = np.abs(got[ok] - y_ref[ok])
     bad = err > tol

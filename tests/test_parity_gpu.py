@@ -13,7 +13,7 @@ import torch
 import oracle as O
 import workloads as W
 from tests._helpers import (assert_codes_close, assert_scales_close, assert_y_close,
-                            bits, codes, dev, static_scale)
+                            bits, codes, dev, static_scale, values16)
 
 pytestmark = pytest.mark.gpu
 
@@ -417,6 +417,48 @@ def test_bf16_dynamic_products_out_of_fp32_range(orc, family, eps, tile):
 def test_zero_rows_eps0_give_nan(orc):
     x = np.zeros((4, 256), np.uint16)
     run_case(orc, dtype="bf16", x=x, res=None, w=None, eps=0.0, hidden=256)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("variance", [None, 500])
+def test_nonfinite_inputs_propagate(orc, dtype, fused, variance):
+    """Infinities and NaNs in the activations follow IEEE arithmetic through
+    the definition: a NaN in the mean makes the whole row NaN; an infinity
+    there makes the mean infinite, so every finite channel comes out as a
+    signed zero and the infinite one as NaN (inf * 0); an infinity outside a
+    smaller variance size passes through as an infinite output; +inf plus
+    -inf in the residual add stores a NaN.  16-bit outputs (e4m3 codes of
+    non-finite y are not specified).  NaN bit patterns are not compared,
+    only where they are."""
+    arn = _arn()
+    hidden, rows = 1000, 7
+    inf, nan = (0x7F80, 0x7FC0) if dtype == "bf16" else (0x7C00, 0x7E00)
+    x = _random(dtype, rows, hidden, hidden, 70)
+    r = _random(dtype, rows, hidden, hidden, 71)
+    x[0, 3] = inf
+    x[1, 10] = nan
+    (r if fused else x)[2, 20] = inf | 0x8000
+    x[3, 30] = inf
+    r[3, 30] = inf | 0x8000  # with the residual: +inf + -inf = NaN
+    x[5, hidden - 1] = inf  # the ragged tail, past a variance size of 500
+    x[6, 600] = nan | 0x8000
+    xd, wd = dev(x, dtype), dev(_random(dtype, 1, hidden, hidden, 72)[0], dtype)
+    w = bits(wd)
+    rd = dev(r, dtype) if fused else None
+    out = arn.norm(xd, wd, 0.0, residual=rd, variance_size=variance)
+    torch.cuda.synchronize()
+    ref = orc.add_rmsnorm(dtype, x, r if fused else None, w, 0.0, variance_size=variance)
+    if fused:
+        got = values16(bits(rd), dtype)
+        want = values16(ref["r16"], dtype)
+        assert np.array_equal(np.isnan(got), np.isnan(want)), "residual NaN positions differ"
+        keep = ~np.isnan(want)
+        assert np.array_equal(bits(rd)[keep], ref["r16"][keep]), "stored residual not bit-exact"
+    assert np.isnan(ref["y"][1]).all()
+    if variance:
+        assert np.isinf(ref["y"][5, hidden - 1]) and np.isfinite(ref["y"][5, :-1]).all()
+    assert_y_close(bits(out), ref["y"], dtype)
 
 
 def test_zero_rows_dynamic_fp8(orc):
