@@ -171,6 +171,26 @@ def test_static_scale_range(orc, s):
     run_glu(orc, "bf16", x, d, fp8="static", s=s)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_nonfinite_inputs_propagate(orc, dtype):
+    """Infinities and NaNs follow IEEE arithmetic through g / (1 + exp(-g))
+    * u: silu(+inf) = inf, silu(-inf) = -inf / inf = NaN, 0 * inf = NaN, a
+    finite nonzero silu times an infinite up is infinite, NaN anywhere gives
+    NaN; other elements of the row are unaffected.  16-bit outputs (e4m3
+    codes of non-finite y are not specified)."""
+    d = 300
+    inf, nan = (0x7F80, 0x7FC0) if dtype == "bf16" else (0x7C00, 0x7E00)
+    one, two, mfive = (0x3F80, 0x4000, 0xC0A0) if dtype == "bf16" else (0x3C00, 0x4000, 0xC500)
+    x = _x(dtype, 2, d, seed=57)
+    cases = [(inf, two), (inf | 0x8000, two), (nan, two), (one, inf), (0, inf),
+             (mfive, inf | 0x8000), (two, nan), (0x8000, inf | 0x8000)]
+    for j, (g, u) in enumerate(cases):
+        x[0, 7 * j] = g
+        x[0, d + 7 * j] = u
+    x[1, 2 * d - 1] = inf  # the last up value of a row
+    run_glu(orc, dtype, x, d)
+
+
 def test_zero_row_dynamic(orc):
     x = _x("bf16", 5, 768, seed=55)
     x[2] = 0
