@@ -12,8 +12,9 @@
 //  * rows of WPR waves, VEC-element 128-bit buffer accesses bounded by the
 //    row length (ragged ends need no branches);
 //  * sigmoid in the form that cannot overflow: e = exp(-|g|),
-//    sigmoid(g) = 1/(1+e) for g >= 0 and e/(1+e) below, so silu stays
-//    accurate for large negative g;
+//    sigmoid(g) = 1/(1+e) for g >= 0 and e/(1+e) below; a lane with a gate
+//    at or below -80, where e nears fp32's subnormal range, forms its
+//    outputs in fp64 instead;
 //  * dynamic e4m3 keeps the row's y in VGPRs while max |y| is reduced (DPP
 //    across the wave, LDS across waves), then scales and converts.
 #include <hip/hip_runtime.h>
@@ -35,11 +36,12 @@ using namespace dev;
 // below, e = exp(-|g|) <= 1, so nothing overflows.  e is computed as
 // 2^(64 - |g| log2(e)) * 2^-64 with the hardware exp2 (v_exp_f32) and the
 // reciprocal with v_rcp_f32 (both about 1 ulp): the exp2 result stays a
-// normal number until |g| > 190, and the exact power-of-two rescale lets
-// large negative gates keep their tiny silu values, including fp32
-// subnormal ones.  Shifting the argument by 64 costs about 2^-18 relative
-// in e, far below the 16-bit output's rounding.  About ten VALU ops per
-// element, which keeps the kernel memory-bound.
+// normal number until |g| > 190 and the power-of-two rescale is exact while
+// e is a normal fp32 number, |g| < 87.3.  (Below that e is subnormal and
+// loses bits; the kernel sends gates at or below -80 to silu_mul_f64.)
+// Shifting the argument by 64 costs about 2^-18 relative in e, far below
+// the 16-bit output's rounding.  About ten VALU ops per element, which
+// keeps the kernel memory-bound.
 __device__ __forceinline__ float silu(float g) {
   const float e =
       __builtin_amdgcn_exp2f(__builtin_fmaf(-fabsf(g), 1.44269504088896341f, 64.0f)) * 0x1p-64f;
@@ -47,7 +49,8 @@ __device__ __forceinline__ float silu(float g) {
   return g * (g >= 0.0f ? r : e * r);
 }
 
-// silu(g) * u in fp64, for rows whose outputs leave fp32's range.
+// silu(g) * u in fp64, for rows whose outputs leave fp32's range and for
+// lanes holding a gate at or below -80.
 // exp(-|g|) = 2^-(n + fr) with n = floor(|g| log2 e) and fr in [0, 1): the
 // hardware exp2 of -fr, then an exact fp64 ldexp by -n, so gates far below
 // -87 (where silu() underflows in fp32) keep their value down to fp64's
@@ -65,11 +68,30 @@ __device__ __forceinline__ float silu(float g) {
   return (double)g * (g >= 0.0f ? r : e * r) * (double)u;
 }
 
+// Elementwise unsigned max of the 16-bit halves of a running word and of
+// every 32-bit word of a raw vector (v_pk_max_u16).
+template <int VEC>
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t acc, const Raw<VEC>& r) {
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  auto mx = [](uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+  };
+  if constexpr (VEC == 1) {
+    return mx(acc, (uint32_t)r);
+  } else if constexpr (VEC == 2) {
+    return mx(acc, r);
+  } else {
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) acc = mx(acc, r[i]);
+    return acc;
+  }
+}
+
 template <int DT, int MODE, int VEC, int NV, int WPR, int RPB>
 __global__ __launch_bounds__(64 * WPR * RPB) void glu_kernel(const GluArgs a) {
   constexpr bool kStatic = MODE == kGluStatic;
   constexpr bool kDynamic = MODE == kGluDynamic;
-  constexpr bool kFp8 = kStatic || kDynamic;
   constexpr int kTPR = 64 * WPR;
   constexpr uint32_t kStep16 = kTPR * VEC * 2;
   constexpr uint32_t kStep8 = kTPR * VEC;
@@ -99,20 +121,92 @@ __global__ __launch_bounds__(64 * WPR * RPB) void glu_kernel(const GluArgs a) {
     ur[k] = load16<VEC, kCacheStream>(urs, off16 + k * kStep16);
   }
 
-  float y[NV][VEC];
-  float mx = 0.0f;
+  // A lane holding a gate at or below -80 forms its outputs in fp64
+  // instead: there exp(-|g|) nears the bottom of fp32's normal range, and
+  // past -87.3 silu() keeps only an fp32 subnormal's few bits, which an up
+  // value as small as 2^5 lifts into a bf16 output's range.  The bits of a
+  // negative 16-bit float order like its magnitude and lie above every
+  // positive one, so one packed unsigned max over the raw gate words finds
+  // such a gate (and -inf or a negative NaN, which the fp64 form also
+  // gives as the definition does).  The branch is skipped when no lane of
+  // the wave needs it, and one element's fp64 temporaries are live at a
+  // time (as in the wide path below).
+  uint32_t gtop = 0;  // running max of the gate words, taken vector by vector
+  auto deep = [&]() __attribute__((always_inline)) {
+    const uint32_t m = __builtin_elementwise_max(gtop & 0xFFFFu, gtop >> 16);
+    return m >= (DT == kBF16 ? 0xC2A0u : 0xD500u);  // -80 in bf16 / fp16
+  };
+  // The fp64 outputs of a lane, one vector at a time, from inputs read
+  // again (L2 or HBM), so the usual path retires its raw registers.
+  auto deep_outputs = [&](auto&& use) __attribute__((always_inline)) {
+    float prev = 0.0f;
 #pragma unroll
-  for (int k = 0; k < NV; ++k) {
+    for (int k = 0; k < NV; ++k) {
+      asm volatile("" ::: "memory");
+      const Raw<VEC> g2 = load16<VEC, kCacheStream>(grs, off16 + k * kStep16);
+      const Raw<VEC> u2 = load16<VEC, kCacheStream>(urs, off16 + k * kStep16);
+      float v[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      y[k][e] = silu(elem<DT, VEC>(gr[k], e)) * elem<DT, VEC>(ur[k], e);
-      if constexpr (kDynamic) mx = fmaxf(mx, fabsf(y[k][e]));
+      for (int e = 0; e < VEC; ++e) {
+        float g = elem<DT, VEC>(g2, e), u = elem<DT, VEC>(u2, e);
+        asm volatile("" : "+v"(g), "+v"(u) : "v"(prev));
+        v[e] = prev = (float)silu_mul_f64(g, u);
+      }
+      use(k, v);
     }
-  }
+  };
 
-  float qmul = 1.0f;
-  if constexpr (kStatic) qmul = 1.0f / *a.scale;
-  if constexpr (kDynamic) {
+  if constexpr (!kDynamic) {
+    // 16-bit or static e4m3 outputs: each lane stores its own vectors.
+    float y[NV][VEC];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      gtop = max_u16x2<VEC>(gtop, gr[k]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) y[k][e] = silu(elem<DT, VEC>(gr[k], e)) * elem<DT, VEC>(ur[k], e);
+    }
+    float qmul = 1.0f;
+    if constexpr (kStatic) qmul = 1.0f / *a.scale;
+    const __amdgpu_buffer_rsrc_t ors =
+        kStatic ? row_rsrc(static_cast<uint8_t*>(a.out) + arow * a.out_stride,
+                           active ? (uint32_t)a.d : 0u)
+                : row_rsrc(static_cast<uint16_t*>(a.out) + arow * a.out_stride, n16);
+    auto emit = [&](int k, float (&v)[VEC]) __attribute__((always_inline)) {
+      if constexpr (kStatic) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[e] *= qmul;
+        store8<VEC>(pack_fp8<VEC>(v), ors, off8 + k * kStep8);
+      } else {
+        store16<VEC>(pack<DT, VEC>(v), ors, off16 + k * kStep16);
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < NV; ++k) emit(k, y[k]);
+    // A lane with a deep gate stores its vectors a second time, from the
+    // fp64 form; the same lane's later store to an address is the one that
+    // stays.  The usual path is left as it would be without the check.
+    if (__builtin_expect(deep(), 0)) deep_outputs(emit);
+  } else {
+    // Dynamic e4m3 keeps the row's outputs while max|y| is reduced.
+    float y[NV][VEC];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      gtop = max_u16x2<VEC>(gtop, gr[k]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) y[k][e] = silu(elem<DT, VEC>(gr[k], e)) * elem<DT, VEC>(ur[k], e);
+    }
+    if (__builtin_expect(deep(), 0)) {
+      deep_outputs([&](int k, float (&v)[VEC]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) y[k][e] = v[e];
+      });
+    }
+    float mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) mx = fmaxf(mx, fabsf(y[k][e]));
+    }
     __shared__ float red_max[WPR * RPB];
     mx = wave_max(mx);
     if constexpr (WPR > 1) {
@@ -194,11 +288,8 @@ __global__ __launch_bounds__(64 * WPR * RPB) void glu_kernel(const GluArgs a) {
     // scale max|y| / 448 are normal fp32 numbers (the reciprocal of mx / 448
     // in [2^-105, 2^120) by the hardware's 1-ulp v_rcp_f32), and an output
     // that lost low bits below 2^-126 is off by less than 2^-54 of the max.
-    qmul = __builtin_amdgcn_rcpf(mx * (1.0f / 448.0f));
+    const float qmul = __builtin_amdgcn_rcpf(mx * (1.0f / 448.0f));
     if (active && t == 0) a.scale[row] = mx * (1.0f / 448.0f);
-  }
-
-  if constexpr (kFp8) {
     const __amdgpu_buffer_rsrc_t ors = row_rsrc(
         static_cast<uint8_t*>(a.out) + arow * a.out_stride, active ? (uint32_t)a.d : 0u);
 #pragma unroll
@@ -208,11 +299,6 @@ __global__ __launch_bounds__(64 * WPR * RPB) void glu_kernel(const GluArgs a) {
       for (int e = 0; e < VEC; ++e) v[e] = y[k][e] * qmul;
       store8<VEC>(pack_fp8<VEC>(v), ors, off8 + k * kStep8);
     }
-  } else {
-    const __amdgpu_buffer_rsrc_t ors =
-        row_rsrc(static_cast<uint16_t*>(a.out) + arow * a.out_stride, n16);
-#pragma unroll
-    for (int k = 0; k < NV; ++k) store16<VEC>(pack<DT, VEC>(y[k]), ors, off16 + k * kStep16);
   }
 }
 

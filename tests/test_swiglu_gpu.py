@@ -155,6 +155,52 @@ def test_dynamic_outputs_out_of_fp32_range(orc, tile):
         arn.set_tile(0, 0)
 
 
+def _deep_gate_rows(d, seed):
+    """Rows whose gates reach far below -87, where exp(-|g|) is under fp32's
+    normal range, with up values large enough to lift silu(g) * u into a
+    bf16 output's range: (gate range, log2 up range, share of such
+    elements; the rest of the row N(0, 1))."""
+    rng = np.random.default_rng(seed)
+    spec = [((-100.0, -80.0), (0, 40), 1.0),
+            ((-130.0, -100.0), (60, 120), 1.0),
+            ((-110.0, -85.0), (20, 100), 0.5),      # lanes mixing both kinds
+            ((-88.0, -87.0), (100, 126), 1.0),      # around the subnormal edge
+            ((-2.0**20, -130.0), (100, 126), 1.0),  # silu below fp64's range
+            ((-110.0, -80.0), (10, 30), 1.0 / 64)]  # a few such gates per row
+    rows = []
+    for (g0, g1), (u0, u1), share in spec:
+        g = rng.standard_normal(d)
+        u = rng.standard_normal(d)
+        pick = rng.random(d) < share
+        g[pick] = rng.uniform(g0, g1, pick.sum())
+        u[pick] = np.where(rng.random(pick.sum()) < 0.5, -1.0, 1.0) * 2.0 ** rng.uniform(
+            u0, u1, pick.sum())
+        rows.append(np.concatenate([g, u]))
+    return W.to_bits(np.stack(rows).astype(np.float32), "bf16")
+
+
+@pytest.mark.parametrize("fp8", [None, "static", "dynamic"])
+@pytest.mark.parametrize("tile", [None, (1, 2), (8, 1), (16, 1)],
+                         ids=["auto", "wpr1", "wpr8", "wpr16"])
+def test_deep_negative_gates(orc, fp8, tile):
+    """silu(g) * u for gates far below -87, whose exp(-|g|) an fp32
+    subnormal would hold with few bits or not at all, times up values up to
+    2^126: outputs within one bf16 ulp of the definition (codes within one
+    step), every output kind and several tile shapes."""
+    import residual_add_rmsnorm_amd as arn
+
+    d = 1000
+    if tile:
+        arn.set_tile(*tile)
+    try:
+        run_glu(orc, "bf16", _deep_gate_rows(d, 63), d, fp8=fp8,
+                s=2.0**-100 if fp8 == "static" else None)
+        if tile:
+            assert f"wpr{tile[0]}/nv{tile[1]}/" in arn.last_plan(), arn.last_plan()
+    finally:
+        arn.set_tile(0, 0)
+
+
 @pytest.mark.parametrize("s", [2.0**-126, 1e-30, 1e-6, 1.0, 1e30, 3.4e38])
 def test_static_scale_range(orc, s):
     """Static e4m3 over the range of normal fp32 scales: saturation at one
