@@ -226,7 +226,10 @@ int arn_sum_add_rmsnorm(const arn_sum_norm_args *args);
  * 2020, FFN_SwiGLU with Swish_1).  The usual layout is one [rows, 2d] tensor
  * from the fused gate/up projection: gate = base, up = base + d, both with
  * that tensor's row stride; separate tensors work too.  All of gate, up and
- * out are of `dtype`; fp32 arithmetic, one rounding of the output.  The
+ * out are of `dtype`; fp32 arithmetic, one rounding of the output (lanes
+ * holding a gate at or below -80, where exp(-|g|) nears fp32's subnormal
+ * range, and rows whose outputs leave fp32's range are formed in fp64, so
+ * every finite input is served to the stated tolerance).  The
  * second kernel of "Custom CUDA kernels juice Llama 3.1 405B on AMD MI300X"
  * (paragraph 2) fuses this activation with the FP8 cast, which is
  * arn_silu_and_mul_fp8.  out may not alias gate or up.  Conventions as above
@@ -239,7 +242,9 @@ int arn_silu_and_mul(void *out, int64_t out_stride,
 
 /* SwiGLU with an OCP e4m3 output; `scale` and fp8_mode as in
  * arn_rmsnorm_fp8 (static: one dequant scale read; dynamic: `rows` scales
- * max_j |y_ij| / 448 written). */
+ * max_j |y_ij| / 448 written).  The static kind forms y in fp32 before the
+ * multiply by 1/s, so an output with |y| >= 2^128 saturates even where y/s
+ * would not. */
 int arn_silu_and_mul_fp8(uint8_t *out, int64_t out_stride, float *scale, int fp8_mode,
                          const void *gate, int64_t gate_stride,
                          const void *up, int64_t up_stride,
