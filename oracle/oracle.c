@@ -456,9 +456,16 @@ int orc_add_rmsnorm_var(int dtype, int64_t rows, int64_t hidden, int64_t varianc
 /* SwiGLU: y = silu(gate) * up.                                          */
 /* --------------------------------------------------------------------- */
 
-/* silu(g) = g * sigmoid(g) = g / (1 + exp(-g)). */
+/* silu(g) = g * sigmoid(g) with sigmoid(g) = 1 / (1 + exp(-g)).  For
+   g < 0 sigmoid is taken in the equal form exp(g) / (1 + exp(g)): exp(-g)
+   overflows fp64 below about -709.8 while sigmoid(g) is still
+   representable down to about -745. */
 double orc_silu(double g)
 {
+    if (g < 0.0) {
+        const double e = exp(g);
+        return g * e / (1.0 + e);
+    }
     return g / (1.0 + exp(-g));
 }
 

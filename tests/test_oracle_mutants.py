@@ -47,6 +47,8 @@ MUTANTS = {
     "overflow_not_inf": ("if (e + f.bias >= emax_field) {", "if (e + f.bias > emax_field) {"),
     "silu_sign": ("return g / (1.0 + exp(-g));", "return g / (1.0 + exp(g));"),
     "silu_no_sigmoid": ("return g / (1.0 + exp(-g));", "return g;"),
+    "silu_negative_sign": ("const double e = exp(g);", "const double e = exp(-g);"),
+    "silu_negative_no_denominator": ("return g * e / (1.0 + e);", "return g * e;"),
     "gate_up_swapped": ("y[j] = orc_silu(g) * u;", "y[j] = orc_silu(u) * g;"),
     "up_row_stride": ("up[i * up_stride + j]", "up[i * gate_stride + j + 0 * up_stride]"),
     "sum_in_double": ("float total = (float)orc_decode16(dtype, parts[0][i * parts_stride + j]);",

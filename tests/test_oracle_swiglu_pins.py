@@ -34,6 +34,20 @@ def test_silu_matches_torch_float64(orc):
     assert np.allclose(got, ref, rtol=2e-15, atol=0)
 
 
+def test_silu_far_negative_follows_g_exp_g(orc):
+    """For g -> -inf, silu(g) = g / (1 + e^-g) = g e^g (1 - e^g + ...), so
+    silu(g) / silu(g - 1) tends to e * g / (g - 1), and silu(g) keeps its
+    magnitude e^g |g| down to fp64's subnormal range (about -745): no cliff
+    where e^-g itself passes fp64's largest value (g below about -709.8)."""
+    gs = [-600.0, -700.0, -709.0, -709.5, -710.0, -711.0, -720.0, -730.0]
+    for g in gs:
+        a, b = orc.silu(g), orc.silu(g - 1.0)
+        assert a < 0.0 and b < 0.0
+        # relative spacing of fp64 numbers near e^-740 is still below 1e-9
+        assert a / b == pytest.approx(math.e * g / (g - 1.0), rel=1e-6)
+    assert orc.silu(-800.0) == 0.0  # g e^g is below fp64's smallest subnormal
+
+
 def test_silu_closed_forms(orc):
     for k in range(1, 12):
         g = math.log(k)
