@@ -181,6 +181,67 @@ def test_random_variance_size_magnitudes(orc, dtype, fp8, rows, hidden, kfrac, f
         assert_y_close(bits(out)[ok], ref["y"][ok], dtype)
 
 
+@pytest.mark.parametrize("fp8", [None, "static", "dynamic"])
+@settings(max_examples=30, deadline=None, derandomize=True, database=None,
+          suppress_health_check=list(HealthCheck))
+@given(rows=st.integers(1, 10),
+       d=st.one_of(st.integers(1, 3000), st.integers(1, 520).map(lambda v: 8 * v)),
+       seed=st.integers(0, 2**31 - 1))
+def test_random_glu_magnitudes(orc, fp8, rows, d, seed):
+    """bf16 SwiGLU rows whose gates and up values are each a power of two
+    drawn from the seed over bf16's whole range (a third of the gates
+    drawn below -80, where exp(-|g|) nears fp32's subnormal range), times
+    N(0, 1), with random signs; static scales over the normal fp32 range.
+    Rows with an output at or above 2^127 are left out for the 16-bit and
+    static kinds, which form y in fp32, and dynamic rows whose scale rounds
+    to zero while an output is exactly zero (its code is e4m3(0 / 0))."""
+    import residual_add_rmsnorm_amd as arn
+    from tests._helpers import assert_codes_close, assert_scales_close, assert_y_close, bits, codes
+    import oracle as O
+
+    rng = np.random.default_rng(seed)
+    log2_s = int(rng.integers(-126, 128))
+    s = 2.0**log2_s
+    gate = np.empty((rows, d))
+    up = np.empty((rows, d))
+    for i in range(rows):
+        lg, lu = int(rng.integers(-133, 127)), int(rng.integers(-133, 127))
+        gate[i] = rng.standard_normal(d) * 2.0**lg
+        if rng.random() < 1 / 3:
+            gate[i] = -rng.uniform(80, 2.0**int(rng.integers(7, 20)), d)
+        up[i] = rng.standard_normal(d) * 2.0**lu
+    lim = 1.9 * 2.0**126
+    x = W.to_bits(np.clip(np.concatenate([gate, up], axis=1), -lim, lim).astype(np.float32),
+                  "bf16")
+    print(f"[case] glu magnitudes rows={rows} d={d} fp8={fp8} s 2^{log2_s} seed={seed}",
+          flush=True)
+    xd = dev(x, "bf16")
+    if fp8 == "dynamic":
+        out = arn.silu_and_mul_fp8(xd, dynamic=True)
+    elif fp8 == "static":
+        out = arn.silu_and_mul_fp8(xd, scale=torch.tensor([s], device="cuda"))
+    else:
+        out = arn.silu_and_mul(xd)
+    torch.cuda.synchronize()
+    mode = {None: O.FP8_NONE, "static": O.FP8_STATIC, "dynamic": O.FP8_DYNAMIC}[fp8]
+    ref = orc.silu_and_mul("bf16", x, d=d, fp8_mode=mode, static_scale=s)
+    ok = np.all(np.isfinite(ref["y"]), axis=1)
+    if fp8 != "dynamic":
+        ok &= np.all(np.abs(ref["y"]) < 2.0**127, axis=1)
+    else:
+        # a scale that rounds to zero under an exact-zero output: 0 / 0
+        ok &= ~((ref["scales"] == 0) & np.any(ref["y"] == 0, axis=1) & np.any(ref["y"] != 0, axis=1))
+    if fp8 == "dynamic":
+        q, sc = out
+        assert_scales_close(sc.cpu().numpy()[ok], ref["scales"][ok], "bf16")
+        assert_codes_close(codes(q)[ok], ref["q"][ok])
+    elif fp8 == "static":
+        q = out[0] if isinstance(out, tuple) else out
+        assert_codes_close(codes(q)[ok], ref["q"][ok])
+    else:
+        assert_y_close(bits(out)[ok], ref["y"][ok], "bf16")
+
+
 @SETTINGS
 @given(m=st.integers(1, 64), n=st.integers(1, 3000), k16=st.integers(1, 512),
        layout=st.sampled_from(["rowmajor", "preshuffled", "splitk"]),
