@@ -3,9 +3,12 @@ with the SwiGLU + e4m3 activation and the e4m3 GEMM that consume its codes.
 
 A thin binding over the C ABI of libarn.so (include/arn.h): each function
 checks and marshals torch tensors into (device pointer, row stride) pairs and
-calls the C entry point of the same name on torch's current stream.  Every
-step of the operator runs in the library's HIP kernels; there is no fallback.
-torch provides device memory and streams only.
+calls the C entry point of the same name on torch's current stream.  For the
+per-step calls (the norm forms, SwiGLU, the GEMM) that marshalling runs in
+the extension module lib/_native (csrc/arn_pyext.cpp), since in Python it
+would cost more host time than a decode-sized kernel takes.  Every step of
+the operator runs in the library's HIP kernels; there is no fallback.  torch
+provides device memory and streams only.
 
 Layouts follow the vLLM API page "vllm.kernels.aiter_ops"
 (flatten_to_2d_is_free): the last dimension must have unit stride and the
@@ -37,34 +40,7 @@ FP8_DTYPE = torch.float8_e4m3fn
 
 def _rows(t: torch.Tensor, name: str):
     """(rows, hidden, row_stride) of a tensor viewed as 2-D rows, no copy."""
-    if t.dim() == 0:
-        raise ValueError(f"{name}: needs at least one dimension")
-    hidden = t.shape[-1]
-    if hidden > 0 and t.is_contiguous():
-        return t.numel() // hidden, hidden, hidden
-    if hidden > 1 and t.stride(-1) != 1:
-        raise ValueError(f"{name}: last dimension must have unit stride")
-    rows = 1
-    for s in t.shape[:-1]:
-        rows *= s
-    pitch = None
-    expected = None
-    for i in range(t.dim() - 2, -1, -1):
-        if t.shape[i] == 1:
-            continue
-        if pitch is None:
-            pitch = t.stride(i)
-            expected = pitch * t.shape[i]
-        else:
-            if t.stride(i) != expected:
-                raise ValueError(f"{name}: leading dims do not flatten to one row pitch "
-                                 "without a copy")
-            expected *= t.shape[i]
-    if pitch is None:
-        pitch = hidden
-    if rows > 1 and pitch < hidden:
-        raise ValueError(f"{name}: rows overlap (row stride {pitch} < hidden {hidden})")
-    return rows, hidden, pitch
+    return _lib.native().row_view(t, name)
 
 
 def _dtype_code(x: torch.Tensor) -> int:
@@ -119,40 +95,14 @@ def _out_like(x, out, dtype, name="out"):
 def rmsnorm(x: torch.Tensor, weight: torch.Tensor | None, eps: float,
             out: torch.Tensor | None = None) -> torch.Tensor:
     """out = x / sqrt(mean(x^2, -1) + eps) * weight  (arn_rmsnorm)."""
-    _check_device(x)
-    dt = _dtype_code(x)
-    rows, hidden, xs = _rows(x, "x")
-    out = _out_like(x, out, x.dtype)
-    _, _, os_ = _rows(out, "out")
-    wp = _check_weight(weight, x, hidden)
-    lib = _lib.load()
-    with _on(x):
-        st = lib.arn_rmsnorm(out.data_ptr(), os_, x.data_ptr(), xs, wp, float(eps),
-                             rows, hidden, dt, _stream(x))
-    _lib.check(st, "arn_rmsnorm")
-    return out
+    return _lib.native().rmsnorm(x, weight, eps, out)
 
 
 def fused_add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, weight: torch.Tensor | None,
                       eps: float, out: torch.Tensor | None = None) -> torch.Tensor:
     """residual <- x + residual (rounded to the 16-bit type, in place);
     returns out = RMSNorm(residual)  (arn_fused_add_rmsnorm)."""
-    _check_device(x)
-    dt = _dtype_code(x)
-    if residual.dtype != x.dtype or residual.shape != x.shape or residual.device != x.device:
-        raise ValueError("residual must match x in shape, dtype and device")
-    rows, hidden, xs = _rows(x, "x")
-    _, _, rs = _rows(residual, "residual")
-    out = _out_like(x, out, x.dtype)
-    _, _, os_ = _rows(out, "out")
-    wp = _check_weight(weight, x, hidden)
-    lib = _lib.load()
-    with _on(x):
-        st = lib.arn_fused_add_rmsnorm(out.data_ptr(), os_, x.data_ptr(), xs,
-                                       residual.data_ptr(), rs, wp, float(eps),
-                                       rows, hidden, dt, _stream(x))
-    _lib.check(st, "arn_fused_add_rmsnorm")
-    return out
+    return _lib.native().fused_add_rmsnorm(x, residual, weight, eps, out)
 
 
 def _fp8_scale(x, rows, scale, dynamic, scales_out):
@@ -179,19 +129,7 @@ def rmsnorm_fp8(x: torch.Tensor, weight: torch.Tensor | None, eps: float,
     Static (``scale`` given, dequant scale s): codes = e4m3(y / s).
     Dynamic: per-row scales = max|y| / 448 are written and returned.
     Returns (codes as float8_e4m3fn, scale tensor)."""
-    _check_device(x)
-    dt = _dtype_code(x)
-    rows, hidden, xs = _rows(x, "x")
-    out = _out_like(x, out, FP8_DTYPE)
-    _, _, os_ = _rows(out, "out")
-    wp = _check_weight(weight, x, hidden)
-    sc, mode = _fp8_scale(x, rows, scale, dynamic, scales_out)
-    lib = _lib.load()
-    with _on(x):
-        st = lib.arn_rmsnorm_fp8(out.data_ptr(), os_, sc.data_ptr(), mode, x.data_ptr(), xs,
-                                 wp, float(eps), rows, hidden, dt, _stream(x))
-    _lib.check(st, "arn_rmsnorm_fp8")
-    return out, sc
+    return _lib.native().rmsnorm_fp8(x, weight, eps, scale, dynamic, out, scales_out)
 
 
 def fused_add_rmsnorm_fp8(x: torch.Tensor, residual: torch.Tensor,
@@ -201,23 +139,8 @@ def fused_add_rmsnorm_fp8(x: torch.Tensor, residual: torch.Tensor,
                           scales_out: torch.Tensor | None = None):
     """residual <- x + residual; codes = e4m3(RMSNorm(residual) / scale)
     (arn_fused_add_rmsnorm_fp8).  Returns (codes, scale tensor)."""
-    _check_device(x)
-    dt = _dtype_code(x)
-    if residual.dtype != x.dtype or residual.shape != x.shape or residual.device != x.device:
-        raise ValueError("residual must match x in shape, dtype and device")
-    rows, hidden, xs = _rows(x, "x")
-    _, _, rs = _rows(residual, "residual")
-    out = _out_like(x, out, FP8_DTYPE)
-    _, _, os_ = _rows(out, "out")
-    wp = _check_weight(weight, x, hidden)
-    sc, mode = _fp8_scale(x, rows, scale, dynamic, scales_out)
-    lib = _lib.load()
-    with _on(x):
-        st = lib.arn_fused_add_rmsnorm_fp8(out.data_ptr(), os_, sc.data_ptr(), mode,
-                                           x.data_ptr(), xs, residual.data_ptr(), rs, wp,
-                                           float(eps), rows, hidden, dt, _stream(x))
-    _lib.check(st, "arn_fused_add_rmsnorm_fp8")
-    return out, sc
+    return _lib.native().fused_add_rmsnorm_fp8(x, residual, weight, eps, scale, dynamic, out,
+                                                scales_out)
 
 
 def norm(x: torch.Tensor, weight: torch.Tensor | None, eps: float,
@@ -228,39 +151,9 @@ def norm(x: torch.Tensor, weight: torch.Tensor | None, eps: float,
     override (mean of squares over the first ``variance_size`` channels).
     ``fp8``: None (16-bit out), "static" (needs ``scale``) or "dynamic".
     Returns out, or (codes, scale tensor) for FP8."""
-    import ctypes
-
-    _check_device(x)
-    dt = _dtype_code(x)
-    rows, hidden, xs = _rows(x, "x")
-    rs = 0
-    if residual is not None:
-        if residual.dtype != x.dtype or residual.shape != x.shape or residual.device != x.device:
-            raise ValueError("residual must match x in shape, dtype and device")
-        _, _, rs = _rows(residual, "residual")
-    out = _out_like(x, out, FP8_DTYPE if fp8 else x.dtype)
-    _, _, os_ = _rows(out, "out")
-    wp = _check_weight(weight, x, hidden)
-    sc = None
-    fmt = _lib.OUT_16BIT
-    if fp8:
-        if fp8 not in ("static", "dynamic"):
-            raise ValueError("fp8 must be None, 'static' or 'dynamic'")
-        sc, _ = _fp8_scale(x, rows, scale, fp8 == "dynamic", scales_out)
-        fmt = _lib.OUT_FP8_DYNAMIC if fp8 == "dynamic" else _lib.OUT_FP8_STATIC
-    args = _lib.NormArgs(
-        struct_size=ctypes.sizeof(_lib.NormArgs), dtype=dt, out_format=fmt,
-        out=out.data_ptr(), out_stride=os_, scale=sc.data_ptr() if sc is not None else None,
-        x=x.data_ptr(), x_stride=xs,
-        residual=residual.data_ptr() if residual is not None else None, residual_stride=rs,
-        weight=wp, eps=float(eps), rows=rows, hidden=hidden,
-        variance_size=0 if variance_size is None else int(variance_size),
-        stream=_stream(x))
-    lib = _lib.load()
-    with _on(x):
-        st = lib.arn_norm(ctypes.byref(args))
-    _lib.check(st, "arn_norm")
-    return (out, sc) if fp8 else out
+    return _lib.native().norm(x, weight, eps, residual,
+                              0 if variance_size is None else int(variance_size), fp8 or "",
+                              scale, out, scales_out)
 
 
 def sum_add_rmsnorm(parts, weight: torch.Tensor | None, eps: float,
@@ -316,55 +209,17 @@ def sum_add_rmsnorm(parts, weight: torch.Tensor | None, eps: float,
     return (out, sc) if fp8 else out
 
 
-def _glu_views(x: torch.Tensor):
-    """(rows, d, row_stride) of a [..., 2d] gate|up tensor, no copy."""
-    _check_device(x)
-    _dtype_code(x)
-    rows, two_d, xs = _rows(x, "x")
-    if two_d % 2:
-        raise ValueError("the last dimension of x must be 2*d (gate | up)")
-    return rows, two_d // 2, xs
-
-
-def _glu_out(x, out, dtype, d):
-    shape = (*x.shape[:-1], d)
-    if out is None:
-        return torch.empty(shape, dtype=dtype, device=x.device)
-    if tuple(out.shape) != shape or out.dtype != dtype or out.device != x.device:
-        raise ValueError(f"out must have shape {shape} and dtype {dtype} on x's device")
-    return out
-
-
 def silu_and_mul(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """out = silu(x[..., :d]) * x[..., d:] for x of shape [..., 2d]
     (arn_silu_and_mul with gate = x, up = x + d)."""
-    rows, d, xs = _glu_views(x)
-    out = _glu_out(x, out, x.dtype, d)
-    _, _, os_ = _rows(out, "out")
-    lib = _lib.load()
-    base = x.data_ptr()
-    with _on(x):
-        st = lib.arn_silu_and_mul(out.data_ptr(), os_, base, xs, base + 2 * d, xs, rows, d,
-                                  _DTYPES[x.dtype], _stream(x))
-    _lib.check(st, "arn_silu_and_mul")
-    return out
+    return _lib.native().silu_and_mul(x, out)
 
 
 def silu_and_mul_fp8(x: torch.Tensor, scale: torch.Tensor | None = None, dynamic: bool = False,
                      out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None):
     """SwiGLU of a [..., 2d] gate|up tensor with an OCP e4m3 output
     (arn_silu_and_mul_fp8).  Returns (codes, scale tensor)."""
-    rows, d, xs = _glu_views(x)
-    out = _glu_out(x, out, FP8_DTYPE, d)
-    _, _, os_ = _rows(out, "out")
-    sc, mode = _fp8_scale(x, rows, scale, dynamic, scales_out)
-    lib = _lib.load()
-    base = x.data_ptr()
-    with _on(x):
-        st = lib.arn_silu_and_mul_fp8(out.data_ptr(), os_, sc.data_ptr(), mode, base, xs,
-                                      base + 2 * d, xs, rows, d, _DTYPES[x.dtype], _stream(x))
-    _lib.check(st, "arn_silu_and_mul_fp8")
-    return out, sc
+    return _lib.native().silu_and_mul_fp8(x, scale, dynamic, out, scales_out)
 
 
 class PreshuffledWeight:
@@ -420,59 +275,12 @@ def fp8_gemm(a: torch.Tensor, scale_a: torch.Tensor, b, scale_b: torch.Tensor,
     (arn_fp8_gemm_preshuffled); scale_a holds M or 1 float32 values,
     scale_b N or 1.  With a workspace (fp8_gemm_workspace) K may also be
     split across blocks (the _ws entry points)."""
-    pre = isinstance(b, PreshuffledWeight)
-    for t, nm in ((a, "a"),) if pre else ((a, "a"), (b, "b")):
-        _check_device(t)
-        if t.dtype not in (FP8_DTYPE, torch.uint8) or t.dim() != 2 or t.stride(1) != 1:
-            raise ValueError(f"{nm} must be a 2-D e4m3 (or uint8) tensor with unit column stride")
-    if pre and b.device != a.device:
-        raise ValueError("a and b must be on the same device")
-    m, k = a.shape
-    n, kb = b.shape
-    if kb != k:
-        raise ValueError("a and b must have the same K")
-    for sc, cnt, nm in ((scale_a, m, "scale_a"), (scale_b, n, "scale_b")):
-        if (sc.dtype != torch.float32 or not sc.is_contiguous() or sc.numel() not in (1, cnt)
-                or sc.device != a.device):
-            raise ValueError(f"{nm} must hold 1 or {cnt} contiguous float32 values")
-    if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
-    if out.shape != (m, n) or out.dtype not in _DTYPES or out.stride(1) != 1:
-        raise ValueError("out must be [M, N] bfloat16/float16 with unit column stride")
-    lib = _lib.load()
-    a_rows = int(scale_a.numel() > 1 or m == 1)
-    b_rows = int(scale_b.numel() > 1 or n == 1)
-    if workspace is not None:
-        if workspace.device != a.device or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous tensor on a's device")
-        ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
-    with _on(a):
-        if pre and workspace is not None:
-            name = "arn_fp8_gemm_preshuffled_ws"
-            st = lib.arn_fp8_gemm_preshuffled_ws(
-                out.data_ptr(), out.stride(0), _DTYPES[out.dtype], a.data_ptr(), a.stride(0),
-                scale_a.data_ptr(), a_rows, b.data.data_ptr(), scale_b.data_ptr(), b_rows,
-                m, n, k, *ws, _stream(a))
-        elif pre:
-            name = "arn_fp8_gemm_preshuffled"
-            st = lib.arn_fp8_gemm_preshuffled(out.data_ptr(), out.stride(0), _DTYPES[out.dtype],
-                                              a.data_ptr(), a.stride(0), scale_a.data_ptr(),
-                                              a_rows, b.data.data_ptr(), scale_b.data_ptr(),
-                                              b_rows, m, n, k, _stream(a))
-        elif workspace is not None:
-            name = "arn_fp8_gemm_ws"
-            st = lib.arn_fp8_gemm_ws(out.data_ptr(), out.stride(0), _DTYPES[out.dtype],
-                                     a.data_ptr(), a.stride(0), scale_a.data_ptr(), a_rows,
-                                     b.data_ptr(), b.stride(0), scale_b.data_ptr(), b_rows,
-                                     m, n, k, *ws, _stream(a))
-        else:
-            name = "arn_fp8_gemm"
-            st = lib.arn_fp8_gemm(out.data_ptr(), out.stride(0), _DTYPES[out.dtype],
-                                  a.data_ptr(), a.stride(0), scale_a.data_ptr(), a_rows,
-                                  b.data_ptr(), b.stride(0), scale_b.data_ptr(), b_rows,
-                                  m, n, k, _stream(a))
-    _lib.check(st, name)
-    return out
+    if isinstance(b, PreshuffledWeight):
+        bt, pre_n, pre_k = b.data, b.n, b.k
+    else:
+        bt, pre_n, pre_k = b, -1, -1
+    return _lib.native().fp8_gemm(a, scale_a, bt, scale_b, _DTYPES.get(out_dtype, -1), out,
+                                  workspace, pre_n, pre_k)
 
 
 def fp8_gemm_preshuffled_noalloc(a: torch.Tensor, scale_a: torch.Tensor, b: "PreshuffledWeight",
@@ -484,30 +292,8 @@ def fp8_gemm_preshuffled_noalloc(a: torch.Tensor, scale_a: torch.Tensor, b: "Pre
     `out` is given.  Calls on one GPU must not overlap."""
     if not isinstance(b, PreshuffledWeight):
         raise ValueError("b must be a PreshuffledWeight")
-    _check_device(a)
-    if a.dtype not in (FP8_DTYPE, torch.uint8) or a.dim() != 2 or a.stride(1) != 1:
-        raise ValueError("a must be a 2-D e4m3 (or uint8) tensor with unit column stride")
-    if b.device != a.device:
-        raise ValueError("a and b must be on the same device")
-    m, k = a.shape
-    n, kb = b.shape
-    if kb != k:
-        raise ValueError("a and b must have the same K")
-    for sc, cnt, nm in ((scale_a, m, "scale_a"), (scale_b, n, "scale_b")):
-        if (sc.dtype != torch.float32 or not sc.is_contiguous() or sc.numel() not in (1, cnt)
-                or sc.device != a.device):
-            raise ValueError(f"{nm} must hold 1 or {cnt} contiguous float32 values")
-    if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
-    if out.shape != (m, n) or out.dtype not in _DTYPES or out.stride(1) != 1:
-        raise ValueError("out must be [M, N] bfloat16/float16 with unit column stride")
-    with _on(a):
-        st = _lib.load().arn_fp8_gemm_preshuffled_noalloc(
-            out.data_ptr(), out.stride(0), _DTYPES[out.dtype], a.data_ptr(), a.stride(0),
-            scale_a.data_ptr(), int(scale_a.numel() > 1 or m == 1), b.data.data_ptr(),
-            scale_b.data_ptr(), int(scale_b.numel() > 1 or n == 1), m, n, k, _stream(a))
-    _lib.check(st, "arn_fp8_gemm_preshuffled_noalloc")
-    return out
+    return _lib.native().fp8_gemm_preshuffled_noalloc(a, scale_a, b.data, b.n, b.k, scale_b,
+                                                      _DTYPES.get(out_dtype, -1), out)
 
 
 def set_tile(waves_per_row: int = 0, vec_per_lane: int = 0) -> None:

@@ -1,4 +1,6 @@
-"""ctypes loader for libarn.so (the C ABI in include/arn.h).
+"""Loaders for libarn.so (the C ABI in include/arn.h, through ctypes) and for
+the extension module lib/_native, which marshals the binding's per-call
+arguments in C++ and calls the same library.
 
 torch is imported first: it ships its own HIP runtime, and loading libarn.so
 afterwards makes the library's libamdhip64.so.7 dependency resolve to that
@@ -8,6 +10,7 @@ valid in the library.
 from __future__ import annotations
 
 import ctypes
+import importlib.util
 import os
 import threading
 
@@ -148,6 +151,44 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             raise ImportError(f"libarn.so ABI {lib.arn_abi_version()} != {ABI_VERSION}")
         _lib = lib
         return lib
+
+
+# The entry points the extension module calls, bound to the addresses of
+# this ctypes handle so that both reach one copy of the library.
+NATIVE_ENTRY_POINTS = (
+    "arn_rmsnorm", "arn_fused_add_rmsnorm", "arn_rmsnorm_fp8", "arn_fused_add_rmsnorm_fp8",
+    "arn_norm", "arn_silu_and_mul", "arn_silu_and_mul_fp8", "arn_fp8_gemm", "arn_fp8_gemm_ws",
+    "arn_fp8_gemm_preshuffled", "arn_fp8_gemm_preshuffled_ws", "arn_fp8_gemm_preshuffled_noalloc",
+)
+
+_native = None
+
+
+def native(path: str | None = None):
+    """The extension module (lib/_native), bound to libarn.so; built first
+    only if it is not there at all."""
+    global _native
+    if _native is not None:
+        return _native
+    with _lock:
+        if _native is not None:
+            return _native
+        path = path or _build.NATIVE_PATH
+        if not os.path.exists(path) and path == _build.NATIVE_PATH:
+            _build.build_native()
+        if not os.path.exists(path):
+            raise ImportError(f"the binding's extension module is not at {path}; run "
+                              "`python -m residual_add_rmsnorm_amd.build`")
+    lib = load()
+    with _lock:
+        if _native is None:
+            spec = importlib.util.spec_from_file_location("residual_add_rmsnorm_amd._native", path)
+            mod = importlib.util.module_from_spec(spec)
+            spec.loader.exec_module(mod)
+            mod.bind({name: ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+                      for name in NATIVE_ENTRY_POINTS}, check)
+            _native = mod
+    return _native
 
 
 def status_str(status: int) -> str:

@@ -10,7 +10,6 @@ import torch
 from hypothesis import HealthCheck, assume, given, settings
 from hypothesis import strategies as st
 
-import residual_add_rmsnorm_amd as arn
 from residual_add_rmsnorm_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -202,26 +201,6 @@ def test_set_tile(lib):
     assert lib.arn_set_tile(1, 16) == _lib.OK
     assert lib.arn_set_tile(16, 8) == _lib.OK
     assert lib.arn_set_tile(0, 0) == _lib.OK
-
-
-def test_binding_row_views():
-    t = torch.empty(4, 6, 100, dtype=torch.bfloat16)
-    assert arn._rows(t, "x") == (24, 100, 100)
-    padded = torch.empty(16, 128, dtype=torch.bfloat16)[:, :96]
-    assert arn._rows(padded, "x") == (16, 96, 128)
-    p3 = torch.empty(2, 8, 128, dtype=torch.bfloat16)[:, :, :96]
-    assert arn._rows(p3, "x") == (16, 96, 128)
-    assert arn._rows(torch.empty(96, dtype=torch.bfloat16), "x") == (1, 96, 96)
-    with pytest.raises(ValueError):
-        arn._rows(torch.empty(8, 96, dtype=torch.bfloat16).t(), "x")
-    with pytest.raises(ValueError):  # would need a copy to flatten
-        arn._rows(torch.empty(4, 8, 96, dtype=torch.bfloat16).transpose(0, 1), "x")
-
-
-def test_binding_refuses_cpu_tensors():
-    x = torch.zeros(2, 8, dtype=torch.bfloat16)
-    with pytest.raises(ValueError):
-        arn.rmsnorm(x, None, 1e-6)
 
 
 def _norm_args(**kw):
