@@ -159,6 +159,7 @@ NATIVE_ENTRY_POINTS = (
     "arn_rmsnorm", "arn_fused_add_rmsnorm", "arn_rmsnorm_fp8", "arn_fused_add_rmsnorm_fp8",
     "arn_norm", "arn_silu_and_mul", "arn_silu_and_mul_fp8", "arn_fp8_gemm", "arn_fp8_gemm_ws",
     "arn_fp8_gemm_preshuffled", "arn_fp8_gemm_preshuffled_ws", "arn_fp8_gemm_preshuffled_noalloc",
+    "arn_fp8_weight_preshuffled_bytes", "arn_status_str",
 )
 
 _native = None

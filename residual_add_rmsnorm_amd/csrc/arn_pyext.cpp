@@ -19,6 +19,11 @@
 // The entry points are reached through addresses that the Python loader
 // takes from its ctypes handle of libarn.so (bind()), so this module and
 // ctypes share one copy of the library and of its per-thread tuning state.
+//
+// The same functions back the torch custom ops of a decode step (arn::*,
+// registered below for the CUDA dispatch key), so a call through torch.ops
+// reaches the C ABI without entering Python; their fake implementations
+// (output shapes for the compiler) are registered from Python.
 #include <torch/extension.h>
 
 #include <c10/core/DeviceGuard.h>
@@ -45,6 +50,8 @@ struct Entry {
   decltype(&arn_fp8_gemm_preshuffled) fp8_gemm_preshuffled = nullptr;
   decltype(&arn_fp8_gemm_preshuffled_ws) fp8_gemm_preshuffled_ws = nullptr;
   decltype(&arn_fp8_gemm_preshuffled_noalloc) fp8_gemm_preshuffled_noalloc = nullptr;
+  decltype(&arn_fp8_weight_preshuffled_bytes) fp8_weight_preshuffled_bytes = nullptr;
+  decltype(&arn_status_str) status_str = nullptr;
 };
 Entry g_entry;
 bool g_bound = false;
@@ -74,25 +81,33 @@ void bind(const py::dict& addrs, const py::object& check) {
   take(addrs, "arn_fp8_gemm_preshuffled", e.fp8_gemm_preshuffled);
   take(addrs, "arn_fp8_gemm_preshuffled_ws", e.fp8_gemm_preshuffled_ws);
   take(addrs, "arn_fp8_gemm_preshuffled_noalloc", e.fp8_gemm_preshuffled_noalloc);
+  take(addrs, "arn_fp8_weight_preshuffled_bytes", e.fp8_weight_preshuffled_bytes);
+  take(addrs, "arn_status_str", e.status_str);
   g_entry = e;
   if (g_check == nullptr) g_check = new py::object(check);
   g_bound = true;
 }
 
 const Entry& entry() {
-  if (!g_bound) throw std::runtime_error("libarn.so entry points not bound");
+  TORCH_CHECK(g_bound, "libarn.so entry points not bound (load the package's binding first)");
   return g_entry;
 }
 
-// A nonzero status becomes the package's ArnError (raised by _lib.check).
+// A nonzero status from the C ABI.  The functions below touch no Python
+// object (a torch op runs them without the interpreter lock); the Python
+// wrappers turn this into the package's ArnError and the torch ops into a
+// RuntimeError.
+struct AbiStatus {
+  int status;
+  const char* name;
+};
+
 void check(int status, const char* name) {
-  if (status != ARN_OK) {
-    (*g_check)(status, name);
-    throw std::runtime_error(std::string(name) + ": status " + std::to_string(status));
-  }
+  if (status != ARN_OK) throw AbiStatus{status, name};
 }
 
-[[noreturn]] void refuse(const std::string& msg) { throw py::value_error(msg); }
+// A refused argument: ValueError in Python, from either path.
+[[noreturn]] void refuse(const std::string& msg) { TORCH_CHECK_VALUE(false, msg); }
 
 std::string dtype_name(at::ScalarType t) {
   switch (t) {
@@ -270,7 +285,9 @@ at::Tensor fused_add_rmsnorm(const at::Tensor& x, const at::Tensor& residual,
   return out;
 }
 
-py::tuple rmsnorm_fp8(const at::Tensor& x, const c10::optional<at::Tensor>& weight, double eps,
+using Pair = std::tuple<at::Tensor, at::Tensor>;
+
+Pair rmsnorm_fp8(const at::Tensor& x, const c10::optional<at::Tensor>& weight, double eps,
                       const c10::optional<at::Tensor>& scale, bool dynamic,
                       const c10::optional<at::Tensor>& out_in,
                       const c10::optional<at::Tensor>& scales_out) {
@@ -290,10 +307,10 @@ py::tuple rmsnorm_fp8(const at::Tensor& x, const c10::optional<at::Tensor>& weig
                        x.data_ptr(), xv.stride, wp, (float)eps, xv.rows, xv.hidden, dt, on.stream);
   }
   check(st, "arn_rmsnorm_fp8");
-  return py::make_tuple(out, sc);
+  return {out, sc};
 }
 
-py::tuple fused_add_rmsnorm_fp8(const at::Tensor& x, const at::Tensor& residual,
+Pair fused_add_rmsnorm_fp8(const at::Tensor& x, const at::Tensor& residual,
                                 const c10::optional<at::Tensor>& weight, double eps,
                                 const c10::optional<at::Tensor>& scale, bool dynamic,
                                 const c10::optional<at::Tensor>& out_in,
@@ -318,12 +335,12 @@ py::tuple fused_add_rmsnorm_fp8(const at::Tensor& x, const at::Tensor& residual,
                                  dt, on.stream);
   }
   check(st, "arn_fused_add_rmsnorm_fp8");
-  return py::make_tuple(out, sc);
+  return {out, sc};
 }
 
-// fp8: "" (16-bit out), "static" or "dynamic".  Returns out, or (codes,
-// scale tensor).
-py::object norm(const at::Tensor& x, const c10::optional<at::Tensor>& weight, double eps,
+// fp8: "" (16-bit out), "static" or "dynamic".  Returns (out, scale
+// tensor); the scale is undefined for a 16-bit output.
+Pair norm(const at::Tensor& x, const c10::optional<at::Tensor>& weight, double eps,
                 const c10::optional<at::Tensor>& residual, int64_t variance_size,
                 const std::string& fp8, const c10::optional<at::Tensor>& scale,
                 const c10::optional<at::Tensor>& out_in, const c10::optional<at::Tensor>& scales_out) {
@@ -369,8 +386,7 @@ py::object norm(const at::Tensor& x, const c10::optional<at::Tensor>& weight, do
     st = e.norm(&a);
   }
   check(st, "arn_norm");
-  if (fp8.empty()) return py::cast(out);
-  return py::make_tuple(out, sc);
+  return {out, sc};
 }
 
 // ---------------------------------------------------------------------------
@@ -416,7 +432,7 @@ at::Tensor silu_and_mul(const at::Tensor& x, const c10::optional<at::Tensor>& ou
   return out;
 }
 
-py::tuple silu_and_mul_fp8(const at::Tensor& x, const c10::optional<at::Tensor>& scale,
+Pair silu_and_mul_fp8(const at::Tensor& x, const c10::optional<at::Tensor>& scale,
                            bool dynamic, const c10::optional<at::Tensor>& out_in,
                            const c10::optional<at::Tensor>& scales_out) {
   const Entry& e = entry();
@@ -436,7 +452,7 @@ py::tuple silu_and_mul_fp8(const at::Tensor& x, const c10::optional<at::Tensor>&
                             on.stream);
   }
   check(st, "arn_silu_and_mul_fp8");
-  return py::make_tuple(out, sc);
+  return {out, sc};
 }
 
 // ---------------------------------------------------------------------------
@@ -488,6 +504,9 @@ at::Tensor fp8_gemm(const at::Tensor& a, const at::Tensor& scale_a, const at::Te
   const int64_t n = pre ? pre_n : b.size(0);
   const int64_t kb = pre ? pre_k : b.size(1);
   if (kb != k) refuse("a and b must have the same K");
+  if (pre && b.numel() * b.element_size() < e.fp8_weight_preshuffled_bytes(n, k)) {
+    refuse("b_shuffled is smaller than a pre-shuffled n x k weight");
+  }
   gemm_scale(scale_a, m, a, "scale_a");
   gemm_scale(scale_b, n, a, "scale_b");
   at::Tensor out = gemm_out(a, m, n, out_code, out_in);
@@ -560,19 +579,175 @@ at::Tensor fp8_gemm_preshuffled_noalloc(const at::Tensor& a, const at::Tensor& s
   return out;
 }
 
+// ---------------------------------------------------------------------------
+// Python entry points: a status from the C ABI becomes the package's
+// ArnError (raised by _lib.check, with the interpreter lock held).
+// ---------------------------------------------------------------------------
+template <typename F>
+auto from_python(F&& f) -> decltype(f()) {
+  try {
+    return f();
+  } catch (const AbiStatus& e) {
+    (*g_check)(e.status, e.name);
+    throw std::runtime_error(std::string(e.name) + ": status " + std::to_string(e.status));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// torch custom ops (CUDA kernels of the arn:: schemas below): a status from
+// the C ABI becomes a RuntimeError naming the entry point and the status.
+// ---------------------------------------------------------------------------
+template <typename F>
+auto from_torch(F&& f) -> decltype(f()) {
+  try {
+    return f();
+  } catch (const AbiStatus& e) {
+    TORCH_CHECK(false, e.name, ": ", entry().status_str(e.status), " (status ", e.status, ")");
+  }
+}
+
+using OptT = c10::optional<at::Tensor>;
+
+at::Tensor op_rmsnorm(const at::Tensor& x, const OptT& w, double eps) {
+  return from_torch([&] { return rmsnorm(x, w, eps, c10::nullopt); });
+}
+at::Tensor op_fused_add_rmsnorm(const at::Tensor& x, at::Tensor& residual, const OptT& w,
+                                double eps) {
+  return from_torch([&] { return fused_add_rmsnorm(x, residual, w, eps, c10::nullopt); });
+}
+at::Tensor op_rmsnorm_fp8_static(const at::Tensor& x, const OptT& w, double eps,
+                                 const at::Tensor& scale) {
+  return from_torch([&] {
+    return std::get<0>(rmsnorm_fp8(x, w, eps, scale, false, c10::nullopt, c10::nullopt));
+  });
+}
+Pair op_rmsnorm_fp8_dynamic(const at::Tensor& x, const OptT& w, double eps) {
+  return from_torch([&] { return rmsnorm_fp8(x, w, eps, c10::nullopt, true, c10::nullopt, c10::nullopt); });
+}
+at::Tensor op_fused_add_rmsnorm_fp8_static(const at::Tensor& x, at::Tensor& residual, const OptT& w,
+                                           double eps, const at::Tensor& scale) {
+  return from_torch([&] {
+    return std::get<0>(
+        fused_add_rmsnorm_fp8(x, residual, w, eps, scale, false, c10::nullopt, c10::nullopt));
+  });
+}
+Pair op_fused_add_rmsnorm_fp8_dynamic(const at::Tensor& x, at::Tensor& residual, const OptT& w,
+                                      double eps) {
+  return from_torch([&] {
+    return fused_add_rmsnorm_fp8(x, residual, w, eps, c10::nullopt, true, c10::nullopt, c10::nullopt);
+  });
+}
+at::Tensor op_silu_and_mul(const at::Tensor& x) {
+  return from_torch([&] { return silu_and_mul(x, c10::nullopt); });
+}
+at::Tensor op_silu_and_mul_fp8_static(const at::Tensor& x, const at::Tensor& scale) {
+  return from_torch(
+      [&] { return std::get<0>(silu_and_mul_fp8(x, scale, false, c10::nullopt, c10::nullopt)); });
+}
+Pair op_silu_and_mul_fp8_dynamic(const at::Tensor& x) {
+  return from_torch([&] { return silu_and_mul_fp8(x, c10::nullopt, true, c10::nullopt, c10::nullopt); });
+}
+int out_code_of(const c10::optional<at::ScalarType>& dt) {
+  return dt.has_value() ? dtype_code(*dt) : ARN_BF16;
+}
+at::Tensor op_fp8_gemm(const at::Tensor& a, const at::Tensor& scale_a, const at::Tensor& b,
+                       const at::Tensor& scale_b, c10::optional<at::ScalarType> out_dtype) {
+  return from_torch([&] {
+    return fp8_gemm(a, scale_a, b, scale_b, out_code_of(out_dtype), c10::nullopt, c10::nullopt, -1, -1);
+  });
+}
+at::Tensor op_fp8_gemm_preshuffled(const at::Tensor& a, const at::Tensor& scale_a,
+                                   const at::Tensor& b_shuffled, int64_t n, int64_t k,
+                                   const at::Tensor& scale_b, c10::optional<at::ScalarType> out_dtype) {
+  return from_torch([&] {
+    if (n < 0 || k <= 0) refuse("n must be >= 0 and k >= 1");
+    return fp8_gemm(a, scale_a, b_shuffled, scale_b, out_code_of(out_dtype), c10::nullopt,
+                    c10::nullopt, n, k);
+  });
+}
+
 }  // namespace
+
+// The ops of a decode step, in the arn namespace (the Python module adds the
+// weight shuffle and the all-reduce form, and every op's fake).
+TORCH_LIBRARY_FRAGMENT(arn, m) {
+  m.def("rmsnorm(Tensor x, Tensor? weight, float eps) -> Tensor");
+  m.def("fused_add_rmsnorm(Tensor x, Tensor(a!) residual, Tensor? weight, float eps) -> Tensor");
+  m.def("rmsnorm_fp8_static(Tensor x, Tensor? weight, float eps, Tensor scale) -> Tensor");
+  m.def("rmsnorm_fp8_dynamic(Tensor x, Tensor? weight, float eps) -> (Tensor, Tensor)");
+  m.def("fused_add_rmsnorm_fp8_static(Tensor x, Tensor(a!) residual, Tensor? weight, float eps, "
+        "Tensor scale) -> Tensor");
+  m.def("fused_add_rmsnorm_fp8_dynamic(Tensor x, Tensor(a!) residual, Tensor? weight, float eps) "
+        "-> (Tensor, Tensor)");
+  m.def("silu_and_mul(Tensor x) -> Tensor");
+  m.def("silu_and_mul_fp8_static(Tensor x, Tensor scale) -> Tensor");
+  m.def("silu_and_mul_fp8_dynamic(Tensor x) -> (Tensor, Tensor)");
+  m.def("fp8_gemm(Tensor a, Tensor scale_a, Tensor b, Tensor scale_b, ScalarType? out_dtype=None) "
+        "-> Tensor");
+  m.def("fp8_gemm_preshuffled(Tensor a, Tensor scale_a, Tensor b_shuffled, int n, int k, "
+        "Tensor scale_b, ScalarType? out_dtype=None) -> Tensor");
+}
+
+TORCH_LIBRARY_IMPL(arn, CUDA, m) {
+  m.impl("rmsnorm", &op_rmsnorm);
+  m.impl("fused_add_rmsnorm", &op_fused_add_rmsnorm);
+  m.impl("rmsnorm_fp8_static", &op_rmsnorm_fp8_static);
+  m.impl("rmsnorm_fp8_dynamic", &op_rmsnorm_fp8_dynamic);
+  m.impl("fused_add_rmsnorm_fp8_static", &op_fused_add_rmsnorm_fp8_static);
+  m.impl("fused_add_rmsnorm_fp8_dynamic", &op_fused_add_rmsnorm_fp8_dynamic);
+  m.impl("silu_and_mul", &op_silu_and_mul);
+  m.impl("silu_and_mul_fp8_static", &op_silu_and_mul_fp8_static);
+  m.impl("silu_and_mul_fp8_dynamic", &op_silu_and_mul_fp8_dynamic);
+  m.impl("fp8_gemm", &op_fp8_gemm);
+  m.impl("fp8_gemm_preshuffled", &op_fp8_gemm_preshuffled);
+}
 
 PYBIND11_MODULE(_native, m) {
   m.doc() = "argument marshalling of the residual_add_rmsnorm_amd binding (C ABI of libarn.so)";
   m.def("bind", &bind);
   m.def("row_view", &py_row_view);
-  m.def("rmsnorm", &rmsnorm);
-  m.def("fused_add_rmsnorm", &fused_add_rmsnorm);
-  m.def("rmsnorm_fp8", &rmsnorm_fp8);
-  m.def("fused_add_rmsnorm_fp8", &fused_add_rmsnorm_fp8);
-  m.def("norm", &norm);
-  m.def("silu_and_mul", &silu_and_mul);
-  m.def("silu_and_mul_fp8", &silu_and_mul_fp8);
-  m.def("fp8_gemm", &fp8_gemm);
-  m.def("fp8_gemm_preshuffled_noalloc", &fp8_gemm_preshuffled_noalloc);
+  m.def("rmsnorm", [](const at::Tensor& x, const OptT& w, double eps, const OptT& out) {
+    return from_python([&] { return rmsnorm(x, w, eps, out); });
+  });
+  m.def("fused_add_rmsnorm",
+        [](const at::Tensor& x, const at::Tensor& res, const OptT& w, double eps, const OptT& out) {
+          return from_python([&] { return fused_add_rmsnorm(x, res, w, eps, out); });
+        });
+  m.def("rmsnorm_fp8", [](const at::Tensor& x, const OptT& w, double eps, const OptT& scale,
+                          bool dynamic, const OptT& out, const OptT& scales_out) {
+    return from_python([&] { return rmsnorm_fp8(x, w, eps, scale, dynamic, out, scales_out); });
+  });
+  m.def("fused_add_rmsnorm_fp8",
+        [](const at::Tensor& x, const at::Tensor& res, const OptT& w, double eps, const OptT& scale,
+           bool dynamic, const OptT& out, const OptT& scales_out) {
+          return from_python(
+              [&] { return fused_add_rmsnorm_fp8(x, res, w, eps, scale, dynamic, out, scales_out); });
+        });
+  // Returns out, or (codes, scale tensor) for an e4m3 output.
+  m.def("norm", [](const at::Tensor& x, const OptT& w, double eps, const OptT& res,
+                   int64_t variance_size, const std::string& fp8, const OptT& scale,
+                   const OptT& out, const OptT& scales_out) -> py::object {
+    const Pair r = from_python(
+        [&] { return norm(x, w, eps, res, variance_size, fp8, scale, out, scales_out); });
+    if (fp8.empty()) return py::cast(std::get<0>(r));
+    return py::cast(r);
+  });
+  m.def("silu_and_mul", [](const at::Tensor& x, const OptT& out) {
+    return from_python([&] { return silu_and_mul(x, out); });
+  });
+  m.def("silu_and_mul_fp8", [](const at::Tensor& x, const OptT& scale, bool dynamic,
+                               const OptT& out, const OptT& scales_out) {
+    return from_python([&] { return silu_and_mul_fp8(x, scale, dynamic, out, scales_out); });
+  });
+  m.def("fp8_gemm", [](const at::Tensor& a, const at::Tensor& sa, const at::Tensor& b,
+                       const at::Tensor& sb, int out_code, const OptT& out, const OptT& ws,
+                       int64_t pre_n, int64_t pre_k) {
+    return from_python([&] { return fp8_gemm(a, sa, b, sb, out_code, out, ws, pre_n, pre_k); });
+  });
+  m.def("fp8_gemm_preshuffled_noalloc",
+        [](const at::Tensor& a, const at::Tensor& sa, const at::Tensor& b, int64_t n, int64_t kb,
+           const at::Tensor& sb, int out_code, const OptT& out) {
+          return from_python(
+              [&] { return fp8_gemm_preshuffled_noalloc(a, sa, b, n, kb, sb, out_code, out); });
+        });
 }

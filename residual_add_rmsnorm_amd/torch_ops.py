@@ -14,13 +14,16 @@ Importing this module registers, in the ``arn`` namespace:
     arn::sum_add_rmsnorm(parts[], residual!, weight, eps) -> y           (residual updated)
     arn::sum_add_rmsnorm_fp8_dynamic(parts[], residual!, weight, eps) -> (codes, scales)
     arn::fp8_weight_preshuffle(b) -> shuffled weight bytes
-    arn::fp8_gemm(a, scale_a, b, scale_b, out_dtype) -> c
-    arn::fp8_gemm_preshuffled(a, scale_a, b_shuffled, n, k, scale_b, out_dtype) -> c
+    arn::fp8_gemm(a, scale_a, b, scale_b, out_dtype=None) -> c        (None: bfloat16)
+    arn::fp8_gemm_preshuffled(a, scale_a, b_shuffled, n, k, scale_b, out_dtype=None) -> c
 
-Each op calls the binding (one kernel on the current stream) and has a fake
-implementation giving output shapes and dtypes, so the ops stay opaque to
-the compiler, as the vLLM API page "vllm.kernels.aiter_ops" describes for
-its aiter_lib fragment of wrapped AITER ops.
+Each op launches one kernel of the library on the current stream and has a
+fake implementation giving output shapes and dtypes, so the ops stay opaque
+to the compiler, as the vLLM API page "vllm.kernels.aiter_ops" describes for
+its aiter_lib fragment of wrapped AITER ops.  The norm, SwiGLU and GEMM ops
+are defined in C++ (csrc/arn_pyext.cpp, CUDA dispatch key) with the
+binding's checks; the weight shuffle and the all-reduce form are Python
+custom ops over the binding.
 """
 from __future__ import annotations
 
@@ -28,9 +31,7 @@ from typing import Optional
 
 import torch
 
-from . import (FP8_DTYPE, PreshuffledWeight, fp8_gemm, fp8_weight_preshuffle, fused_add_rmsnorm,
-               fused_add_rmsnorm_fp8, rmsnorm, rmsnorm_fp8, silu_and_mul, silu_and_mul_fp8,
-               sum_add_rmsnorm)
+from . import FP8_DTYPE, _lib, fp8_weight_preshuffle, sum_add_rmsnorm
 
 Tensor = torch.Tensor
 
@@ -44,100 +45,54 @@ def _glu_shape(x: Tensor):
     return (*x.shape[:-1], x.shape[-1] // 2)
 
 
-@torch.library.custom_op("arn::rmsnorm", mutates_args=())
-def rmsnorm_op(x: Tensor, weight: Optional[Tensor], eps: float) -> Tensor:
-    return rmsnorm(x, weight, eps)
+# The ops of a decode step are defined and implemented in C++ (the binding's
+# extension module, for the CUDA dispatch key), so an eager call through
+# torch.ops reaches the library without running Python; loading the module
+# registers them.  Their fakes follow.
+_lib.native()
 
 
-@rmsnorm_op.register_fake
+@torch.library.register_fake("arn::rmsnorm")
 def _(x, weight, eps):
     return torch.empty_like(x)
 
 
-@torch.library.custom_op("arn::fused_add_rmsnorm", mutates_args=("residual",))
-def fused_add_rmsnorm_op(x: Tensor, residual: Tensor, weight: Optional[Tensor],
-                         eps: float) -> Tensor:
-    return fused_add_rmsnorm(x, residual, weight, eps)
-
-
-@fused_add_rmsnorm_op.register_fake
+@torch.library.register_fake("arn::fused_add_rmsnorm")
 def _(x, residual, weight, eps):
     return torch.empty_like(x)
 
 
-@torch.library.custom_op("arn::rmsnorm_fp8_static", mutates_args=())
-def rmsnorm_fp8_static_op(x: Tensor, weight: Optional[Tensor], eps: float,
-                          scale: Tensor) -> Tensor:
-    return rmsnorm_fp8(x, weight, eps, scale=scale)[0]
-
-
-@rmsnorm_fp8_static_op.register_fake
+@torch.library.register_fake("arn::rmsnorm_fp8_static")
 def _(x, weight, eps, scale):
     return torch.empty(x.shape, dtype=FP8_DTYPE, device=x.device)
 
 
-@torch.library.custom_op("arn::rmsnorm_fp8_dynamic", mutates_args=())
-def rmsnorm_fp8_dynamic_op(x: Tensor, weight: Optional[Tensor],
-                           eps: float) -> tuple[Tensor, Tensor]:
-    q, s = rmsnorm_fp8(x, weight, eps, dynamic=True)
-    return q, s
-
-
-@rmsnorm_fp8_dynamic_op.register_fake
+@torch.library.register_fake("arn::rmsnorm_fp8_dynamic")
 def _(x, weight, eps):
     return torch.empty(x.shape, dtype=FP8_DTYPE, device=x.device), _scales_like(x)
 
 
-@torch.library.custom_op("arn::fused_add_rmsnorm_fp8_static", mutates_args=("residual",))
-def fused_add_rmsnorm_fp8_static_op(x: Tensor, residual: Tensor, weight: Optional[Tensor],
-                                    eps: float, scale: Tensor) -> Tensor:
-    return fused_add_rmsnorm_fp8(x, residual, weight, eps, scale=scale)[0]
-
-
-@fused_add_rmsnorm_fp8_static_op.register_fake
+@torch.library.register_fake("arn::fused_add_rmsnorm_fp8_static")
 def _(x, residual, weight, eps, scale):
     return torch.empty(x.shape, dtype=FP8_DTYPE, device=x.device)
 
 
-@torch.library.custom_op("arn::fused_add_rmsnorm_fp8_dynamic", mutates_args=("residual",))
-def fused_add_rmsnorm_fp8_dynamic_op(x: Tensor, residual: Tensor, weight: Optional[Tensor],
-                                     eps: float) -> tuple[Tensor, Tensor]:
-    q, s = fused_add_rmsnorm_fp8(x, residual, weight, eps, dynamic=True)
-    return q, s
-
-
-@fused_add_rmsnorm_fp8_dynamic_op.register_fake
+@torch.library.register_fake("arn::fused_add_rmsnorm_fp8_dynamic")
 def _(x, residual, weight, eps):
     return torch.empty(x.shape, dtype=FP8_DTYPE, device=x.device), _scales_like(x)
 
 
-@torch.library.custom_op("arn::silu_and_mul", mutates_args=())
-def silu_and_mul_op(x: Tensor) -> Tensor:
-    return silu_and_mul(x)
-
-
-@silu_and_mul_op.register_fake
+@torch.library.register_fake("arn::silu_and_mul")
 def _(x):
     return torch.empty(_glu_shape(x), dtype=x.dtype, device=x.device)
 
 
-@torch.library.custom_op("arn::silu_and_mul_fp8_static", mutates_args=())
-def silu_and_mul_fp8_static_op(x: Tensor, scale: Tensor) -> Tensor:
-    return silu_and_mul_fp8(x, scale=scale)[0]
-
-
-@silu_and_mul_fp8_static_op.register_fake
+@torch.library.register_fake("arn::silu_and_mul_fp8_static")
 def _(x, scale):
     return torch.empty(_glu_shape(x), dtype=FP8_DTYPE, device=x.device)
 
 
-@torch.library.custom_op("arn::silu_and_mul_fp8_dynamic", mutates_args=())
-def silu_and_mul_fp8_dynamic_op(x: Tensor) -> tuple[Tensor, Tensor]:
-    q, s = silu_and_mul_fp8(x, dynamic=True)
-    return q, s
-
-
-@silu_and_mul_fp8_dynamic_op.register_fake
+@torch.library.register_fake("arn::silu_and_mul_fp8_dynamic")
 def _(x):
     return torch.empty(_glu_shape(x), dtype=FP8_DTYPE, device=x.device), _scales_like(x)
 
@@ -158,29 +113,15 @@ def _(b):
                        device=b.device)
 
 
-@torch.library.custom_op("arn::fp8_gemm", mutates_args=())
-def fp8_gemm_op(a: Tensor, scale_a: Tensor, b: Tensor, scale_b: Tensor,
-                out_dtype: torch.dtype = torch.bfloat16) -> Tensor:
-    return fp8_gemm(a, scale_a, b, scale_b, out_dtype=out_dtype)
+@torch.library.register_fake("arn::fp8_gemm")
+def _(a, scale_a, b, scale_b, out_dtype=None):
+    return torch.empty((a.shape[0], b.shape[0]), dtype=out_dtype or torch.bfloat16,
+                       device=a.device)
 
 
-@fp8_gemm_op.register_fake
-def _(a, scale_a, b, scale_b, out_dtype=torch.bfloat16):
-    return torch.empty((a.shape[0], b.shape[0]), dtype=out_dtype, device=a.device)
-
-
-@torch.library.custom_op("arn::fp8_gemm_preshuffled", mutates_args=())
-def fp8_gemm_preshuffled_op(a: Tensor, scale_a: Tensor, b_shuffled: Tensor, n: int, k: int,
-                            scale_b: Tensor, out_dtype: torch.dtype = torch.bfloat16) -> Tensor:
-    if b_shuffled.numel() < _preshuffled_bytes(n, k):
-        raise ValueError("b_shuffled is smaller than a pre-shuffled n x k weight")
-    return fp8_gemm(a, scale_a, PreshuffledWeight(b_shuffled, n, k), scale_b,
-                    out_dtype=out_dtype)
-
-
-@fp8_gemm_preshuffled_op.register_fake
-def _(a, scale_a, b_shuffled, n, k, scale_b, out_dtype=torch.bfloat16):
-    return torch.empty((a.shape[0], n), dtype=out_dtype, device=a.device)
+@torch.library.register_fake("arn::fp8_gemm_preshuffled")
+def _(a, scale_a, b_shuffled, n, k, scale_b, out_dtype=None):
+    return torch.empty((a.shape[0], n), dtype=out_dtype or torch.bfloat16, device=a.device)
 
 
 @torch.library.custom_op("arn::sum_add_rmsnorm", mutates_args=("residual",))

@@ -109,3 +109,25 @@ def test_allocated_outputs():
     assert c.shape == (3, 16) and c.dtype == torch.float16
     torch.cuda.synchronize()
     assert bool((c == 0).all())
+
+
+def test_torch_ops_refusals_and_status():
+    import residual_add_rmsnorm_amd.torch_ops  # noqa: F401  (registers arn::*)
+
+    x = torch.zeros(1, 65537, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RuntimeError, match="arn_rmsnorm.*status 2"):
+        torch.ops.arn.rmsnorm(x, None, 1e-6)
+    with pytest.raises(ValueError, match="bfloat16 or float16"):
+        torch.ops.arn.rmsnorm(x.float(), None, 1e-6)
+    g = _t(2, 64)
+    with pytest.raises(ValueError, match="one float32 value"):
+        torch.ops.arn.silu_and_mul_fp8_static(g, torch.ones(2, device="cuda"))
+    a = torch.zeros(1, 256, dtype=torch.uint8, device="cuda")
+    s1 = torch.ones(1, device="cuda")
+    small = torch.zeros(2048, dtype=torch.uint8, device="cuda")  # one of the weight's two 16 x 128 tiles
+    with pytest.raises(ValueError, match="smaller than a pre-shuffled"):
+        torch.ops.arn.fp8_gemm_preshuffled(a, s1, small, 16, 256, s1)
+    c = torch.ops.arn.fp8_gemm_preshuffled(a, s1, torch.zeros(4096, dtype=torch.uint8,
+                                                              device="cuda"), 16, 256, s1)
+    torch.cuda.synchronize()
+    assert c.shape == (1, 16) and c.dtype == torch.bfloat16 and bool((c == 0).all())
