@@ -580,12 +580,15 @@ at::Tensor fp8_gemm_preshuffled_noalloc(const at::Tensor& a, const at::Tensor& s
 }
 
 // ---------------------------------------------------------------------------
-// Python entry points: a status from the C ABI becomes the package's
-// ArnError (raised by _lib.check, with the interpreter lock held).
+// Python entry points.  The checks and the launch run without the
+// interpreter lock (as a ctypes call or a torch op would), so other Python
+// threads keep running during the launch; a status from the C ABI then
+// becomes the package's ArnError (raised by _lib.check, lock held again).
 // ---------------------------------------------------------------------------
 template <typename F>
 auto from_python(F&& f) -> decltype(f()) {
   try {
+    py::gil_scoped_release unlocked;
     return f();
   } catch (const AbiStatus& e) {
     (*g_check)(e.status, e.name);
