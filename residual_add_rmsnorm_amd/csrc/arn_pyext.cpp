@@ -288,9 +288,9 @@ at::Tensor fused_add_rmsnorm(const at::Tensor& x, const at::Tensor& residual,
 using Pair = std::tuple<at::Tensor, at::Tensor>;
 
 Pair rmsnorm_fp8(const at::Tensor& x, const c10::optional<at::Tensor>& weight, double eps,
-                      const c10::optional<at::Tensor>& scale, bool dynamic,
-                      const c10::optional<at::Tensor>& out_in,
-                      const c10::optional<at::Tensor>& scales_out) {
+                 const c10::optional<at::Tensor>& scale, bool dynamic,
+                 const c10::optional<at::Tensor>& out_in,
+                 const c10::optional<at::Tensor>& scales_out) {
   const Entry& e = entry();
   need_gpu(x);
   const int dt = act_dtype(x);
@@ -311,10 +311,10 @@ Pair rmsnorm_fp8(const at::Tensor& x, const c10::optional<at::Tensor>& weight, d
 }
 
 Pair fused_add_rmsnorm_fp8(const at::Tensor& x, const at::Tensor& residual,
-                                const c10::optional<at::Tensor>& weight, double eps,
-                                const c10::optional<at::Tensor>& scale, bool dynamic,
-                                const c10::optional<at::Tensor>& out_in,
-                                const c10::optional<at::Tensor>& scales_out) {
+                           const c10::optional<at::Tensor>& weight, double eps,
+                           const c10::optional<at::Tensor>& scale, bool dynamic,
+                           const c10::optional<at::Tensor>& out_in,
+                           const c10::optional<at::Tensor>& scales_out) {
   const Entry& e = entry();
   need_gpu(x);
   const int dt = act_dtype(x);
@@ -341,9 +341,9 @@ Pair fused_add_rmsnorm_fp8(const at::Tensor& x, const at::Tensor& residual,
 // fp8: "" (16-bit out), "static" or "dynamic".  Returns (out, scale
 // tensor); the scale is undefined for a 16-bit output.
 Pair norm(const at::Tensor& x, const c10::optional<at::Tensor>& weight, double eps,
-                const c10::optional<at::Tensor>& residual, int64_t variance_size,
-                const std::string& fp8, const c10::optional<at::Tensor>& scale,
-                const c10::optional<at::Tensor>& out_in, const c10::optional<at::Tensor>& scales_out) {
+          const c10::optional<at::Tensor>& residual, int64_t variance_size, const std::string& fp8,
+          const c10::optional<at::Tensor>& scale, const c10::optional<at::Tensor>& out_in,
+          const c10::optional<at::Tensor>& scales_out) {
   const Entry& e = entry();
   need_gpu(x);
   const int dt = act_dtype(x);
@@ -432,9 +432,9 @@ at::Tensor silu_and_mul(const at::Tensor& x, const c10::optional<at::Tensor>& ou
   return out;
 }
 
-Pair silu_and_mul_fp8(const at::Tensor& x, const c10::optional<at::Tensor>& scale,
-                           bool dynamic, const c10::optional<at::Tensor>& out_in,
-                           const c10::optional<at::Tensor>& scales_out) {
+Pair silu_and_mul_fp8(const at::Tensor& x, const c10::optional<at::Tensor>& scale, bool dynamic,
+                      const c10::optional<at::Tensor>& out_in,
+                      const c10::optional<at::Tensor>& scales_out) {
   const Entry& e = entry();
   const RowView xv = glu_view(x);
   const int64_t d = xv.hidden / 2;
