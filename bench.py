@@ -554,6 +554,11 @@ def measure_workload(name: str, steps: int, warmup: int, ceilings: dict | None,
     elif rows < 1024:
         b = Batch(w, 8)
         entry["device_us_per_call_graph"] = round(time_graph(b, calls=64, replays=20), 3)
+        # eager calls, 200 back to back as for the decode rows, so the final
+        # synchronisation does not dominate the host wall time per call
+        e_ms, wall = time_steps(b, 200, 20)
+        entry["eager_200"] = {"event_us_per_call": round(e_ms * 1e3 / 200, 3),
+                              "host_wall_us_per_call": round(wall * 1e3 / 200, 3)}
         entry["empty_kernel_launch"] = launch_floor()
         del b
     del batch
