@@ -241,6 +241,27 @@ def test_fused_dynamic_many_rows_automatic_tiles(orc, hidden, tile):
     assert f"/vec8/{tile}/" in arn.last_plan(), arn.last_plan()
 
 
+@pytest.mark.parametrize("hidden,per_cu,tile", [
+    (5120, 1.0, "wpr4/nv3/rpb1"), (7168, 1.25, "wpr4/nv4/rpb1"), (8192, 1.0, "wpr4/nv4/rpb1"),
+    (4104, 0.75, "wpr4/nv3/rpb1"), (8192, 0.5, "wpr8/nv2/rpb1"), (7168, 1.5, "wpr8/nv2/rpb1"),
+    (4096, 1.0, "wpr8/nv1/rpb1")])
+@pytest.mark.parametrize("fp8", [None, "static", "dynamic"])
+def test_fused_rows_near_cu_count_automatic_tiles(orc, hidden, per_cu, tile, fp8):
+    """Fused rows 4097-8192 wide with more than half and at most one and a
+    quarter rows per CU take four-wave rows; half a row per CU, one and a
+    half, and 4096-wide rows keep the eight-wave rule.  Every row against
+    the oracle, plan asserted."""
+    arn = _arn()
+    rows = int(per_cu * torch.cuda.get_device_properties(0).multi_processor_count)
+    dtype = "fp16" if hidden % 3 else "bf16"
+    x = _random(dtype, rows, hidden, hidden, 90 + hidden % 89)
+    r = _random(dtype, rows, hidden, hidden, 91)
+    w = _random(dtype, 1, hidden, hidden, 92)[0]
+    run_case(orc, dtype=dtype, x=x, res=r, w=w, eps=1e-6, hidden=hidden, fp8=fp8,
+             s=0.01 if fp8 == "static" else None)
+    assert f"/vec8/{tile}/" in arn.last_plan(), arn.last_plan()
+
+
 @pytest.mark.parametrize("rows", [1, 2, 255, 256, 257, 1025, 4099])
 def test_row_counts(orc, rows):
     x = _random("bf16", rows, 1024, 1024, 7)
