@@ -163,19 +163,24 @@ int pow2_ceil(int64_t v) {
 //    Rows too wide for that take the rule above.
 //  * few rows (decode): eight waves per row, up to four vectors per lane,
 //    finish each row soonest.
-//  * `four_waves`: the fused kinds on 128-bit accesses, rows 4097-8192
-//    elements wide, more than half and at most one and a quarter rows per
-//    CU (decode batches near the CU count): rows of four waves with three or
-//    four vectors per lane.  Measured against eight-wave rows at 5120, 7168
-//    and 8192 wide, 16-bit, static and dynamic e4m3, fp16 and bf16: at one
-//    row per CU 0.1-15% less time in every case; over 160-320 rows on 256
-//    CUs up to 7% less for fp16 and within +-3.3% for bf16; at 384 rows the
-//    8192-wide rows lost up to 4%, so the band stops below that.
+//  * `waves` > 0 (fused kinds on 128-bit accesses, rows 4097-8192 elements
+//    wide, more than half and at most two rows per CU: decode batches near
+//    the CU count): rows of that many waves.  Measured against eight-wave
+//    rows at 5120, 7168 and 8192 wide, 16-bit, static and dynamic e4m3,
+//    fp16 and bf16, on 256 CUs:
+//      - up to 1.25 rows per CU, four waves: at 256 rows 0.1-15% less time
+//        in every case; over 160-320 rows up to 7% less for fp16 and
+//        within +-3.3% for bf16;
+//      - 1.25 to 2 rows per CU, two waves with eight vectors per lane when
+//        that covers the row with little idle (more than 768 vectors, i.e.
+//        7168-8192 wide): 0.2-20% less time in all 36 cases of 384-512
+//        rows (from 2.5 rows per CU on it loses 3-22%); narrower rows keep
+//        four waves there (5120 wide: -5% to +1.7%).
 // Among the compiled tiles of the chosen wave count, the one with the
 // fewest per-lane vectors that covers the row (and at least `min_nv`) is
 // taken; failing that, any tile that covers the row.
 const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t rows, int cus,
-                        bool lean = false, int compact_nv = 0, bool four_waves = false) {
+                        bool lean = false, int compact_nv = 0, int waves = 0) {
   const int forced = g_forced_tile;
   if (forced != 0) {
     const int fw = forced >> 8, fn = forced & 0xFF;
@@ -188,12 +193,14 @@ const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t r
     return nullptr;
   }
   const bool many_rows = rows >= (int64_t)4 * cus;
-  if (four_waves) {
-    const int64_t per_lane = (nvec + 255) / 256;
+  if (waves > 0) {
+    const int64_t per_lane = (nvec + 64 * waves - 1) / (64 * waves);
     const Tile* pick = nullptr;
     for (int i = 0; i < table->count; ++i) {
       const Tile& t = table->tiles[i];
-      if (t.vec == vec && t.wpr == 4 && t.nv >= per_lane && (!pick || t.nv < pick->nv)) pick = &t;
+      if (t.vec == vec && t.wpr == waves && t.nv >= per_lane && (!pick || t.nv < pick->nv)) {
+        pick = &t;
+      }
     }
     if (pick) return pick;
   }
@@ -289,10 +296,12 @@ int run(const Request& r) {
     compact = 2;
   }
   const int cus = cu_count();
-  const bool four_waves = (r.kind & arn::kFused) && !r.parts && vec == 8 && nvec > 512 &&
-                          nvec <= 1024 && 2 * r.rows > cus && 4 * r.rows <= 5 * (int64_t)cus;
-  const Tile* tile =
-      choose_tile(table, vec, nvec, r.rows, cus, r.nparts >= 4, compact, four_waves);
+  int waves = 0;
+  if ((r.kind & arn::kFused) && !r.parts && vec == 8 && nvec > 512 && nvec <= 1024 &&
+      2 * r.rows > cus && r.rows <= 2 * (int64_t)cus) {
+    waves = (4 * r.rows > 5 * (int64_t)cus && nvec > 768) ? 2 : 4;
+  }
+  const Tile* tile = choose_tile(table, vec, nvec, r.rows, cus, r.nparts >= 4, compact, waves);
   if (!tile) return ARN_EUNSUPPORTED;
 
   const int esize_out = fp8 ? 1 : 2;
