@@ -164,13 +164,17 @@ int pow2_ceil(int64_t v) {
 //  * few rows (decode): eight waves per row, up to four vectors per lane,
 //    finish each row soonest.
 //  * `waves` > 0 (fused kinds on 128-bit accesses, rows 4097-8192 elements
-//    wide, more than half and at most two rows per CU: decode batches near
-//    the CU count): rows of that many waves.  Measured against eight-wave
+//    wide, at most two rows per CU: decode batches up to twice the CU
+//    count): rows of that many waves.  Measured against eight-wave
 //    rows at 5120, 7168 and 8192 wide, 16-bit, static and dynamic e4m3,
 //    fp16 and bf16, on 256 CUs:
 //      - up to 1.25 rows per CU, four waves: at 256 rows 0.1-15% less time
 //        in every case; over 160-320 rows up to 7% less for fp16 and
 //        within +-3.3% for bf16;
+//      - at most half a row per CU, four waves for fp16 rows only (1-128
+//        rows: 2.9% less time over 54 cases, -8.8% to +1.5%); bf16 rows,
+//        whose add has no packed form and so more VALU work per element,
+//        ran up to 5% slower with four waves there and keep eight;
 //      - 1.25 to 2 rows per CU, two waves with eight vectors per lane when
 //        that covers the row with little idle (more than 768 vectors, i.e.
 //        7168-8192 wide): 0.2-20% less time in all 36 cases of 384-512
@@ -298,8 +302,12 @@ int run(const Request& r) {
   const int cus = cu_count();
   int waves = 0;
   if ((r.kind & arn::kFused) && !r.parts && vec == 8 && nvec > 512 && nvec <= 1024 &&
-      2 * r.rows > cus && r.rows <= 2 * (int64_t)cus) {
-    waves = (4 * r.rows > 5 * (int64_t)cus && nvec > 768) ? 2 : 4;
+      r.rows <= 2 * (int64_t)cus) {
+    if (2 * r.rows > cus) {
+      waves = (4 * r.rows > 5 * (int64_t)cus && nvec > 768) ? 2 : 4;
+    } else if (r.dtype == ARN_FP16) {
+      waves = 4;
+    }
   }
   const Tile* tile = choose_tile(table, vec, nvec, r.rows, cus, r.nparts >= 4, compact, waves);
   if (!tile) return ARN_EUNSUPPORTED;

@@ -241,22 +241,24 @@ def test_fused_dynamic_many_rows_automatic_tiles(orc, hidden, tile):
     assert f"/vec8/{tile}/" in arn.last_plan(), arn.last_plan()
 
 
-@pytest.mark.parametrize("hidden,per_cu,tile", [
-    (5120, 1.0, "wpr4/nv3/rpb1"), (7168, 1.25, "wpr4/nv4/rpb1"), (8192, 1.0, "wpr4/nv4/rpb1"),
-    (4104, 0.75, "wpr4/nv3/rpb1"), (7168, 1.5, "wpr2/nv8/rpb2"), (8192, 2.0, "wpr2/nv8/rpb2"),
-    (5120, 1.75, "wpr4/nv3/rpb1"), (8192, 0.5, "wpr8/nv2/rpb1"), (8192, 2.5, "wpr8/nv2/rpb1"),
-    (4096, 1.0, "wpr8/nv1/rpb1")])
+@pytest.mark.parametrize("hidden,per_cu,dtype,tile", [
+    (5120, 1.0, "fp16", "wpr4/nv3/rpb1"), (7168, 1.25, "bf16", "wpr4/nv4/rpb1"),
+    (8192, 1.0, "fp16", "wpr4/nv4/rpb1"), (4104, 0.75, "bf16", "wpr4/nv3/rpb1"),
+    (7168, 1.5, "bf16", "wpr2/nv8/rpb2"), (8192, 2.0, "fp16", "wpr2/nv8/rpb2"),
+    (5120, 1.75, "bf16", "wpr4/nv3/rpb1"), (8192, 0.5, "bf16", "wpr8/nv2/rpb1"),
+    (8192, 0.5, "fp16", "wpr4/nv4/rpb1"), (7168, 0.25, "fp16", "wpr4/nv4/rpb1"),
+    (7168, 0.0, "fp16", "wpr4/nv4/rpb1"), (7168, 0.25, "bf16", "wpr8/nv2/rpb1"),
+    (8192, 2.5, "fp16", "wpr8/nv2/rpb1"), (4096, 1.0, "fp16", "wpr8/nv1/rpb1")])
 @pytest.mark.parametrize("fp8", [None, "static", "dynamic"])
-def test_fused_rows_near_cu_count_automatic_tiles(orc, hidden, per_cu, tile, fp8):
-    """Fused rows 4097-8192 wide with more than half and at most two rows
-    per CU take four-wave rows up to one and a quarter rows per CU, then
-    two-wave rows of eight vectors when the row has more than 768 vectors
-    (four waves below that); half a row per CU, two and a half, and
-    4096-wide rows keep the eight-wave rule.  Every row against the oracle,
-    plan asserted."""
+def test_fused_rows_near_cu_count_automatic_tiles(orc, hidden, per_cu, dtype, tile, fp8):
+    """Fused rows 4097-8192 wide with at most two rows per CU take four-wave
+    rows up to one and a quarter rows per CU (at half a row per CU or fewer
+    for fp16 only), then two-wave rows of eight vectors when the row has
+    more than 768 vectors (four waves below that); bf16 rows at half a row
+    per CU, two and a half rows per CU, and 4096-wide rows keep the
+    eight-wave rule.  Every row against the oracle, plan asserted."""
     arn = _arn()
-    rows = int(per_cu * torch.cuda.get_device_properties(0).multi_processor_count)
-    dtype = "fp16" if hidden % 3 else "bf16"
+    rows = max(1, int(per_cu * torch.cuda.get_device_properties(0).multi_processor_count))
     x = _random(dtype, rows, hidden, hidden, 90 + hidden % 89)
     r = _random(dtype, rows, hidden, hidden, 91)
     w = _random(dtype, 1, hidden, hidden, 92)[0]
