@@ -248,7 +248,8 @@ def test_fused_dynamic_many_rows_automatic_tiles(orc, hidden, tile):
     (5120, 1.75, "bf16", "wpr4/nv3/rpb1"), (8192, 0.5, "bf16", "wpr8/nv2/rpb1"),
     (8192, 0.5, "fp16", "wpr4/nv4/rpb1"), (7168, 0.25, "fp16", "wpr4/nv4/rpb1"),
     (7168, 0.0, "fp16", "wpr4/nv4/rpb1"), (7168, 0.25, "bf16", "wpr8/nv2/rpb1"),
-    (8192, 2.5, "fp16", "wpr8/nv2/rpb1"), (4096, 1.0, "fp16", "wpr8/nv1/rpb1")])
+    (8192, 2.5, "fp16", "wpr8/nv2/rpb1"), (4096, 1.0, "fp16", "wpr8/nv1/rpb1"),
+    (7168, 1.504, "bf16", "wpr2/nv8/rpb2")])  # 385 rows on 256 CUs: a half-empty last block
 @pytest.mark.parametrize("fp8", [None, "static", "dynamic"])
 def test_fused_rows_near_cu_count_automatic_tiles(orc, hidden, per_cu, dtype, tile, fp8):
     """Fused rows 4097-8192 wide with at most two rows per CU take four-wave
