@@ -52,6 +52,21 @@ int arn_set_gemm_splits(int splits);
  */
 int arn_last_plan(char *buf, size_t len);
 
+/*
+ * arn_norm_plan answers, without any HIP call and without launching, which
+ * kernel arn_norm(args) would launch on a device with `compute_units` CUs:
+ * it runs arn_norm's argument checks and shape choice (the calling thread's
+ * forced tile included) and copies into buf (size len, NUL-terminated,
+ * truncated to fit; 160 bytes always suffice) the description arn_last_plan
+ * would give after that call, with grid = the blocks of its last launch.
+ * The pointers in args are only compared and their alignment read; nothing
+ * is dereferenced.  Returns the status arn_norm would return before
+ * launching (buf is left empty unless ARN_OK with rows > 0); ARN_EINVAL for
+ * compute_units <= 0.  (struct arn_norm_args is declared in arn.h.)
+ */
+struct arn_norm_args;
+int arn_norm_plan(const struct arn_norm_args *args, int compute_units, char *buf, size_t len);
+
 #ifdef __cplusplus
 }
 #endif

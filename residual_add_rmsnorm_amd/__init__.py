@@ -31,7 +31,7 @@ __all__ = [
     "silu_and_mul", "silu_and_mul_fp8",
     "fp8_gemm", "fp8_weight_preshuffle", "PreshuffledWeight", "fp8_gemm_workspace",
     "fp8_gemm_preshuffled_noalloc",
-    "set_tile", "set_gemm_config", "set_gemm_splits", "last_plan", "ArnError",
+    "set_tile", "set_gemm_config", "set_gemm_splits", "last_plan", "norm_plan", "ArnError",
 ]
 
 _DTYPES = {torch.bfloat16: _lib.BF16, torch.float16: _lib.FP16}
@@ -312,6 +312,36 @@ def set_gemm_splits(splits: int = 0) -> None:
     """Force the number of K splits of this thread's later workspace GEMM
     calls (0 = automatic; other threads are not affected)."""
     _lib.check(_lib.load().arn_set_gemm_splits(splits), "arn_set_gemm_splits")
+
+
+def norm_plan(dtype: str, rows: int, hidden: int, *, fused: bool = False, fp8: str | None = None,
+              stride: int | None = None, variance_size: int = 0, weight: bool = True,
+              compute_units: int = 256, align: int = 16) -> str:
+    """The kernel arn_norm would launch for rows of `hidden` elements (row
+    stride `stride`, every base aligned to `align` bytes) on a device with
+    `compute_units` CUs, from arn_norm_plan: nothing is launched and no
+    memory is touched (the pointers passed are stand-in addresses).
+    Returns arn_last_plan's description, "" for rows == 0; raises ArnError
+    for a call arn_norm would refuse."""
+    import ctypes
+
+    if dtype not in ("bf16", "fp16"):
+        raise ValueError("dtype must be 'bf16' or 'fp16'")
+    stride = hidden if stride is None else stride
+    base = 1 << 40  # stand-in device addresses, far apart, `align`-aligned
+    fmt = {None: _lib.OUT_16BIT, "static": _lib.OUT_FP8_STATIC,
+           "dynamic": _lib.OUT_FP8_DYNAMIC}[fp8]
+    args = _lib.NormArgs(
+        struct_size=ctypes.sizeof(_lib.NormArgs), dtype=_lib.BF16 if dtype == "bf16" else _lib.FP16,
+        out_format=fmt, out=base + 4 * align, out_stride=stride,
+        scale=base + (1 << 36) if fp8 else None, x=base + (2 << 36) + align, x_stride=stride,
+        residual=base + (3 << 36) + 2 * align if fused else None, residual_stride=stride,
+        weight=base + (4 << 36) + 3 * align if weight else None, eps=1e-6, rows=rows,
+        hidden=hidden, variance_size=variance_size, stream=None)
+    buf = ctypes.create_string_buffer(160)
+    st = _lib.load().arn_norm_plan(ctypes.byref(args), compute_units, buf, len(buf))
+    _lib.check(st, "arn_norm_plan")
+    return buf.value.decode()
 
 
 def last_plan() -> str:

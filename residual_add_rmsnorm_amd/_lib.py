@@ -67,6 +67,7 @@ SIGNATURES = {
     "arn_set_gemm_config": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "arn_set_gemm_splits": (ctypes.c_int, [ctypes.c_int]),
     "arn_last_plan": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_size_t]),
+    "arn_norm_plan": (ctypes.c_int, [_vp, ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t]),
 }
 
 ABI_VERSION = 6

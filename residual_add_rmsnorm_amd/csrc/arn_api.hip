@@ -254,9 +254,16 @@ const Tile* choose_tile(const TileTable* table, int vec, int64_t nvec, int64_t r
 // Grid limit per launch; larger row counts are split into several launches.
 constexpr int64_t kMaxBlocksPerLaunch = int64_t(1) << 22;
 
-int run(const Request& r) {
+// The launch plan of one norm call: the access width and the tile.  The
+// arguments are checked first; `cus` <= 0 then reads the current device's
+// CU count (the first HIP call), otherwise no HIP call is made.
+struct Plan {
+  int vec = 0;
+  const Tile* tile = nullptr;
+};
+
+int plan_norm(const Request& r, int cus, Plan* out) {
   const bool fp8 = (r.kind & 6) != 0;
-  const bool dynamic = (r.kind & 4) != 0;
 
   // ---- argument checks (no HIP call before they pass) ----
   if (r.dtype != ARN_BF16 && r.dtype != ARN_FP16) return ARN_EINVAL;
@@ -299,7 +306,7 @@ int run(const Request& r) {
   } else if (r.kind == arn::kFusedFp8Dynamic) {
     compact = 2;
   }
-  const int cus = cu_count();
+  if (cus <= 0) cus = cu_count();
   int waves = 0;
   if ((r.kind & arn::kFused) && !r.parts && vec == 8 && nvec > 512 && nvec <= 1024 &&
       r.rows <= 2 * (int64_t)cus) {
@@ -311,6 +318,59 @@ int run(const Request& r) {
   }
   const Tile* tile = choose_tile(table, vec, nvec, r.rows, cus, r.nparts >= 4, compact, waves);
   if (!tile) return ARN_EUNSUPPORTED;
+  out->vec = vec;
+  out->tile = tile;
+  return ARN_OK;
+}
+
+// The blocks of the last launch of a call (calls past the grid limit are
+// split into several launches).
+int64_t last_grid(int64_t rows, const Tile* tile) {
+  const int64_t rows_per_launch = kMaxBlocksPerLaunch * tile->rpb;
+  const int64_t n = rows - (rows - 1) / rows_per_launch * rows_per_launch;
+  return (n + tile->rpb - 1) / tile->rpb;
+}
+
+int describe_plan(const Request& r, const Plan& p, int64_t grid, char* buf, size_t len) {
+  return std::snprintf(buf, len, "%s%s/%s/vec%d/wpr%d/nv%d/rpb%d/grid%lld",
+                       r.parts ? "sum_" : "", kKindNames[r.kind],
+                       r.dtype == ARN_BF16 ? "bf16" : "fp16", p.vec, p.tile->wpr, p.tile->nv,
+                       p.tile->rpb, (long long)grid);
+}
+
+// The request of an arn_norm descriptor (its struct size and output format
+// checked here, the rest by plan_norm).
+int norm_request(const arn_norm_args* p, Request* r) {
+  if (!p || p->struct_size < sizeof(arn_norm_args)) return ARN_EINVAL;
+  int kind;
+  switch (p->out_format) {
+    case ARN_OUT_16BIT:
+      kind = arn::kPlain;
+      break;
+    case ARN_OUT_FP8_STATIC:
+      kind = arn::kPlainFp8Static;
+      break;
+    case ARN_OUT_FP8_DYNAMIC:
+      kind = arn::kPlainFp8Dynamic;
+      break;
+    default:
+      return ARN_EINVAL;
+  }
+  if (p->residual) kind |= arn::kFused;
+  *r = Request{kind,        p->dtype,           p->out,    p->out_stride,
+               p->x,        p->x_stride,        p->residual, p->residual_stride,
+               p->weight,   kind & 6 ? p->scale : nullptr, p->eps, p->rows,
+               p->hidden,   p->stream,          p->variance_size};
+  return ARN_OK;
+}
+
+int run(const Request& r) {
+  const bool fp8 = (r.kind & 6) != 0;
+  const bool dynamic = (r.kind & 4) != 0;
+  Plan p;
+  const int st = plan_norm(r, 0, &p);
+  if (st != ARN_OK || r.rows == 0) return st;
+  const Tile* tile = p.tile;
 
   const int esize_out = fp8 ? 1 : 2;
   const int64_t rows_per_launch = kMaxBlocksPerLaunch * tile->rpb;
@@ -346,11 +406,7 @@ int run(const Request& r) {
     done += n;
   }
 
-  g_last_plan_len = std::snprintf(g_last_plan, sizeof(g_last_plan),
-                                  "%s%s/%s/vec%d/wpr%d/nv%d/rpb%d/grid%lld",
-                                  r.parts ? "sum_" : "", kKindNames[r.kind],
-                                  r.dtype == ARN_BF16 ? "bf16" : "fp16", vec, tile->wpr, tile->nv,
-                                  tile->rpb, (long long)grid);
+  g_last_plan_len = describe_plan(r, p, grid, g_last_plan, sizeof(g_last_plan));
   return ARN_OK;
 }
 
@@ -828,26 +884,22 @@ int arn_fused_add_rmsnorm_fp8(uint8_t* out, int64_t out_stride, float* scale, in
 }
 
 int arn_norm(const arn_norm_args* p) {
-  if (!p || p->struct_size < sizeof(arn_norm_args)) return ARN_EINVAL;
-  int kind;
-  switch (p->out_format) {
-    case ARN_OUT_16BIT:
-      kind = arn::kPlain;
-      break;
-    case ARN_OUT_FP8_STATIC:
-      kind = arn::kPlainFp8Static;
-      break;
-    case ARN_OUT_FP8_DYNAMIC:
-      kind = arn::kPlainFp8Dynamic;
-      break;
-    default:
-      return ARN_EINVAL;
-  }
-  if (p->residual) kind |= arn::kFused;
-  Request r{kind,      p->dtype,  p->out,    p->out_stride, p->x,      p->x_stride,
-            p->residual, p->residual_stride, p->weight, kind & 6 ? p->scale : nullptr, p->eps,
-            p->rows,   p->hidden, p->stream, p->variance_size};
-  return run(r);
+  Request r{};
+  const int st = norm_request(p, &r);
+  return st != ARN_OK ? st : run(r);
+}
+
+int arn_norm_plan(const arn_norm_args* p, int compute_units, char* buf, size_t len) {
+  if (buf && len > 0) buf[0] = '\0';
+  if (compute_units <= 0) return ARN_EINVAL;
+  Request r{};
+  int st = norm_request(p, &r);
+  if (st != ARN_OK) return st;
+  Plan pl;
+  st = plan_norm(r, compute_units, &pl);
+  if (st != ARN_OK || r.rows == 0) return st;
+  if (buf && len > 0) describe_plan(r, pl, last_grid(r.rows, pl.tile), buf, len);
+  return ARN_OK;
 }
 
 int arn_sum_add_rmsnorm(const arn_sum_norm_args* p) {

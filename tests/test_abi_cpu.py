@@ -37,8 +37,8 @@ def test_header_declares_the_bound_functions():
     assert sorted(product + tuning) == sorted(_lib.SIGNATURES)
     # the product header declares nothing that sets state
     assert not any(n.startswith("arn_set_") for n in product)
-    assert tuning == ["arn_last_plan", "arn_set_gemm_config", "arn_set_gemm_splits",
-                      "arn_set_tile"]
+    assert tuning == ["arn_last_plan", "arn_norm_plan", "arn_set_gemm_config",
+                      "arn_set_gemm_splits", "arn_set_tile"]
 
 
 def test_library_exports_every_declared_function(lib):

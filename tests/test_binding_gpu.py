@@ -131,3 +131,23 @@ def test_torch_ops_refusals_and_status():
                                                               device="cuda"), 16, 256, s1)
     torch.cuda.synchronize()
     assert c.shape == (1, 16) and c.dtype == torch.bfloat16 and bool((c == 0).all())
+
+
+@pytest.mark.parametrize("dtype,rows,hidden,fused,fp8", [
+    ("fp16", 1, 16384, True, "static"), ("bf16", 256, 8192, True, None),
+    ("fp16", 384, 7168, True, "dynamic"), ("fp16", 100, 5120, True, None),
+    ("bf16", 1030, 1024, False, "dynamic"), ("bf16", 64, 4096, False, None),
+    ("bf16", 4100, 3840, True, None)])
+def test_plan_query_matches_the_launch(dtype, rows, hidden, fused, fp8):
+    """arn_norm_plan, given this device's CU count, names the kernel the
+    call then launches (arn_last_plan)."""
+    td = torch.bfloat16 if dtype == "bf16" else torch.float16
+    x = torch.randn(rows, hidden, device="cuda").to(td)
+    res = torch.randn(rows, hidden, device="cuda").to(td) if fused else None
+    w = torch.ones(hidden, device="cuda", dtype=td)
+    s = torch.full((1,), 0.05, device="cuda")
+    arn.norm(x, w, 1e-6, residual=res, fp8=fp8, scale=s)
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert arn.last_plan() == arn.norm_plan(dtype, rows, hidden, fused=fused, fp8=fp8,
+                                            compute_units=cus)
