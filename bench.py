@@ -567,11 +567,13 @@ def measure_workload(name: str, steps: int, warmup: int, ceilings: dict | None,
 
 
 def bench_workload(name: str, steps: int, warmup: int, with_cpu: bool,
-                   with_ceiling: bool = True, others: tuple = ()) -> dict:
+                   with_ceiling: bool = True, others: tuple = (),
+                   head_min_warm_ms: float = 0.0) -> dict:
     """The JSON line of one workload (`name`), optionally with entries for
-    `others` under config.per_workload."""
+    `others` under config.per_workload; `head_min_warm_ms` warms `name`
+    for at least that long after its `warmup` calls."""
     ceilings = {} if with_ceiling else None
-    head = measure_workload(name, steps, warmup, ceilings)
+    head = measure_workload(name, steps, warmup, ceilings, head_min_warm_ms)
     per = {}
     for other in others:
         per[other] = measure_workload(other, steps, warmup, ceilings, OTHER_MIN_WARM_MS)
@@ -786,10 +788,14 @@ def main() -> int:
             copy_calibration()
         return 0
     names = list(workloads.WORKLOADS) if args.workload == "all" else [args.workload]
+    # one line per workload: each is warmed like the default run's
+    # non-headline configurations (a single named workload takes exactly the
+    # requested warm-up calls, as the profiled commands assume)
+    warm_ms = OTHER_MIN_WARM_MS if args.workload == "all" else 0.0
     for n in names:
         line = bench_workload(n, args.steps, args.warmup,
                               with_cpu=not args.no_cpu_baseline and n == names[0],
-                              with_ceiling=not args.no_ceiling)
+                              with_ceiling=not args.no_ceiling, head_min_warm_ms=warm_ms)
         print(json.dumps(line), flush=True)
     if args.calibrate_copy:
         copy_calibration()
