@@ -132,3 +132,43 @@ def test_tp_block_tail(orc, compiled):
     ref = orc.sum_add_rmsnorm("bf16", ph, r, w, 1e-6, fp8_mode=O.FP8_DYNAMIC)
     assert np.array_equal(bits(rd), ref["r16"])
     assert_codes_close(codes(q), ref["q"])
+
+
+def test_decode_mlp_captured_in_a_graph():
+    """The decode MLP through torch.ops (outputs allocated inside each op)
+    captured in one CUDA graph: every replay, with eager work between the
+    replays, equals the eager chain on the same inputs."""
+    rng = np.random.default_rng(73)
+    rows, hidden, inter = 8, 1024, 1536
+    x = dev(W.to_bits(rng.standard_normal((rows, hidden)).astype(np.float32), "bf16"), "bf16")
+    r0 = dev(W.to_bits(rng.standard_normal((rows, hidden)).astype(np.float32), "bf16"), "bf16")
+    w = dev(W.to_bits((1 + 0.1 * rng.standard_normal(hidden)).astype(np.float32), "bf16"), "bf16")
+    w1 = torch.ops.arn.fp8_weight_preshuffle(
+        torch.from_numpy(W.e4m3_codes(rng.standard_normal((2 * inter, hidden)) * 4)).cuda())
+    w2 = torch.ops.arn.fp8_weight_preshuffle(
+        torch.from_numpy(W.e4m3_codes(rng.standard_normal((hidden, inter)) * 4)).cuda())
+    s1 = torch.full((2 * inter,), 0.01, device="cuda")
+    s2 = torch.full((hidden,), 0.01, device="cuda")
+
+    r_eager = r0.clone()
+    want = decode_mlp(x, r_eager, w, w1, s1, w2, s2, 2 * inter, hidden)
+    torch.cuda.synchronize()
+
+    r_graph = r0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the allocator outside the capture
+        decode_mlp(x, r0.clone(), w, w1, s1, w2, s2, 2 * inter, hidden)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = decode_mlp(x, r_graph, w, w1, s1, w2, s2, 2 * inter, hidden)
+    for rep in range(4):
+        r_graph.copy_(r0)  # each replay starts from the same residual
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), rep
+        assert torch.equal(r_graph, r_eager), rep
+        torch.ops.arn.rmsnorm(x, w, 1e-6)  # eager work between replays
+        torch.cuda.synchronize()
