@@ -1,7 +1,8 @@
 /*
  * abi_driver.c -- drives the host side of libarn's C ABI (argument checks,
- * status strings, size queries, tuning knobs, the plan buffer) along the
- * paths that return before any HIP call: refused arguments and empty calls.
+ * status strings, size queries, tuning knobs, the plan buffer, the plan
+ * query) along the paths that return before any HIP call: refused
+ * arguments, empty calls and plan queries.
  * tests/sanitize/build.py links it with the library's objects, the host
  * code of arn_api.hip built under AddressSanitizer and
  * UndefinedBehaviorSanitizer, so an out-of-bounds access or undefined
@@ -163,6 +164,43 @@ int main(void) {
   EXPECT_EQ(arn_last_plan(buf, 1), len, "plan into one byte");
   EXPECT_EQ(buf[0], 0, "one-byte plan is empty");
   EXPECT_EQ(arn_last_plan(NULL, 0), len, "plan length only");
+
+  /* the plan query: a decode batch of fused rows, its buffer at every
+     length, and its refusals (distinct stand-ins, so no aliasing refusal) */
+  arn_norm_args q;
+  memset(&q, 0, sizeof(q));
+  q.struct_size = sizeof(q);
+  q.dtype = ARN_BF16;
+  q.out_format = ARN_OUT_16BIT;
+  q.out = (void *)(uintptr_t)0x1000000;
+  q.x = (const void *)(uintptr_t)0x2000000;
+  q.residual = (void *)(uintptr_t)0x3000000;
+  q.weight = (const void *)(uintptr_t)0x4000000;
+  q.out_stride = q.x_stride = q.residual_stride = 8192;
+  q.eps = 1e-6f;
+  q.rows = 256;
+  q.hidden = 8192;
+  char pbuf[160];
+  EXPECT_EQ(arn_norm_plan(&q, 256, pbuf, sizeof(pbuf)), ARN_OK, "plan query");
+  EXPECT_EQ(strcmp(pbuf, "fused_add/bf16/vec8/wpr4/nv4/rpb1/grid256"), 0, "plan of 256 rows");
+  char small[4];
+  EXPECT_EQ(arn_norm_plan(&q, 256, small, sizeof(small)), ARN_OK, "plan query, short buffer");
+  EXPECT_EQ(strlen(small), 3, "short plan truncated and NUL-terminated");
+  EXPECT_EQ(arn_norm_plan(&q, 256, NULL, 0), ARN_OK, "plan query, no buffer");
+  EXPECT_EQ(arn_norm_plan(&q, 0, pbuf, sizeof(pbuf)), ARN_EINVAL, "no compute units");
+  EXPECT_EQ(pbuf[0], 0, "refused plan leaves the buffer empty");
+  q.rows = 0;
+  EXPECT_EQ(arn_norm_plan(&q, 256, pbuf, sizeof(pbuf)), ARN_OK, "plan of no rows");
+  EXPECT_EQ(pbuf[0], 0, "no rows, no plan");
+  q.rows = 4;
+  q.hidden = 65537;
+  q.out_stride = q.x_stride = q.residual_stride = 65537;
+  EXPECT_EQ(arn_norm_plan(&q, 256, pbuf, sizeof(pbuf)), ARN_EUNSUPPORTED, "row too long");
+  q.residual = (void *)q.x;
+  EXPECT_EQ(arn_norm_plan(&q, 256, pbuf, sizeof(pbuf)), ARN_EINVAL, "residual aliases x");
+  q.struct_size = 8;
+  EXPECT_EQ(arn_norm_plan(&q, 256, pbuf, sizeof(pbuf)), ARN_EINVAL, "descriptor too small");
+  EXPECT_EQ(arn_norm_plan(NULL, 256, pbuf, sizeof(pbuf)), ARN_EINVAL, "no descriptor");
 
   if (failures) {
     fprintf(stderr, "%d check(s) failed\n", failures);
